@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA chunkwise forward pass on one MI355X.
+
+One step = one full forward pass (chunk table, decay cumsum, WY/UT transform,
+state propagation, output) over the headline workload: bf16 inputs, fp32
+state, B=1, H=32, T=65536, d_k=d_v=128, chunk 64, S0 ~ 0.02 N(0,1).  Inputs,
+outputs and workspace are resident in HBM before the timed region.
+
+Prints one JSON line.  Besides tokens/s it reports the MFMA-roofline fraction
+of the whole pass, a per-kernel roofline for the kernel that takes the most
+time (its duration measured with HIP events on the stream the kernels run
+on), and the fp64 CPU oracle timed on a bounded sample of the same inputs.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA chunked-fwd tokens/s and MFMA TFLOP/s (% of peak), H=32 d=128 T=64K"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E
+
+
+def flop_per_token_head(C, dk, dv):
+    """Algorithmic FLOP of the chunked pass per (token, head), exact triangles."""
+    return 6 * dk * dv + (3 * C - 1) * dk + 2 * C * dv + C * C / 3.0
+
+
+def min_bytes_per_token_head(dk, dv, es=2):
+    """Minimum HBM bytes per (token, head): read q, k, log_alpha, v, beta; write o."""
+    return es * (3 * dk + dv + 1) + es * dv
+
+
+def kernel_bytes_per_token_head(name, C, D, es=2):
+    """Algorithmic bytes each kernel of this design moves per (token, head):
+    its inputs read once and its outputs written once."""
+    per_chunk_state = es * D * D / C          # one D x D state per chunk
+    return {
+        "k_cumsum": es * D + 4 * D,                                   # g -> b (fp32)
+        "k_wy": (3 * es * D + es + 4 * D) + (3 * es * D + 4 * D / C),  # k, v, beta, b -> W, U, K^, Gamma_L
+        "k_state": (3 * es * D + 4 * D / C) + (per_chunk_state + es * D),  # W, U, K^, Gamma_L -> S chunks, U~
+        "k_output": (2 * es * D + 4 * D + per_chunk_state + es * D) + es * D,  # q, k, b, S, U~ -> o
+        "k_chunk_table": 0.0,
+    }[name]
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for f in ("kda_kernels.hip", "kda_device.h"):
+        with open(os.path.join(ROOT, "gated_delta_rule_30_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel, workload_key):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    ent = rec.get(kernel + "|" + workload_key)
+    if not ent or ent.get("source_sha") != source_sha():
+        return None
+    return ent["bytes_per_launch"]
+
+
+def cpu_baseline(inp, n_heads_sample):
+    import numpy as np
+    import oracle
+    H = inp.spec.n_heads
+    heads = list(range(n_heads_sample))
+    sl = lambda t: t[:, heads].float().cpu().numpy()
+    q, k, v, g, beta = sl(inp.q), sl(inp.k), sl(inp.v), sl(inp.g), sl(inp.beta)
+    S0 = None if inp.S0 is None else inp.S0[:, heads].cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.forward(q, k, v, beta, g, S0, inp.cu_seqlens, want_state=True)
+    dt = time.perf_counter() - t0
+    tokens_equiv = inp.spec.total_tokens * n_heads_sample / H
+    return {"value": tokens_equiv / dt, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": "fp64 recurrence on %d of %d heads x all %d tokens of the same inputs (%.1f s); "
+                      "tokens/s counts a token once all %d heads are done"
+                      % (n_heads_sample, H, inp.spec.total_tokens, dt, H),
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2 = headline)")
+    ap.add_argument("--profile-reps", type=int, default=10)
+    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (heads and sequences shard "
+              "with no exchange; see the sharding notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_30_amd as kda
+    import kda_inputs as ki
+
+    dev = torch.device("cuda:0")
+    spec = ki.headline_configs()[args.config]
+    inp = ki.generate_torch(spec, dev)
+    T, H, dk, dv, C = spec.total_tokens, spec.n_heads, spec.d_k, spec.d_v, spec.chunk
+    dt_code = kda.KDA_BF16 if spec.dtype == "bf16" else kda.KDA_F32
+    ws = torch.empty(kda.workspace_size(T, spec.n_seqs, H, dk, dv, C, dt_code), dtype=torch.uint8, device=dev)
+    o = torch.empty((T, H, dv), dtype=inp.q.dtype, device=dev)
+    ST = torch.empty((spec.n_seqs, H, dk, dv), dtype=torch.float32, device=dev)
+    cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev) if spec.varlen else None
+
+    def step():
+        kda.chunk_fwd(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, cu_seqlens=cu, n_seqs=spec.n_seqs,
+                      o=o, S_T=ST, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations: HIP events recorded between launches on the same stream
+    stage_ms = {}
+    for _ in range(args.profile_reps):
+        _, _, d = kda.chunk_fwd_profile(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, cu_seqlens=cu,
+                                        n_seqs=spec.n_seqs, o=o, S_T=ST, workspace=ws)
+        for k_, v_ in d.items():
+            stage_ms[k_] = stage_ms.get(k_, 0.0) + v_ / args.profile_reps
+    dom = max(stage_ms, key=stage_ms.get)
+
+    token_heads = T * H
+    F = flop_per_token_head(C, dk, dv)
+    tflops = token_heads * F / (ms * 1e-3) / 1e12
+    tokens_s = T / (ms * 1e-3)
+    pass_bytes = token_heads * min_bytes_per_token_head(dk, dv, 2 if spec.dtype == "bf16" else 4)
+    workload = ("KDA chunked forward, %s inputs / fp32 state, N=%d H=%d T_total=%d d_k=d_v=%d, chunk %d "
+                "(16-token sub-tiles), %s" % (spec.dtype, spec.n_seqs, H, T, dk, C,
+                                              "S0 ~ 0.02 N(0,1)" if spec.s0_std else "zero S0"))
+    wkey = "%s_N%d_H%d_T%d_d%d" % (spec.dtype, spec.n_seqs, H, T, dk)
+    kb = kernel_bytes_per_token_head(dom, C, dk, 2 if spec.dtype == "bf16" else 4) * token_heads
+    roof = {"bound": "hbm", "kernel": dom, "achieved": kb / (stage_ms[dom] * 1e-3) / 1e9,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for(dom, wkey)
+    roof["kernel_ms"] = stage_ms[dom]
+    roof["algorithmic_bytes_per_launch"] = kb
+
+    out = {
+        "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": spec.dtype, "data": "synthetic",
+        "config": {"workload": workload, "global_batch": spec.n_seqs, "seq_len": T // spec.n_seqs, "heads": H,
+                   "d_k": dk, "d_v": dv, "chunk": C, "parallelism": "single GPU"},
+        "tflops": tflops, "mfma_peak_tflops": PEAK_BF16_TFLOPS, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
+        "flop_per_token_head": F,
+        "pass_hbm_gbs_algorithmic": pass_bytes / (ms * 1e-3) / 1e9,
+        "pass_hbm_frac": pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+        "stage_ms": stage_ms, "roofline": roof, "wall_s_timed": wall,
+        "device": torch.cuda.get_device_name(dev), "source_sha": source_sha(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_heads, H))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

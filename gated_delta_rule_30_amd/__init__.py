@@ -1,0 +1,163 @@
+"""MI355X-native chunkwise KDA forward -- thin Python binding over libkda.so.
+
+Every step of the forward pass runs in the HIP kernels of `libkda.so`; this
+module only checks tensors, allocates outputs and workspace with torch, and
+passes raw pointers and the current HIP stream through the C ABI declared in
+include/kda.h.  There is no CPU or PyTorch fallback: if the library is
+missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["chunk_fwd", "chunk_fwd_profile", "stage_names", "workspace_size", "status_string", "lib_path",
+           "KDA_F32", "KDA_BF16", "KdaError"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libkda.so")
+_lib = None
+
+KDA_F32, KDA_BF16 = 0, 1
+CHUNK = 64
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError("libkda.so is not built (%s); run gated_delta_rule_30_amd/build.py "
+                               "or __graft_entry__.build()" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        lib.kda_chunk_fwd_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, ctypes.c_int]
+        lib.kda_chunk_fwd_workspace_size.restype = SZ
+        lib.kda_chunk_fwd.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, I32,
+                                      P, P, P, P, P, P, P, P, P, P, SZ, P]
+        lib.kda_chunk_fwd.restype = ctypes.c_int
+        lib.kda_status_string.argtypes = [ctypes.c_int]
+        lib.kda_status_string.restype = ctypes.c_char_p
+        lib.kda_version.restype = ctypes.c_char_p
+        lib.kda_chunk_fwd_profile.argtypes = lib.kda_chunk_fwd.argtypes + [P]
+        lib.kda_chunk_fwd_profile.restype = ctypes.c_int
+        lib.kda_profile_num_stages.restype = ctypes.c_int32
+        lib.kda_profile_stage_name.argtypes = [ctypes.c_int32]
+        lib.kda_profile_stage_name.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return _load().kda_status_string(int(code)).decode()
+
+
+def workspace_size(total_tokens: int, n_seqs: int, n_heads: int, d_k: int, d_v: int,
+                   chunk: int = CHUNK, dtype_code: int = KDA_BF16) -> int:
+    return int(_load().kda_chunk_fwd_workspace_size(int(total_tokens), int(n_seqs), int(n_heads), int(d_k),
+                                                    int(d_v), int(chunk), int(dtype_code)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def stage_names():
+    lib = _load()
+    return [lib.kda_profile_stage_name(i).decode() for i in range(lib.kda_profile_num_stages())]
+
+
+def chunk_fwd_profile(*args, **kw):
+    """Same as chunk_fwd, but through the measurement entry point: blocks until
+    done and returns (o, S_T, {kernel name: milliseconds})."""
+    ms = (ctypes.c_float * _load().kda_profile_num_stages())()
+    o, ST = chunk_fwd(*args, _stage_ms=ms, **kw)
+    return o, ST, dict(zip(stage_names(), [float(x) for x in ms]))
+
+
+def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = CHUNK,
+              output_final_state: bool = True, o=None, S_T=None, workspace=None, n_seqs=None, _stage_ms=None):
+    """KDA chunkwise forward on the GPU.
+
+    q, k, log_alpha: [T_total, H, d_k] or [B, T, H, d_k]; v: [..., H, d_v];
+    beta: [..., H] -- all float32 or all bfloat16, contiguous, on one GPU.
+    S0: [N, H, d_k, d_v] float32 or None.  cu_seqlens: int32 device tensor
+    [N+1] (packed variable-length batch) or None (B equal sequences for 4-D
+    inputs, one sequence for 3-D inputs; `n_seqs` overrides).  Optional
+    preallocated `o`, `S_T` and `workspace` (uint8) tensors are used as given.
+    Returns (o, S_T) with o shaped like v and S_T None unless requested.
+    """
+    import torch
+    lib = _load()
+    dt = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}.get(q.dtype)
+    if dt is None:
+        raise TypeError("q must be float32 or bfloat16, got %s" % q.dtype)
+    for name, t in (("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    batched = q.dim() == 4
+    if batched:
+        B = q.shape[0]
+        q, k, v, log_alpha = (t.reshape(-1, *t.shape[2:]) for t in (q, k, v, log_alpha))
+        beta = beta.reshape(-1, beta.shape[-1])
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (T, H, dk) or log_alpha.shape != (T, H, dk) or v.shape != (T, H, dv) or beta.shape != (T, H):
+        raise ValueError("inconsistent shapes q%s k%s v%s beta%s log_alpha%s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(beta.shape),
+                            tuple(log_alpha.shape)))
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on %s" % (name, dev))
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor on %s" % dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = n_seqs if n_seqs is not None else (B if batched else 1)
+    if S0 is not None:
+        if S0.dtype != torch.float32 or S0.shape != (N, H, dk, dv) or S0.device != dev or not S0.is_contiguous():
+            raise ValueError("S0 must be contiguous float32 [%d, %d, %d, %d] on %s" % (N, H, dk, dv, dev))
+    ws_bytes = int(lib.kda_chunk_fwd_workspace_size(T, N, H, dk, dv, chunk, dt))
+    if ws_bytes == 0:
+        code = lib.kda_chunk_fwd(dt, T, N, H, dk, dv, chunk, None, None, None, None, None, None, None,
+                                 None, None, None, 0, None)
+        raise KdaError(code, lib.kda_status_string(code).decode())
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif workspace.device != dev or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on %s" % dev)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    elif o.shape != (T, H, dv) or o.dtype != q.dtype or o.device != dev or not o.is_contiguous():
+        raise ValueError("o must be contiguous %s [%d, %d, %d] on %s" % (q.dtype, T, H, dv, dev))
+    if output_final_state and S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif S_T is not None and (S_T.shape != (N, H, dk, dv) or S_T.dtype != torch.float32 or S_T.device != dev
+                              or not S_T.is_contiguous()):
+        raise ValueError("S_T must be contiguous float32 [%d, %d, %d, %d] on %s" % (N, H, dk, dv, dev))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = (dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+            _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    if _stage_ms is None:
+        code = lib.kda_chunk_fwd(*args)
+    else:
+        code = lib.kda_chunk_fwd_profile(*args, _stage_ms)
+    if code != 0:
+        raise KdaError(code, lib.kda_status_string(code).decode())
+    if batched:
+        o = o.reshape(B, -1, H, dv)
+    return o, (S_T if output_final_state else None)

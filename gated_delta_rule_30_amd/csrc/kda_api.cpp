@@ -1,0 +1,156 @@
+// C ABI of the KDA chunkwise forward library: argument validation, workspace
+// carve-up and the launch sequence on the caller's stream.  No device code.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kda_internal.h"
+
+namespace kda {
+
+static constexpr int64_t kChunkTokens = 64;
+static constexpr size_t kAlign = 256;
+
+static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+size_t carve_workspace(Plan* p, void* base) {
+    const size_t es = p->bf16 ? 2 : 4;
+    const size_t T = (size_t)p->total_tokens, H = (size_t)p->n_heads, D = (size_t)p->d;
+    const size_t mc = (size_t)p->max_chunks;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return base ? (void*)((char*)base + at) : nullptr;
+    };
+    p->ws_n_chunks = (int32_t*)take(sizeof(int32_t));
+    p->ws_seq_chunk0 = (int32_t*)take(sizeof(int32_t) * ((size_t)p->n_seqs + 1));
+    p->ws_tab = (ChunkInfo*)take(sizeof(ChunkInfo) * mc);
+    p->ws_b = (float*)take(4 * T * H * D);
+    p->ws_W = take(es * T * H * D);
+    p->ws_U = take(es * T * H * D);
+    p->ws_Kh = take(es * T * H * D);
+    p->ws_gam = (float*)take(4 * mc * H * D);
+    p->ws_Ut = take(es * mc * H * D * kChunkTokens);
+    p->ws_Sc = take(es * mc * H * D * D);
+    return off;
+}
+
+}  // namespace kda
+
+using kda::Plan;
+
+static kda_status plan_sizes(Plan* p, kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                             int32_t d_k, int32_t d_v, int32_t chunk, bool varlen) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (total_tokens < 0 || n_seqs < 1 || n_heads < 1 || d_k < 1 || d_v < 1 || chunk < 1) return KDA_ERR_SHAPE;
+    if (!varlen && total_tokens % n_seqs != 0) return KDA_ERR_SHAPE;
+    if (d_k != d_v || (d_k != 64 && d_k != 128) || chunk != kda::kChunkTokens) return KDA_ERR_UNSUPPORTED;
+    if (dt == KDA_F32 && d_k != 64) return KDA_ERR_UNSUPPORTED;
+    if (total_tokens >= ((int64_t)1 << 31) || n_heads > 65535) return KDA_ERR_UNSUPPORTED;
+    const int64_t max_chunks = total_tokens / kda::kChunkTokens + n_seqs;
+    if (max_chunks >= ((int64_t)1 << 31) || (int64_t)n_seqs * n_heads * (d_v / 32) >= ((int64_t)1 << 31))
+        return KDA_ERR_UNSUPPORTED;
+    p->bf16 = dt == KDA_BF16;
+    p->d = d_k;
+    p->total_tokens = total_tokens;
+    p->n_seqs = n_seqs;
+    p->n_heads = n_heads;
+    p->fixed_len = varlen ? 0 : total_tokens / n_seqs;
+    p->max_chunks = (int32_t)max_chunks;
+    return KDA_OK;
+}
+
+extern "C" {
+
+size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                                    int32_t d_v, int32_t chunk, kda_dtype dt) {
+    Plan p{};
+    // Size for the variable-length case: it never needs less than equal lengths.
+    if (plan_sizes(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, true) != KDA_OK) return 0;
+    return kda::carve_workspace(&p, nullptr);
+}
+
+static kda_status prepare(Plan* p, kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                          int32_t d_k, int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
+                          const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
+                          void* o, float* S_T, void* workspace, size_t workspace_bytes) {
+    kda_status s = plan_sizes(p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, cu_seqlens != nullptr);
+    if (s != KDA_OK) return s;
+    if (total_tokens > 0 && (!q || !k || !v || !beta || !log_alpha || !o)) return KDA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, beta, log_alpha, S0, cu_seqlens, o, S_T};
+    for (const void* ptr : ptrs)
+        if (ptr && ((uintptr_t)ptr % 16) != 0) return KDA_ERR_SHAPE;
+    if (!workspace) return KDA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace % kda::kAlign != 0) return KDA_ERR_WORKSPACE;
+    Plan sz = *p;
+    if (workspace_bytes < kda::carve_workspace(&sz, nullptr)) return KDA_ERR_WORKSPACE;
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->beta = beta;
+    p->g = log_alpha;
+    p->S0 = S0;
+    p->cu_seqlens = cu_seqlens;
+    p->o = o;
+    p->S_T = S_T;
+    kda::carve_workspace(p, workspace);
+    return KDA_OK;
+}
+
+kda_status kda_chunk_fwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                         int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
+                         const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
+                         void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p{};
+    kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
+                           cu_seqlens, o, S_T, workspace, workspace_bytes);
+    if (s != KDA_OK) return s;
+    hipError_t e = kda::launch(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int32_t kda_profile_num_stages(void) { return kda::kNumStages; }
+
+const char* kda_profile_stage_name(int32_t i) {
+    return (i >= 0 && i < kda::kNumStages) ? kda::kStageNames[i] : nullptr;
+}
+
+kda_status kda_chunk_fwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                                 int32_t d_k, int32_t d_v, int32_t chunk, const void* q, const void* k,
+                                 const void* v, const void* beta, const void* log_alpha, const float* S0,
+                                 const int32_t* cu_seqlens, void* o, float* S_T, void* workspace,
+                                 size_t workspace_bytes, void* stream, float* stage_ms) {
+    if (!stage_ms) return KDA_ERR_NULL;
+    Plan p{};
+    kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
+                           cu_seqlens, o, S_T, workspace, workspace_bytes);
+    if (s != KDA_OK) return s;
+    hipEvent_t ev[kda::kNumStages + 1];
+    int made = 0;
+    hipError_t e = hipSuccess;
+    for (; made <= kda::kNumStages && e == hipSuccess; ++made) e = hipEventCreate(&ev[made]);
+    if (e != hipSuccess) made -= 1;
+    if (e == hipSuccess) e = kda::launch(p, static_cast<hipStream_t>(stream), ev);
+    if (e == hipSuccess) e = hipEventSynchronize(ev[kda::kNumStages]);
+    for (int i = 0; e == hipSuccess && i < kda::kNumStages; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    for (int i = 0; i < made; ++i) hipEventDestroy(ev[i]);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK: success";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL: a required pointer is NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE: inconsistent sizes or misaligned tensor";
+        case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE: unknown dtype";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: sizes not supported by this build";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP: kernel launch failed";
+    }
+    return "KDA: unknown status";
+}
+
+const char* kda_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal launch plan shared by the C ABI (kda_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct ChunkInfo {
+    int64_t tok0;   // first packed token of the chunk
+    int32_t seq;    // sequence index
+    int32_t len;    // valid tokens in the chunk, 1..64
+};
+
+struct Plan {
+    bool bf16;
+    int d;                    // d_k == d_v
+    int64_t total_tokens;
+    int32_t n_seqs, n_heads;
+    int64_t fixed_len;        // tokens per sequence when cu_seqlens is NULL
+    int32_t max_chunks;       // upper bound on the number of chunks
+    const void *q, *k, *v, *beta, *g;
+    const float* S0;
+    const int32_t* cu_seqlens;
+    void* o;
+    float* S_T;
+    // workspace carve-up
+    int32_t* ws_n_chunks;
+    int32_t* ws_seq_chunk0;
+    ChunkInfo* ws_tab;
+    float* ws_b;              // [T, H, D] cumulative log-decay
+    void *ws_W, *ws_U, *ws_Kh;  // [T, H, D] operand dtype
+    float* ws_gam;            // [max_chunks, H, D]
+    void* ws_Ut;              // [max_chunks, H, D(col), 64(token)]
+    void* ws_Sc;              // [max_chunks, H, D(col), D(channel)]
+};
+
+// Byte offsets of every workspace region for the given sizes; returns the
+// total size.  `base` may be NULL (size query only).
+size_t carve_workspace(Plan* p, void* base);
+
+// Kernel launches of one forward pass, in order.
+constexpr int kNumStages = 5;
+extern const char* const kStageNames[kNumStages];
+
+// Enqueues the forward pass on `stream`.  If `ev` is non-NULL it must hold
+// kNumStages + 1 events; ev[i] is recorded before stage i and
+// ev[kNumStages] after the last.
+hipError_t launch(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
+
+}  // namespace kda

@@ -1,0 +1,126 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) chunkwise-parallel KDA forward pass.
+ *
+ * Kimi Delta Attention (KDA) is a gated delta-rule recurrence with a
+ * per-channel decay.  Per sequence and head, with state S (d_k x d_v):
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t                         alpha_t = exp(log_alpha_t)
+ *
+ * (ogis-ri NLP primer on Kimi K3, §3.1 "KDA（Kimi Delta Attention）": state and
+ * operand shapes, the decay / probe / delta / write decomposition, and the
+ * read-out).  The library evaluates it chunk by chunk (same page, §3.1, the
+ * chunkwise form and "chunk 内の減衰と、その数値範囲"), relying on the bounded
+ * log-decay log_alpha >= -5 so that every 16-token diagonal sub-tile is an
+ * ordinary dense matrix product (orkas.ai "Kimi K3 architecture",
+ * §"GPU のコードパスを一本消した「下界」").
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers on the current HIP device,
+ *     contiguous, token-major with heads interleaved:
+ *         q, k, log_alpha : [total_tokens, n_heads, d_k]   (dtype dt)
+ *         v, o            : [total_tokens, n_heads, d_v]   (dtype dt)
+ *         beta            : [total_tokens, n_heads]        (dtype dt)
+ *         S0, S_T         : [n_seqs, n_heads, d_k, d_v]    (float32, row = key channel)
+ *         cu_seqlens      : [n_seqs + 1] int32, cu[0] = 0, nondecreasing,
+ *                           cu[n_seqs] = total_tokens (packed variable-length
+ *                           batch); NULL = n_seqs equal lengths.
+ *     Each sequence starts from its own S0[n] (zeros if S0 == NULL); there is
+ *     no leakage across sequences.  o has the input dtype (rounded to nearest
+ *     even for bf16); S_T is float32.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     never allocates, frees or synchronises; work is enqueued on `stream`
+ *     and the call returns once it is queued.  There is no global mutable
+ *     state; concurrent calls on different workspaces are safe.
+ *   - Argument errors are detected on the host before anything is enqueued;
+ *     on error nothing is written.  Value ranges are not checked: log_alpha
+ *     must lie in [-5, 0] and beta in [0, 1] for the documented accuracy
+ *     (values outside give finite but unspecified results, never a memory
+ *     access outside the buffers described here).  Device-side cu_seqlens
+ *     that break the rules above give unspecified results but every access
+ *     stays inside the buffers.
+ *   - Supported: dt == KDA_BF16 with d_k == d_v in {64, 128}, or
+ *     dt == KDA_F32 with d_k == d_v == 64; chunk == 64; total_tokens < 2^31;
+ *     n_heads <= 65535.  Anything else returns KDA_ERR_UNSUPPORTED.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,          /* a required pointer is NULL */
+    KDA_ERR_SHAPE = 2,         /* inconsistent sizes (e.g. total_tokens not divisible by n_seqs) */
+    KDA_ERR_DTYPE = 3,         /* unknown dtype code */
+    KDA_ERR_UNSUPPORTED = 4,   /* valid but unsupported sizes */
+    KDA_ERR_WORKSPACE = 5,     /* workspace NULL, too small or misaligned */
+    KDA_ERR_HIP = 6            /* a kernel launch failed (hipGetLastError) */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Bytes of device workspace kda_chunk_fwd needs for these sizes (0 if the
+ * sizes are invalid or unsupported).  The workspace must be 256-byte aligned. */
+size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                                    int32_t d_k, int32_t d_v, int32_t chunk, kda_dtype dt);
+
+/* Chunkwise-parallel KDA forward: o and (optionally) the final per-sequence
+ * states S_T for the recurrence above (ogis-ri NLP primer on Kimi K3, §3.1
+ * "KDA"), over a packed batch of n_seqs sequences.
+ *   q, k, v, beta, log_alpha : inputs, layouts above (read only)
+ *   S0         : initial states or NULL (zeros)
+ *   cu_seqlens : device int32 [n_seqs+1] or NULL (equal lengths)
+ *   o          : output [total_tokens, n_heads, d_v], dtype dt (required)
+ *   S_T        : output [n_seqs, n_heads, d_k, d_v] float32, or NULL
+ *   workspace  : >= kda_chunk_fwd_workspace_size(...) bytes of device memory
+ *   stream     : HIP stream (hipStream_t) the work is queued on; NULL = default
+ * total_tokens == 0 is valid: o is empty and S_T (if given) receives S0
+ * (or zeros).  Every tensor pointer must be 16-byte aligned (KDA_ERR_SHAPE
+ * otherwise). */
+kda_status kda_chunk_fwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                         int32_t d_k, int32_t d_v, int32_t chunk,
+                         const void* q, const void* k, const void* v,
+                         const void* beta, const void* log_alpha,
+                         const float* S0, const int32_t* cu_seqlens,
+                         void* o, float* S_T,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement entry point: the same work as kda_chunk_fwd (same arguments,
+ * same results), with a HIP event recorded on `stream` before and after each
+ * kernel launch.  Unlike kda_chunk_fwd it BLOCKS until the pass has finished
+ * (it synchronises on its last event), then writes each launch's duration in
+ * milliseconds to stage_ms[0 .. kda_profile_num_stages()-1] (host memory,
+ * required).  It creates and destroys its events; it allocates no device
+ * memory.  Errors as for kda_chunk_fwd; KDA_ERR_NULL if stage_ms is NULL. */
+kda_status kda_chunk_fwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                                 int32_t d_k, int32_t d_v, int32_t chunk,
+                                 const void* q, const void* k, const void* v,
+                                 const void* beta, const void* log_alpha,
+                                 const float* S0, const int32_t* cu_seqlens,
+                                 void* o, float* S_T,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 float* stage_ms);
+
+/* Number of kernel launches one forward pass makes, and the name of launch i
+ * (NULL when i is out of range); names match the kernel symbols a profiler
+ * reports. */
+int32_t kda_profile_num_stages(void);
+const char* kda_profile_stage_name(int32_t i);
+
+/* Static description of a status code (never NULL). */
+const char* kda_status_string(kda_status s);
+
+/* Library version, e.g. "0.1.0". */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -131,14 +131,16 @@ def forward(q, k, v, beta, g, S0=None, cu_seqlens=None, out_range=None, n_thread
     return o, ST
 
 
-def parity_error(x, ref, cu_seqlens=None, token_axis=0, head_axis=1):
-    """Worst per-(sequence, head) slice of max|x - ref| / max|ref|.
+def parity_error(x, ref, cu_seqlens=None, token_axis=0, head_axis=1, floor=1e-30):
+    """Worst per-(sequence, head) slice of max|x - ref| / max(max|ref|, floor).
 
     For o-shaped arrays [T, H, d] slices are (sequence, head); pass
     cu_seqlens=None to treat all tokens as one sequence.  For state-shaped
     arrays [N, H, dk, dv] call with cu_seqlens=None, token_axis=0 meaning
-    sequence axis (each [n, h] slice is one state).  A slice whose reference
-    is all zero is compared by max|x| instead."""
+    sequence axis (each [n, h] slice is one state).  `floor` keeps a slice
+    whose reference has decayed below any fp32-meaningful scale (a state
+    decayed by e^-750 is ~1e-326) from turning rounding to zero into a
+    relative error of 1."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert x.shape == ref.shape, (x.shape, ref.shape)
@@ -156,8 +158,8 @@ def parity_error(x, ref, cu_seqlens=None, token_axis=0, head_axis=1):
         for h in range(x.shape[head_axis]):
             xh = np.take(xs, h, axis=head_axis)
             rh = np.take(rs, h, axis=head_axis)
-            den = np.max(np.abs(rh))
-            num = np.max(np.abs(xh - rh))
-            err = num / den if den > 0 else num
+            den = max(float(np.max(np.abs(rh))), floor)
+            num = float(np.max(np.abs(xh - rh)))
+            err = num / den
             worst = max(worst, float(err))
     return worst

@@ -1,0 +1,107 @@
+"""The C-ABI library: it loads, exports every function include/kda.h declares,
+sizes its workspace, and rejects bad arguments on the host with the
+documented status before anything is enqueued.  No GPU needed: every call
+here fails validation, so no kernel is ever launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_30_amd as kda
+
+ROOT = os.path.abspath(os.path.join(os.path.dirname(__file__), ".."))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(7)
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.lib_path()):
+        pytest.fail("libkda.so not built; run __graft_entry__.build()")
+    return kda._load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(names) >= {"kda_chunk_fwd", "kda_chunk_fwd_workspace_size", "kda_status_string", "kda_version"}
+    for n in names:
+        assert hasattr(lib, n), "libkda.so does not export %s" % n
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        s = kda.status_string(code)
+        assert s.startswith("KDA_")
+    assert "unknown" in kda.status_string(99)
+    assert lib.kda_version().decode().count(".") == 2
+
+
+def test_workspace_size():
+    a = kda.workspace_size(65536, 1, 32, 128, 128, 64, kda.KDA_BF16)
+    b = kda.workspace_size(65536, 1, 32, 128, 128, 64, kda.KDA_F32)
+    assert a > 0 and b == 0                    # fp32 operands only at d = 64
+    assert kda.workspace_size(256, 1, 2, 64, 64, 64, kda.KDA_F32) > 0
+    assert kda.workspace_size(256, 1, 2, 96, 96, 64, kda.KDA_BF16) == 0
+    assert kda.workspace_size(256, 1, 2, 64, 64, 32, kda.KDA_BF16) == 0
+    assert kda.workspace_size(-1, 1, 2, 64, 64, 64, kda.KDA_BF16) == 0
+    assert kda.workspace_size(1 << 31, 1, 2, 64, 64, 64, kda.KDA_BF16) == 0
+    # monotone in tokens and heads; 256-byte granularity
+    s1 = kda.workspace_size(1000, 3, 4, 64, 64, 64, kda.KDA_BF16)
+    s2 = kda.workspace_size(2000, 3, 4, 64, 64, 64, kda.KDA_BF16)
+    s3 = kda.workspace_size(1000, 3, 8, 64, 64, 64, kda.KDA_BF16)
+    assert s1 < s2 and s1 < s3 and s1 % 256 == 0
+    assert kda.workspace_size(0, 2, 4, 128, 128, 64, kda.KDA_BF16) > 0
+
+
+def _call(lib, dt=kda.KDA_BF16, T=128, N=1, H=2, dk=64, dv=64, C=64, ptrs=None, S0=None, cu=None,
+          ST=None, ws=0x100000, ws_bytes=None):
+    P = ctypes.c_void_p
+    fake = 0x7f0000000000          # never dereferenced: every case below fails validation
+    p = dict(q=fake, k=fake, v=fake, beta=fake, g=fake, o=fake)
+    if ptrs:
+        p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = 0
+    return lib.kda_chunk_fwd(dt, T, N, H, dk, dv, C, P(p["q"]), P(p["k"]), P(p["v"]), P(p["beta"]), P(p["g"]),
+                             P(S0), P(cu), P(p["o"]), P(ST), P(ws), ws_bytes, None)
+
+
+def test_rejects_bad_arguments(lib):
+    assert _call(lib, dt=7) == ERR_DTYPE
+    assert _call(lib, T=-5) == ERR_SHAPE
+    assert _call(lib, N=0) == ERR_SHAPE
+    assert _call(lib, H=0) == ERR_SHAPE
+    assert _call(lib, T=100, N=3) == ERR_SHAPE              # equal lengths must divide
+    assert _call(lib, dk=64, dv=128) == ERR_UNSUPPORTED
+    assert _call(lib, dk=96, dv=96) == ERR_UNSUPPORTED
+    assert _call(lib, C=128) == ERR_UNSUPPORTED
+    assert _call(lib, dt=kda.KDA_F32, dk=128, dv=128) == ERR_UNSUPPORTED
+    assert _call(lib, T=1 << 31) == ERR_UNSUPPORTED
+    assert _call(lib, H=70000) == ERR_UNSUPPORTED
+    for name in ("q", "k", "v", "beta", "g", "o"):
+        assert _call(lib, ptrs={name: None}) == ERR_NULL, name
+    assert _call(lib, ptrs={"q": 0x7f0000000008}) == ERR_SHAPE   # misaligned
+    assert _call(lib, S0=0x7f0000000004) == ERR_SHAPE
+    assert _call(lib, ws=None) == ERR_WORKSPACE
+    assert _call(lib, ws=0x100010, ws_bytes=1 << 40) == ERR_WORKSPACE   # misaligned workspace
+    need = kda.workspace_size(128, 1, 2, 64, 64, 64, kda.KDA_BF16)
+    assert _call(lib, ws_bytes=need - 1) == ERR_WORKSPACE
+    # varlen sizing: the workspace for N sequences covers any split of the tokens
+    assert _call(lib, T=100, N=3, cu=0x7f0000001000, ws_bytes=10) == ERR_WORKSPACE
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 2, 64)
+    with pytest.raises(ValueError):
+        kda.chunk_fwd(x, x, x, torch.zeros(4, 2), x)
+    with pytest.raises(TypeError):
+        kda.chunk_fwd(x.double(), x, x, torch.zeros(4, 2), x)

@@ -291,3 +291,22 @@ def test_pins_catch_planted_mistake(name, tmp_path):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, "planted mistake %s passed every pin" % name
+
+
+def test_parity_metric():
+    """max|x - ref| / max|ref| per (sequence, head) slice, with an absolute
+    floor for references that decayed to nothing."""
+    ref = np.zeros((6, 2, 3))
+    ref[:4, 0] = 2.0
+    ref[4:, 0] = 10.0
+    ref[:, 1] = 1e-300
+    x = ref.copy()
+    x[1, 0, 0] += 0.2            # seq 0 head 0: 0.2 / 2
+    x[5, 0, 2] -= 0.5            # seq 1 head 0: 0.5 / 10
+    x[:, 1] = 0.0                # decayed-to-nothing head: absolute
+    assert math.isclose(oracle.parity_error(x, ref, [0, 4, 6]), 0.1)
+    assert math.isclose(oracle.parity_error(x, ref, None), 0.5 / 10)
+    S = np.ones((2, 2, 3, 3))
+    S2 = S.copy()
+    S2[1, 1, 2, 2] = 1.03
+    assert math.isclose(oracle.parity_error(S2, S), 0.03, rel_tol=1e-9)
