@@ -97,7 +97,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = headline)")
     ap.add_argument("--profile-reps", type=int, default=10)
-    ap.add_argument("--cpu-heads", type=int, default=16, help="heads in the CPU-oracle sample")
+    ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
