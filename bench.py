@@ -38,13 +38,12 @@ def min_bytes_per_token_head(dk, dv, es=2):
 
 def kernel_bytes_per_token_head(name, C, D, es=2):
     """Algorithmic bytes each kernel of this design moves per (token, head):
-    its inputs read once and its outputs written once."""
-    per_chunk_state = es * D * D / C          # one D x D state per chunk
+    its inputs read once and its outputs written once (the value-column slabs
+    of one head re-read the chunk operands through L2; that is not counted)."""
+    ops = 3 * es * D + 2 * es * C + 4 * D / C     # Q.Gamma, K.Gamma, K^T, T diag(beta), M, Gamma_L
     return {
-        "k_cumsum": es * D + 4 * D,                                   # g -> b (fp32)
-        "k_wy": (3 * es * D + es + 4 * D) + (3 * es * D + 4 * D / C),  # k, v, beta, b -> W, U, K^, Gamma_L
-        "k_state": (3 * es * D + 4 * D / C) + (per_chunk_state + es * D),  # W, U, K^, Gamma_L -> S chunks, U~
-        "k_output": (2 * es * D + 4 * D + per_chunk_state + es * D) + es * D,  # q, k, b, S, U~ -> o
+        "k_prep": (3 * es * D + es) + ops,        # q, k, g, beta -> chunk operands
+        "k_recur": ops + es * D + es * D,         # chunk operands, v -> o
         "k_chunk_table": 0.0,
     }[name]
 
@@ -99,7 +98,19 @@ def main():
     ap.add_argument("--profile-reps", type=int, default=10)
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES bytes 3 times (yardstick for the "
+                         "profiler's HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(args.calibrate_copy // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": src.numel() * 4, "copies": 3}), flush=True)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (heads and sequences shard "
               "with no exchange; see the sharding notes). Run with --gpus 1.", file=sys.stderr)

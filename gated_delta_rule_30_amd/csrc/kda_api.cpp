@@ -15,7 +15,7 @@ static size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 size_t carve_workspace(Plan* p, void* base) {
     const size_t es = p->bf16 ? 2 : 4;
-    const size_t T = (size_t)p->total_tokens, H = (size_t)p->n_heads, D = (size_t)p->d;
+    const size_t H = (size_t)p->n_heads, D = (size_t)p->d;
     const size_t mc = (size_t)p->max_chunks;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -26,13 +26,12 @@ size_t carve_workspace(Plan* p, void* base) {
     p->ws_n_chunks = (int32_t*)take(sizeof(int32_t));
     p->ws_seq_chunk0 = (int32_t*)take(sizeof(int32_t) * ((size_t)p->n_seqs + 1));
     p->ws_tab = (ChunkInfo*)take(sizeof(ChunkInfo) * mc);
-    p->ws_b = (float*)take(4 * T * H * D);
-    p->ws_W = take(es * T * H * D);
-    p->ws_U = take(es * T * H * D);
-    p->ws_Kh = take(es * T * H * D);
+    p->ws_TB = take(es * mc * H * kChunkTokens * kChunkTokens);
+    p->ws_M = take(es * mc * H * kChunkTokens * kChunkTokens);
+    p->ws_Qg = take(es * mc * H * kChunkTokens * D);
+    p->ws_Kg = take(es * mc * H * kChunkTokens * D);
+    p->ws_KhT = take(es * mc * H * D * kChunkTokens);
     p->ws_gam = (float*)take(4 * mc * H * D);
-    p->ws_Ut = take(es * mc * H * D * kChunkTokens);
-    p->ws_Sc = take(es * mc * H * D * D);
     return off;
 }
 
@@ -49,7 +48,7 @@ static kda_status plan_sizes(Plan* p, kda_dtype dt, int64_t total_tokens, int32_
     if (dt == KDA_F32 && d_k != 64) return KDA_ERR_UNSUPPORTED;
     if (total_tokens >= ((int64_t)1 << 31) || n_heads > 65535) return KDA_ERR_UNSUPPORTED;
     const int64_t max_chunks = total_tokens / kda::kChunkTokens + n_seqs;
-    if (max_chunks >= ((int64_t)1 << 31) || (int64_t)n_seqs * n_heads * (d_v / 32) >= ((int64_t)1 << 31))
+    if (max_chunks >= ((int64_t)1 << 31) || (int64_t)n_seqs * n_heads * (d_v / 16) >= ((int64_t)1 << 31))
         return KDA_ERR_UNSUPPORTED;
     p->bf16 = dt == KDA_BF16;
     p->d = d_k;
@@ -134,7 +133,7 @@ kda_status kda_chunk_fwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_s
     if (e == hipSuccess) e = kda::launch(p, static_cast<hipStream_t>(stream), ev);
     if (e == hipSuccess) e = hipEventSynchronize(ev[kda::kNumStages]);
     for (int i = 0; e == hipSuccess && i < kda::kNumStages; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
-    for (int i = 0; i < made; ++i) hipEventDestroy(ev[i]);
+    for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -29,11 +29,13 @@ struct Plan {
     int32_t* ws_n_chunks;
     int32_t* ws_seq_chunk0;
     ChunkInfo* ws_tab;
-    float* ws_b;              // [T, H, D] cumulative log-decay
-    void *ws_W, *ws_U, *ws_Kh;  // [T, H, D] operand dtype
-    float* ws_gam;            // [max_chunks, H, D]
-    void* ws_Ut;              // [max_chunks, H, D(col), 64(token)]
-    void* ws_Sc;              // [max_chunks, H, D(col), D(channel)]
+    // chunk operands, head-major: slot h * max_chunks + chunk
+    void* ws_TB;              // [H, max_chunks, 64, 64] T diag(beta), operand dtype
+    void* ws_M;               // [H, max_chunks, 64, 64] decayed causal Q K^T, operand dtype
+    void* ws_Qg;              // [H, max_chunks, 64, D] Q . Gamma
+    void* ws_Kg;              // [H, max_chunks, 64, D] K . Gamma
+    void* ws_KhT;             // [H, max_chunks, D, 64] (K . exp(b_L - b))^T
+    float* ws_gam;            // [H, max_chunks, D] exp(b_L), fp32
 };
 
 // Byte offsets of every workspace region for the given sizes; returns the
@@ -41,7 +43,7 @@ struct Plan {
 size_t carve_workspace(Plan* p, void* base);
 
 // Kernel launches of one forward pass, in order.
-constexpr int kNumStages = 5;
+constexpr int kNumStages = 3;
 extern const char* const kStageNames[kNumStages];
 
 // Enqueues the forward pass on `stream`.  If `ev` is non-NULL it must hold

@@ -11,31 +11,62 @@
 //              (§3.1 "chunk 内の減衰と、その数値範囲": Gamma_j / Gamma_i)
 //   A[r,i]   = beta_r sum_c k_rc k_ic exp(b_rc - b_ic)      (i < r)
 //   T        = (I + A)^-1                       delta-rule correction
-//   W = T diag(beta) (K . Gamma),   U = T diag(beta) V
-//   U~ = U - W S                                 written deltas of the chunk
-//   O  = (Q . Gamma) S + M U~,    M[r,i] = sum_c q_rc k_ic exp(b_rc - b_ic)  (i <= r)
+//   M[r,i]   = sum_c q_rc k_ic exp(b_rc - b_ic)             (i <= r)
+//   U~ = T diag(beta) (V - (K . Gamma) S)        written deltas of the chunk
+//   O  = (Q . Gamma) S + M U~
 //   S' = Diag(Gamma_L) S + (K . exp(b_L - b))^T U~
 //
 // Sub-tiling (orkas.ai "Kimi K3 architecture", §"GPU のコードパスを一本消した
-// 「下界」"): with g >= -5, b varies by less than 80 inside a 16-token
-// sub-tile, so for row sub-tile R with reference rho_R = b at the end of
-// sub-tile R-1 (0 at the chunk start) the operands
-//   row    : x_r . exp(b_r - rho_R)      factor in (e^-80, 1]
-//   column : k_i . exp(rho_R - b_i)      factor in [1, e^80) on the diagonal
-//                                        sub-tile, <= 1 left of it
-// stay inside bf16 range, and every (R, J <= R) block of A and M -- the
-// diagonal ones included -- is one dense MFMA contraction over d_k.
+// 「下界」"): with g >= -5, b falls by at most 80 inside a 16-token sub-tile.
+// For row sub-tile R let rho_R = b at the end of sub-tile R-1 (0 at the chunk
+// start).  The diagonal block (R, R) of A and M is the product of
+//   row operand    x_r . exp(b_r - rho_R)      factor in [e^-80, 1]
+//   column operand k_i . exp(rho_R - b_i)      factor in [1, e^80]
+// and an off-diagonal block (R, J < R) of
+//   row operand    x_r . exp(b_r - rho_R)
+//   column operand k_i . exp(rho_{J+1} - b_i) . exp(rho_R - rho_{J+1})   factors <= 1
+// All factors stay inside bf16 range, so every block -- the diagonal ones
+// included -- is one dense MFMA contraction over d_k.
 //
-// Kernels (one launch each, all on the caller's stream):
+// Launches (all on the caller's stream):
 //   k_chunk_table : chunk list from cu_seqlens (device side, no host sync)
-//   k_cumsum      : b per chunk
-//   k_wy          : A, T (LDS, fp32), W, U, K^ = K . exp(b_L - b), Gamma_L
-//   k_state       : sequential over chunks per (sequence, head, value slab)
-//   k_output      : M and O per chunk
+//   k_prep        : per (chunk, head), chunk-parallel: decay cumsum, A and M
+//                   by sub-tiled MFMA, T = (I + A)^-1 in LDS (fp32); writes
+//                   T diag(beta) and M
+//   k_recur       : per (sequence, head, 16-column slab of S), sequential over
+//                   the chunks: decay cumsum, Q . Gamma, K . Gamma,
+//                   K . exp(b_L - b), the state step and the chunk output
+//
+// Lane geometry shared by both kernels.  Wave w of a 256-thread workgroup
+// owns token rows 16w .. 16w+15 of the chunk; lane = 16 * lg + li holds token
+// 16w + li and the contiguous key-channel range [lg * D/4, (lg+1) * D/4).
+// That is exactly the A-operand fragment of the 16-row tile w for a
+// contraction over channels (k-step m covers channels lg*D/4 + m*KW + j), and
+// also the B-operand fragment of column block w, so the diagonal sub-tile
+// products need no data exchange.  The per-channel cumulative sum over
+// tokens is a 16-lane row scan (DPP row shifts) plus carries between waves.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
+
+// ---------------------------------------------------------------- sequences
+// Token range [start, start + len) of sequence n.  Device-side offsets are
+// clamped to [0, total_tokens) so that malformed cu_seqlens can never address
+// outside the tensors.
+__device__ inline void seq_range(const int32_t* __restrict__ cu, int32_t n, int64_t total_tokens,
+                                 int64_t fixed_len, int64_t& start, int64_t& len) {
+    if (cu) {
+        int64_t a = cu[n], e = cu[n + 1];
+        a = a < 0 ? 0 : (a > total_tokens ? total_tokens : a);
+        e = e < a ? a : (e > total_tokens ? total_tokens : e);
+        start = a;
+        len = e - a;
+    } else {
+        start = (int64_t)n * fixed_len;
+        len = fixed_len;
+    }
+}
 
 // ---------------------------------------------------------------- chunk table
 // One workgroup.  Sequence n contributes ceil(len_n / 64) chunks; chunks are
@@ -53,19 +84,7 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
     for (int32_t base = 0; base < n_seqs; base += 1024) {
         const int32_t n = base + tid;
         int64_t start = 0, len = 0;
-        if (n < n_seqs) {
-            if (cu) {
-                start = cu[n];
-                int64_t end = cu[n + 1];
-                // Clamp so that malformed offsets can never address outside [0, total_tokens).
-                start = start < 0 ? 0 : (start > total_tokens ? total_tokens : start);
-                end = end < start ? start : (end > total_tokens ? total_tokens : end);
-                len = end - start;
-            } else {
-                start = (int64_t)n * fixed_len;
-                len = fixed_len;
-            }
-        }
+        if (n < n_seqs) seq_range(cu, n, total_tokens, fixed_len, start, len);
         const int32_t cnt = (int32_t)((len + kChunk - 1) / kChunk);
         s_scan[tid] = cnt;
         __syncthreads();
@@ -101,171 +120,286 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
     }
 }
 
-// ---------------------------------------------------------------- cumsum
-// b[t, h, c] = sum of g over the chunk's tokens up to and including t.
-// One thread per key channel; grid (chunk, head).
+// ---------------------------------------------------------------- shared stages
 template <typename E, int D>
-__global__ __launch_bounds__(D) void k_cumsum(const E* __restrict__ g, const ChunkInfo* __restrict__ tab,
-                                              const int32_t* __restrict__ n_chunks_p, int32_t H,
-                                              float* __restrict__ bcum) {
+struct Geo {
+    using M = Mma<E>;
+    static constexpr int CPL = D / 4;                 // key channels per lane
+    static constexpr int NKC = D / M::KS;             // k-steps of a contraction over channels
+    static constexpr int EPV = 16 / (int)sizeof(E);   // elements per 16-byte vector
+    static constexpr int VPL = CPL / EPV;             // 16-byte vectors per lane per row
+    static constexpr int NKT = kChunk / M::KS;        // k-steps of a contraction over the chunk's tokens
+    static constexpr int NVT = kChunk / 4 / EPV;      // 16-byte vectors per lane of a token contraction
+    // chunk token of lane-element i (k-step order) for lane group lg
+    __device__ static inline int tok_of(int i, int lg) { return M::KS * (i / M::KW) + M::KW * lg + i % M::KW; }
+};
+
+// One token row slice (this lane's channels) of a [T, H, D] tensor, as raw
+// 16-byte vectors.  The load is unconditional (callers pass an address inside
+// the tensor); rows past the chunk end read as zero through get().  Keeping
+// the load free of branches lets prefetched loads stay in flight.
+template <typename E, int D>
+struct RowSlice {
+    uint4 v[Geo<E, D>::VPL];
+    bool ok;
+    __device__ inline void load(const E* __restrict__ p, bool valid) {
+        ok = valid;
+#pragma unroll
+        for (int i = 0; i < Geo<E, D>::VPL; ++i) v[i] = reinterpret_cast<const uint4*>(p)[i];
+    }
+    __device__ inline float get(int j) const {
+        const E* e = reinterpret_cast<const E*>(v);
+        return ok ? to_f(e[j]) : 0.f;
+    }
+};
+
+// 16-lane inclusive prefix sum along a row of 16 lanes (DPP row_shr, zero fill).
+template <int kShift>
+__device__ inline float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | kShift, 0xf, 0xf, true));
+}
+
+__device__ inline float row_scan16(float x) {
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    return x;
+}
+
+// Per-channel cumulative log-decay of the chunk for this lane's token and
+// channels.  On return b[j] is inclusive from the chunk start.  sTot, sCarry:
+// LDS [4][D] and [5][D] fp32; sCarry[w][c] = b at the end of sub-tile w-1
+// (0 for w = 0), sCarry[4][c] = b at the chunk end.  Contains two workgroup
+// barriers; every thread of the workgroup must call it.
+template <typename E, int D>
+__device__ inline void chunk_cumsum(const RowSlice<E, D>& g, float* b, float* sTot, float* sCarry) {
+    constexpr int CPL = Geo<E, D>::CPL;
+    const int w = wave_id(), li = lane_id() & 15, lg = lane_id() >> 4;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) b[j] = row_scan16(g.get(j));
+    if (li == 15) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) sTot[w * D + lg * CPL + j] = b[j];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < D; c += kThreads) {
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < kNSub; ++r) {
+            sCarry[r * D + c] = run;
+            run += sTot[r * D + c];
+        }
+        sCarry[kNSub * D + c] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) b[j] += sCarry[w * D + lg * CPL + j];
+}
+
+// Chunk operands written by k_prep for k_recur, stored head-major: the
+// operands of chunk ci of head h sit at slot h * max_chunks + ci, so one
+// head's chunks are contiguous and the sequential kernel streams through
+// memory.  Per slot (operand dtype E unless stated):
+//   TB  64 x 64    T diag(beta), upper sub-tile blocks zero
+//   Mm  64 x 64    M (decayed causal Q K^T incl. diagonal), upper blocks zero
+//   Qg  64 x D     Q . Gamma
+//   Kg  64 x D     K . Gamma
+//   KhT D x 64     (K . exp(b_L - b))^T
+//   gam [D] fp32   Gamma_L = exp(b_L)
+// The matrices are stored fragment-major: each is a sequence of 16-row
+// A-operand tiles, and a tile is [NV][64 lanes][16 bytes], where lane
+// 16 * lg + li holds row li's contraction elements in k-step order (over
+// channels: lg*D/4 + i; over the chunk's tokens: KS*(i/KW) + KW*lg + i%KW).
+// One wave then loads a fragment vector as 1 KB of contiguous memory.
+struct ChunkOps {
+    void *TB, *Mm, *Qg, *Kg, *KhT;
+    float* gam;
+    int64_t max_chunks;   // slots per head
+};
+
+// ---------------------------------------------------------------- k_prep
+template <typename E, int D>
+__global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
+                                                   const E* __restrict__ g, const E* __restrict__ beta,
+                                                   const ChunkInfo* __restrict__ tab,
+                                                   const int32_t* __restrict__ n_chunks_p, int32_t H,
+                                                   ChunkOps ops) {
+    using G = Geo<E, D>;
+    using M = Mma<E>;
+    constexpr int C = kChunk, CPL = G::CPL, EPV = G::EPV;
+    constexpr int PC = D + 8;      // row pitch of the column-operand tiles
+    constexpr int PT = C + 4;      // row pitch of fp32 C x C matrices
+    constexpr int PM = C + 8;      // row pitch of the M staging tile (elements)
+    constexpr int PK = C + 8;      // row pitch of the K^T staging tile (elements)
+    // Region R holds A, T and the T-inverse scratch; before A exists it stages K^T.
+    constexpr int kRA = C * PT, kRT = C * PT, kRX = 4 * 16 * 17;
+    constexpr int kRBytes = (kRA + kRT + kRX) * 4;
+    static_assert(D * PK * (int)sizeof(E) <= kRBytes, "K^T staging must fit in region R");
+    __shared__ __attribute__((aligned(16))) float sR[kRA + kRT + kRX];
+    __shared__ __attribute__((aligned(16))) E sColB[(kNSub - 1) * kSub * PC];
+    __shared__ float sTot[kNSub * D];
+    __shared__ float sCarry[(kNSub + 1) * D];
+    __shared__ __attribute__((aligned(16))) E sM[C * PM];
+    __shared__ float sBeta[C];
+    float* sA = sR;
+    float* sT = sR + kRA;
+    float* sX = sR + kRA + kRT;
+    E* sKt = reinterpret_cast<E*>(sR);
+
     const int32_t ci = blockIdx.x;
     if (ci >= *n_chunks_p) return;
     const ChunkInfo info = tab[ci];
+    const int h = blockIdx.y, len = info.len;
+    const int tid = threadIdx.x, w = wave_id(), li = lane_id() & 15, lg = lane_id() >> 4;
+    const int tok = kSub * w + li;
+    const bool ok = tok < len;
     const int64_t rs = (int64_t)H * D;
-    const int64_t base = (info.tok0 * H + blockIdx.y) * D + threadIdx.x;
-    float acc = 0.f;
-    float buf[16];
-    for (int r0 = 0; r0 < info.len; r0 += 16) {
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-            buf[j] = (r0 + j < info.len) ? to_f(g[base + (r0 + j) * rs]) : 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            acc += buf[j];
-            if (r0 + j < info.len) bcum[base + (r0 + j) * rs] = acc;
-        }
-    }
-}
+    const int64_t off = (info.tok0 * H + h) * D + (int64_t)(ok ? tok : 0) * rs + lg * CPL;
+    const int64_t cbase = (int64_t)h * ops.max_chunks + ci;   // head-major operand slot
 
-// Strictly-lower (A, with beta) or inclusive-lower (M) block (R, J<=R) of the
-// decayed Gram matrix between row operand X (q or k) and the keys, evaluated
-// with the sub-tile reference of row block R.  sX/sK: [64][PE] elements,
-// sB: [64][PB] fp32 cumulative log-decay.  Returns the MFMA accumulator.
-template <typename E, int D, int PE, int PB>
-__device__ inline f32x4 decayed_gram_block(const E* sX, const E* sK, const float* sB, int R, int J) {
-    using M = Mma<E>;
-    const int li = lane_id() & 15, lg = lane_id() >> 4;
-    const int r = kSub * R + li;        // row token of this lane's A fragment
-    const int i = kSub * J + li;        // column token of this lane's B fragment
-    const float* rho = R ? sB + (kSub * R - 1) * PB : nullptr;
-    f32x4 acc = zero4();
+    RowSlice<E, D> xq, xk, xg;
+    xq.load(q + off, ok);
+    xk.load(k + off, ok);
+    xg.load(g + off, ok);
+    const float bet = ok ? to_f(beta[(info.tok0 + tok) * H + h]) : 0.f;
+    if (lg == 0) sBeta[tok] = bet;
+
+    float b[CPL];
+    chunk_cumsum<E, D>(xg, b, sTot, sCarry);
+
+    // Operands of the decayed Gram blocks (rows scaled by exp(b - rho_w); the
+    // diagonal column operand by exp(rho_w - b); the column base for later row
+    // blocks by exp(rho_{w+1} - b)) and the inter-chunk operands
+    // Q . Gamma, K . Gamma, K . exp(b_L - b).
+    typename M::frag rq[G::NKC], rk[G::NKC], cd[G::NKC];
+    {
+        const float* rho = sCarry + w * D + lg * CPL;
+        const float* rho1 = sCarry + (w + 1) * D + lg * CPL;
+        const float* bl = sCarry + kNSub * D + lg * CPL;
+        E* cb = sColB + (w * kSub + li) * PC + lg * CPL;
+        uint4 vq[G::VPL], vk[G::VPL];
+        E* eq = reinterpret_cast<E*>(vq);
+        E* ek = reinterpret_cast<E*>(vk);
 #pragma unroll
-    for (int k0 = 0; k0 < D; k0 += M::KS) {
-        typename M::frag a, b;
-        if constexpr (M::KW == 1) {
-            const int c = k0 + lg;
-            const float rh = rho ? rho[c] : 0.f;
-            a = to_f(sX[r * PE + c]) * __expf(sB[r * PB + c] - rh);
-            b = to_f(sK[i * PE + c]) * __expf(rh - sB[i * PB + c]);
-        } else {
+        for (int m = 0; m < G::NKC; ++m) {
 #pragma unroll
             for (int j = 0; j < M::KW; ++j) {
-                const int c = k0 + lg * M::KW + j;
-                const float rh = rho ? rho[c] : 0.f;
-                a[j] = from_f<E>(to_f(sX[r * PE + c]) * __expf(sB[r * PB + c] - rh));
-                b[j] = from_f<E>(to_f(sK[i * PE + c]) * __expf(rh - sB[i * PB + c]));
+                const int c = m * M::KW + j;
+                const float x = b[c] - rho[c];
+                const float fr = __expf(x), fd = __expf(-x), gm = __expf(b[c]);
+                const float kv = xk.get(c), qv = xq.get(c);
+                if constexpr (M::KW == 1) {
+                    rq[m] = qv * fr;
+                    rk[m] = kv * fr;
+                    cd[m] = kv * fd;
+                } else {
+                    rq[m][j] = from_f<E>(qv * fr);
+                    rk[m][j] = from_f<E>(kv * fr);
+                    cd[m][j] = from_f<E>(kv * fd);
+                }
+                if (w < kNSub - 1) cb[c] = from_f<E>(kv * __expf(rho1[c] - b[c]));
+                eq[c] = from_f<E>(qv * gm);
+                ek[c] = from_f<E>(kv * gm);
+                sKt[(lg * CPL + c) * PK + tok] = from_f<E>(kv * __expf(bl[c] - b[c]));
             }
         }
-        acc = M::mma(a, b, acc);
-    }
-    return acc;
-}
-
-__device__ inline void block_of(int blk, int& R, int& J) {
-    // (0,0) (1,0) (1,1) (2,0) (2,1) (2,2) (3,0) (3,1) (3,2) (3,3)
-    R = blk < 1 ? 0 : blk < 3 ? 1 : blk < 6 ? 2 : 3;
-    J = blk - (R * (R + 1)) / 2;
-}
-
-// ---------------------------------------------------------------- WY / UT transform
-template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void k_wy(const E* __restrict__ k, const E* __restrict__ v,
-                                                 const E* __restrict__ beta, const float* __restrict__ bcum,
-                                                 const ChunkInfo* __restrict__ tab,
-                                                 const int32_t* __restrict__ n_chunks_p, int32_t H,
-                                                 E* __restrict__ W, E* __restrict__ U, E* __restrict__ Kh,
-                                                 float* __restrict__ gam) {
-    using M = Mma<E>;
-    constexpr int C = kChunk;
-    constexpr int PE = D + 8;     // row pitch (elements) of [token][channel] tiles
-    constexpr int PB = D + 4;     // row pitch of the fp32 log-decay tile
-    constexpr int PT = C + 4;     // row pitch of the fp32 C x C matrices
-    constexpr int PO = C + 8;     // row pitch (elements) of [n][token] operand tiles
-    // Region 1 (k tile, log-decay tile) is dead once A and (K . Gamma)^T are
-    // formed; region 2 (T, scratch, T diag(beta)) reuses its bytes.
-    constexpr int kReg1 = C * PE * (int)sizeof(E) + C * PB * 4;
-    constexpr int kReg2 = C * PT * 4 + 4 * 16 * 17 * 4 + C * PO * (int)sizeof(E);
-    __shared__ __attribute__((aligned(16))) unsigned char sR[kReg1 > kReg2 ? kReg1 : kReg2];
-    E* sK = reinterpret_cast<E*>(sR);
-    float* sB = reinterpret_cast<float*>(sR + C * PE * sizeof(E));
-    float* sT = reinterpret_cast<float*>(sR);
-    float* sX = sT + C * PT;
-    E* sTo = reinterpret_cast<E*>(sX + 4 * 16 * 17);
-    __shared__ __attribute__((aligned(16))) float sA[C * PT];
-    __shared__ __attribute__((aligned(16))) E sKgt[D * PO];
-    __shared__ __attribute__((aligned(16))) E sVt[D * PO];
-    __shared__ float sBeta[C];
-
-    const int32_t ci = blockIdx.x;
-    if (ci >= *n_chunks_p) return;
-    const ChunkInfo info = tab[ci];
-    const int h = blockIdx.y;
-    const int len = info.len;
-    const int tid = threadIdx.x, wave = wave_id(), li = lane_id() & 15, lg = lane_id() >> 4;
-    const int64_t rs = (int64_t)H * D;
-    const int64_t base = (info.tok0 * H + h) * D;
-
-    // 1. stage k, b, v^T and beta; rows past the chunk end are zero (b copies the last row)
-    for (int idx = tid; idx < C * D; idx += kThreads) {
-        const int r = idx / D, c = idx % D;
-        const bool ok = r < len;
-        const int64_t off = base + (int64_t)(ok ? r : len - 1) * rs + c;
-        sK[r * PE + c] = ok ? k[off] : from_f<E>(0.f);
-        sB[r * PB + c] = bcum[off];
-        sVt[c * PO + r] = ok ? v[off] : from_f<E>(0.f);
-    }
-    for (int r = tid; r < C; r += kThreads)
-        sBeta[r] = r < len ? to_f(beta[(info.tok0 + r) * H + h]) : 0.f;
-    __syncthreads();
-
-    // 2. A = diag(beta) StrictTril(decayed K K^T), 10 sub-tile blocks over 4 waves
-    for (int blk = wave; blk < 10; blk += 4) {
-        int R, J;
-        block_of(blk, R, J);
-        const f32x4 acc = decayed_gram_block<E, D, PE, PB>(sK, sK, sB, R, J);
+        uint4* qg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Qg) + cbase * C * D);
+        uint4* kg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Kg) + cbase * C * D);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = kSub * R + 4 * lg + rr, col = kSub * J + li;
-            sA[row * PT + col] = (J < R || col < row) ? sBeta[row] * acc[rr] : 0.f;
+        for (int i = 0; i < G::VPL; ++i) {
+            qg[(w * G::VPL + i) * 64 + lane_id()] = vq[i];
+            kg[(w * G::VPL + i) * 64 + lane_id()] = vk[i];
         }
+        for (int c = tid; c < D; c += kThreads) ops.gam[cbase * D + c] = __expf(sCarry[kNSub * D + c]);
     }
-    // 3. (K . Gamma)^T for W, and K^ = K . exp(b_L - b), Gamma_L to global
+    __syncthreads();
     {
-        const float* bL = sB + (len - 1) * PB;
-        for (int idx = tid; idx < C * D; idx += kThreads) {
-            const int r = idx / D, c = idx % D;
-            const float kv = to_f(sK[r * PE + c]);
-            const float bv = sB[r * PB + c];
-            sKgt[c * PO + r] = from_f<E>(kv * __expf(bv));
-            if (r < len) Kh[base + (int64_t)r * rs + c] = from_f<E>(kv * __expf(bL[c] - bv));
+        uint4* kt = reinterpret_cast<uint4*>(static_cast<E*>(ops.KhT) + cbase * D * C);
+        for (int vi = tid; vi < D * C / EPV; vi += kThreads) {
+            const int ln = vi % 64, v = (vi / 64) % G::NVT, ct = vi / (64 * G::NVT);
+            const int r = kSub * ct + (ln & 15), lgp = ln >> 4;
+            uint4 pk;
+            E* pe = reinterpret_cast<E*>(&pk);
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) pe[e] = sKt[r * PK + G::tok_of(v * EPV + e, lgp)];
+            kt[vi] = pk;
         }
-        for (int c = tid; c < D; c += kThreads) gam[((int64_t)ci * H + h) * D + c] = __expf(bL[c]);
     }
     __syncthreads();
 
-    // 4a. inverses of the four unit-lower-triangular diagonal blocks (forward substitution)
+    // Blocks (w, J) for J <= w of A (strict lower, rows scaled by beta) and M (inclusive lower).
+    for (int J = 0; J <= w; ++J) {
+        f32x4 accA = zero4(), accM = zero4();
+        if (J == w) {
+#pragma unroll
+            for (int m = 0; m < G::NKC; ++m) {
+                accA = M::mma(rk[m], cd[m], accA);
+                accM = M::mma(rq[m], cd[m], accM);
+            }
+        } else {
+            // column operand: base of block J times exp(rho_w - rho_{J+1}) (1 when J = w-1)
+            const E* cb = sColB + (J * kSub + li) * PC + lg * CPL;
+            const float* rw = sCarry + w * D + lg * CPL;
+            const float* rj = sCarry + (J + 1) * D + lg * CPL;
+            const bool scale = J < w - 1;
+#pragma unroll
+            for (int m = 0; m < G::NKC; ++m) {
+                typename M::frag cf;
+                if constexpr (M::KW == 1) {
+                    const int c = m;
+                    cf = scale ? to_f(cb[c]) * __expf(rw[c] - rj[c]) : to_f(cb[c]);
+                } else {
+                    cf = M::load(cb + m * M::KW);
+                    if (scale) {
+#pragma unroll
+                        for (int j = 0; j < M::KW; ++j) {
+                            const int c = m * M::KW + j;
+                            cf[j] = from_f<E>(to_f(cf[j]) * __expf(rw[c] - rj[c]));
+                        }
+                    }
+                }
+                accA = M::mma(rk[m], cf, accA);
+                accM = M::mma(rq[m], cf, accM);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = kSub * w + 4 * lg + r, col = kSub * J + li;
+            sA[row * PT + col] = (J < w || col < row) ? sBeta[row] * accA[r] : 0.f;
+            sM[row * PM + col] = from_f<E>((J < w || col <= row) ? accM[r] : 0.f);
+        }
+    }
+    // upper blocks: zero in M and T
+    for (int idx = tid; idx < C * C; idx += kThreads) {
+        const int r = idx / C, c = idx % C;
+        if ((c >> 4) > (r >> 4)) {
+            sM[r * PM + c] = from_f<E>(0.f);
+            sT[r * PT + c] = 0.f;
+        }
+    }
+    __syncthreads();
+
+    // T = (I + A)^-1.  Diagonal 16 x 16 blocks by forward substitution (one
+    // column per lane), then the off-diagonal blocks by distance R - J:
+    // T_RJ = -T_RR sum_{K=J}^{R-1} A_RK T_KJ  (fp32 MFMA).
     if (lg == 0) {
-        const int R = wave, j = li;
+        const int R = w, jc = li;
         float x[kSub];
 #pragma unroll
         for (int r = 0; r < kSub; ++r) {
-            float s = (r == j) ? 1.f : 0.f;
+            float s = (r == jc) ? 1.f : 0.f;
 #pragma unroll
             for (int i = 0; i < r; ++i) s -= sA[(kSub * R + r) * PT + kSub * R + i] * x[i];
             x[r] = s;
         }
 #pragma unroll
-        for (int r = 0; r < kSub; ++r) sT[(kSub * R + r) * PT + kSub * R + j] = x[r];
-    }
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        const int r = idx / C, c = idx % C;
-        if ((c >> 4) > (r >> 4)) sT[r * PT + c] = 0.f;
+        for (int r = 0; r < kSub; ++r) sT[(kSub * R + r) * PT + kSub * R + jc] = x[r];
     }
     __syncthreads();
-    // 4b. off-diagonal blocks: T_RJ = -T_RR sum_{K=J}^{R-1} A_RK T_KJ, by distance R-J
     for (int d = 1; d < kNSub; ++d) {
-        const bool act = wave < kNSub - d;
-        const int J = wave, R = wave + d;
+        const bool act = w < kNSub - d;
+        const int J = w, R = w + d;
         if (act) {
             f32x4 acc = zero4();
             for (int K = J; K < R; ++K)
@@ -274,307 +408,389 @@ __global__ __launch_bounds__(kThreads) void k_wy(const E* __restrict__ k, const 
                     acc = mma_f32(sA[(kSub * R + li) * PT + kSub * K + kk + lg],
                                   sT[(kSub * K + kk + lg) * PT + kSub * J + li], acc);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sX[wave * 272 + (4 * lg + rr) * 17 + li] = acc[rr];
+            for (int r = 0; r < 4; ++r) sX[w * 272 + (4 * lg + r) * 17 + li] = acc[r];
         }
         __syncthreads();
         if (act) {
             f32x4 acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < kSub; kk += 4)
-                acc = mma_f32(sT[(kSub * R + li) * PT + kSub * R + kk + lg],
-                              sX[wave * 272 + (kk + lg) * 17 + li], acc);
+                acc = mma_f32(sT[(kSub * R + li) * PT + kSub * R + kk + lg], sX[w * 272 + (kk + lg) * 17 + li],
+                              acc);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sT[(kSub * R + 4 * lg + rr) * PT + kSub * J + li] = -acc[rr];
+            for (int r = 0; r < 4; ++r) sT[(kSub * R + 4 * lg + r) * PT + kSub * J + li] = -acc[r];
         }
         __syncthreads();
     }
-    // 5. T diag(beta) in the operand dtype
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        const int r = idx / C, i = idx % C;
-        sTo[r * PO + i] = from_f<E>(sT[r * PT + i] * sBeta[i]);
-    }
-    __syncthreads();
-    // 6. W = T diag(beta) (K . Gamma),  U = T diag(beta) V
-    constexpr int NCT = D / kSub;
-    for (int t = wave; t < 2 * kNSub * NCT; t += 4) {
-        const int mat = t / (kNSub * NCT), rem = t % (kNSub * NCT);
-        const int R = rem / NCT, ct = rem % NCT;
-        const E* Bt = mat ? sVt : sKgt;
-        const int kend = ((kSub * (R + 1) + M::KS - 1) / M::KS) * M::KS;
-        f32x4 acc = zero4();
-        for (int k0 = 0; k0 < kend; k0 += M::KS)
-            acc = M::mma(M::load(&sTo[(kSub * R + li) * PO + k0 + lg * M::KW]),
-                         M::load(&Bt[(kSub * ct + li) * PO + k0 + lg * M::KW]), acc);
-        E* out = mat ? U : W;
+
+    // Stores: T diag(beta) and M, fragment-major 16-byte vectors.
+    uint4* otb = reinterpret_cast<uint4*>(static_cast<E*>(ops.TB) + cbase * C * C);
+    uint4* omm = reinterpret_cast<uint4*>(static_cast<E*>(ops.Mm) + cbase * C * C);
+    for (int vi = tid; vi < C * C / EPV; vi += kThreads) {
+        const int ln = vi % 64, v = (vi / 64) % G::NVT, wr = vi / (64 * G::NVT);
+        const int r = kSub * wr + (ln & 15), lgp = ln >> 4;
+        uint4 pt, pm;
+        E* et = reinterpret_cast<E*>(&pt);
+        E* em = reinterpret_cast<E*>(&pm);
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = kSub * R + 4 * lg + rr;
-            if (row < len) out[base + (int64_t)row * rs + kSub * ct + li] = from_f<E>(acc[rr]);
+        for (int e = 0; e < EPV; ++e) {
+            const int t = G::tok_of(v * EPV + e, lgp);
+            et[e] = from_f<E>(sT[r * PT + t] * sBeta[t]);
+            em[e] = sM[r * PM + t];
         }
+        otb[vi] = pt;
+        omm[vi] = pm;
     }
 }
 
-// ---------------------------------------------------------------- state propagation
-// Sequential over the chunks of one sequence, for one head and one slab of
-// kSlab value columns (columns of S evolve independently).  S stays in fp32
-// registers; per chunk:  U~ = U - W S,  S <- Diag(Gamma_L) S + K^T U~.
-// Emits S^T at every chunk start and U~^T (both in the operand dtype) for the
-// output kernel, and S_T at the end.
-constexpr int kSlab = 32;
+// ---------------------------------------------------------------- k_recur
+// Sequential over the chunks of one sequence for one head and one slab of
+// 16 * CT value columns (columns of S evolve independently).  Per chunk:
+//   X = (K . Gamma) S,  P = (Q . Gamma) S        rows 16w.. of wave w
+//   U~ = T diag(beta) (V - X)                    rows 16w..
+//   O  = P + M U~                                rows 16w.. -> o
+//   S <- Diag(Gamma_L) S + (K . exp(b_L - b))^T U~
+// S stays in fp32 registers in accumulator layout: wave w holds key-channel
+// tiles RT*w .. RT*w+RT-1 of every column tile.  All chunk operands come
+// from k_prep and are prefetched one chunk ahead into registers.
+template <typename E, int D, int CT>
+struct RecurIn {
+    using G = Geo<E, D>;
+    using F = typename Mma<E>::frag;
+    static constexpr int RT = D / 64;
+    uint4 qg[G::VPL], kg[G::VPL];            // A fragments over channels (rows 16w..)
+    uint4 kt[RT][G::NVT];                    // A fragments of K^T (channel tiles), over tokens
+    uint4 tb[G::NVT], mm[G::NVT];            // A fragments over tokens (rows 16w..)
+    f32x4 gam[RT];                           // Gamma_L for this lane's state rows
+    E v[CT][4];                              // value entries of rows 16w + 4lg + r (zeroed past the end at use)
+    int len;
+};
 
+// Base pointers of one (sequence, head, slab) problem; chunk j of the
+// sequence is chunk c0 + j of the workspace and starts at token start + 64 j.
 template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void k_state(const E* __restrict__ W, const E* __restrict__ U,
-                                                    const E* __restrict__ Kh, const float* __restrict__ gam,
-                                                    const ChunkInfo* __restrict__ tab,
-                                                    const int32_t* __restrict__ seq_chunk0, int32_t H,
-                                                    const float* __restrict__ S0, float* __restrict__ ST,
-                                                    E* __restrict__ Sc, E* __restrict__ Utg) {
+struct RecurPtrs {
+    const E *qg, *kg, *kt, *tb, *mm, *v;
+    const float* gam;
+    int64_t ops_step;     // elements between consecutive chunks of one head (C x D operands)
+    int64_t sq_step;      // elements between consecutive chunks of one head (C x C operands)
+    int64_t gam_step;     // floats between consecutive chunks of one head
+    int64_t tok_step;     // elements between consecutive chunks in [T, H, D] tensors
+};
+
+// The operand loads of one chunk, in three groups that k_recur issues at
+// three different points of a step, so the memory pipeline drains them in
+// the background of the matrix work instead of stalling one burst.
+// P.qg / P.kg / P.kt / P.tb / P.mm point at this lane's first 16-byte vector
+// of chunk 0; vectors of one lane are 64 vectors apart.
+template <typename E, int D, int CT>
+__device__ inline void recur_load_a(RecurIn<E, D, CT>& in, const RecurPtrs<E, D>& P, int j) {
+    using G = Geo<E, D>;
+    const uint4* qg = reinterpret_cast<const uint4*>(P.qg + j * P.ops_step);
+    const uint4* kg = reinterpret_cast<const uint4*>(P.kg + j * P.ops_step);
+#pragma unroll
+    for (int i = 0; i < G::VPL; ++i) {
+        in.qg[i] = qg[i * 64];
+        in.kg[i] = kg[i * 64];
+    }
+}
+
+template <typename E, int D, int CT>
+__device__ inline void recur_load_b(RecurIn<E, D, CT>& in, const RecurPtrs<E, D>& P, int j) {
+    using G = Geo<E, D>;
+    constexpr int RT = D / 64;
+    const int w = wave_id();
+    const uint4* kt = reinterpret_cast<const uint4*>(P.kt + j * P.ops_step);
+#pragma unroll
+    for (int v = 0; v < G::NVT; ++v)
+#pragma unroll
+        for (int a = 0; a < RT; ++a) in.kt[a][v] = kt[(a * G::NVT + v) * 64];
+#pragma unroll
+    for (int a = 0; a < RT; ++a)
+        in.gam[a] = *reinterpret_cast<const f32x4*>(P.gam + j * P.gam_step + kSub * (RT * w + a));
+}
+
+template <typename E, int D, int CT>
+__device__ inline void recur_load_c(RecurIn<E, D, CT>& in, const RecurPtrs<E, D>& P, int j, int len) {
+    using G = Geo<E, D>;
+    const int w = wave_id(), lg = lane_id() >> 4;
+    const uint4* tb = reinterpret_cast<const uint4*>(P.tb + j * P.sq_step);
+    const uint4* mm = reinterpret_cast<const uint4*>(P.mm + j * P.sq_step);
+#pragma unroll
+    for (int v = 0; v < G::NVT; ++v) {
+        in.tb[v] = tb[v * 64];
+        in.mm[v] = mm[v * 64];
+    }
+    in.len = len;
+    const E* vj = P.v + j * P.tok_step;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int t = kSub * w + 4 * lg + r;
+        const int64_t roff = (int64_t)(t < len ? t : len - 1) * ((int64_t)(P.tok_step / kChunk));
+#pragma unroll
+        for (int c = 0; c < CT; ++c) in.v[c][r] = vj[roff + kSub * c];
+    }
+}
+
+template <typename E, int D, int CT>
+__global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, ChunkOps ops,
+                                                    const int32_t* __restrict__ cu, int64_t total_tokens,
+                                                    int64_t fixed_len, const int32_t* __restrict__ seq_chunk0,
+                                                    int32_t NH, int32_t H, const float* __restrict__ S0,
+                                                    float* __restrict__ ST, E* __restrict__ o) {
+    using G = Geo<E, D>;
     using M = Mma<E>;
-    constexpr int C = kChunk;
-    constexpr int NS = D / kSlab;          // slabs per head
-    constexpr int RT = D / 64;             // 16-row state tiles per wave
-    constexpr int PS = D + 8, PW = D + 8, PK = C + 8, PU = C + 8;
-    __shared__ __attribute__((aligned(16))) E sSt[kSlab * PS];   // S^T  [col][channel]
-    __shared__ __attribute__((aligned(16))) E sW[C * PW];        // W    [token][channel]
-    __shared__ __attribute__((aligned(16))) E sKt[D * PK];       // K^T  [channel][token]
-    __shared__ __attribute__((aligned(16))) E sUt[kSlab * PU];   // U~^T [col][token]
-    __shared__ float sGam[D];
+    using F = typename M::frag;
+    constexpr int C = kChunk, CPL = G::CPL;
+    constexpr int SW = kSub * CT;      // slab width (value columns)
+    constexpr int NS = D / SW;         // slabs per head
+    constexpr int RT = D / 64;         // key-channel tiles of S per wave
+    constexpr int PS = D + 8;          // pitch of S^T      [col][channel]
+    constexpr int PY = C + 8;          // pitch of Y^T, U~^T [col][token]
+    __shared__ __attribute__((aligned(16))) E sSt[SW * PS];
+    __shared__ __attribute__((aligned(16))) E sYt[SW * PY];
+    __shared__ __attribute__((aligned(16))) E sUt[SW * PY];
 
-    const int sl = blockIdx.x % NS;
-    const int h = (blockIdx.x / NS) % H;
-    const int n = blockIdx.x / (NS * H);
-    const int tid = threadIdx.x, wave = wave_id(), li = lane_id() & 15, lg = lane_id() >> 4;
+    // Workgroup -> (sequence*head, slab).  When the (sequence, head) count is
+    // a multiple of 8, all slabs of one (sequence, head) get workgroup ids
+    // congruent mod 8 and so run on one XCD, sharing that XCD's L2 for the
+    // chunk operands.
+    int nh, sl;
+    {
+        const int bid = blockIdx.x;
+        if (NH % 8 == 0) {
+            sl = (bid / 8) % NS;
+            nh = (bid % 8) + 8 * (bid / (8 * NS));
+        } else {
+            sl = bid % NS;
+            nh = bid / NS;
+        }
+    }
+    const int n = nh / H, h = nh % H;
+    const int w = wave_id(), li = lane_id() & 15, lg = lane_id() >> 4;
+    const int col0 = sl * SW;
     const int64_t rs = (int64_t)H * D;
-    const int col0 = sl * kSlab;
 
-    // S[a][b][rr] = state[channel 16*(RT*wave + a) + 4*lg + rr][column col0 + 16*b + li]
-    f32x4 S[RT][2];
+    // Chunks of this sequence: c0 .. c0 + nch - 1 (the same list k_prep walked).
+    int64_t s_start, s_len;
+    seq_range(cu, n, total_tokens, fixed_len, s_start, s_len);
+    const int32_t c0 = seq_chunk0[n];
+    int32_t nch = (int32_t)((s_len + C - 1) / C);
+    if (nch > seq_chunk0[n + 1] - c0) nch = seq_chunk0[n + 1] - c0;
+
+    RecurPtrs<E, D> P;
+    {
+        const int64_t cb = (int64_t)h * ops.max_chunks + c0;   // head-major operand slot
+        const int tok = kSub * w + li;
+        P.ops_step = (int64_t)C * D;
+        P.sq_step = (int64_t)C * C;
+        P.gam_step = (int64_t)D;
+        P.tok_step = (int64_t)C * rs;
+        const int lane = lane_id();
+        P.qg = static_cast<const E*>(ops.Qg) + cb * C * D + (int64_t)(w * G::VPL * 64 + lane) * G::EPV;
+        P.kg = static_cast<const E*>(ops.Kg) + cb * C * D + (int64_t)(w * G::VPL * 64 + lane) * G::EPV;
+        P.kt = static_cast<const E*>(ops.KhT) + cb * D * C + (int64_t)(RT * w * G::NVT * 64 + lane) * G::EPV;
+        P.tb = static_cast<const E*>(ops.TB) + cb * C * C + (int64_t)(w * G::NVT * 64 + lane) * G::EPV;
+        P.mm = static_cast<const E*>(ops.Mm) + cb * C * C + (int64_t)(w * G::NVT * 64 + lane) * G::EPV;
+        (void)tok;
+        P.gam = ops.gam + cb * D + 4 * lg;
+        P.v = v + (s_start * H + h) * D + col0 + li;
+    }
+    E* const o_base = o + (s_start * H + h) * D + col0 + li;
+
+    // S[a][c][r] = state[channel 16*(RT*w + a) + 4*lg + r][column col0 + 16*c + li]
+    f32x4 S[RT][CT];
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
 #pragma unroll
     for (int a = 0; a < RT; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int c = 0; c < CT; ++c)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int ch = kSub * (RT * wave + a) + 4 * lg + rr;
-                S[a][b][rr] = S0 ? S0[sbase + (int64_t)ch * D + col0 + kSub * b + li] : 0.f;
+            for (int r = 0; r < 4; ++r) {
+                const int ch = kSub * (RT * w + a) + 4 * lg + r;
+                S[a][c][r] = S0 ? S0[sbase + (int64_t)ch * D + col0 + kSub * c + li] : 0.f;
             }
+    auto put_state = [&]() {
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sSt[(kSub * c + li) * PS + kSub * (RT * w + a) + 4 * lg + r] = from_f<E>(S[a][c][r]);
+    };
+    put_state();
 
-    const int32_t c_begin = seq_chunk0[n], c_end = seq_chunk0[n + 1];
-    for (int32_t ci = c_begin; ci < c_end; ++ci) {
-        const ChunkInfo info = tab[ci];
-        const int len = info.len;
-        const int64_t base = (info.tok0 * H + h) * D;
-        const int64_t cbase = ((int64_t)ci * H + h) * D;
-        // S (operand dtype) to LDS as S^T and to the workspace for the output kernel
+    auto chunk_len = [&](int j) -> int {
+        const int64_t rem = s_len - (int64_t)j * C;
+        return (int)(rem < C ? rem : C);
+    };
+
+    // One chunk step with the operands in `cur`; meanwhile the operands of
+    // chunk jp (clamped to the last chunk) are loaded into `pre`, one group
+    // after each barrier.  The scheduling barriers keep the three load groups
+    // where they are placed.
+    auto step = [&](const RecurIn<E, D, CT>& cur, int j, RecurIn<E, D, CT>& pre, int jp) {
+        jp = jp < nch ? jp : nch - 1;
+        __syncthreads();   // S^T of the previous step is in LDS
+        __builtin_amdgcn_sched_barrier(0);
+        recur_load_a<E, D, CT>(pre, P, jp);
+        __builtin_amdgcn_sched_barrier(0);
+        const F* fq = reinterpret_cast<const F*>(cur.qg);
+        const F* fk = reinterpret_cast<const F*>(cur.kg);
+        const F* ftb = reinterpret_cast<const F*>(cur.tb);
+        const F* fmm = reinterpret_cast<const F*>(cur.mm);
+        // X = (K . Gamma) S and P = (Q . Gamma) S for token rows 16w..
+        f32x4 accX[CT], accO[CT];
 #pragma unroll
-        for (int a = 0; a < RT; ++a)
+        for (int c = 0; c < CT; ++c) {
+            accX[c] = zero4();
+            accO[c] = zero4();
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int ch = kSub * (RT * wave + a) + 4 * lg + rr, col = kSub * b + li;
-                    const E sv = from_f<E>(S[a][b][rr]);
-                    sSt[col * PS + ch] = sv;
-                    Sc[(cbase + col0 + col) * D + ch] = sv;
-                }
-        for (int idx = tid; idx < C * D; idx += kThreads) {
-            const int r = idx / D, c = idx % D;
-            const bool ok = r < len;
-            sW[r * PW + c] = ok ? W[base + (int64_t)r * rs + c] : from_f<E>(0.f);
-            sKt[c * PK + r] = ok ? Kh[base + (int64_t)r * rs + c] : from_f<E>(0.f);
-        }
-        for (int c = tid; c < D; c += kThreads) sGam[c] = gam[cbase + c];
-        __syncthreads();
-        // U~ = U - W S : wave -> token rows 16*wave.., two 16-column tiles
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            f32x4 acc = zero4();
-#pragma unroll
-            for (int k0 = 0; k0 < D; k0 += M::KS)
-                acc = M::mma(M::load(&sW[(kSub * wave + li) * PW + k0 + lg * M::KW]),
-                             M::load(&sSt[(kSub * b + li) * PS + k0 + lg * M::KW]), acc);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int tok = kSub * wave + 4 * lg + rr, col = kSub * b + li;
-                const float u = tok < len ? to_f(U[base + (int64_t)tok * rs + col0 + col]) : 0.f;
-                const E ut = from_f<E>(tok < len ? u - acc[rr] : 0.f);
-                sUt[col * PU + tok] = ut;
-                Utg[(cbase + col0 + col) * C + tok] = ut;
+            for (int m = 0; m < G::NKC; ++m) {
+                const F bs = M::load(&sSt[(kSub * c + li) * PS + lg * CPL + m * M::KW]);
+                accX[c] = M::mma(fk[m], bs, accX[c]);
+                accO[c] = M::mma(fq[m], bs, accO[c]);
             }
         }
+        // Y = V - X, transposed to LDS
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = kSub * w + 4 * lg + r;
+                const float vv = t < cur.len ? to_f(cur.v[c][r]) : 0.f;
+                sYt[(kSub * c + li) * PY + t] = from_f<E>(vv - accX[c][r]);
+            }
         __syncthreads();
-        // S <- Diag(Gamma_L) S + K^T U~
+        __builtin_amdgcn_sched_barrier(0);
+        recur_load_b<E, D, CT>(pre, P, jp);
+        __builtin_amdgcn_sched_barrier(0);
+        // U~ = T diag(beta) Y  (rows 16w..; k-steps past the diagonal block skipped)
 #pragma unroll
-        for (int a = 0; a < RT; ++a)
+        for (int c = 0; c < CT; ++c) {
+            f32x4 accU = zero4();
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
+            for (int m = 0; m < G::NKT; ++m)
+                accU = M::mma(ftb[m], M::load(&sYt[(kSub * c + li) * PY + m * M::KS + lg * M::KW]), accU);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sUt[(kSub * c + li) * PY + kSub * w + 4 * lg + r] = from_f<E>(accU[r]);
+        }
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        recur_load_c<E, D, CT>(pre, P, jp, chunk_len(jp));
+        __builtin_amdgcn_sched_barrier(0);
+        // S <- Diag(Gamma_L) S + K^T U~, then O = P + M U~ -> output rows 16w..
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+            F bu[G::NKT];
+#pragma unroll
+            for (int m = 0; m < G::NKT; ++m) bu[m] = M::load(&sUt[(kSub * c + li) * PY + m * M::KS + lg * M::KW]);
+#pragma unroll
+            for (int a = 0; a < RT; ++a) {
                 f32x4 acc = zero4();
+                const F* fkt = reinterpret_cast<const F*>(cur.kt[a]);
 #pragma unroll
-                for (int k0 = 0; k0 < C; k0 += M::KS)
-                    acc = M::mma(M::load(&sKt[(kSub * (RT * wave + a) + li) * PK + k0 + lg * M::KW]),
-                                 M::load(&sUt[(kSub * b + li) * PU + k0 + lg * M::KW]), acc);
+                for (int m = 0; m < G::NKT; ++m) acc = M::mma(fkt[m], bu[m], acc);
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int ch = kSub * (RT * wave + a) + 4 * lg + rr;
-                    S[a][b][rr] = sGam[ch] * S[a][b][rr] + acc[rr];
-                }
+                for (int r = 0; r < 4; ++r) S[a][c][r] = cur.gam[a][r] * S[a][c][r] + acc[r];
             }
-        __syncthreads();
+#pragma unroll
+            for (int m = 0; m < G::NKT; ++m) accO[c] = M::mma(fmm[m], bu[m], accO[c]);
+        }
+        // S^T is last read before the Y barrier of this step, so writing it
+        // here is safe; the barrier at the top of the next step publishes it.
+        put_state();
+        E* oj = o_base + (int64_t)j * C * rs;
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = kSub * w + 4 * lg + r;
+                if (t < cur.len) oj[(int64_t)t * rs + kSub * c] = from_f<E>(accO[c][r]);
+            }
+    };
+
+    // Three operand buffers in rotation: while chunk j is processed, the
+    // operands of chunk j+1 are already in flight and those of chunk j+2 are
+    // issued.  Prefetching is unconditional (indices are clamped to the last
+    // chunk): with no path that skips it, the compiler's load counters let
+    // the prefetched loads stay outstanding across whole steps instead of
+    // draining them before the first matrix product.
+    RecurIn<E, D, CT> A, B, Cb;
+    if (nch > 0) {
+        auto prefetch_all = [&](RecurIn<E, D, CT>& buf, int jj) {
+            jj = jj < nch ? jj : nch - 1;
+            recur_load_a<E, D, CT>(buf, P, jj);
+            recur_load_b<E, D, CT>(buf, P, jj);
+            recur_load_c<E, D, CT>(buf, P, jj, chunk_len(jj));
+        };
+        prefetch_all(A, 0);
+        prefetch_all(B, 1);
+        for (int j = 0; j < nch; j += 3) {
+            step(A, j, Cb, j + 2);
+            if (j + 1 >= nch) break;
+            step(B, j + 1, A, j + 3);
+            if (j + 2 >= nch) break;
+            step(Cb, j + 2, B, j + 4);
+        }
     }
     if (ST) {
 #pragma unroll
         for (int a = 0; a < RT; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int c = 0; c < CT; ++c)
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int ch = kSub * (RT * wave + a) + 4 * lg + rr;
-                    ST[sbase + (int64_t)ch * D + col0 + kSub * b + li] = S[a][b][rr];
+                for (int r = 0; r < 4; ++r) {
+                    const int ch = kSub * (RT * w + a) + 4 * lg + r;
+                    ST[sbase + (int64_t)ch * D + col0 + kSub * c + li] = S[a][c][r];
                 }
-    }
-}
-
-// ---------------------------------------------------------------- output
-// O = (Q . Gamma) S + M U~ per chunk and head.
-template <typename E, int D>
-__global__ __launch_bounds__(kThreads) void k_output(const E* __restrict__ q, const E* __restrict__ k,
-                                                     const float* __restrict__ bcum,
-                                                     const E* __restrict__ Sc, const E* __restrict__ Utg,
-                                                     const ChunkInfo* __restrict__ tab,
-                                                     const int32_t* __restrict__ n_chunks_p, int32_t H,
-                                                     E* __restrict__ o) {
-    using M = Mma<E>;
-    constexpr int C = kChunk;
-    constexpr int PE = D + 8, PB = D + 4, PM = C + 8, PS = D + 8, PU = C + 8;
-    __shared__ __attribute__((aligned(16))) E sQ[C * PE];
-    __shared__ __attribute__((aligned(16))) E sK[C * PE];
-    __shared__ __attribute__((aligned(16))) float sB[C * PB];
-    __shared__ __attribute__((aligned(16))) E sM[C * PM];
-    __shared__ __attribute__((aligned(16))) E sSt[D * PS];
-    __shared__ __attribute__((aligned(16))) E sUt[D * PU];
-
-    const int32_t ci = blockIdx.x;
-    if (ci >= *n_chunks_p) return;
-    const ChunkInfo info = tab[ci];
-    const int h = blockIdx.y;
-    const int len = info.len;
-    const int tid = threadIdx.x, wave = wave_id(), li = lane_id() & 15, lg = lane_id() >> 4;
-    const int64_t rs = (int64_t)H * D;
-    const int64_t base = (info.tok0 * H + h) * D;
-    const int64_t cbase = ((int64_t)ci * H + h) * D;
-
-    for (int idx = tid; idx < C * D; idx += kThreads) {
-        const int r = idx / D, c = idx % D;
-        const bool ok = r < len;
-        const int64_t off = base + (int64_t)(ok ? r : len - 1) * rs + c;
-        sQ[r * PE + c] = ok ? q[off] : from_f<E>(0.f);
-        sK[r * PE + c] = ok ? k[off] : from_f<E>(0.f);
-        sB[r * PB + c] = bcum[off];
-    }
-    for (int idx = tid; idx < D * D; idx += kThreads) {
-        const int col = idx / D, ch = idx % D;
-        sSt[col * PS + ch] = Sc[(cbase + col) * D + ch];
-    }
-    for (int idx = tid; idx < D * C; idx += kThreads) {
-        const int col = idx / C, tok = idx % C;
-        sUt[col * PU + tok] = Utg[(cbase + col) * C + tok];
-    }
-    __syncthreads();
-    // M = Tril_incl(decayed Q K^T), 10 blocks; upper blocks zero
-    for (int blk = wave; blk < 10; blk += 4) {
-        int R, J;
-        block_of(blk, R, J);
-        const f32x4 acc = decayed_gram_block<E, D, PE, PB>(sQ, sK, sB, R, J);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = kSub * R + 4 * lg + rr, col = kSub * J + li;
-            sM[row * PM + col] = from_f<E>((J < R || col <= row) ? acc[rr] : 0.f);
-        }
-    }
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        const int r = idx / C, c = idx % C;
-        if ((c >> 4) > (r >> 4)) sM[r * PM + c] = from_f<E>(0.f);
-    }
-    __syncthreads();
-    // Q . Gamma in place
-    for (int idx = tid; idx < C * D; idx += kThreads) {
-        const int r = idx / D, c = idx % D;
-        sQ[r * PE + c] = from_f<E>(to_f(sQ[r * PE + c]) * __expf(sB[r * PB + c]));
-    }
-    __syncthreads();
-    constexpr int NCT = D / kSub;
-    for (int t = wave; t < kNSub * NCT; t += 4) {
-        const int R = t / NCT, ct = t % NCT;
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < D; k0 += M::KS)
-            acc = M::mma(M::load(&sQ[(kSub * R + li) * PE + k0 + lg * M::KW]),
-                         M::load(&sSt[(kSub * ct + li) * PS + k0 + lg * M::KW]), acc);
-        const int kend = ((kSub * (R + 1) + M::KS - 1) / M::KS) * M::KS;
-        for (int k0 = 0; k0 < kend; k0 += M::KS)
-            acc = M::mma(M::load(&sM[(kSub * R + li) * PM + k0 + lg * M::KW]),
-                         M::load(&sUt[(kSub * ct + li) * PU + k0 + lg * M::KW]), acc);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int row = kSub * R + 4 * lg + rr;
-            if (row < len) o[base + (int64_t)row * rs + kSub * ct + li] = from_f<E>(acc[rr]);
-        }
     }
 }
 
 // ---------------------------------------------------------------- launch sequence
 // `ev`, when given, holds kNumStages + 1 events: ev[i] is recorded before
-// stage i and ev[kNumStages] after the last one (stages that do not run for
-// these sizes still get their pair of records, with nothing between them).
+// stage i and ev[kNumStages] after the last one (a stage that does not run
+// for these sizes still gets its pair of records, with nothing between them).
 template <typename E, int D>
 static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     auto mark = [&](int i) {
-        if (ev) hipEventRecord(ev[i], st);
+        if (ev) (void)hipEventRecord(ev[i], st);
     };
+    constexpr int CT = 1;
     const E* q = static_cast<const E*>(p.q);
     const E* kk = static_cast<const E*>(p.k);
     const E* v = static_cast<const E*>(p.v);
     const E* beta = static_cast<const E*>(p.beta);
     const E* g = static_cast<const E*>(p.g);
-    E* W = static_cast<E*>(p.ws_W);
-    E* U = static_cast<E*>(p.ws_U);
-    E* Kh = static_cast<E*>(p.ws_Kh);
-    E* Sc = static_cast<E*>(p.ws_Sc);
-    E* Ut = static_cast<E*>(p.ws_Ut);
+    ChunkOps ops{p.ws_TB, p.ws_M, p.ws_Qg, p.ws_Kg, p.ws_KhT, p.ws_gam, p.max_chunks};
     const int32_t H = p.n_heads;
-
+    const int32_t NH = p.n_seqs * H;
     const bool work = p.total_tokens > 0;
-    const dim3 cgrid(p.max_chunks, H);
+
     mark(0);
     hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(1024), 0, st, p.cu_seqlens, p.n_seqs, p.total_tokens,
                        p.fixed_len, p.max_chunks, p.ws_tab, p.ws_seq_chunk0, p.ws_n_chunks);
     mark(1);
-    if (work) hipLaunchKernelGGL((k_cumsum<E, D>), cgrid, dim3(D), 0, st, g, p.ws_tab, p.ws_n_chunks, H, p.ws_b);
+    if (work)
+        hipLaunchKernelGGL((k_prep<E, D>), dim3(p.max_chunks, H), dim3(kThreads), 0, st, q, kk, g, beta, p.ws_tab,
+                           p.ws_n_chunks, H, ops);
     mark(2);
-    if (work)
-        hipLaunchKernelGGL((k_wy<E, D>), cgrid, dim3(kThreads), 0, st, kk, v, beta, p.ws_b, p.ws_tab,
-                           p.ws_n_chunks, H, W, U, Kh, p.ws_gam);
+    hipLaunchKernelGGL((k_recur<E, D, CT>), dim3(NH * (D / (kSub * CT))), dim3(kThreads), 0, st, v, ops,
+                       p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, H, p.S0, p.S_T,
+                       static_cast<E*>(p.o));
     mark(3);
-    hipLaunchKernelGGL((k_state<E, D>), dim3(p.n_seqs * H * (D / kSlab)), dim3(kThreads), 0, st, W, U, Kh,
-                       p.ws_gam, p.ws_tab, p.ws_seq_chunk0, H, p.S0, p.S_T, Sc, Ut);
-    mark(4);
-    if (work)
-        hipLaunchKernelGGL((k_output<E, D>), cgrid, dim3(kThreads), 0, st, q, kk, p.ws_b, Sc, Ut, p.ws_tab,
-                           p.ws_n_chunks, H, static_cast<E*>(p.o));
-    mark(5);
     return hipGetLastError();
 }
 
-const char* const kStageNames[kNumStages] = {"k_chunk_table", "k_cumsum", "k_wy", "k_state", "k_output"};
+const char* const kStageNames[kNumStages] = {"k_chunk_table", "k_prep", "k_recur"};
 
 hipError_t launch(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     if (p.bf16) {
         if (p.d == 128) return launch_all<__bf16, 128>(p, st, ev);
         return launch_all<__bf16, 64>(p, st, ev);
     }
-    // fp32 operands are built for d = 64 only (their LDS tiles at d = 128
-    // exceed one workgroup's LDS); the C ABI rejects other sizes.
+    // fp32 operands are built for d = 64 only; the C ABI rejects other sizes.
     return launch_all<float, 64>(p, st, ev);
 }
 

@@ -140,7 +140,7 @@ def parity_error(x, ref, cu_seqlens=None, token_axis=0, head_axis=1, floor=1e-30
     sequence axis (each [n, h] slice is one state).  `floor` keeps a slice
     whose reference has decayed below any fp32-meaningful scale (a state
     decayed by e^-750 is ~1e-326) from turning rounding to zero into a
-    relative error of 1."""
+    relative error of 1.  Any non-finite value in `x` gives inf."""
     x = np.asarray(x, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert x.shape == ref.shape, (x.shape, ref.shape)
@@ -158,8 +158,9 @@ def parity_error(x, ref, cu_seqlens=None, token_axis=0, head_axis=1, floor=1e-30
         for h in range(x.shape[head_axis]):
             xh = np.take(xs, h, axis=head_axis)
             rh = np.take(rs, h, axis=head_axis)
+            if not np.all(np.isfinite(xh)):
+                return float("inf")
             den = max(float(np.max(np.abs(rh))), floor)
             num = float(np.max(np.abs(xh - rh)))
-            err = num / den
-            worst = max(worst, float(err))
+            worst = max(worst, num / den)
     return worst

@@ -310,3 +310,12 @@ def test_parity_metric():
     S2 = S.copy()
     S2[1, 1, 2, 2] = 1.03
     assert math.isclose(oracle.parity_error(S2, S), 0.03, rel_tol=1e-9)
+
+
+def test_parity_metric_rejects_nonfinite():
+    ref = np.ones((4, 1, 2))
+    x = ref.copy()
+    x[2, 0, 1] = np.nan
+    assert oracle.parity_error(x, ref) == float("inf")
+    x[2, 0, 1] = np.inf
+    assert oracle.parity_error(x, ref) == float("inf")
