@@ -748,6 +748,366 @@ __global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, Chu
     }
 }
 
+// ---------------------------------------------------------------- k_recur_lds
+// bf16 form of k_recur with producer waves.  The chunk operands travel
+// global -> LDS by direct loads (global_load_lds_dwordx4: each lane moves 16
+// bytes to LDS at M0 + 16 * lane), issued by four producer waves that do
+// nothing else, one per compute wave.  A wave issues its instructions in
+// order, so a compute wave that issued its own share of the loads would sit
+// behind them for as long as the CU needs to stream a chunk's operands; with
+// producers the streaming overlaps the compute waves' matrix work.  (One
+// producer is not enough: a single wave moves about 1 KB per 80 clocks this
+// way, so the load issue is spread over four.)
+//
+// Buffers: two, alternating by chunk parity.  While the compute waves work on
+// chunk j from one, the producers fill the other with chunk j+1 and wait for
+// their loads before the barrier that opens step j+1.  The two are distinct
+// LDS arrays so that the compiler can tell the producers' loads into one
+// from reads of the other.  Synchronisation is plain s_barrier with explicit
+// counter waits: the workgroup fence of __syncthreads would drain the
+// producers' in-flight loads at every barrier.
+//
+// L2 warm-up: three chunks ahead, the producers read one dword of each
+// 128-byte line of a share of that chunk's data (operands, Gamma_L and the
+// head's value rows); the slab workgroups of a head take disjoint shares, so
+// the direct loads of every slab later hit L2 rather than HBM.  These reads
+// are issued last in a step and left in flight by the wait that ends it:
+// vector memory operations of a wave complete in issue order.
+#define KDA_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4 (7 = no wait), lgkmcnt in 11:8 (15 = no wait).
+constexpr unsigned waitcnt_imm(int vm, int lgkm) {
+    return (unsigned)((vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8));
+}
+template <int VM, int LGKM>
+__device__ inline void wait_counts() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(VM, LGKM));
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// This wave's LDS operations complete, then workgroup barrier.
+__device__ inline void barrier_lds() {
+    wait_counts<63, 0>();
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+constexpr int kRecurWaves = 4;                              // compute waves
+constexpr int kRecurLdsThreads = 2 * kRecurWaves * 64;       // + as many producers
+
+// Buffer layout: one region per compute wave w, in 1 KB blocks (64 lanes x
+// 16 bytes: the fragment-major tiles of k_prep copied as they are):
+//   [kQg, +VPL)  Q . Gamma, row tile w       [kKg, +VPL)  K . Gamma, row tile w
+//   [kTb, +NVT)  T diag(beta), row tile w    [kMm, +NVT)  M, row tile w
+//   [kKt, +RT*NVT) K^T, channel tiles RT*w ..
+//   kMisc: bytes [0, 512) value rows 16w .. 16w+15 x the slab's 16 columns
+//          (bf16, row-major); bytes [512, 512 + 64 RT) Gamma_L of channels
+//          16 RT w .. (fp32); the rest unused.
+template <int D>
+struct LdsGeo {
+    using G = Geo<__bf16, D>;
+    static constexpr int RT = D / 64;
+    static constexpr int kQg = 0;
+    static constexpr int kKg = kQg + G::VPL;
+    static constexpr int kTb = kKg + G::VPL;
+    static constexpr int kMm = kTb + G::NVT;
+    static constexpr int kKt = kMm + G::NVT;
+    static constexpr int kMisc = kKt + RT * G::NVT;
+    static constexpr int kBlocks = kMisc + 1;
+    static constexpr int kWaveVec = kBlocks * 64;     // 16-byte vectors per compute wave per buffer
+    static constexpr int kBufVec = kRecurWaves * kWaveVec;
+};
+
+template <int D>
+__global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
+    const __bf16* __restrict__ v, ChunkOps ops, const int32_t* __restrict__ cu, int64_t total_tokens,
+    int64_t fixed_len, const int32_t* __restrict__ seq_chunk0, int32_t NH, int32_t H, const float* __restrict__ S0,
+    float* __restrict__ ST, __bf16* __restrict__ o) {
+    using E = __bf16;
+    using G = Geo<E, D>;
+    using L = LdsGeo<D>;
+    using M = Mma<E>;
+    using F = typename M::frag;
+    static_assert(G::VPL == G::NKC && G::NVT == G::NKT, "one 16-byte vector per bf16 fragment");
+    static_assert(kRecurWaves == kNSub, "one compute wave per 16-token row tile");
+    constexpr int C = kChunk, CPL = G::CPL, RT = L::RT;
+    constexpr int SW = kSub;           // slab width (value columns)
+    constexpr int NS = D / SW;         // slabs per head
+    constexpr int PS = D + 8;          // pitch of S^T      [col][channel]
+    constexpr int PY = C + 8;          // pitch of Y^T, U~^T [col][token]
+    __shared__ __attribute__((aligned(16))) uint4 sBuf0[L::kBufVec];
+    __shared__ __attribute__((aligned(16))) uint4 sBuf1[L::kBufVec];
+    __shared__ __attribute__((aligned(16))) E sSt[SW * PS];
+    __shared__ __attribute__((aligned(16))) E sYt[SW * PY];
+    __shared__ __attribute__((aligned(16))) E sUt[SW * PY];
+
+    // Workgroup -> (sequence*head, slab); slabs of one (sequence, head) share
+    // an XCD (and its L2) when the (sequence, head) count is a multiple of 8.
+    int nh, sl;
+    {
+        const int bid = blockIdx.x;
+        if (NH % 8 == 0) {
+            sl = (bid / 8) % NS;
+            nh = (bid % 8) + 8 * (bid / (8 * NS));
+        } else {
+            sl = bid % NS;
+            nh = bid / NS;
+        }
+    }
+    const int n = nh / H, h = nh % H;
+    const int w = wave_id(), lane = lane_id(), li = lane & 15, lg = lane >> 4;
+    const int col0 = sl * SW;
+    const int64_t rs = (int64_t)H * D;
+
+    int64_t s_start, s_len;
+    seq_range(cu, n, total_tokens, fixed_len, s_start, s_len);
+    const int32_t c0 = seq_chunk0[n];
+    int32_t nch = (int32_t)((s_len + C - 1) / C);
+    if (nch > seq_chunk0[n + 1] - c0) nch = seq_chunk0[n + 1] - c0;
+    const int64_t cb = (int64_t)h * ops.max_chunks + c0;   // head-major operand slot of chunk 0
+    auto chunk_len = [&](int j) -> int {
+        const int64_t rem = s_len - (int64_t)j * C;
+        return (int)(rem < C ? rem : C);
+    };
+
+    if (w >= kRecurWaves) {
+        // ------------------------------------------------ producer waves
+        const int cw = w - kRecurWaves;   // the compute wave whose operands this wave loads
+        const E* qg = static_cast<const E*>(ops.Qg) + cb * C * D + lane * G::EPV;
+        const E* kg = static_cast<const E*>(ops.Kg) + cb * C * D + lane * G::EPV;
+        const E* kt = static_cast<const E*>(ops.KhT) + cb * D * C + lane * G::EPV;
+        const E* tb = static_cast<const E*>(ops.TB) + cb * C * C + lane * G::EPV;
+        const E* mm = static_cast<const E*>(ops.Mm) + cb * C * C + lane * G::EPV;
+        const E* vv = v + (s_start * H + h) * D + col0 + 8 * (lane & 1);
+        const int gi = (lane >= 32 && lane < 32 + 4 * RT) ? lane - 32 : 0;
+        const float* gm = ops.gam + cb * D + 4 * gi;
+        auto dma = [](const void* src, uint4* lds) {
+            __builtin_amdgcn_global_load_lds(src, KDA_LDS_PTR(lds), 16, 0, 0);
+        };
+        auto issue = [&](uint4* buf, int j) {
+            const int len = chunk_len(j);
+            const int64_t oo = (int64_t)j * C * D, so = (int64_t)j * C * C;
+            {
+                uint4* dst = buf + cw * L::kWaveVec;
+#pragma unroll
+                for (int i = 0; i < G::VPL; ++i) {
+                    dma(qg + oo + (cw * G::VPL + i) * 64 * G::EPV, dst + (L::kQg + i) * 64);
+                    dma(kg + oo + (cw * G::VPL + i) * 64 * G::EPV, dst + (L::kKg + i) * 64);
+                }
+#pragma unroll
+                for (int i = 0; i < G::NVT; ++i) {
+                    dma(tb + so + (cw * G::NVT + i) * 64 * G::EPV, dst + (L::kTb + i) * 64);
+                    dma(mm + so + (cw * G::NVT + i) * 64 * G::EPV, dst + (L::kMm + i) * 64);
+                }
+#pragma unroll
+                for (int i = 0; i < RT * G::NVT; ++i)
+                    dma(kt + oo + (cw * RT * G::NVT + i) * 64 * G::EPV, dst + (L::kKt + i) * 64);
+                int row = kSub * cw + (lane >> 1);
+                row = row < len ? row : len - 1;
+                const void* misc = lane < 32 ? static_cast<const void*>(vv + ((int64_t)j * C + row) * rs)
+                                             : static_cast<const void*>(gm + (int64_t)j * D + kSub * RT * cw);
+                dma(misc, dst + L::kMisc * 64);
+            }
+        };
+
+        // Warm-up lines of this slab: kTouch per producer lane, over one
+        // chunk's operands, Gamma_L and the head's value rows.
+        constexpr int kAhead = 3;
+        constexpr int64_t kBq = (int64_t)C * D * 2, kBs = (int64_t)C * C * 2;   // bytes per chunk slot
+        constexpr int kOpsLines = (int)((3 * kBq + 2 * kBs) / 128);
+        constexpr int kGamLines = D * 4 / 128;
+        constexpr int kVRowLines = D * 2 / 128;
+        constexpr int kLines = kOpsLines + kGamLines + kChunk * kVRowLines;
+        constexpr int kPerSlab = (kLines + NS - 1) / NS;
+        constexpr int kTouch = (kPerSlab + 64 * kRecurWaves - 1) / (64 * kRecurWaves);
+        const char* t_base[kTouch];   // line in chunk 0 (operands, Gamma_L) or at token 0 (value rows)
+        int64_t t_step[kTouch];       // bytes between chunks (operands, Gamma_L)
+        int t_vrow[kTouch];           // value row in the chunk, or -1
+#pragma unroll
+        for (int k = 0; k < kTouch; ++k) {
+            int q = cw * 64 + lane + 64 * kRecurWaves * k;
+            q = q < kPerSlab ? q : kPerSlab - 1;
+            int line = sl * kPerSlab + q;
+            line = line < kLines ? line : kLines - 1;
+            const int64_t off = (int64_t)line * 128;
+            t_vrow[k] = -1;
+            if (off < kBq) { t_base[k] = (const char*)ops.Qg + cb * kBq + off; t_step[k] = kBq; }
+            else if (off < 2 * kBq) { t_base[k] = (const char*)ops.Kg + cb * kBq + off - kBq; t_step[k] = kBq; }
+            else if (off < 3 * kBq) { t_base[k] = (const char*)ops.KhT + cb * kBq + off - 2 * kBq; t_step[k] = kBq; }
+            else if (off < 3 * kBq + kBs) { t_base[k] = (const char*)ops.TB + cb * kBs + off - 3 * kBq; t_step[k] = kBs; }
+            else if (line < kOpsLines) { t_base[k] = (const char*)ops.Mm + cb * kBs + off - 3 * kBq - kBs; t_step[k] = kBs; }
+            else if (line < kOpsLines + kGamLines) {
+                t_base[k] = (const char*)(ops.gam + cb * D) + (int64_t)(line - kOpsLines) * 128;
+                t_step[k] = (int64_t)D * 4;
+            } else {
+                const int vl = line - kOpsLines - kGamLines;
+                t_vrow[k] = vl / kVRowLines;
+                t_base[k] = (const char*)(v + (s_start * H + h) * D) + (int64_t)(vl % kVRowLines) * 128;
+                t_step[k] = 0;
+            }
+        }
+        // Reads one dword per line of chunk j + kAhead (clamped to the last chunk).
+        auto touch = [&](int j, unsigned (&out)[kTouch]) {
+            const int jt = j + kAhead < nch ? j + kAhead : nch - 1;
+#pragma unroll
+            for (int k = 0; k < kTouch; ++k) {
+                const char* p;
+                if (t_vrow[k] >= 0) {
+                    const int64_t tok = (int64_t)jt * C + t_vrow[k];
+                    p = t_base[k] + (tok < s_len ? tok : s_len - 1) * rs * 2;
+                } else {
+                    p = t_base[k] + jt * t_step[k];
+                }
+                out[k] = *reinterpret_cast<const unsigned*>(p);
+            }
+        };
+        // One step: open it, fill the other buffer with chunk j+1, warm up
+        // chunk j+kAhead, follow the compute waves' two inner barriers, then
+        // wait for the fill (the warm-up reads may stay in flight).  `tch`
+        // holds warm-up values read two steps ago, which have landed; using
+        // them keeps the reads from being optimised away.
+        auto pstep = [&](uint4* nxt, int j, unsigned (&tch)[kTouch]) {
+            barrier_lds();
+#pragma unroll
+            for (int k = 0; k < kTouch; ++k) asm volatile("" ::"v"(tch[k]));
+            if (j + 1 < nch) issue(nxt, j + 1);
+            touch(j, tch);
+            barrier_lds();
+            barrier_lds();
+            wait_counts<kTouch, 15>();
+        };
+        if (nch > 0) {
+            unsigned tA[kTouch], tB[kTouch];
+            issue(sBuf0, 0);
+            wait_counts<0, 15>();
+            touch(-2, tA);
+            touch(-1, tB);
+            for (int j = 0; j < nch; j += 2) {
+                pstep(sBuf1, j, tA);
+                if (j + 1 >= nch) break;
+                pstep(sBuf0, j + 1, tB);
+            }
+#pragma unroll
+            for (int k = 0; k < kTouch; ++k) asm volatile("" ::"v"(tA[k]), "v"(tB[k]));
+        }
+        wait_counts<0, 15>();   // no direct LDS load may outlive the workgroup
+        return;
+    }
+
+    // ---------------------------------------------------- compute waves
+    __bf16* const o_base = o + (s_start * H + h) * D + col0 + li;
+    // S[a][r] = state[channel 16*(RT*w + a) + 4*lg + r][column col0 + li]
+    f32x4 S[RT];
+    const int64_t sbase = ((int64_t)n * H + h) * D * D;
+#pragma unroll
+    for (int a = 0; a < RT; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ch = kSub * (RT * w + a) + 4 * lg + r;
+            S[a][r] = S0 ? S0[sbase + (int64_t)ch * D + col0 + li] : 0.f;
+        }
+    auto put_state = [&]() {
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sSt[li * PS + kSub * (RT * w + a) + 4 * lg + r] = from_f<E>(S[a][r]);
+    };
+    put_state();
+
+    auto step = [&](const uint4* buf, int j) {
+        const int len = chunk_len(j);
+        const uint4* cur = buf + w * L::kWaveVec;
+        barrier_lds();   // chunk j's operands are in `buf`; S^T of the previous step is in LDS
+        const F* fr = reinterpret_cast<const F*>(cur) + lane;
+        F fq[G::NKC], fk[G::NKC];
+#pragma unroll
+        for (int m = 0; m < G::NKC; ++m) {
+            fq[m] = fr[(L::kQg + m) * 64];
+            fk[m] = fr[(L::kKg + m) * 64];
+        }
+        // X = (K . Gamma) S and P = (Q . Gamma) S for token rows 16w..
+        f32x4 accX = zero4(), accO = zero4();
+#pragma unroll
+        for (int m = 0; m < G::NKC; ++m) {
+            const F bs = M::load(&sSt[li * PS + lg * CPL + m * M::KW]);
+            accX = M::mma(fk[m], bs, accX);
+            accO = M::mma(fq[m], bs, accO);
+        }
+        // Y = V - X, transposed to LDS (rows past the chunk end are zero)
+        const E* vrows = reinterpret_cast<const E*>(cur + L::kMisc * 64);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = kSub * w + 4 * lg + r;
+            const float vv = to_f(vrows[(4 * lg + r) * SW + li]);
+            sYt[li * PY + t] = from_f<E>(t < len ? vv - accX[r] : 0.f);
+        }
+        F ftb[G::NKT], fmm[G::NKT], fkt[RT][G::NKT];
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m) {
+            ftb[m] = fr[(L::kTb + m) * 64];
+            fmm[m] = fr[(L::kMm + m) * 64];
+        }
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int m = 0; m < G::NKT; ++m) fkt[a][m] = fr[(L::kKt + a * G::NKT + m) * 64];
+        f32x4 gam[RT];
+        const float* gl = reinterpret_cast<const float*>(cur + L::kMisc * 64) + 128;
+#pragma unroll
+        for (int a = 0; a < RT; ++a) gam[a] = *reinterpret_cast<const f32x4*>(gl + kSub * a + 4 * lg);
+        barrier_lds();
+        // U~ = T diag(beta) Y  (rows 16w..)
+        {
+            f32x4 accU = zero4();
+#pragma unroll
+            for (int m = 0; m < G::NKT; ++m)
+                accU = M::mma(ftb[m], M::load(&sYt[li * PY + m * M::KS + lg * M::KW]), accU);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sUt[li * PY + kSub * w + 4 * lg + r] = from_f<E>(accU[r]);
+        }
+        barrier_lds();
+        // S <- Diag(Gamma_L) S + K^T U~, then O = P + M U~ (rows 16w..)
+        F bu[G::NKT];
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m) bu[m] = M::load(&sUt[li * PY + m * M::KS + lg * M::KW]);
+#pragma unroll
+        for (int a = 0; a < RT; ++a) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int m = 0; m < G::NKT; ++m) acc = M::mma(fkt[a][m], bu[m], acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[a][r] = gam[a][r] * S[a][r] + acc[r];
+        }
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m) accO = M::mma(fmm[m], bu[m], accO);
+        // S^T is last read before the Y barrier of this step; the barrier at
+        // the top of the next step publishes the new one.
+        put_state();
+        E* oj = o_base + (int64_t)j * C * rs;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = kSub * w + 4 * lg + r;
+            if (t < len) oj[(int64_t)t * rs] = from_f<E>(accO[r]);
+        }
+    };
+
+    for (int j = 0; j < nch; j += 2) {
+        step(sBuf0, j);
+        if (j + 1 >= nch) break;
+        step(sBuf1, j + 1);
+    }
+    if (ST) {
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ch = kSub * (RT * w + a) + 4 * lg + r;
+                ST[sbase + (int64_t)ch * D + col0 + li] = S[a][r];
+            }
+    }
+}
+
 // ---------------------------------------------------------------- launch sequence
 // `ev`, when given, holds kNumStages + 1 events: ev[i] is recorded before
 // stage i and ev[kNumStages] after the last one (a stage that does not run
@@ -776,9 +1136,13 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         hipLaunchKernelGGL((k_prep<E, D>), dim3(p.max_chunks, H), dim3(kThreads), 0, st, q, kk, g, beta, p.ws_tab,
                            p.ws_n_chunks, H, ops);
     mark(2);
-    hipLaunchKernelGGL((k_recur<E, D, CT>), dim3(NH * (D / (kSub * CT))), dim3(kThreads), 0, st, v, ops,
-                       p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, H, p.S0, p.S_T,
-                       static_cast<E*>(p.o));
+    if constexpr (sizeof(E) == 2)
+        hipLaunchKernelGGL((k_recur_lds<D>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st, v, ops, p.cu_seqlens,
+                           p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, H, p.S0, p.S_T, static_cast<E*>(p.o));
+    else
+        hipLaunchKernelGGL((k_recur<E, D, CT>), dim3(NH * (D / (kSub * CT))), dim3(kThreads), 0, st, v, ops,
+                           p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, H, p.S0, p.S_T,
+                           static_cast<E*>(p.o));
     mark(3);
     return hipGetLastError();
 }
