@@ -71,12 +71,17 @@ __device__ inline void seq_range(const int32_t* __restrict__ cu, int32_t n, int6
 // ---------------------------------------------------------------- chunk table
 // One workgroup.  Sequence n contributes ceil(len_n / 64) chunks; chunks are
 // aligned to each sequence's first token and the last one may be partial.
+// Sequences are taken 1024 at a time: a prefix sum of their chunk counts
+// gives each one's first chunk, then the whole workgroup writes the batch's
+// chunk records, finding each chunk's sequence by binary search in the sums.
 __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict__ cu, int32_t n_seqs,
                                                       int64_t total_tokens, int64_t fixed_len,
                                                       int32_t max_chunks, ChunkInfo* __restrict__ tab,
                                                       int32_t* __restrict__ seq_chunk0,
                                                       int32_t* __restrict__ n_chunks_out) {
-    __shared__ int32_t s_scan[1024];
+    __shared__ int32_t s_scan[1024];     // inclusive prefix sum of chunk counts in the batch
+    __shared__ int64_t s_start[1024];
+    __shared__ int64_t s_len[1024];
     __shared__ int32_t s_carry;
     const int tid = threadIdx.x;
     if (tid == 0) s_carry = 0;
@@ -87,6 +92,8 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
         if (n < n_seqs) seq_range(cu, n, total_tokens, fixed_len, start, len);
         const int32_t cnt = (int32_t)((len + kChunk - 1) / kChunk);
         s_scan[tid] = cnt;
+        s_start[tid] = start;
+        s_len[tid] = len;
         __syncthreads();
         for (int off = 1; off < 1024; off <<= 1) {
             int32_t add = tid >= off ? s_scan[tid - off] : 0;
@@ -95,22 +102,29 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
             __syncthreads();
         }
         const int32_t carry = s_carry;
-        const int32_t first = carry + s_scan[tid] - cnt;
         if (n < n_seqs) {
+            const int32_t first = carry + s_scan[tid] - cnt;
             seq_chunk0[n] = first < max_chunks ? first : max_chunks;
-            for (int32_t j = 0; j < cnt; ++j) {
-                const int32_t c = first + j;
-                if (c >= max_chunks) break;
-                ChunkInfo ci;
-                ci.tok0 = start + (int64_t)j * kChunk;
-                ci.seq = n;
-                const int64_t rem = len - (int64_t)j * kChunk;
-                ci.len = (int32_t)(rem < kChunk ? rem : kChunk);
-                tab[c] = ci;
+        }
+        const int32_t batch = s_scan[1023];
+        for (int32_t c = tid; c < batch; c += 1024) {
+            const int32_t cg = carry + c;
+            if (cg >= max_chunks) break;
+            int lo = 0, hi = 1023;   // first i with s_scan[i] > c
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (s_scan[mid] > c) hi = mid; else lo = mid + 1;
             }
+            const int32_t j = c - (lo > 0 ? s_scan[lo - 1] : 0);
+            ChunkInfo ci;
+            ci.tok0 = s_start[lo] + (int64_t)j * kChunk;
+            ci.seq = base + lo;
+            const int64_t rem = s_len[lo] - (int64_t)j * kChunk;
+            ci.len = (int32_t)(rem < kChunk ? rem : kChunk);
+            tab[cg] = ci;
         }
         __syncthreads();
-        if (tid == 1023) s_carry = carry + s_scan[1023];
+        if (tid == 1023) s_carry = carry + batch;
         __syncthreads();
     }
     if (tid == 0) {
@@ -751,28 +765,32 @@ __global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, Chu
 // ---------------------------------------------------------------- k_recur_lds
 // bf16 form of k_recur with producer waves.  The chunk operands travel
 // global -> LDS by direct loads (global_load_lds_dwordx4: each lane moves 16
-// bytes to LDS at M0 + 16 * lane), issued by four producer waves that do
-// nothing else, one per compute wave.  A wave issues its instructions in
-// order, so a compute wave that issued its own share of the loads would sit
-// behind them for as long as the CU needs to stream a chunk's operands; with
-// producers the streaming overlaps the compute waves' matrix work.  (One
-// producer is not enough: a single wave moves about 1 KB per 80 clocks this
-// way, so the load issue is spread over four.)
+// bytes to LDS at M0 + 16 * lane), issued by producer waves that do nothing
+// else, one per compute wave.  A wave issues its instructions in order, so a
+// compute wave that issued its own share of the loads would sit behind them
+// for as long as the CU needs to stream a chunk's operands; with producers
+// the streaming overlaps the compute waves' matrix work.  (A single producer
+// is too slow -- one wave moves about 1 KB per 80 clocks this way -- and
+// eight were slower than four: they take issue slots from the compute waves
+// on the same SIMDs.)
 //
-// Buffers: two, alternating by chunk parity.  While the compute waves work on
-// chunk j from one, the producers fill the other with chunk j+1 and wait for
-// their loads before the barrier that opens step j+1.  The two are distinct
-// LDS arrays so that the compiler can tell the producers' loads into one
-// from reads of the other.  Synchronisation is plain s_barrier with explicit
+// Buffers: two, alternating by chunk parity.  The compute waves read every
+// operand of chunk j into registers before the second barrier of step j, so
+// from that barrier on the buffer of chunk j is free and the producers fill
+// it with chunk j+2; before the barrier that opens step j+1 they wait for
+// chunk j+1 only (loads of one wave complete in issue order), so the loads of
+// the next chunk stay in flight across the barriers.  The two buffers are
+// distinct LDS arrays so that the compiler can tell the producers' loads into
+// one from reads of the other.  Synchronisation is plain s_barrier with explicit
 // counter waits: the workgroup fence of __syncthreads would drain the
 // producers' in-flight loads at every barrier.
 //
-// L2 warm-up: three chunks ahead, the producers read one dword of each
+// L2 warm-up: four chunks ahead, the producers load one dword of each
 // 128-byte line of a share of that chunk's data (operands, Gamma_L and the
-// head's value rows); the slab workgroups of a head take disjoint shares, so
-// the direct loads of every slab later hit L2 rather than HBM.  These reads
-// are issued last in a step and left in flight by the wait that ends it:
-// vector memory operations of a wave complete in issue order.
+// head's value rows) into an LDS scratch that nothing reads; the slab
+// workgroups of a head take disjoint shares, so the direct loads of every
+// slab later hit L2 rather than HBM.  Landing in LDS, these loads hold no
+// registers and nothing waits for them except the counted waits below.
 #define KDA_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
@@ -793,8 +811,19 @@ __device__ inline void barrier_lds() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int N, int I = 0, typename Fn>
+__device__ inline void static_for(Fn&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<N, I + 1>(f);
+    }
+}
+
 constexpr int kRecurWaves = 4;                              // compute waves
-constexpr int kRecurLdsThreads = 2 * kRecurWaves * 64;       // + as many producers
+constexpr int kProdPerWave = 1;                             // producer waves per compute wave
+constexpr int kProducers = kRecurWaves * kProdPerWave;
+constexpr int kRecurLdsThreads = (kRecurWaves + kProducers) * 64;
 
 // Buffer layout: one region per compute wave w, in 1 KB blocks (64 lanes x
 // 16 bytes: the fragment-major tiles of k_prep copied as they are):
@@ -841,6 +870,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     __shared__ __attribute__((aligned(16))) E sSt[SW * PS];
     __shared__ __attribute__((aligned(16))) E sYt[SW * PY];
     __shared__ __attribute__((aligned(16))) E sUt[SW * PY];
+    __shared__ unsigned sTouch[kProducers * 64];   // warm-up loads land here, never read
 
     // Workgroup -> (sequence*head, slab); slabs of one (sequence, head) share
     // an XCD (and its L2) when the (sequence, head) count is a multiple of 8.
@@ -873,7 +903,9 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 
     if (w >= kRecurWaves) {
         // ------------------------------------------------ producer waves
-        const int cw = w - kRecurWaves;   // the compute wave whose operands this wave loads
+        const int pw = w - kRecurWaves;
+        const int cw = pw / kProdPerWave;   // the compute wave whose operands this wave loads
+        const int part = pw % kProdPerWave; // which of its blocks: part, part + kProdPerWave, ...
         const E* qg = static_cast<const E*>(ops.Qg) + cb * C * D + lane * G::EPV;
         const E* kg = static_cast<const E*>(ops.Kg) + cb * C * D + lane * G::EPV;
         const E* kt = static_cast<const E*>(ops.KhT) + cb * D * C + lane * G::EPV;
@@ -885,48 +917,64 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         auto dma = [](const void* src, uint4* lds) {
             __builtin_amdgcn_global_load_lds(src, KDA_LDS_PTR(lds), 16, 0, 0);
         };
-        auto issue = [&](uint4* buf, int j) {
-            const int len = chunk_len(j);
+        // Direct loads per producer wave and chunk: blocks part, part + P, ...
+        // of its compute wave's region; a part with one block fewer repeats
+        // its last one, so that every producer issues the same count.
+        constexpr int kDma = (L::kBlocks + kProdPerWave - 1) / kProdPerWave;
+        // Block b of region cw for chunk j (b is a compile-time constant).
+        auto block = [&](auto b_c, uint4* dst, int j, int len) {
+            constexpr int b = decltype(b_c)::value;
             const int64_t oo = (int64_t)j * C * D, so = (int64_t)j * C * C;
-            {
-                uint4* dst = buf + cw * L::kWaveVec;
-#pragma unroll
-                for (int i = 0; i < G::VPL; ++i) {
-                    dma(qg + oo + (cw * G::VPL + i) * 64 * G::EPV, dst + (L::kQg + i) * 64);
-                    dma(kg + oo + (cw * G::VPL + i) * 64 * G::EPV, dst + (L::kKg + i) * 64);
-                }
-#pragma unroll
-                for (int i = 0; i < G::NVT; ++i) {
-                    dma(tb + so + (cw * G::NVT + i) * 64 * G::EPV, dst + (L::kTb + i) * 64);
-                    dma(mm + so + (cw * G::NVT + i) * 64 * G::EPV, dst + (L::kMm + i) * 64);
-                }
-#pragma unroll
-                for (int i = 0; i < RT * G::NVT; ++i)
-                    dma(kt + oo + (cw * RT * G::NVT + i) * 64 * G::EPV, dst + (L::kKt + i) * 64);
+            if constexpr (b < L::kKg)
+                dma(qg + oo + (cw * G::VPL + b - L::kQg) * 64 * G::EPV, dst + b * 64);
+            else if constexpr (b < L::kTb)
+                dma(kg + oo + (cw * G::VPL + b - L::kKg) * 64 * G::EPV, dst + b * 64);
+            else if constexpr (b < L::kMm)
+                dma(tb + so + (cw * G::NVT + b - L::kTb) * 64 * G::EPV, dst + b * 64);
+            else if constexpr (b < L::kKt)
+                dma(mm + so + (cw * G::NVT + b - L::kMm) * 64 * G::EPV, dst + b * 64);
+            else if constexpr (b < L::kMisc)
+                dma(kt + oo + (cw * RT * G::NVT + b - L::kKt) * 64 * G::EPV, dst + b * 64);
+            else {
                 int row = kSub * cw + (lane >> 1);
                 row = row < len ? row : len - 1;
                 const void* misc = lane < 32 ? static_cast<const void*>(vv + ((int64_t)j * C + row) * rs)
                                              : static_cast<const void*>(gm + (int64_t)j * D + kSub * RT * cw);
-                dma(misc, dst + L::kMisc * 64);
+                dma(misc, dst + b * 64);
             }
+        };
+        auto issue_part = [&](auto part_c, uint4* dst, int j, int len) {
+            constexpr int pt = decltype(part_c)::value;
+            static_for<kDma>([&](auto i_c) {
+                constexpr int b0 = pt + kProdPerWave * decltype(i_c)::value;
+                constexpr int b = b0 < L::kBlocks ? b0 : b0 - kProdPerWave;
+                block(std::integral_constant<int, b>{}, dst, j, len);
+            });
+        };
+        auto issue = [&](uint4* buf, int j) {
+            const int len = chunk_len(j);
+            uint4* dst = buf + cw * L::kWaveVec;
+            static_for<kProdPerWave>([&](auto p_c) {
+                if (part == decltype(p_c)::value) issue_part(p_c, dst, j, len);
+            });
         };
 
         // Warm-up lines of this slab: kTouch per producer lane, over one
         // chunk's operands, Gamma_L and the head's value rows.
-        constexpr int kAhead = 3;
+        constexpr int kAhead = 4;
         constexpr int64_t kBq = (int64_t)C * D * 2, kBs = (int64_t)C * C * 2;   // bytes per chunk slot
         constexpr int kOpsLines = (int)((3 * kBq + 2 * kBs) / 128);
         constexpr int kGamLines = D * 4 / 128;
         constexpr int kVRowLines = D * 2 / 128;
         constexpr int kLines = kOpsLines + kGamLines + kChunk * kVRowLines;
         constexpr int kPerSlab = (kLines + NS - 1) / NS;
-        constexpr int kTouch = (kPerSlab + 64 * kRecurWaves - 1) / (64 * kRecurWaves);
+        constexpr int kTouch = (kPerSlab + 64 * kProducers - 1) / (64 * kProducers);
         const char* t_base[kTouch];   // line in chunk 0 (operands, Gamma_L) or at token 0 (value rows)
         int64_t t_step[kTouch];       // bytes between chunks (operands, Gamma_L)
         int t_vrow[kTouch];           // value row in the chunk, or -1
 #pragma unroll
         for (int k = 0; k < kTouch; ++k) {
-            int q = cw * 64 + lane + 64 * kRecurWaves * k;
+            int q = pw * 64 + lane + 64 * kProducers * k;
             q = q < kPerSlab ? q : kPerSlab - 1;
             int line = sl * kPerSlab + q;
             line = line < kLines ? line : kLines - 1;
@@ -947,8 +995,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 t_step[k] = 0;
             }
         }
-        // Reads one dword per line of chunk j + kAhead (clamped to the last chunk).
-        auto touch = [&](int j, unsigned (&out)[kTouch]) {
+        // Loads one dword per line of chunk j + kAhead (clamped to the last chunk).
+        auto touch = [&](int j) {
             const int jt = j + kAhead < nch ? j + kAhead : nch - 1;
 #pragma unroll
             for (int k = 0; k < kTouch; ++k) {
@@ -959,39 +1007,45 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 } else {
                     p = t_base[k] + jt * t_step[k];
                 }
-                out[k] = *reinterpret_cast<const unsigned*>(p);
+                __builtin_amdgcn_global_load_lds(p, KDA_LDS_PTR(sTouch + pw * 64), 4, 0, 0);
             }
         };
-        // One step: open it, fill the other buffer with chunk j+1, warm up
-        // chunk j+kAhead, follow the compute waves' two inner barriers, then
-        // wait for the fill (the warm-up reads may stay in flight).  `tch`
-        // holds warm-up values read two steps ago, which have landed; using
-        // them keeps the reads from being optimised away.
-        auto pstep = [&](uint4* nxt, int j, unsigned (&tch)[kTouch]) {
-            barrier_lds();
-#pragma unroll
-            for (int k = 0; k < kTouch; ++k) asm volatile("" ::"v"(tch[k]));
-            if (j + 1 < nch) issue(nxt, j + 1);
-            touch(j, tch);
+        // One step j: open it; after the compute waves' first inner barrier
+        // refill chunk j's buffer with chunk j+2 and warm up chunk j+kAhead;
+        // after the second, wait until chunk j+1 has landed (the loads issued
+        // after it -- the previous step's warm-up, this step's fill and
+        // warm-up -- may stay in flight).
+        auto pstep = [&](uint4* buf, int j) {
             barrier_lds();
             barrier_lds();
-            wait_counts<kTouch, 15>();
+            const bool fill = j + 2 < nch;
+            if (fill) issue(buf, j + 2);
+            touch(j);
+            barrier_lds();
+            if (fill)
+                wait_counts<2 * kTouch + kDma, 15>();
+            else
+                wait_counts<2 * kTouch, 15>();
         };
         if (nch > 0) {
-            unsigned tA[kTouch], tB[kTouch];
             issue(sBuf0, 0);
-            wait_counts<0, 15>();
-            touch(-2, tA);
-            touch(-1, tB);
+            if (nch > 1) issue(sBuf1, 1);
+            touch(-2);
+            touch(-1);
+            if (nch > 1)   // chunk 0 has landed
+                wait_counts<2 * kTouch + kDma, 15>();
+            else
+                wait_counts<2 * kTouch, 15>();
             for (int j = 0; j < nch; j += 2) {
-                pstep(sBuf1, j, tA);
+                pstep(sBuf0, j);
                 if (j + 1 >= nch) break;
-                pstep(sBuf0, j + 1, tB);
+                pstep(sBuf1, j + 1);
             }
-#pragma unroll
-            for (int k = 0; k < kTouch; ++k) asm volatile("" ::"v"(tA[k]), "v"(tB[k]));
         }
-        wait_counts<0, 15>();   // no direct LDS load may outlive the workgroup
+        // No direct LDS load may outlive the workgroup.  (The compiler drops a
+        // counter wait right before the end of the program, which waits by
+        // itself; this one is kept explicit.)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         return;
     }
 

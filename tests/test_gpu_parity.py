@@ -121,6 +121,22 @@ def test_edge_cases(torch_dev, dtype, lengths, H, d, special):
     _check(inp, o, ST, what="edge %s %s %s" % (dtype, lengths, special))
 
 
+def test_many_sequences(torch_dev):
+    """2100 sequences (three 1024-sequence batches of the chunk table), lengths
+    0..70 with empty ones, so chunk records straddle batch boundaries."""
+    torch, dev = torch_dev
+    import numpy as np
+    lengths = [int(x) for x in np.random.default_rng(11).integers(0, 71, size=2100)]
+    lengths[0] = 0
+    lengths[1023] = 0
+    lengths[1024] = 70
+    spec = ki.custom("many", "bf16", lengths, 2, 64, s0_std=0.3, varlen=True, seed=5)
+    inp = ki.generate_numpy(spec)
+    _say("many sequences: N=%d T=%d H=2 d=64" % (len(lengths), sum(lengths)))
+    o, ST = _run_numpy_inputs(torch, dev, inp)
+    _check(inp, o, ST, what="many sequences")
+
+
 def test_s0_null_equals_zeros(torch_dev):
     torch, dev = torch_dev
     import gated_delta_rule_30_amd as kda
