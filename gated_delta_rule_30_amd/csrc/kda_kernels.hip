@@ -181,36 +181,6 @@ __device__ inline float row_scan16(float x) {
     return x;
 }
 
-// Per-channel cumulative log-decay of the chunk for this lane's token and
-// channels.  On return b[j] is inclusive from the chunk start.  sTot, sCarry:
-// LDS [4][D] and [5][D] fp32; sCarry[w][c] = b at the end of sub-tile w-1
-// (0 for w = 0), sCarry[4][c] = b at the chunk end.  Contains two workgroup
-// barriers; every thread of the workgroup must call it.
-template <typename E, int D>
-__device__ inline void chunk_cumsum(const RowSlice<E, D>& g, float* b, float* sTot, float* sCarry) {
-    constexpr int CPL = Geo<E, D>::CPL;
-    const int w = wave_id(), li = lane_id() & 15, lg = lane_id() >> 4;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) b[j] = row_scan16(g.get(j));
-    if (li == 15) {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) sTot[w * D + lg * CPL + j] = b[j];
-    }
-    __syncthreads();
-    for (int c = threadIdx.x; c < D; c += kThreads) {
-        float run = 0.f;
-#pragma unroll
-        for (int r = 0; r < kNSub; ++r) {
-            sCarry[r * D + c] = run;
-            run += sTot[r * D + c];
-        }
-        sCarry[kNSub * D + c] = run;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) b[j] += sCarry[w * D + lg * CPL + j];
-}
-
 // Chunk operands written by k_prep for k_recur, stored head-major: the
 // operands of chunk ci of head h sit at slot h * max_chunks + ci, so one
 // head's chunks are contiguous and the sequential kernel streams through
@@ -233,6 +203,16 @@ struct ChunkOps {
 };
 
 // ---------------------------------------------------------------- k_prep
+// One workgroup per (chunk, head), chunk-parallel.
+//
+// Decay factors.  With rho_w = b at the end of sub-tile w-1 and x = b - rho_w
+// in [-80, 0] for the tokens of sub-tile w, every factor is a product of
+// exponentials of bounded arguments:
+//   exp(b)               = exp(rho_w) . exp(x)
+//   exp(rho_{w+1} - b)   = exp(rho_{w+1} - rho_w) . exp(-x)
+//   exp(rho_w - rho_{J+1}) = prod_{R=J+1}^{w-1} exp(rho_{R+1} - rho_R)
+// The per-channel factors are computed once per chunk; per element only
+// exp(x), exp(-x) and exp(b_L - b) remain.
 template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ g, const E* __restrict__ beta,
@@ -246,20 +226,28 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     constexpr int PT = C + 4;      // row pitch of fp32 C x C matrices
     constexpr int PM = C + 8;      // row pitch of the M staging tile (elements)
     constexpr int PK = C + 8;      // row pitch of the K^T staging tile (elements)
-    // Region R holds A, T and the T-inverse scratch; before A exists it stages K^T.
-    constexpr int kRA = C * PT, kRT = C * PT, kRX = 4 * 16 * 17;
-    constexpr int kRBytes = (kRA + kRT + kRX) * 4;
-    static_assert(D * PK * (int)sizeof(E) <= kRBytes, "K^T staging must fit in region R");
-    __shared__ __attribute__((aligned(16))) float sR[kRA + kRT + kRX];
-    __shared__ __attribute__((aligned(16))) E sColB[(kNSub - 1) * kSub * PC];
-    __shared__ float sTot[kNSub * D];
-    __shared__ float sCarry[(kNSub + 1) * D];
+    // Region 1: A and the T-inverse scratch; before A exists it stages K^T.
+    // Region 2: the column bases; after the Gram blocks, T.
+    constexpr int kR1 = C * PT + 4 * 16 * 17;
+    constexpr int kColBytes = (kNSub - 1) * kSub * PC * (int)sizeof(E);
+    constexpr int kR2 = (kColBytes > C * PT * 4 ? kColBytes : C * PT * 4) / 4;
+    static_assert(D * PK * (int)sizeof(E) <= kR1 * 4, "K^T staging must fit in region 1");
+    __shared__ __attribute__((aligned(16))) float sR1[kR1];
+    __shared__ __attribute__((aligned(16))) float sR2[kR2];
+    __shared__ float sTot[kNSub * D];         // exp(rho_{R+1} - rho_R)
+    __shared__ float sP30[D];                 // exp(rho_3 - rho_1)
+    __shared__ float sERho[kNSub * D];        // exp(rho_R)
+    __shared__ float sCarry[(kNSub + 1) * D]; // rho_0 .. rho_3, b_L
     __shared__ __attribute__((aligned(16))) E sM[C * PM];
     __shared__ float sBeta[C];
-    float* sA = sR;
-    float* sT = sR + kRA;
-    float* sX = sR + kRA + kRT;
-    E* sKt = reinterpret_cast<E*>(sR);
+    float* sA = sR1;
+    float* sX = sR1 + C * PT;
+    E* sKt = reinterpret_cast<E*>(sR1);
+    E* sColB = reinterpret_cast<E*>(sR2);
+    float* sT = sR2;
+    // K^T staging: the token index is rotated by 16 per channel group, so
+    // the four lane groups that write one token column hit different banks.
+    auto kt_at = [](int ch, int t_) { return ch * PK + ((t_ + kSub * (ch / CPL)) & (C - 1)); };
 
     const int32_t ci = blockIdx.x;
     if (ci >= *n_chunks_p) return;
@@ -279,29 +267,55 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     const float bet = ok ? to_f(beta[(info.tok0 + tok) * H + h]) : 0.f;
     if (lg == 0) sBeta[tok] = bet;
 
+    // Cumulative log-decay: 16-lane row scan per sub-tile, carries between
+    // sub-tiles, and the per-channel factors.
     float b[CPL];
-    chunk_cumsum<E, D>(xg, b, sTot, sCarry);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) b[j] = row_scan16(xg.get(j));
+    if (li == 15) {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) sTot[w * D + lg * CPL + j] = b[j];
+    }
+    __syncthreads();
+    for (int c = tid; c < D; c += kThreads) {
+        float run = 0.f;
+#pragma unroll
+        for (int r = 0; r < kNSub; ++r) {
+            const float t = sTot[r * D + c];
+            sCarry[r * D + c] = run;
+            sERho[r * D + c] = __expf(run);
+            sTot[r * D + c] = __expf(t);
+            run += t;
+        }
+        sCarry[kNSub * D + c] = run;
+        sP30[c] = sTot[1 * D + c] * sTot[2 * D + c];
+        ops.gam[cbase * D + c] = __expf(run);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) b[j] += sCarry[w * D + lg * CPL + j];
 
-    // Operands of the decayed Gram blocks (rows scaled by exp(b - rho_w); the
-    // diagonal column operand by exp(rho_w - b); the column base for later row
-    // blocks by exp(rho_{w+1} - b)) and the inter-chunk operands
-    // Q . Gamma, K . Gamma, K . exp(b_L - b).
+    // Operands: Gram rows scaled by exp(b - rho_w), the diagonal column
+    // operand by exp(rho_w - b), the column base for later row blocks by
+    // exp(rho_{w+1} - b), and the inter-chunk operands Q . Gamma, K . Gamma,
+    // K . exp(b_L - b).
     typename M::frag rq[G::NKC], rk[G::NKC], cd[G::NKC];
     {
         const float* rho = sCarry + w * D + lg * CPL;
-        const float* rho1 = sCarry + (w + 1) * D + lg * CPL;
+        const float* erho = sERho + w * D + lg * CPL;
         const float* bl = sCarry + kNSub * D + lg * CPL;
-        E* cb = sColB + (w * kSub + li) * PC + lg * CPL;
-        uint4 vq[G::VPL], vk[G::VPL];
+        const float* esub = sTot + w * D + lg * CPL;
+        uint4 vq[G::VPL], vk[G::VPL], vc[G::VPL];
         E* eq = reinterpret_cast<E*>(vq);
         E* ek = reinterpret_cast<E*>(vk);
+        E* ec = reinterpret_cast<E*>(vc);
 #pragma unroll
         for (int m = 0; m < G::NKC; ++m) {
 #pragma unroll
             for (int j = 0; j < M::KW; ++j) {
                 const int c = m * M::KW + j;
                 const float x = b[c] - rho[c];
-                const float fr = __expf(x), fd = __expf(-x), gm = __expf(b[c]);
+                const float fr = __expf(x), fd = __expf(-x), gm = erho[c] * fr;
                 const float kv = xk.get(c), qv = xq.get(c);
                 if constexpr (M::KW == 1) {
                     rq[m] = qv * fr;
@@ -312,10 +326,10 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
                     rk[m][j] = from_f<E>(kv * fr);
                     cd[m][j] = from_f<E>(kv * fd);
                 }
-                if (w < kNSub - 1) cb[c] = from_f<E>(kv * __expf(rho1[c] - b[c]));
+                ec[c] = from_f<E>(kv * (esub[c] * fd));
                 eq[c] = from_f<E>(qv * gm);
                 ek[c] = from_f<E>(kv * gm);
-                sKt[(lg * CPL + c) * PK + tok] = from_f<E>(kv * __expf(bl[c] - b[c]));
+                sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(kv * __expf(bl[c] - b[c]));
             }
         }
         uint4* qg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Qg) + cbase * C * D);
@@ -325,7 +339,11 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
             qg[(w * G::VPL + i) * 64 + lane_id()] = vq[i];
             kg[(w * G::VPL + i) * 64 + lane_id()] = vk[i];
         }
-        for (int c = tid; c < D; c += kThreads) ops.gam[cbase * D + c] = __expf(sCarry[kNSub * D + c]);
+        if (w < kNSub - 1) {
+            uint4* cb = reinterpret_cast<uint4*>(sColB + (w * kSub + li) * PC + lg * CPL);
+#pragma unroll
+            for (int i = 0; i < G::VPL; ++i) cb[i] = vc[i];
+        }
     }
     __syncthreads();
     {
@@ -336,13 +354,14 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
             uint4 pk;
             E* pe = reinterpret_cast<E*>(&pk);
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) pe[e] = sKt[r * PK + G::tok_of(v * EPV + e, lgp)];
+            for (int e = 0; e < EPV; ++e) pe[e] = sKt[kt_at(r, G::tok_of(v * EPV + e, lgp))];
             kt[vi] = pk;
         }
     }
     __syncthreads();
 
-    // Blocks (w, J) for J <= w of A (strict lower, rows scaled by beta) and M (inclusive lower).
+    // Blocks (w, J) for J <= w of A (strict lower, rows scaled by beta) and M
+    // (inclusive lower); blocks above the diagonal are never formed.
     for (int J = 0; J <= w; ++J) {
         f32x4 accA = zero4(), accM = zero4();
         if (J == w) {
@@ -352,25 +371,22 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
                 accM = M::mma(rq[m], cd[m], accM);
             }
         } else {
-            // column operand: base of block J times exp(rho_w - rho_{J+1}) (1 when J = w-1)
+            // column operand: base of block J times exp(rho_w - rho_{J+1})
+            // (1 when J = w-1; otherwise a per-channel factor from the table)
             const E* cb = sColB + (J * kSub + li) * PC + lg * CPL;
-            const float* rw = sCarry + w * D + lg * CPL;
-            const float* rj = sCarry + (J + 1) * D + lg * CPL;
+            const float* pf = (J == w - 2 ? sTot + (w - 1) * D : sP30) + lg * CPL;
             const bool scale = J < w - 1;
 #pragma unroll
             for (int m = 0; m < G::NKC; ++m) {
                 typename M::frag cf;
                 if constexpr (M::KW == 1) {
-                    const int c = m;
-                    cf = scale ? to_f(cb[c]) * __expf(rw[c] - rj[c]) : to_f(cb[c]);
+                    cf = scale ? cb[m] * pf[m] : cb[m];
                 } else {
                     cf = M::load(cb + m * M::KW);
                     if (scale) {
 #pragma unroll
-                        for (int j = 0; j < M::KW; ++j) {
-                            const int c = m * M::KW + j;
-                            cf[j] = from_f<E>(to_f(cf[j]) * __expf(rw[c] - rj[c]));
-                        }
+                        for (int j = 0; j < M::KW; ++j)
+                            cf[j] = from_f<E>(to_f(cf[j]) * pf[m * M::KW + j]);
                     }
                 }
                 accA = M::mma(rk[m], cf, accA);
@@ -384,15 +400,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
             sM[row * PM + col] = from_f<E>((J < w || col <= row) ? accM[r] : 0.f);
         }
     }
-    // upper blocks: zero in M and T
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-        const int r = idx / C, c = idx % C;
-        if ((c >> 4) > (r >> 4)) {
-            sM[r * PM + c] = from_f<E>(0.f);
-            sT[r * PT + c] = 0.f;
-        }
-    }
-    __syncthreads();
+    __syncthreads();   // the column bases are dead from here; region 2 holds T
 
     // T = (I + A)^-1.  Diagonal 16 x 16 blocks by forward substitution (one
     // column per lane), then the off-diagonal blocks by distance R - J:
@@ -449,8 +457,9 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const int t = G::tok_of(v * EPV + e, lgp);
-            et[e] = from_f<E>(sT[r * PT + t] * sBeta[t]);
-            em[e] = sM[r * PM + t];
+            const bool upper = (t >> 4) > (r >> 4);   // blocks above the diagonal are zero
+            et[e] = from_f<E>(upper ? 0.f : sT[r * PT + t] * sBeta[t]);
+            em[e] = upper ? from_f<E>(0.f) : sM[r * PM + t];
         }
         otb[vi] = pt;
         omm[vi] = pm;
