@@ -11,8 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_profile", "stage_names", "workspace_size", "status_string", "lib_path",
-           "KDA_F32", "KDA_BF16", "KdaError"]
+__all__ = ["chunk_fwd", "chunk_fwd_profile", "recurrent_fwd", "validate_inputs", "stage_names", "workspace_size",
+           "status_string", "lib_path", "KDA_F32", "KDA_BF16", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -53,6 +53,10 @@ def _load():
         lib.kda_profile_num_stages.restype = ctypes.c_int32
         lib.kda_profile_stage_name.argtypes = [ctypes.c_int32]
         lib.kda_profile_stage_name.restype = ctypes.c_char_p
+        lib.kda_recurrent_fwd.argtypes = [ctypes.c_int, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P]
+        lib.kda_recurrent_fwd.restype = ctypes.c_int
+        lib.kda_validate_inputs.argtypes = [ctypes.c_int, I64, I32, I32, I32, P, P, P, P, P]
+        lib.kda_validate_inputs.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -161,3 +165,95 @@ def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = C
     if batched:
         o = o.reshape(B, -1, H, dv)
     return o, (S_T if output_final_state else None)
+
+
+def _check_common(q, k, v, beta, log_alpha):
+    import torch
+    dt = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}.get(q.dtype)
+    if dt is None:
+        raise TypeError("q must be float32 or bfloat16, got %s" % q.dtype)
+    for name, t in (("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on %s" % (name, dev))
+    return dt, dev
+
+
+def recurrent_fwd(q, k, v, beta, log_alpha, S_in=None, S_out=None, n_seqs=None, o=None):
+    """Token-by-token KDA update for decoding (kda_recurrent_fwd).
+
+    q, k, log_alpha: [N*n, H, d_k] or [N, n, H, d_k]; v: [..., H, d_v];
+    beta: [..., H] -- n tokens for each of N sequences (N from the 4-D shape
+    or `n_seqs`, default 1).  S_in: [N, H, d_k, d_v] float32 or None (zeros).
+    S_out: preallocated output state (may be S_in itself for an in-place
+    update) or None (allocated).  Returns (o, S_out).
+    """
+    import torch
+    lib = _load()
+    dt, dev = _check_common(q, k, v, beta, log_alpha)
+    batched = q.dim() == 4
+    if batched:
+        N = q.shape[0]
+        q, k, v, log_alpha = (t.reshape(-1, *t.shape[2:]) for t in (q, k, v, log_alpha))
+        beta = beta.reshape(-1, beta.shape[-1])
+    else:
+        N = 1 if n_seqs is None else int(n_seqs)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != (T, H, dk) or log_alpha.shape != (T, H, dk) or v.shape != (T, H, dv) or beta.shape != (T, H):
+        raise ValueError("inconsistent shapes")
+    if N < 1 or T % N != 0:
+        raise ValueError("%d tokens do not split into %d equal sequences" % (T, N))
+    for name, t in (("S_in", S_in), ("S_out", S_out)):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (N, H, dk, dv) or t.device != dev
+                              or not t.is_contiguous()):
+            raise ValueError("%s must be contiguous float32 [%d, %d, %d, %d] on %s" % (name, N, H, dk, dv, dev))
+    if S_out is None:
+        S_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    elif o.shape != (T, H, dv) or o.dtype != q.dtype or o.device != dev or not o.is_contiguous():
+        raise ValueError("o must be contiguous %s [%d, %d, %d] on %s" % (q.dtype, T, H, dv, dev))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    code = lib.kda_recurrent_fwd(dt, N, T // N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
+                                 _ptr(S_in), _ptr(S_out), _ptr(o), ctypes.c_void_p(stream))
+    if code != 0:
+        raise KdaError(code, lib.kda_status_string(code).decode())
+    if batched:
+        o = o.reshape(N, -1, H, dv)
+    return o, S_out
+
+
+def validate_inputs(beta, log_alpha, cu_seqlens=None, n_seqs=None):
+    """Counts value-range violations on the GPU (kda_validate_inputs) and
+    returns {"log_alpha": n, "beta": n, "cu_seqlens": n}; synchronises the
+    current stream to read the counts."""
+    import torch
+    lib = _load()
+    dt = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}.get(log_alpha.dtype)
+    if dt is None or beta.dtype != log_alpha.dtype:
+        raise TypeError("beta and log_alpha must both be float32 or bfloat16")
+    if log_alpha.dim() == 4:
+        log_alpha = log_alpha.reshape(-1, *log_alpha.shape[2:])
+        beta = beta.reshape(-1, beta.shape[-1])
+    T, H, dk = log_alpha.shape
+    dev = log_alpha.device
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor on %s" % dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = 1 if n_seqs is None else int(n_seqs)
+    counts = torch.empty(3, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    code = lib.kda_validate_inputs(dt, T, N, H, dk, _ptr(beta.contiguous()), _ptr(log_alpha.contiguous()),
+                                   _ptr(cu_seqlens), _ptr(counts), ctypes.c_void_p(stream.cuda_stream))
+    if code != 0:
+        raise KdaError(code, lib.kda_status_string(code).decode())
+    c = counts.cpu().tolist()
+    return {"log_alpha": c[0], "beta": c[1], "cu_seqlens": c[2]}

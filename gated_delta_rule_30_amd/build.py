@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = [os.path.join(CSRC, "kda_kernels.hip"), os.path.join(CSRC, "kda_api.cpp")]
+SOURCES = [os.path.join(CSRC, "kda_kernels.hip"), os.path.join(CSRC, "kda_aux.hip"),
+           os.path.join(CSRC, "kda_api.cpp")]
 
 # Device flags: gfx950 only; packed-fp32 instructions are turned off (the
 # compiler still emits ordinary fp32 VALU code for the same arithmetic).

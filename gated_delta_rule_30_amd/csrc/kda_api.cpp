@@ -137,6 +137,48 @@ kda_status kda_chunk_fwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_s
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_recurrent_fwd(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t d_k,
+                             int32_t d_v, const void* q, const void* k, const void* v, const void* beta,
+                             const void* log_alpha, const float* S_in, float* S_out, void* o, void* stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (n_seqs < 1 || n_tokens < 1 || n_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
+    if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)n_seqs * n_tokens >= ((int64_t)1 << 31) || (int64_t)n_seqs * n_heads * (d_k / 64) >= ((int64_t)1 << 31))
+        return KDA_ERR_UNSUPPORTED;
+    if (!q || !k || !v || !beta || !log_alpha || !S_out || !o) return KDA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, beta, log_alpha, S_in, S_out, o};
+    for (const void* ptr : ptrs)
+        if (ptr && ((uintptr_t)ptr % 16) != 0) return KDA_ERR_SHAPE;
+    kda::DecodePlan p{};
+    p.bf16 = dt == KDA_BF16;
+    p.d = d_k;
+    p.n_seqs = n_seqs;
+    p.n_tokens = n_tokens;
+    p.n_heads = n_heads;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.beta = beta;
+    p.g = log_alpha;
+    p.S_in = S_in;
+    p.S_out = S_out;
+    p.o = o;
+    hipError_t e = kda::launch_decode(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_validate_inputs(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                               const void* beta, const void* log_alpha, const int32_t* cu_seqlens,
+                               unsigned long long* counts, void* stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (total_tokens < 0 || n_seqs < 1 || n_heads < 1 || d_k < 1) return KDA_ERR_SHAPE;
+    if (!counts || (total_tokens > 0 && (!beta || !log_alpha))) return KDA_ERR_NULL;
+    if ((uintptr_t)counts % 8 != 0) return KDA_ERR_SHAPE;
+    hipError_t e = kda::launch_validate(dt == KDA_BF16, total_tokens, n_seqs, n_heads, d_k, beta, log_alpha,
+                                        cu_seqlens, counts, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 const char* kda_status_string(kda_status s) {
     switch (s) {
         case KDA_OK: return "KDA_OK: success";

@@ -1,0 +1,158 @@
+// Token-by-token KDA update for decoding, and the input validator.
+//
+// Decoding advances each cached state by a few tokens with the recurrence
+// itself (ogis-ri NLP primer on Kimi K3, §3.1 "KDA（Kimi Delta Attention）":
+// decay, probe, delta, write, read-out):
+//   S <- Diag(alpha_t) S;  p = S^T k_t;  S <- S + beta_t k_t (v_t - p)^T;  o_t = S^T q_t
+// which is exactly the order the chunked pass reproduces in bulk.  The work
+// is bound by moving the fp32 state (2 d_k d_v 4 bytes per sequence and head
+// and call), so one workgroup owns a 64-column block of one state, keeps it in
+// registers for all the call's tokens, and reads and writes it once.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+// ---------------------------------------------------------------- k_decode
+// Workgroup: (sequence, head, 64-column block of S), 256 threads.  Thread
+// (rg, col) = (tid / 64, tid % 64) holds rows [rg*D/4, (rg+1)*D/4) of column
+// col0 + col; a wave therefore reads and writes whole 256-byte row segments.
+// The two contractions over key channels (S^T k and S^T q) sum per thread,
+// then across the four row groups through LDS.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_decode(const E* __restrict__ q, const E* __restrict__ k,
+                                                const E* __restrict__ v, const E* __restrict__ beta,
+                                                const E* __restrict__ g, const float* S_in, float* S_out,
+                                                E* __restrict__ o, int32_t n_tokens, int32_t H) {
+    constexpr int RPT = D / 4;          // rows per thread
+    constexpr int NCB = D / 64;         // column blocks per state
+    __shared__ float sQ[D], sK[D], sA[D];
+    __shared__ float sPart[4][64];
+    const int tid = threadIdx.x, rg = tid >> 6, col = tid & 63;
+    const int cb = blockIdx.x % NCB;
+    const int64_t sh = blockIdx.x / NCB;     // sequence * H + head
+    const int64_t n = sh / H, h = sh % H;
+    const int c = cb * 64 + col;
+    const int64_t sbase = sh * D * D;
+
+    float S[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) S[r] = S_in ? S_in[sbase + (int64_t)(rg * RPT + r) * D + c] : 0.f;
+
+    for (int t = 0; t < n_tokens; ++t) {
+        const int64_t tok = n * n_tokens + t;
+        const int64_t row = (tok * H + h) * D;
+        __syncthreads();   // the previous token's LDS reads are done
+        for (int i = tid; i < 3 * D; i += 256) {
+            const int ch = i % D;
+            if (i < D) sQ[ch] = to_f(q[row + ch]);
+            else if (i < 2 * D) sK[ch] = to_f(k[row + ch]);
+            else sA[ch] = __expf(to_f(g[row + ch]));
+        }
+        const float bt = to_f(beta[tok * H + h]);
+        const float vt = to_f(v[row + c]);
+        __syncthreads();
+        // decay, then probe p = S^T k
+        float p = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            S[r] *= sA[rg * RPT + r];
+            p += sK[rg * RPT + r] * S[r];
+        }
+        sPart[rg][col] = p;
+        __syncthreads();
+        p = sPart[0][col] + sPart[1][col] + sPart[2][col] + sPart[3][col];
+        // delta write, then read-out o = S^T q
+        const float e = bt * (vt - p);
+        float y = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            S[r] += sK[rg * RPT + r] * e;
+            y += sQ[rg * RPT + r] * S[r];
+        }
+        __syncthreads();   // everyone has read sPart
+        sPart[rg][col] = y;
+        __syncthreads();
+        if (rg == 0) o[row + c] = from_f<E>(sPart[0][col] + sPart[1][col] + sPart[2][col] + sPart[3][col]);
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) S_out[sbase + (int64_t)(rg * RPT + r) * D + c] = S[r];
+}
+
+template <typename E, int D>
+static hipError_t launch_decode_t(const DecodePlan& p, hipStream_t st) {
+    const int64_t grid = (int64_t)p.n_seqs * p.n_heads * (D / 64);
+    hipLaunchKernelGGL((k_decode<E, D>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const E*>(p.q),
+                       static_cast<const E*>(p.k), static_cast<const E*>(p.v), static_cast<const E*>(p.beta),
+                       static_cast<const E*>(p.g), p.S_in, p.S_out, static_cast<E*>(p.o), p.n_tokens,
+                       p.n_heads);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
+    if (p.n_seqs == 0 || p.n_heads == 0) return hipSuccess;
+    if (p.bf16) return p.d == 128 ? launch_decode_t<__bf16, 128>(p, st) : launch_decode_t<__bf16, 64>(p, st);
+    return p.d == 128 ? launch_decode_t<float, 128>(p, st) : launch_decode_t<float, 64>(p, st);
+}
+
+// ---------------------------------------------------------------- validator
+// counts[0]: log_alpha elements outside [-5, 0] or not finite
+// counts[1]: beta elements outside [0, 1] or not finite
+// counts[2]: cu_seqlens entries that break cu[0] = 0, cu[i] <= cu[i+1],
+//            cu[n_seqs] = total_tokens
+__global__ __launch_bounds__(64) void k_validate_clear(unsigned long long* counts) {
+    if (threadIdx.x < 3) counts[threadIdx.x] = 0ull;
+}
+
+template <typename E>
+__global__ __launch_bounds__(256) void k_validate(const E* __restrict__ g, int64_t n_g, const E* __restrict__ beta,
+                                                  int64_t n_beta, const int32_t* __restrict__ cu, int32_t n_seqs,
+                                                  int64_t total_tokens, unsigned long long* counts) {
+    unsigned long long bad_g = 0, bad_b = 0, bad_cu = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_g; i += stride) {
+        const float x = to_f(g[i]);
+        bad_g += !(x >= -5.f && x <= 0.f);   // NaN fails both comparisons
+    }
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_beta; i += stride) {
+        const float x = to_f(beta[i]);
+        bad_b += !(x >= 0.f && x <= 1.f);
+    }
+    if (cu) {
+        for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i <= n_seqs; i += stride) {
+            const int64_t a = cu[i];
+            if (i == 0) bad_cu += a != 0;
+            if (i == n_seqs) bad_cu += a != total_tokens;
+            if (i < n_seqs) bad_cu += a > (int64_t)cu[i + 1];
+        }
+    }
+    // wave sums, then one vector atomic per wave and counter
+    for (int off = 32; off > 0; off >>= 1) {
+        bad_g += __shfl_down(bad_g, off);
+        bad_b += __shfl_down(bad_b, off);
+        bad_cu += __shfl_down(bad_cu, off);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        if (bad_g) atomicAdd(&counts[0], bad_g);
+        if (bad_b) atomicAdd(&counts[1], bad_b);
+        if (bad_cu) atomicAdd(&counts[2], bad_cu);
+    }
+}
+
+hipError_t launch_validate(bool bf16, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                           const void* beta, const void* g, const int32_t* cu, unsigned long long* counts,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(k_validate_clear, dim3(1), dim3(64), 0, st, counts);
+    const int64_t n_g = total_tokens * n_heads * d_k, n_beta = total_tokens * n_heads;
+    const int64_t want = (n_g + 255) / 256;
+    const unsigned grid = (unsigned)(want < 1 ? 1 : (want > 4096 ? 4096 : want));
+    if (bf16)
+        hipLaunchKernelGGL((k_validate<__bf16>), dim3(grid), dim3(256), 0, st, static_cast<const __bf16*>(g), n_g,
+                           static_cast<const __bf16*>(beta), n_beta, cu, n_seqs, total_tokens, counts);
+    else
+        hipLaunchKernelGGL((k_validate<float>), dim3(grid), dim3(256), 0, st, static_cast<const float*>(g), n_g,
+                           static_cast<const float*>(beta), n_beta, cu, n_seqs, total_tokens, counts);
+    return hipGetLastError();
+}
+
+}  // namespace kda

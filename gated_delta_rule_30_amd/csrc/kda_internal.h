@@ -51,4 +51,22 @@ extern const char* const kStageNames[kNumStages];
 // ev[kNumStages] after the last.
 hipError_t launch(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
 
+// Token-by-token update for decoding (kda_recurrent_fwd).
+struct DecodePlan {
+    bool bf16;
+    int d;                    // d_k == d_v, 64 or 128
+    int32_t n_seqs, n_tokens, n_heads;
+    const void *q, *k, *v, *beta, *g;
+    const float* S_in;        // may be NULL (zeros); may equal S_out
+    float* S_out;
+    void* o;
+};
+hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
+
+// Input validator (kda_validate_inputs): clears counts[0..2] and adds the
+// number of violations found; see the header.
+hipError_t launch_validate(bool bf16, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                           const void* beta, const void* g, const int32_t* cu, unsigned long long* counts,
+                           hipStream_t stream);
+
 }  // namespace kda

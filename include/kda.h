@@ -107,6 +107,41 @@ kda_status kda_chunk_fwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_s
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  float* stage_ms);
 
+/* Token-by-token KDA update for decoding: each of n_seqs sequences advances
+ * its cached state by n_tokens >= 1 tokens with the recurrence above, taken
+ * one token at a time (ogis-ri NLP primer on Kimi K3, §3.1 "KDA": decay,
+ * probe, delta, write, read-out), and emits their outputs.  Same layouts as
+ * kda_chunk_fwd with n_seqs equal-length sequences of n_tokens tokens:
+ *   q, k, log_alpha : [n_seqs * n_tokens, n_heads, d_k]   (dtype dt)
+ *   v, o            : [n_seqs * n_tokens, n_heads, d_v]   (dtype dt)
+ *   beta            : [n_seqs * n_tokens, n_heads]        (dtype dt)
+ *   S_in            : [n_seqs, n_heads, d_k, d_v] float32, or NULL (zeros)
+ *   S_out           : [n_seqs, n_heads, d_k, d_v] float32 (required); may be
+ *                     the same buffer as S_in (updated in place)
+ * Meant for a few tokens per call (the work per sequence and head is
+ * sequential over its tokens); longer spans belong to kda_chunk_fwd, which
+ * gives the same results.  Needs no workspace.  Supported: d_k == d_v in
+ * {64, 128}, dt KDA_F32 or KDA_BF16; n_seqs * n_tokens < 2^31.  Enqueued on
+ * `stream`, never synchronises; errors as for kda_chunk_fwd. */
+kda_status kda_recurrent_fwd(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                             int32_t d_k, int32_t d_v,
+                             const void* q, const void* k, const void* v,
+                             const void* beta, const void* log_alpha,
+                             const float* S_in, float* S_out, void* o, void* stream);
+
+/* Debug check of the value-range preconditions that the compute entry points
+ * do not check: counts[0] receives the number of log_alpha elements outside
+ * [-5, 0] or not finite, counts[1] the number of beta elements outside
+ * [0, 1] or not finite, counts[2] the number of cu_seqlens entries that break
+ * cu[0] == 0, cu[i] <= cu[i+1], cu[n_seqs] == total_tokens (0 when
+ * cu_seqlens is NULL).  `counts` is caller-owned DEVICE memory for 3
+ * uint64 values (8-byte aligned); the call clears and fills it on `stream`
+ * and returns without synchronising, so read it after the stream has
+ * reached this point.  Argument errors as for kda_chunk_fwd. */
+kda_status kda_validate_inputs(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                               int32_t d_k, const void* beta, const void* log_alpha,
+                               const int32_t* cu_seqlens, unsigned long long* counts, void* stream);
+
 /* Number of kernel launches one forward pass makes, and the name of launch i
  * (NULL when i is out of range); names match the kernel symbols a profiler
  * reports. */

@@ -105,3 +105,37 @@ def test_binding_rejects_host_tensors():
         kda.chunk_fwd(x, x, x, torch.zeros(4, 2), x)
     with pytest.raises(TypeError):
         kda.chunk_fwd(x.double(), x, x, torch.zeros(4, 2), x)
+
+
+def test_recurrent_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    fake = 0x7f0000000000          # never dereferenced: every case fails validation
+
+    def call(dt=kda.KDA_BF16, N=2, n=1, H=2, dk=64, dv=64, q=fake, S_in=None, S_out=fake, o=fake):
+        return lib.kda_recurrent_fwd(dt, N, n, H, dk, dv, P(q), P(fake), P(fake), P(fake), P(fake),
+                                     P(S_in), P(S_out), P(o), None)
+    assert call(dt=5) == ERR_DTYPE
+    assert call(N=0) == ERR_SHAPE
+    assert call(n=0) == ERR_SHAPE
+    assert call(dk=96, dv=96) == ERR_UNSUPPORTED
+    assert call(dk=64, dv=128) == ERR_UNSUPPORTED
+    assert call(N=1 << 20, n=1 << 12) == ERR_UNSUPPORTED
+    assert call(q=None) == ERR_NULL
+    assert call(S_out=None) == ERR_NULL
+    assert call(o=None) == ERR_NULL
+    assert call(o=fake + 4) == ERR_SHAPE
+    assert call(S_in=fake + 8) == ERR_SHAPE
+
+
+def test_validate_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    fake = 0x7f0000000000
+
+    def call(dt=kda.KDA_BF16, T=16, N=1, H=2, dk=64, beta=fake, g=fake, counts=fake):
+        return lib.kda_validate_inputs(dt, T, N, H, dk, P(beta), P(g), None, P(counts), None)
+    assert call(dt=9) == ERR_DTYPE
+    assert call(T=-1) == ERR_SHAPE
+    assert call(N=0) == ERR_SHAPE
+    assert call(counts=None) == ERR_NULL
+    assert call(beta=None) == ERR_NULL
+    assert call(counts=fake + 4) == ERR_SHAPE
