@@ -89,6 +89,41 @@ def cpu_baseline(inp, n_heads_sample):
             "seconds": dt}
 
 
+def decode_measure(torch, kda, dev, reps=50):
+    """Serving decode step: 64 sequences x 32 heads, d=128, bf16, one token per
+    sequence per call, state updated in place.  Bound by moving the fp32 state
+    (read + write 2 d^2 4 B per sequence and head)."""
+    N, H, d, n = 64, 32, 128, 1
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device=dev, dtype=torch.float32)
+    q = torch.nn.functional.normalize(rnd(N * n, H, d), dim=-1).to(torch.bfloat16)
+    k = torch.nn.functional.normalize(rnd(N * n, H, d), dim=-1).to(torch.bfloat16)
+    v = rnd(N * n, H, d).to(torch.bfloat16)
+    beta = torch.sigmoid(rnd(N * n, H)).to(torch.bfloat16)
+    la = (-5.0 * torch.sigmoid(2.0 * rnd(N * n, H, d))).to(torch.bfloat16)
+    S = 0.02 * rnd(N, H, d, d)
+    o = torch.empty_like(v)
+    for _ in range(3):
+        kda.recurrent_fwd(q, k, v, beta, la, S_in=S, S_out=S, n_seqs=N, o=o)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        kda.recurrent_fwd(q, k, v, beta, la, S_in=S, S_out=S, n_seqs=N, o=o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = N * H * (2 * d * d * 4 + n * (4 * d * 2 + 2 + d * 2))
+    return {"workload": "decode, bf16, N=%d sequences x %d token, H=%d, d=%d, fp32 state in place" % (N, n, H, d),
+            "us_per_call": us, "tokens_per_s": N * n / (us * 1e-6),
+            "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                         "algorithmic_bytes_per_call": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +224,7 @@ def main():
         "stage_ms": stage_ms, "roofline": roof, "wall_s_timed": wall,
         "device": torch.cuda.get_device_name(dev), "source_sha": source_sha(),
     }
+    out["decode"] = decode_measure(torch, kda, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_heads, H))
     print(json.dumps(out), flush=True)
