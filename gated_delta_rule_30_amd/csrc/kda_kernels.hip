@@ -217,21 +217,26 @@ template <typename E, int D>
 __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ g, const E* __restrict__ beta,
                                                    const ChunkInfo* __restrict__ tab,
-                                                   const int32_t* __restrict__ n_chunks_p, int32_t H,
-                                                   ChunkOps ops) {
+                                                   const int32_t* __restrict__ n_chunks_p, int64_t fixed_len,
+                                                   int32_t fixed_chunks, int32_t H, ChunkOps ops) {
     using G = Geo<E, D>;
     using M = Mma<E>;
     constexpr int C = kChunk, CPL = G::CPL, EPV = G::EPV;
     constexpr int PC = D + 8;      // row pitch of the column-operand tiles
-    constexpr int PT = C + 4;      // row pitch of fp32 C x C matrices
     constexpr int PM = C + 8;      // row pitch of the M staging tile (elements)
     constexpr int PK = C + 8;      // row pitch of the K^T staging tile (elements)
+    // A and T are unit / strictly lower block-triangular: only their ten
+    // 16 x 16 blocks (R, J <= R) are stored, block (R, J) at slot
+    // R (R + 1) / 2 + J, rows of BP floats.
+    constexpr int BP = kSub + 4;
+    constexpr int kBlk = kSub * BP;
+    constexpr int kTri = kNSub * (kNSub + 1) / 2 * kBlk;
     // Region 1: A and the T-inverse scratch; before A exists it stages K^T.
     // Region 2: the column bases; after the Gram blocks, T.
-    constexpr int kR1 = C * PT + 4 * 16 * 17;
+    constexpr int kKtBytes = D * PK * (int)sizeof(E);
+    constexpr int kR1 = (kKtBytes / 4 > kTri + 4 * 16 * 17 ? kKtBytes / 4 : kTri + 4 * 16 * 17);
     constexpr int kColBytes = (kNSub - 1) * kSub * PC * (int)sizeof(E);
-    constexpr int kR2 = (kColBytes > C * PT * 4 ? kColBytes : C * PT * 4) / 4;
-    static_assert(D * PK * (int)sizeof(E) <= kR1 * 4, "K^T staging must fit in region 1");
+    constexpr int kR2 = (kColBytes / 4 > kTri ? kColBytes / 4 : kTri);
     __shared__ __attribute__((aligned(16))) float sR1[kR1];
     __shared__ __attribute__((aligned(16))) float sR2[kR2];
     __shared__ float sTot[kNSub * D];         // exp(rho_{R+1} - rho_R)
@@ -241,17 +246,34 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     __shared__ __attribute__((aligned(16))) E sM[C * PM];
     __shared__ float sBeta[C];
     float* sA = sR1;
-    float* sX = sR1 + C * PT;
+    float* sX = sR1 + kTri;
     E* sKt = reinterpret_cast<E*>(sR1);
     E* sColB = reinterpret_cast<E*>(sR2);
     float* sT = sR2;
     // K^T staging: the token index is rotated by 16 per channel group, so
     // the four lane groups that write one token column hit different banks.
     auto kt_at = [](int ch, int t_) { return ch * PK + ((t_ + kSub * (ch / CPL)) & (C - 1)); };
+    // element (row, col) of a lower block-triangular 64 x 64 matrix (col's block <= row's block)
+    auto blk = [](int R, int J) { return (R * (R + 1) / 2 + J) * kBlk; };
+    auto tri = [&](int row, int col) { return blk(row >> 4, col >> 4) + (row & 15) * BP + (col & 15); };
 
+    // Chunk ci: for equal-length sequences (fixed_len > 0) it follows from
+    // the index (fixed_chunks chunks per sequence, in sequence order, as the
+    // chunk table lists them); otherwise it is read from the chunk table.
     const int32_t ci = blockIdx.x;
-    if (ci >= *n_chunks_p) return;
-    const ChunkInfo info = tab[ci];
+    ChunkInfo info;
+    if (fixed_len > 0) {
+        const int32_t per = (int32_t)((fixed_len + kChunk - 1) / kChunk);
+        if (ci >= fixed_chunks) return;
+        const int32_t seq = ci / per, j = ci % per;
+        const int64_t rem = fixed_len - (int64_t)j * kChunk;
+        info.tok0 = (int64_t)seq * fixed_len + (int64_t)j * kChunk;
+        info.seq = seq;
+        info.len = (int32_t)(rem < kChunk ? rem : kChunk);
+    } else {
+        if (ci >= *n_chunks_p) return;
+        info = tab[ci];
+    }
     const int h = blockIdx.y, len = info.len;
     const int tid = threadIdx.x, w = wave_id(), li = lane_id() & 15, lg = lane_id() >> 4;
     const int tok = kSub * w + li;
@@ -299,18 +321,27 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     // operand by exp(rho_w - b), the column base for later row blocks by
     // exp(rho_{w+1} - b), and the inter-chunk operands Q . Gamma, K . Gamma,
     // K . exp(b_L - b).
-    typename M::frag rq[G::NKC], rk[G::NKC], cd[G::NKC];
+    // The diagonal block (w, w) is accumulated here, as each k-step's
+    // operands are formed, so its column operand is never held in full.
+    typename M::frag rq[G::NKC], rk[G::NKC];
+    f32x4 accAd = zero4(), accMd = zero4();
     {
         const float* rho = sCarry + w * D + lg * CPL;
         const float* erho = sERho + w * D + lg * CPL;
         const float* bl = sCarry + kNSub * D + lg * CPL;
         const float* esub = sTot + w * D + lg * CPL;
-        uint4 vq[G::VPL], vk[G::VPL], vc[G::VPL];
-        E* eq = reinterpret_cast<E*>(vq);
-        E* ek = reinterpret_cast<E*>(vk);
-        E* ec = reinterpret_cast<E*>(vc);
+        uint4* qg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Qg) + cbase * C * D);
+        uint4* kg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Kg) + cbase * C * D);
+        uint4* cbv = reinterpret_cast<uint4*>(sColB + (w * kSub + li) * PC + lg * CPL);
+        // Q . Gamma, K . Gamma and the column base are stored one 16-byte
+        // vector at a time, as soon as each is complete.
+        uint4 vq, vk, vc;
+        E* eq = reinterpret_cast<E*>(&vq);
+        E* ek = reinterpret_cast<E*>(&vk);
+        E* ec = reinterpret_cast<E*>(&vc);
 #pragma unroll
         for (int m = 0; m < G::NKC; ++m) {
+            typename M::frag cd;
 #pragma unroll
             for (int j = 0; j < M::KW; ++j) {
                 const int c = m * M::KW + j;
@@ -320,29 +351,26 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
                 if constexpr (M::KW == 1) {
                     rq[m] = qv * fr;
                     rk[m] = kv * fr;
-                    cd[m] = kv * fd;
+                    cd = kv * fd;
                 } else {
                     rq[m][j] = from_f<E>(qv * fr);
                     rk[m][j] = from_f<E>(kv * fr);
-                    cd[m][j] = from_f<E>(kv * fd);
+                    cd[j] = from_f<E>(kv * fd);
                 }
-                ec[c] = from_f<E>(kv * (esub[c] * fd));
-                eq[c] = from_f<E>(qv * gm);
-                ek[c] = from_f<E>(kv * gm);
+                const int cv = c % EPV;   // element within the current 16-byte vector
+                ec[cv] = from_f<E>(kv * (esub[c] * fd));
+                eq[cv] = from_f<E>(qv * gm);
+                ek[cv] = from_f<E>(kv * gm);
                 sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(kv * __expf(bl[c] - b[c]));
+                if (cv == EPV - 1) {
+                    const int i = c / EPV;
+                    qg[(w * G::VPL + i) * 64 + lane_id()] = vq;
+                    kg[(w * G::VPL + i) * 64 + lane_id()] = vk;
+                    if (w < kNSub - 1) cbv[i] = vc;
+                }
             }
-        }
-        uint4* qg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Qg) + cbase * C * D);
-        uint4* kg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Kg) + cbase * C * D);
-#pragma unroll
-        for (int i = 0; i < G::VPL; ++i) {
-            qg[(w * G::VPL + i) * 64 + lane_id()] = vq[i];
-            kg[(w * G::VPL + i) * 64 + lane_id()] = vk[i];
-        }
-        if (w < kNSub - 1) {
-            uint4* cb = reinterpret_cast<uint4*>(sColB + (w * kSub + li) * PC + lg * CPL);
-#pragma unroll
-            for (int i = 0; i < G::VPL; ++i) cb[i] = vc[i];
+            accAd = M::mma(rk[m], cd, accAd);
+            accMd = M::mma(rq[m], cd, accMd);
         }
     }
     __syncthreads();
@@ -363,14 +391,10 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     // Blocks (w, J) for J <= w of A (strict lower, rows scaled by beta) and M
     // (inclusive lower); blocks above the diagonal are never formed.
     for (int J = 0; J <= w; ++J) {
-        f32x4 accA = zero4(), accM = zero4();
-        if (J == w) {
-#pragma unroll
-            for (int m = 0; m < G::NKC; ++m) {
-                accA = M::mma(rk[m], cd[m], accA);
-                accM = M::mma(rq[m], cd[m], accM);
-            }
-        } else {
+        f32x4 accA = accAd, accM = accMd;
+        if (J < w) {
+            accA = zero4();
+            accM = zero4();
             // column operand: base of block J times exp(rho_w - rho_{J+1})
             // (1 when J = w-1; otherwise a per-channel factor from the table)
             const E* cb = sColB + (J * kSub + li) * PC + lg * CPL;
@@ -396,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = kSub * w + 4 * lg + r, col = kSub * J + li;
-            sA[row * PT + col] = (J < w || col < row) ? sBeta[row] * accA[r] : 0.f;
+            sA[tri(row, col)] = (J < w || col < row) ? sBeta[row] * accA[r] : 0.f;
             sM[row * PM + col] = from_f<E>((J < w || col <= row) ? accM[r] : 0.f);
         }
     }
@@ -412,11 +436,11 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
         for (int r = 0; r < kSub; ++r) {
             float s = (r == jc) ? 1.f : 0.f;
 #pragma unroll
-            for (int i = 0; i < r; ++i) s -= sA[(kSub * R + r) * PT + kSub * R + i] * x[i];
+            for (int i = 0; i < r; ++i) s -= sA[blk(R, R) + r * BP + i] * x[i];
             x[r] = s;
         }
 #pragma unroll
-        for (int r = 0; r < kSub; ++r) sT[(kSub * R + r) * PT + kSub * R + jc] = x[r];
+        for (int r = 0; r < kSub; ++r) sT[blk(R, R) + r * BP + jc] = x[r];
     }
     __syncthreads();
     for (int d = 1; d < kNSub; ++d) {
@@ -427,8 +451,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
             for (int K = J; K < R; ++K)
 #pragma unroll
                 for (int kk = 0; kk < kSub; kk += 4)
-                    acc = mma_f32(sA[(kSub * R + li) * PT + kSub * K + kk + lg],
-                                  sT[(kSub * K + kk + lg) * PT + kSub * J + li], acc);
+                    acc = mma_f32(sA[blk(R, K) + li * BP + kk + lg], sT[blk(K, J) + (kk + lg) * BP + li], acc);
 #pragma unroll
             for (int r = 0; r < 4; ++r) sX[w * 272 + (4 * lg + r) * 17 + li] = acc[r];
         }
@@ -437,10 +460,10 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
             f32x4 acc = zero4();
 #pragma unroll
             for (int kk = 0; kk < kSub; kk += 4)
-                acc = mma_f32(sT[(kSub * R + li) * PT + kSub * R + kk + lg], sX[w * 272 + (kk + lg) * 17 + li],
+                acc = mma_f32(sT[blk(R, R) + li * BP + kk + lg], sX[w * 272 + (kk + lg) * 17 + li],
                               acc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sT[(kSub * R + 4 * lg + r) * PT + kSub * J + li] = -acc[r];
+            for (int r = 0; r < 4; ++r) sT[blk(R, J) + (4 * lg + r) * BP + li] = -acc[r];
         }
         __syncthreads();
     }
@@ -458,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
         for (int e = 0; e < EPV; ++e) {
             const int t = G::tok_of(v * EPV + e, lgp);
             const bool upper = (t >> 4) > (r >> 4);   // blocks above the diagonal are zero
-            et[e] = from_f<E>(upper ? 0.f : sT[r * PT + t] * sBeta[t]);
+            et[e] = from_f<E>(upper ? 0.f : sT[tri(r, upper ? r : t)] * sBeta[t]);
             em[e] = upper ? from_f<E>(0.f) : sM[r * PM + t];
         }
         otb[vi] = pt;
@@ -1197,7 +1220,8 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     mark(1);
     if (work)
         hipLaunchKernelGGL((k_prep<E, D>), dim3(p.max_chunks, H), dim3(kThreads), 0, st, q, kk, g, beta, p.ws_tab,
-                           p.ws_n_chunks, H, ops);
+                           p.ws_n_chunks, p.cu_seqlens ? (int64_t)0 : p.fixed_len,
+                           p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk)), H, ops);
     mark(2);
     if constexpr (sizeof(E) == 2)
         hipLaunchKernelGGL((k_recur_lds<D>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st, v, ops, p.cu_seqlens,
