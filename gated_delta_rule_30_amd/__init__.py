@@ -11,8 +11,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_profile", "recurrent_fwd", "validate_inputs", "stage_names", "workspace_size",
-           "status_string", "lib_path", "KDA_F32", "KDA_BF16", "KdaError"]
+__all__ = ["chunk_fwd", "chunk_fwd_profile", "recurrent_fwd", "validate_inputs", "chunk_transition",
+           "compose_states", "sequence_parallel_fwd", "stage_names", "workspace_size", "status_string", "lib_path",
+           "KDA_F32", "KDA_BF16", "KdaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libkda.so")
@@ -57,6 +58,10 @@ def _load():
         lib.kda_recurrent_fwd.restype = ctypes.c_int
         lib.kda_validate_inputs.argtypes = [ctypes.c_int, I64, I32, I32, I32, P, P, P, P, P]
         lib.kda_validate_inputs.restype = ctypes.c_int
+        lib.kda_chunk_transition.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]
+        lib.kda_chunk_transition.restype = ctypes.c_int
+        lib.kda_compose_states.argtypes = [I32, I32, I32, P, P, P, P, P]
+        lib.kda_compose_states.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -257,3 +262,78 @@ def validate_inputs(beta, log_alpha, cu_seqlens=None, n_seqs=None):
         raise KdaError(code, lib.kda_status_string(code).decode())
     c = counts.cpu().tolist()
     return {"log_alpha": c[0], "beta": c[1], "cu_seqlens": c[2]}
+
+
+def chunk_transition(k, beta, log_alpha, cu_seqlens=None, n_seqs=None, workspace=None):
+    """Transition matrices P [N, H, d, d] (kda_chunk_transition): each
+    sequence maps an incoming state S to P S + Z (Z its zero-start state)."""
+    import torch
+    lib = _load()
+    if k.dtype != torch.bfloat16 or beta.dtype != k.dtype or log_alpha.dtype != k.dtype:
+        raise TypeError("chunk_transition takes bfloat16 k, beta, log_alpha")
+    if k.dim() == 4:
+        B = k.shape[0]
+        k, log_alpha = (t.reshape(-1, *t.shape[2:]) for t in (k, log_alpha))
+        beta = beta.reshape(-1, beta.shape[-1])
+    else:
+        B = 1
+    T, H, d = k.shape
+    dev = k.device
+    for name, t in (("k", k), ("beta", beta), ("log_alpha", log_alpha)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on %s" % (name, dev))
+    if cu_seqlens is not None:
+        N = cu_seqlens.numel() - 1
+    else:
+        N = n_seqs if n_seqs is not None else B
+    ws_bytes = int(lib.kda_chunk_fwd_workspace_size(T, N, H, d, d, CHUNK, KDA_BF16))
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    P_out = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    code = lib.kda_chunk_transition(KDA_BF16, T, N, H, d, CHUNK, _ptr(k), _ptr(beta), _ptr(log_alpha),
+                                    _ptr(cu_seqlens), _ptr(P_out), _ptr(workspace),
+                                    0 if workspace is None else workspace.numel(), ctypes.c_void_p(stream))
+    if code != 0:
+        raise KdaError(code, lib.kda_status_string(code).decode())
+    return P_out
+
+
+def compose_states(P, Z, S0=None):
+    """States entering consecutive segments (kda_compose_states):
+    S_in[0] = S0, S_in[g+1] = P[g] S_in[g] + Z[g]; returns [G+1, H, d, d]."""
+    import torch
+    lib = _load()
+    G, H, d, _ = P.shape
+    for name, t in (("P", P), ("Z", Z)):
+        if t.dtype != torch.float32 or t.shape != (G, H, d, d) or not t.is_contiguous():
+            raise ValueError("%s must be contiguous float32 [%d, %d, %d, %d]" % (name, G, H, d, d))
+    if S0 is not None and (S0.dtype != torch.float32 or S0.shape != (H, d, d) or not S0.is_contiguous()):
+        raise ValueError("S0 must be contiguous float32 [%d, %d, %d]" % (H, d, d))
+    S_in = torch.empty((G + 1, H, d, d), dtype=torch.float32, device=P.device)
+    stream = torch.cuda.current_stream(P.device).cuda_stream
+    code = lib.kda_compose_states(G, H, d, _ptr(P), _ptr(Z), _ptr(S0), _ptr(S_in), ctypes.c_void_p(stream))
+    if code != 0:
+        raise KdaError(code, lib.kda_status_string(code).decode())
+    return S_in
+
+
+def sequence_parallel_fwd(q, k, v, beta, log_alpha, S0=None, n_segments=4):
+    """One long sequence ([T, H, d] bf16) by sequence-parallel state passing,
+    on one GPU: the token axis is cut into `n_segments` segments; per segment
+    the zero-start final state Z_g (kda_chunk_fwd, S0 = 0) and the transition
+    P_g (kda_chunk_transition) -- the work each device would do on its own
+    segment --, then the incoming states by composition (kda_compose_states;
+    across devices this is where the one all-gather of (P_g, Z_g) goes), then
+    every segment's outputs from its incoming state.  Returns (o, S_T) equal,
+    to rounding, to chunk_fwd over the whole sequence."""
+    import torch
+    T, H, d = q.shape
+    G = max(1, min(int(n_segments), T))
+    bounds = [round(i * T / G) for i in range(G + 1)]
+    cu = torch.tensor(bounds, dtype=torch.int32, device=q.device)
+    _, Z = chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=cu)
+    P = chunk_transition(k, beta, log_alpha, cu_seqlens=cu)
+    S_in = compose_states(P, Z, None if S0 is None else S0.reshape(H, d, d).contiguous())
+    o, _ = chunk_fwd(q, k, v, beta, log_alpha, S0=S_in[:G].contiguous(), cu_seqlens=cu, output_final_state=False)
+    return o, S_in[G].reshape(1, H, d, d)

@@ -73,10 +73,10 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_
 static kda_status prepare(Plan* p, kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
                           int32_t d_k, int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
                           const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
-                          void* o, float* S_T, void* workspace, size_t workspace_bytes) {
+                          void* o, float* S_T, void* workspace, size_t workspace_bytes, bool no_output = false) {
     kda_status s = plan_sizes(p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, cu_seqlens != nullptr);
     if (s != KDA_OK) return s;
-    if (total_tokens > 0 && (!q || !k || !v || !beta || !log_alpha || !o)) return KDA_ERR_NULL;
+    if (total_tokens > 0 && (!q || !k || !v || !beta || !log_alpha || (!o && !no_output))) return KDA_ERR_NULL;
     const void* ptrs[] = {q, k, v, beta, log_alpha, S0, cu_seqlens, o, S_T};
     for (const void* ptr : ptrs)
         if (ptr && ((uintptr_t)ptr % 16) != 0) return KDA_ERR_SHAPE;
@@ -134,6 +134,34 @@ kda_status kda_chunk_fwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_s
     if (e == hipSuccess) e = hipEventSynchronize(ev[kda::kNumStages]);
     for (int i = 0; e == hipSuccess && i < kda::kNumStages; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
     for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunk_transition(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                                int32_t chunk, const void* k, const void* beta, const void* log_alpha,
+                                const int32_t* cu_seqlens, float* P, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    if (dt == KDA_F32) return KDA_ERR_UNSUPPORTED;
+    if (!P) return KDA_ERR_NULL;
+    Plan p{};
+    // q and v are not read: k stands in for both (sizes and alignment only)
+    kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_k, chunk, k, k, k, beta, log_alpha,
+                           nullptr, cu_seqlens, nullptr, P, workspace, workspace_bytes, true);
+    if (s != KDA_OK) return s;
+    hipError_t e = kda::launch_transition(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_compose_states(int32_t n_segments, int32_t n_heads, int32_t d, const float* P, const float* Z,
+                              const float* S0, float* S_in, void* stream) {
+    if (n_segments < 1 || n_heads < 1 || d < 1) return KDA_ERR_SHAPE;
+    if (d != 64 && d != 128) return KDA_ERR_UNSUPPORTED;
+    if ((int64_t)n_heads * (d / 64) >= ((int64_t)1 << 31)) return KDA_ERR_UNSUPPORTED;
+    if (!P || !Z || !S_in) return KDA_ERR_NULL;
+    const void* ptrs[] = {P, Z, S0, S_in};
+    for (const void* ptr : ptrs)
+        if (ptr && ((uintptr_t)ptr % 16) != 0) return KDA_ERR_SHAPE;
+    hipError_t e = kda::launch_compose(n_segments, n_heads, d, P, Z, S0, S_in, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

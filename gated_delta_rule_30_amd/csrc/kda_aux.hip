@@ -95,6 +95,86 @@ hipError_t launch_decode(const DecodePlan& p, hipStream_t st) {
     return p.d == 128 ? launch_decode_t<float, 128>(p, st) : launch_decode_t<float, 64>(p, st);
 }
 
+// ---------------------------------------------------------------- k_compose
+// Sequence-parallel state passing (orkas.ai "Kimi K3 architecture",
+// §"請求書はサービング側に回ってくる": a segment's final state is its transition
+// applied to the incoming state plus its zero-start state, so the states
+// entering consecutive segments follow by composition):
+//   S_in[0] = S0,  S_in[g+1] = P[g] S_in[g] + Z[g].
+// Columns of S are independent, so a workgroup owns a 64-column block of one
+// head and walks the segments in order, its block resident in LDS.  Thread
+// (tr, tc) = (tid / 16, tid % 16) computes rows [tr*D/16, (tr+1)*D/16) x
+// columns [4 tc, 4 tc + 4) of each product in fp32, P staged through LDS in
+// 32-column panels.
+template <int D>
+__global__ __launch_bounds__(256) void k_compose(const float* __restrict__ P, const float* __restrict__ Z,
+                                                 const float* __restrict__ S0, float* __restrict__ S_in,
+                                                 int32_t G, int32_t H) {
+    constexpr int RPT = D / 16, KP = 32;
+    __shared__ float sS[D][64 + 4];
+    __shared__ float sP[D][KP + 1];
+    const int tid = threadIdx.x, tr = tid >> 4, tc = tid & 15;
+    const int h = blockIdx.x / (D / 64), cb = blockIdx.x % (D / 64);
+    const int col0 = cb * 64;
+    const int64_t hs = (int64_t)D * D;          // one head's state
+    const int64_t gs = (int64_t)H * hs;         // one segment's states
+    for (int i = tid; i < D * 64; i += 256) {
+        const int r = i / 64, c = i % 64;
+        const float x = S0 ? S0[h * hs + (int64_t)r * D + col0 + c] : 0.f;
+        sS[r][c] = x;
+        S_in[h * hs + (int64_t)r * D + col0 + c] = x;
+    }
+    for (int g = 0; g < G; ++g) {
+        float acc[RPT][4];
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+        const float* Pg = P + g * gs + h * hs;
+        for (int l0 = 0; l0 < D; l0 += KP) {
+            __syncthreads();   // sS is complete / the previous panel is consumed
+            for (int i = tid; i < D * KP; i += 256) sP[i / KP][i % KP] = Pg[(int64_t)(i / KP) * D + l0 + i % KP];
+            __syncthreads();
+#pragma unroll 4
+            for (int l = 0; l < KP; ++l) {
+                float b[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) b[c] = sS[l0 + l][4 * tc + c];
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) {
+                    const float a = sP[tr * RPT + r][l];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) acc[r][c] += a * b[c];
+                }
+            }
+        }
+        __syncthreads();   // every product has read sS
+        const float* Zg = Z + g * gs + h * hs;
+        float* Sg = S_in + (g + 1) * gs + h * hs;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int row = tr * RPT + r;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int col = col0 + 4 * tc + c;
+                const float x = acc[r][c] + Zg[(int64_t)row * D + col];
+                sS[row][4 * tc + c] = x;
+                Sg[(int64_t)row * D + col] = x;
+            }
+        }
+    }
+}
+
+hipError_t launch_compose(int32_t G, int32_t H, int32_t d, const float* P, const float* Z, const float* S0,
+                          float* S_in, hipStream_t st) {
+    const unsigned grid = (unsigned)((int64_t)H * (d / 64));
+    if (d == 128)
+        hipLaunchKernelGGL((k_compose<128>), dim3(grid), dim3(256), 0, st, P, Z, S0, S_in, G, H);
+    else
+        hipLaunchKernelGGL((k_compose<64>), dim3(grid), dim3(256), 0, st, P, Z, S0, S_in, G, H);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- validator
 // counts[0]: log_alpha elements outside [-5, 0] or not finite
 // counts[1]: beta elements outside [0, 1] or not finite

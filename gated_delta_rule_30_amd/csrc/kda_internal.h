@@ -51,6 +51,14 @@ extern const char* const kStageNames[kNumStages];
 // ev[kNumStages] after the last.
 hipError_t launch(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
 
+// The forward pass with v = 0 from S0 = I and no output (bf16 only): S_T
+// receives each sequence's transition matrix (kda_chunk_transition).
+hipError_t launch_transition(const Plan& p, hipStream_t stream);
+
+// S_in[0] = S0 (or zeros), S_in[g+1] = P[g] S_in[g] + Z[g] (kda_compose_states).
+hipError_t launch_compose(int32_t n_segments, int32_t n_heads, int32_t d, const float* P, const float* Z,
+                          const float* S0, float* S_in, hipStream_t stream);
+
 // Token-by-token update for decoding (kda_recurrent_fwd).
 struct DecodePlan {
     bool bf16;

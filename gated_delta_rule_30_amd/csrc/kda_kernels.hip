@@ -880,7 +880,12 @@ struct LdsGeo {
     static constexpr int kBufVec = kRecurWaves * kWaveVec;
 };
 
-template <int D>
+// kTransition: the same chunk steps with v = 0 from S = I and no output, so
+// that S_T is the sequence's transition matrix prod_t (I - beta_t k_t k_t^T)
+// Diag(alpha_t) (orkas.ai "Kimi K3 architecture", §"請求書はサービング側に回ってくる":
+// a segment's final state is its transition applied to the incoming state
+// plus its zero-start state).  v, S0 and o are not accessed.
+template <int D, bool kTransition>
 __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     const __bf16* __restrict__ v, ChunkOps ops, const int32_t* __restrict__ cu, int64_t total_tokens,
     int64_t fixed_len, const int32_t* __restrict__ seq_chunk0, int32_t NH, int32_t H, const float* __restrict__ S0,
@@ -970,8 +975,9 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             else {
                 int row = kSub * cw + (lane >> 1);
                 row = row < len ? row : len - 1;
-                const void* misc = lane < 32 ? static_cast<const void*>(vv + ((int64_t)j * C + row) * rs)
-                                             : static_cast<const void*>(gm + (int64_t)j * D + kSub * RT * cw);
+                const void* misc = (lane < 32 && !kTransition)
+                                       ? static_cast<const void*>(vv + ((int64_t)j * C + row) * rs)
+                                       : static_cast<const void*>(gm + (int64_t)j * D + kSub * RT * cw);
                 dma(misc, dst + b * 64);
             }
         };
@@ -1019,6 +1025,9 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             else if (line < kOpsLines) { t_base[k] = (const char*)ops.Mm + cb * kBs + off - 3 * kBq - kBs; t_step[k] = kBs; }
             else if (line < kOpsLines + kGamLines) {
                 t_base[k] = (const char*)(ops.gam + cb * D) + (int64_t)(line - kOpsLines) * 128;
+                t_step[k] = (int64_t)D * 4;
+            } else if (kTransition) {   // no value rows: warm Gamma_L again instead
+                t_base[k] = (const char*)(ops.gam + cb * D);
                 t_step[k] = (int64_t)D * 4;
             } else {
                 const int vl = line - kOpsLines - kGamLines;
@@ -1082,7 +1091,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     }
 
     // ---------------------------------------------------- compute waves
-    __bf16* const o_base = o + (s_start * H + h) * D + col0 + li;
+    const int64_t o_off = (s_start * H + h) * D + col0 + li;
     // S[a][r] = state[channel 16*(RT*w + a) + 4*lg + r][column col0 + li]
     f32x4 S[RT];
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
@@ -1091,7 +1100,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int ch = kSub * (RT * w + a) + 4 * lg + r;
-            S[a][r] = S0 ? S0[sbase + (int64_t)ch * D + col0 + li] : 0.f;
+            if constexpr (kTransition) S[a][r] = ch == col0 + li ? 1.f : 0.f;
+            else S[a][r] = S0 ? S0[sbase + (int64_t)ch * D + col0 + li] : 0.f;
         }
     auto put_state = [&]() {
 #pragma unroll
@@ -1125,7 +1135,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = kSub * w + 4 * lg + r;
-            const float vv = to_f(vrows[(4 * lg + r) * SW + li]);
+            const float vv = kTransition ? 0.f : to_f(vrows[(4 * lg + r) * SW + li]);
             sYt[li * PY + t] = from_f<E>(t < len ? vv - accX[r] : 0.f);
         }
         F ftb[G::NKT], fmm[G::NKT], fkt[RT][G::NKT];
@@ -1170,11 +1180,13 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         // S^T is last read before the Y barrier of this step; the barrier at
         // the top of the next step publishes the new one.
         put_state();
-        E* oj = o_base + (int64_t)j * C * rs;
+        if constexpr (!kTransition) {
+            E* oj = o + o_off + (int64_t)j * C * rs;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = kSub * w + 4 * lg + r;
-            if (t < len) oj[(int64_t)t * rs] = from_f<E>(accO[r]);
+            for (int r = 0; r < 4; ++r) {
+                const int t = kSub * w + 4 * lg + r;
+                if (t < len) oj[(int64_t)t * rs] = from_f<E>(accO[r]);
+            }
         }
     };
 
@@ -1198,13 +1210,13 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 // `ev`, when given, holds kNumStages + 1 events: ev[i] is recorded before
 // stage i and ev[kNumStages] after the last one (a stage that does not run
 // for these sizes still gets its pair of records, with nothing between them).
-template <typename E, int D>
+template <typename E, int D, bool kTransition = false>
 static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     auto mark = [&](int i) {
         if (ev) (void)hipEventRecord(ev[i], st);
     };
     constexpr int CT = 1;
-    const E* q = static_cast<const E*>(p.q);
+    const E* q = static_cast<const E*>(kTransition ? p.k : p.q);   // the transition does not use q
     const E* kk = static_cast<const E*>(p.k);
     const E* v = static_cast<const E*>(p.v);
     const E* beta = static_cast<const E*>(p.beta);
@@ -1223,9 +1235,11 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
                            p.ws_n_chunks, p.cu_seqlens ? (int64_t)0 : p.fixed_len,
                            p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk)), H, ops);
     mark(2);
+    static_assert(!kTransition || sizeof(E) == 2, "transition pass: bf16 operands only");
     if constexpr (sizeof(E) == 2)
-        hipLaunchKernelGGL((k_recur_lds<D>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st, v, ops, p.cu_seqlens,
-                           p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, H, p.S0, p.S_T, static_cast<E*>(p.o));
+        hipLaunchKernelGGL((k_recur_lds<D, kTransition>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st, v, ops,
+                           p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, H, p.S0, p.S_T,
+                           static_cast<E*>(p.o));
     else
         hipLaunchKernelGGL((k_recur<E, D, CT>), dim3(NH * (D / (kSub * CT))), dim3(kThreads), 0, st, v, ops,
                            p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, H, p.S0, p.S_T,
@@ -1243,6 +1257,11 @@ hipError_t launch(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     }
     // fp32 operands are built for d = 64 only; the C ABI rejects other sizes.
     return launch_all<float, 64>(p, st, ev);
+}
+
+hipError_t launch_transition(const Plan& p, hipStream_t st) {
+    if (p.d == 128) return launch_all<__bf16, 128, true>(p, st, nullptr);
+    return launch_all<__bf16, 64, true>(p, st, nullptr);
 }
 
 }  // namespace kda

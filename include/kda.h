@@ -107,6 +107,40 @@ kda_status kda_chunk_fwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_s
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  float* stage_ms);
 
+/* Transition matrices of a packed batch: for each sequence n and head h,
+ *     P[n, h] = prod over its tokens, last first, of (I - beta_t k_t k_t^T) Diag(alpha_t)
+ * so that the sequence maps an incoming state S to P S + Z, Z being its
+ * zero-start final state (kda_chunk_fwd with S0 = NULL).  This is the
+ * segment transition of sequence-parallel state passing (orkas.ai "Kimi K3
+ * architecture", §"請求書はサービング側に回ってくる"): with a long sequence cut into
+ * segments, the states entering the segments follow from every segment's
+ * (P, Z) by kda_compose_states, after which each segment's outputs are
+ * kda_chunk_fwd from its incoming state.  Computed by the chunked pass with
+ * v = 0 from S0 = I (no output is produced).
+ *   k, beta, log_alpha, cu_seqlens : as for kda_chunk_fwd (q and v are not used)
+ *   P : output [n_seqs, n_heads, d_k, d_k] float32
+ *   workspace : >= kda_chunk_fwd_workspace_size(total_tokens, n_seqs, n_heads,
+ *               d_k, d_k, chunk, dt) bytes
+ * Supported: dt == KDA_BF16, d_k in {64, 128}, chunk == 64; otherwise as
+ * kda_chunk_fwd.  Enqueued on `stream`, never synchronises. */
+kda_status kda_chunk_transition(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                                int32_t d_k, int32_t chunk,
+                                const void* k, const void* beta, const void* log_alpha,
+                                const int32_t* cu_seqlens, float* P,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* State composition of sequence-parallel state passing: for n_segments
+ * consecutive segments of one sequence with transitions P[g] and zero-start
+ * states Z[g] (per head), the states entering the segments:
+ *     S_in[0] = S0 (zeros if NULL),  S_in[g+1] = P[g] S_in[g] + Z[g]
+ * (S_in[n_segments] is the final state).  fp32 throughout.
+ *   P    : [n_segments, n_heads, d, d]       Z : [n_segments, n_heads, d, d]
+ *   S0   : [n_heads, d, d] or NULL           S_in : output [n_segments + 1, n_heads, d, d]
+ * Supported: d in {64, 128}; n_segments >= 1.  S_in must not overlap P, Z
+ * or S0.  Enqueued on `stream`, never synchronises. */
+kda_status kda_compose_states(int32_t n_segments, int32_t n_heads, int32_t d, const float* P,
+                              const float* Z, const float* S0, float* S_in, void* stream);
+
 /* Token-by-token KDA update for decoding: each of n_seqs sequences advances
  * its cached state by n_tokens >= 1 tokens with the recurrence above, taken
  * one token at a time (ogis-ri NLP primer on Kimi K3, §3.1 "KDA": decay,

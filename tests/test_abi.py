@@ -139,3 +139,25 @@ def test_validate_rejects_bad_arguments(lib):
     assert call(counts=None) == ERR_NULL
     assert call(beta=None) == ERR_NULL
     assert call(counts=fake + 4) == ERR_SHAPE
+
+
+def test_transition_and_compose_reject_bad_arguments(lib):
+    P = ctypes.c_void_p
+    fake = 0x7f0000000000
+
+    def tr(dt=kda.KDA_BF16, T=128, N=1, H=2, d=64, C=64, Pout=fake, ws=0x100000, ws_bytes=0):
+        return lib.kda_chunk_transition(dt, T, N, H, d, C, P(fake), P(fake), P(fake), None, P(Pout), P(ws),
+                                        ws_bytes, None)
+    assert tr(dt=kda.KDA_F32) == ERR_UNSUPPORTED
+    assert tr(Pout=None) == ERR_NULL
+    assert tr(d=96) == ERR_UNSUPPORTED
+    assert tr(C=32) == ERR_UNSUPPORTED
+    assert tr(ws_bytes=16) == ERR_WORKSPACE
+
+    def comp(G=2, H=2, d=64, Pp=fake, Z=fake, S0=None, S=fake):
+        return lib.kda_compose_states(G, H, d, P(Pp), P(Z), P(S0), P(S), None)
+    assert comp(G=0) == ERR_SHAPE
+    assert comp(d=96) == ERR_UNSUPPORTED
+    assert comp(Pp=None) == ERR_NULL
+    assert comp(S=None) == ERR_NULL
+    assert comp(Z=fake + 4) == ERR_SHAPE
