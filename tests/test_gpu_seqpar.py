@@ -31,15 +31,21 @@ def _bf(torch, dev, x):
     return torch.from_numpy(np.ascontiguousarray(x)).to(dev).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("lengths,H,d", [([300], 2, 128), ([150, 77, 0, 64, 200], 3, 64), ([1, 65], 2, 128)],
-                         ids=["one-seq-d128", "varlen-d64", "tiny-d128"])
-def test_transition_matches_oracle(torch_dev, lengths, H, d):
+# With the workloads' decay (mean log-decay -2.5) a transition over more than
+# a few tokens is ~exp(-2.5 T) and compares as zero; `weak` rescales the
+# log-decay into (-0.025, 0) so the products of (I - beta k k^T) stay O(1).
+@pytest.mark.parametrize("lengths,H,d,weak", [([300], 2, 128, True), ([150, 77, 0, 64, 200], 3, 64, True),
+                                              ([1, 65], 2, 128, False), ([300], 2, 128, False)],
+                         ids=["one-seq-d128-weak", "varlen-d64-weak", "tiny-d128", "one-seq-d128"])
+def test_transition_matches_oracle(torch_dev, lengths, H, d, weak):
     """P = prod (I - beta k k^T) Diag(alpha): the oracle's recurrence with
     v = 0 from S0 = I gives it exactly (its S_T)."""
     import gated_delta_rule_30_amd as kda
     torch, dev = torch_dev
     spec = ki.custom("tr", "bf16", lengths, H, d, varlen=True, seed=len(lengths) + d)
     inp = ki.generate_numpy(spec)
+    if weak:
+        inp.g[:] = ki.round_bf16(inp.g * 0.005)
     cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
     P = kda.chunk_transition(_bf(torch, dev, inp.k), _bf(torch, dev, inp.beta), _bf(torch, dev, inp.g),
                              cu_seqlens=cu)
@@ -48,7 +54,7 @@ def test_transition_matches_oracle(torch_dev, lengths, H, d):
     eye = np.broadcast_to(np.eye(d), (N, H, d, d)).copy()
     _, P_ref = oracle.forward(inp.k, inp.k, np.zeros_like(inp.v), inp.beta, inp.g, eye, inp.cu_seqlens)
     err = oracle.parity_error(P.cpu().numpy(), P_ref)
-    _say("transition %s H=%d d=%d: err %.3e" % (lengths, H, d, err))
+    _say("transition %s H=%d d=%d weak=%s: err %.3e (max|P| %.2e)" % (lengths, H, d, weak, err, np.abs(P_ref).max()))
     assert err <= 2e-2
     for n, L in enumerate(lengths):
         if L == 0:
@@ -74,12 +80,15 @@ def test_compose_states_matches_definition(torch_dev):
         assert err <= 1e-5
 
 
-@pytest.mark.parametrize("T,H,d,G", [(1000, 2, 128, 4), (777, 3, 64, 5), (4096, 2, 128, 8)])
-def test_sequence_parallel_matches_single_pass_oracle(torch_dev, T, H, d, G):
+@pytest.mark.parametrize("T,H,d,G,weak", [(1000, 2, 128, 4, False), (777, 3, 64, 5, False), (4096, 2, 128, 8, False),
+                                          (1000, 2, 128, 4, True), (777, 3, 64, 5, True)])
+def test_sequence_parallel_matches_single_pass_oracle(torch_dev, T, H, d, G, weak):
     import gated_delta_rule_30_amd as kda
     torch, dev = torch_dev
     spec = ki.custom("sp", "bf16", [T], H, d, s0_std=0.3, varlen=False, seed=T + G)
     inp = ki.generate_numpy(spec)
+    if weak:   # incoming states carry across segments
+        inp.g[:] = ki.round_bf16(inp.g * 0.005)
     t = [_bf(torch, dev, getattr(inp, name)) for name in ("q", "k", "v", "beta", "g")]
     S0 = torch.from_numpy(inp.S0).to(dev)
     o, ST = kda.sequence_parallel_fwd(*t, S0=S0, n_segments=G)
@@ -87,5 +96,5 @@ def test_sequence_parallel_matches_single_pass_oracle(torch_dev, T, H, d, G):
     o_ref, S_ref = oracle.forward(inp.q, inp.k, inp.v, inp.beta, inp.g, inp.S0, inp.cu_seqlens)
     eo = oracle.parity_error(o.float().cpu().numpy(), o_ref, inp.cu_seqlens)
     es = oracle.parity_error(ST.cpu().numpy(), S_ref)
-    _say("sequence-parallel T=%d H=%d d=%d G=%d: o %.3e  S_T %.3e" % (T, H, d, G, eo, es))
+    _say("sequence-parallel T=%d H=%d d=%d G=%d weak=%s: o %.3e  S_T %.3e" % (T, H, d, G, weak, eo, es))
     assert eo <= 2e-2 and es <= 2e-2
