@@ -124,6 +124,37 @@ def decode_measure(torch, kda, dev, reps=50):
                          "algorithmic_bytes_per_call": nbytes}}
 
 
+def seqpar_measure(torch, kda, inp, ms_single, reps=3):
+    """Sequence-parallel state passing on one GPU over the same workload (8
+    segments): per segment the zero-start state and the transition, the
+    composition, and the per-segment forward from the composed states.  On
+    G GPUs each does 1/G of the two passes and the rerun; one GPU does all of
+    them, so this shows the extra work of the scheme, not a speed-up."""
+    G = 8
+    q, k, v, beta, g, S0 = inp.q, inp.k, inp.v, inp.beta, inp.g, inp.S0   # [T, H, d], one sequence
+    kda.sequence_parallel_fwd(q, k, v, beta, g, S0=S0, n_segments=G)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        kda.sequence_parallel_fwd(q, k, v, beta, g, S0=S0, n_segments=G)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / reps * 1e3
+    H, d = q.shape[1], q.shape[2]
+    P = torch.zeros((G, H, d, d), dtype=torch.float32, device=q.device)
+    Z = torch.zeros_like(P)
+    kda.compose_states(P, Z)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        kda.compose_states(P, Z)
+    e1.record()
+    torch.cuda.synchronize()
+    return {"segments": G, "ms_per_pass": ms, "vs_single_pass": ms / ms_single,
+            "compose_us": e0.elapsed_time(e1) / 10 * 1e3,
+            "note": "one GPU runs every segment: Z pass + transition pass + rerun, about 3 single passes"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +256,8 @@ def main():
         "device": torch.cuda.get_device_name(dev), "source_sha": source_sha(),
     }
     out["decode"] = decode_measure(torch, kda, dev)
+    if spec.dtype == "bf16" and spec.n_seqs == 1:
+        out["sequence_parallel"] = seqpar_measure(torch, kda, inp, ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_heads, H))
     print(json.dumps(out), flush=True)
