@@ -49,6 +49,10 @@ def _bind(path):
         P, P, P, P, P, P, P, ctypes.c_int64, ctypes.c_int64, P, P, ctypes.c_int]
     lib.kda_oracle_forward.restype = ctypes.c_int
     lib.kda_oracle_max_threads.restype = ctypes.c_int
+    lib.kda_oracle_backward.argtypes = [
+        ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+        P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_int]
+    lib.kda_oracle_backward.restype = ctypes.c_int
     return lib
 
 
@@ -74,6 +78,7 @@ def compile_variant(src_text: str, out_path: str):
 
     def fwd(*args, **kw):
         return forward(*args, _lib=lib, **kw)
+    fwd.backward = lambda *args, **kw: backward(*args, _lib=lib, **kw)
     return fwd
 
 
@@ -129,6 +134,32 @@ def forward(q, k, v, beta, g, S0=None, cu_seqlens=None, out_range=None, n_thread
     if rc != 0:
         raise ValueError("kda_oracle_forward failed with code %d" % rc)
     return o, ST
+
+
+def backward(q, k, v, beta, g, dO, S0=None, dS_T=None, cu_seqlens=None, n_threads=0, _lib=None):
+    """Gradients of the fp64 recurrence for output gradients dO [T_total, H,
+    d_v] and final-state gradients dS_T [N, H, d_k, d_v] (None = zeros).
+    Returns dict(dq, dk, dv, dbeta, dg, dS0) in fp64 (dg is the gradient of
+    log alpha)."""
+    q, k, v, beta, g, S0, dO, dS_T = (_f64(a) for a in (q, k, v, beta, g, S0, dO, dS_T))
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    cu = (np.array([0, T], dtype=np.int64) if cu_seqlens is None
+          else np.ascontiguousarray(np.asarray(cu_seqlens), dtype=np.int64))
+    N = len(cu) - 1
+    assert dO.shape == (T, H, dv)
+    if dS_T is not None:
+        assert dS_T.shape == (N, H, dk, dv)
+    out = dict(dq=np.zeros((T, H, dk)), dk=np.zeros((T, H, dk)), dv=np.zeros((T, H, dv)),
+               dbeta=np.zeros((T, H)), dg=np.zeros((T, H, dk)), dS0=np.zeros((N, H, dk, dv)))
+    lib = _lib if _lib is not None else _load()
+    rc = lib.kda_oracle_backward(T, N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0),
+                                 _ptr(cu), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]),
+                                 _ptr(out["dv"]), _ptr(out["dbeta"]), _ptr(out["dg"]), _ptr(out["dS0"]),
+                                 int(n_threads))
+    if rc != 0:
+        raise ValueError("kda_oracle_backward failed with code %d" % rc)
+    return out
 
 
 def parity_error(x, ref, cu_seqlens=None, token_axis=0, head_axis=1, floor=1e-30):
