@@ -282,8 +282,11 @@ MUTATIONS = {
 def test_pins_catch_planted_mistake(name, tmp_path):
     old, new = MUTATIONS[name]
     src = oracle.source_text()
-    assert src.count(old) == 1, name
-    fwd = oracle.compile_variant(src.replace(old, new), str(tmp_path / ("oracle_%s.so" % name)))
+    # plant in the forward recurrence only (the backward follows it in the file)
+    cut = src.index("int kda_oracle_backward(")
+    fwd_src, rest = src[:cut], src[cut:]
+    assert fwd_src.count(old) == 1, name
+    fwd = oracle.compile_variant(fwd_src.replace(old, new) + rest, str(tmp_path / ("oracle_%s.so" % name)))
     caught = []
     for pin in PINS:
         try:
