@@ -99,3 +99,18 @@ def test_planted_backward_mistakes_are_caught(tmp_path, what, old, new):
     c = _case(9, [4, 3], 1, 3, 2)
     grads = fwd.backward(c["q"], c["k"], c["v"], c["beta"], c["g"], c["dO"], c["S0"], c["dST"], c["cu"])
     assert _fd_error(c, grads) > 1e-4, what
+
+
+@pytest.mark.parametrize("lengths,chunk", [([37, 20], 16), ([70], 64), ([5, 0, 9], 4), ([130], 64)],
+                         ids=["varlen-c16", "one-c64", "empty-c4", "three-chunks-c64"])
+def test_chunked_backward_matches_recurrence_backward(lengths, chunk):
+    """The chunk-level backward algebra (the form the GPU backward follows)
+    gives the recurrence oracle's gradients to rounding, at any chunk size."""
+    from oracle import chunked
+    c = _case(sum(lengths) + chunk, lengths, 2, 8, 6)
+    ref = oracle.backward(c["q"], c["k"], c["v"], c["beta"], c["g"], c["dO"], c["S0"], c["dST"], c["cu"])
+    got = chunked.backward_chunked(c["q"], c["k"], c["v"], c["beta"], c["g"], c["dO"], c["S0"], c["dST"],
+                                   c["cu"], chunk=chunk)
+    for _, gname in NAMES:
+        err = np.max(np.abs(got[gname] - ref[gname])) / max(1e-30, np.max(np.abs(ref[gname])))
+        assert err < 1e-12, (gname, err)
