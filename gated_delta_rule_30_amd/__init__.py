@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_profile", "recurrent_fwd", "validate_inputs", "chunk_transition",
+__all__ = ["chunk_fwd", "chunk_fwd_profile", "chunk_bwd", "chunk_bwd_profile", "bwd_stage_names", "recurrent_fwd", "validate_inputs", "chunk_transition",
            "compose_states", "sequence_parallel_fwd", "stage_names", "workspace_size", "status_string", "lib_path",
            "KDA_F32", "KDA_BF16", "KdaError"]
 
@@ -62,6 +62,16 @@ def _load():
         lib.kda_chunk_transition.restype = ctypes.c_int
         lib.kda_compose_states.argtypes = [I32, I32, I32, P, P, P, P, P]
         lib.kda_compose_states.restype = ctypes.c_int
+        lib.kda_chunk_bwd_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, ctypes.c_int]
+        lib.kda_chunk_bwd_workspace_size.restype = SZ
+        lib.kda_chunk_bwd.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, I32,
+                                      P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P]
+        lib.kda_chunk_bwd.restype = ctypes.c_int
+        lib.kda_chunk_bwd_profile.argtypes = lib.kda_chunk_bwd.argtypes + [P]
+        lib.kda_chunk_bwd_profile.restype = ctypes.c_int
+        lib.kda_profile_bwd_num_stages.restype = ctypes.c_int32
+        lib.kda_profile_bwd_stage_name.argtypes = [ctypes.c_int32]
+        lib.kda_profile_bwd_stage_name.restype = ctypes.c_char_p
         _lib = lib
     return _lib
 
@@ -170,6 +180,76 @@ def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = C
     if batched:
         o = o.reshape(B, -1, H, dv)
     return o, (S_T if output_final_state else None)
+
+
+def bwd_stage_names():
+    lib = _load()
+    return [lib.kda_profile_bwd_stage_name(i).decode() for i in range(lib.kda_profile_bwd_num_stages())]
+
+
+def chunk_bwd_profile(*args, **kw):
+    """Same as chunk_bwd, through the measurement entry point: blocks until
+    done and returns (grads, {kernel name: milliseconds})."""
+    ms = (ctypes.c_float * _load().kda_profile_bwd_num_stages())()
+    grads = chunk_bwd(*args, _stage_ms=ms, **kw)
+    return grads, dict(zip(bwd_stage_names(), [float(x) for x in ms]))
+
+
+def chunk_bwd(q, k, v, beta, log_alpha, dO, S0=None, dS_T=None, cu_seqlens=None, chunk: int = CHUNK,
+              n_seqs=None, workspace=None, _stage_ms=None):
+    """KDA chunkwise backward on the GPU (kda_chunk_bwd).
+
+    Inputs as for chunk_fwd (bfloat16, 3-D packed [T, H, d] or 4-D [B, T, H, d]);
+    dO shaped like v; dS_T [N, H, d_k, d_v] float32 or None.  Returns a dict
+    with dq, dk, dv, dbeta, dg (gradient of log_alpha; shapes and dtype of the
+    inputs) and dS0 ([N, H, d_k, d_v] float32)."""
+    import torch
+    lib = _load()
+    dt, dev = _check_common(q, k, v, beta, log_alpha)
+    batched = q.dim() == 4
+    shape_q, shape_v, shape_b = q.shape, v.shape, beta.shape
+    if batched:
+        B = q.shape[0]
+        q, k, v, log_alpha, dO = (t.reshape(-1, *t.shape[2:]) for t in (q, k, v, log_alpha, dO))
+        beta = beta.reshape(-1, beta.shape[-1])
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    if (k.shape != (T, H, dk) or log_alpha.shape != (T, H, dk) or v.shape != (T, H, dv)
+            or beta.shape != (T, H) or dO.shape != (T, H, dv)):
+        raise ValueError("inconsistent shapes")
+    if dO.dtype != q.dtype or dO.device != dev or not dO.is_contiguous():
+        raise ValueError("dO must be contiguous %s on %s" % (q.dtype, dev))
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor on %s" % dev)
+        N = cu_seqlens.numel() - 1
+    else:
+        N = n_seqs if n_seqs is not None else (B if batched else 1)
+    for name, t in (("S0", S0), ("dS_T", dS_T)):
+        if t is not None and (t.dtype != torch.float32 or t.shape != (N, H, dk, dv) or t.device != dev
+                              or not t.is_contiguous()):
+            raise ValueError("%s must be contiguous float32 [%d, %d, %d, %d] on %s" % (name, N, H, dk, dv, dev))
+    ws_bytes = int(lib.kda_chunk_bwd_workspace_size(T, N, H, dk, dv, chunk, dt))
+    if ws_bytes == 0:
+        code = lib.kda_chunk_bwd(dt, T, N, H, dk, dv, chunk, *([None] * 15), 0, None)
+        raise KdaError(code, lib.kda_status_string(code).decode())
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dbeta=torch.empty_like(beta), dg=torch.empty_like(log_alpha),
+               dS0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev))
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    args = (dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(S0),
+            _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+            _ptr(out["dbeta"]), _ptr(out["dg"]), _ptr(out["dS0"]), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    code = lib.kda_chunk_bwd(*args) if _stage_ms is None else lib.kda_chunk_bwd_profile(*args, _stage_ms)
+    if code != 0:
+        raise KdaError(code, lib.kda_status_string(code).decode())
+    if batched:
+        for key, shp in (("dq", shape_q), ("dk", shape_q), ("dg", shape_q), ("dv", shape_v), ("dbeta", shape_b)):
+            out[key] = out[key].reshape(shp)
+    return out
 
 
 def _check_common(q, k, v, beta, log_alpha):

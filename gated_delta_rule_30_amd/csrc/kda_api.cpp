@@ -32,6 +32,15 @@ size_t carve_workspace(Plan* p, void* base) {
     p->ws_Kg = take(es * mc * H * kChunkTokens * D);
     p->ws_KhT = take(es * mc * H * D * kChunkTokens);
     p->ws_gam = (float*)take(4 * mc * H * D);
+    if (p->bwd) {
+        const size_t T = (size_t)p->total_tokens;
+        p->ws_bet = (float*)take(4 * mc * H * kChunkTokens);
+        p->ws_ckS = take(2 * mc * H * D * D);
+        p->ws_ckdS = take(2 * mc * H * D * D);
+        p->ws_Y = take(2 * T * H * D);
+        p->ws_U = take(2 * T * H * D);
+        p->ws_dZ = take(2 * T * H * D);
+    }
     return off;
 }
 
@@ -204,6 +213,97 @@ kda_status kda_validate_inputs(kda_dtype dt, int64_t total_tokens, int32_t n_seq
     if ((uintptr_t)counts % 8 != 0) return KDA_ERR_SHAPE;
     hipError_t e = kda::launch_validate(dt == KDA_BF16, total_tokens, n_seqs, n_heads, d_k, beta, log_alpha,
                                         cu_seqlens, counts, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_chunk_bwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                                    int32_t d_v, int32_t chunk, kda_dtype dt) {
+    if (dt != KDA_BF16) return 0;
+    Plan p{};
+    if (plan_sizes(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, true) != KDA_OK) return 0;
+    p.bwd = true;
+    return kda::carve_workspace(&p, nullptr);
+}
+
+static kda_status prepare_bwd(Plan* p, kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                              int32_t d_k, int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
+                              const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
+                              const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dbeta,
+                              void* dlog_alpha, float* dS0, void* workspace, size_t workspace_bytes) {
+    if (dt == KDA_F32) return KDA_ERR_UNSUPPORTED;
+    kda_status s = plan_sizes(p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, cu_seqlens != nullptr);
+    if (s != KDA_OK) return s;
+    p->bwd = true;
+    if (total_tokens > 0 && (!q || !k || !v || !beta || !log_alpha || !dO || !dq || !dk || !dv || !dbeta ||
+                             !dlog_alpha))
+        return KDA_ERR_NULL;
+    const void* ptrs[] = {q, k, v, beta, log_alpha, S0, cu_seqlens, dO, dS_T, dq, dk, dv, dbeta, dlog_alpha, dS0};
+    for (const void* ptr : ptrs)
+        if (ptr && ((uintptr_t)ptr % 16) != 0) return KDA_ERR_SHAPE;
+    if (!workspace || (uintptr_t)workspace % kda::kAlign != 0) return KDA_ERR_WORKSPACE;
+    Plan sz = *p;
+    if (workspace_bytes < kda::carve_workspace(&sz, nullptr)) return KDA_ERR_WORKSPACE;
+    p->q = q;
+    p->k = k;
+    p->v = v;
+    p->beta = beta;
+    p->g = log_alpha;
+    p->S0 = S0;
+    p->cu_seqlens = cu_seqlens;
+    p->dO = dO;
+    p->dS_T = dS_T;
+    p->dq = dq;
+    p->dk = dk;
+    p->dv = dv;
+    p->dbeta = dbeta;
+    p->dg = dlog_alpha;
+    p->dS0 = dS0;
+    kda::carve_workspace(p, workspace);
+    return KDA_OK;
+}
+
+kda_status kda_chunk_bwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                         int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v, const void* beta,
+                         const void* log_alpha, const float* S0, const int32_t* cu_seqlens, const void* dO,
+                         const float* dS_T, void* dq, void* dk, void* dv, void* dbeta, void* dlog_alpha, float* dS0,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    Plan p{};
+    kda_status s = prepare_bwd(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
+                               cu_seqlens, dO, dS_T, dq, dk, dv, dbeta, dlog_alpha, dS0, workspace,
+                               workspace_bytes);
+    if (s != KDA_OK) return s;
+    hipError_t e = kda::launch_bwd(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+int32_t kda_profile_bwd_num_stages(void) { return kda::kNumBwdStages; }
+
+const char* kda_profile_bwd_stage_name(int32_t i) {
+    return (i >= 0 && i < kda::kNumBwdStages) ? kda::kBwdStageNames[i] : nullptr;
+}
+
+kda_status kda_chunk_bwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                                 int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
+                                 const void* beta, const void* log_alpha, const float* S0,
+                                 const int32_t* cu_seqlens, const void* dO, const float* dS_T, void* dq, void* dk,
+                                 void* dv, void* dbeta, void* dlog_alpha, float* dS0, void* workspace,
+                                 size_t workspace_bytes, void* stream, float* stage_ms) {
+    if (!stage_ms) return KDA_ERR_NULL;
+    Plan p{};
+    kda_status s = prepare_bwd(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
+                               cu_seqlens, dO, dS_T, dq, dk, dv, dbeta, dlog_alpha, dS0, workspace,
+                               workspace_bytes);
+    if (s != KDA_OK) return s;
+    constexpr int NS = kda::kNumBwdStages;
+    hipEvent_t ev[NS + 1];
+    int made = 0;
+    hipError_t e = hipSuccess;
+    for (; made <= NS && e == hipSuccess; ++made) e = hipEventCreate(&ev[made]);
+    if (e != hipSuccess) made -= 1;
+    if (e == hipSuccess) e = kda::launch_bwd(p, static_cast<hipStream_t>(stream), ev);
+    if (e == hipSuccess) e = hipEventSynchronize(ev[NS]);
+    for (int i = 0; e == hipSuccess && i < NS; ++i) e = hipEventElapsedTime(&stage_ms[i], ev[i], ev[i + 1]);
+    for (int i = 0; i < made; ++i) (void)hipEventDestroy(ev[i]);
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -1,0 +1,376 @@
+// KDA backward: the per-chunk gradient kernel (gfx950).
+//
+// The backward pass of the chunkwise forward (ogis-ri NLP primer on Kimi K3,
+// §3.1 "KDA": the chunked form; orkas.ai "Kimi K3 architecture",
+// §"GPU のコードパスを一本消した「下界」": the 16-token sub-tiles) runs as
+//   k_prep + k_recur_lds<kCkpt>  forward again, keeping per chunk the
+//                                incoming state S and per token Y = V - (K.Gamma)S
+//                                and U~ = T diag(beta) Y
+//   k_prep<kBwd> + k_recur_lds<kBwd>  the state-gradient recurrence, last
+//                                chunk first: dv, dZ = T^T dU~ per token, the
+//                                outgoing-state gradient dS' per chunk, dS0
+//   k_grad (here)                everything else, chunk-parallel.
+//
+// Per chunk (b = cumsum of log alpha inside the chunk, Gamma = exp(b),
+// gamma = Gamma at the last token, K^ = K . exp(b_L - b), dY = dv):
+//   d(Q.Gamma) = dO S^T     d(K.Gamma) = -dY S^T     dK^ = U~ dS'^T
+//   dgamma_c = sum_j dS'_cj S_cj
+//   dA  = -tril(dZ U~^T, -1)    (= -T^T dU~ Z^T T^T with Z = diag(beta) Y)
+//   dGq =  tril(dO U~^T)
+//   dbeta_r = sum_j dZ_rj Y_rj + sum_{i<r} dA_ri Gk_ri
+// where Gk and Gq are the decayed Gram matrices sum_c x_rc k_ic exp(b_rc - b_ic)
+// of K and Q with K (A = diag(beta) Gk, M = Gq).  Their gradients reach the
+// tokens' q, k and b:
+//   row side    dKr = diag(beta) dKrA,  dKrA_rc = sum_i dA_ri k_ic e^{b_rc - b_ic}
+//               dQr_rc = sum_i dGq_ri k_ic e^{b_rc - b_ic}
+//   column side dKc_ic = sum_r (beta_r dA_ri k_rc + dGq_ri q_rc) e^{b_rc - b_ic}
+// and sum_i dA_ri Gk_ri = sum_c k_rc dKrA_rc gives the second dbeta term.
+// db collects every e^{+-b} factor's derivative; dg is its reverse
+// cumulative sum over the chunk (b is the cumulative sum of g).
+//
+// Decay factors follow the forward's sub-tiling: with rho_R = b at the end of
+// sub-tile R-1, every MFMA operand carries a factor <= 1 and the remaining
+// factor in [1, e^80] is applied to the fp32 result:
+//   row side, r in R, i in J <= R:
+//     e^{b_r - b_i} = e^{b_r - rho_{R+1}} . e^{rho_{R+1} - rho_{J+1}} . e^{rho_{J+1} - b_i}
+//   column side, i in J, r in R >= J:
+//     e^{b_r - b_i} = e^{b_r - rho_R} . e^{rho_R - rho_J} . e^{rho_J - b_i}
+//
+// Geometry: one workgroup of 8 waves per (chunk, head).  Wave v handles the
+// chunk's token tile w = v & 3 and half hh = v >> 2 of the key channels.
+// Every product is formed transposed (rows = key channels, columns =
+// tokens), so that lane 16 lg + li ends up holding token 16w + li and
+// channels 16n + 4lg + r (n in its half, r < 4) of every result: the decay
+// cumulative sum over tokens is a 16-lane row scan, and all per-element
+// terms combine in registers.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr int kGradThreads = 512;
+
+// 8 bf16 from LDS, each scaled by s in fp32, as an MFMA fragment
+__device__ inline bf16x8 load_scaled(const __bf16* p, float s) {
+    bf16x8 f = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = (__bf16)((float)f[e] * s);
+    return f;
+}
+
+__device__ inline bf16x8 as_frag(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+template <int D>
+__global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
+    using E = __bf16;
+    using M = Mma<E>;
+    using F = M::frag;
+    constexpr int C = kChunk;
+    constexpr int NT = D / 16;        // channel tiles
+    constexpr int NTH = NT / 2;       // channel tiles per half
+    constexpr int CH = 4 * NTH;       // channels per lane
+    constexpr int KV = D / M::KS;     // k-steps of a contraction over value columns
+    constexpr int PSd = D + 8;        // pitch of the staged states (elements)
+    constexpr int PT = C + 8;         // pitch of token-indexed rows
+    constexpr int kX = (2 * D * PSd > 3 * D * PT) ? 2 * D * PSd : 3 * D * PT;
+    // Region X: S and dS' ([channel][value column]); later the Gram operands
+    // ([channel][token]).
+    __shared__ __attribute__((aligned(16))) E sX[kX];
+    __shared__ __attribute__((aligned(16))) E sdA[C * PT];     // dA      [r][i]
+    __shared__ __attribute__((aligned(16))) E sdGq[C * PT];    // dGq     [r][i]
+    __shared__ __attribute__((aligned(16))) E sdGkT[C * PT];   // beta dA [i][r]
+    __shared__ __attribute__((aligned(16))) E sdGqT[C * PT];   // dGq     [i][r]
+    __shared__ float sRho[(kNSub + 1) * D];   // rho_0 .. rho_3, b_L
+    __shared__ float sTot[kNSub * D];         // sub-tile sums of log alpha
+    __shared__ float sCol[kNSub * D];         // per tile: sum over tokens of dK^ . K^
+    __shared__ float sRev[kNSub * D];         // per tile: sum of db
+    __shared__ float sDgam[D];
+    __shared__ float sBeta[C];
+    __shared__ float sDb2[2 * C];
+    E* sS = sX;
+    E* sdS = sX + D * PSd;
+    E* sKD = sX;               // k_i e^{rho_{J+1} - b_i}
+    E* sKr = sX + D * PT;      // k_r e^{b_r - rho_R}
+    E* sQr = sX + 2 * D * PT;  // q_r e^{b_r - rho_R}
+
+    const int32_t ci = blockIdx.x;
+    ChunkInfo info;
+    if (a.fixed_len > 0) {
+        const int32_t per = (int32_t)((a.fixed_len + C - 1) / C);
+        if (ci >= a.fixed_chunks) return;
+        const int32_t seq = ci / per, j = ci % per;
+        const int64_t rem = a.fixed_len - (int64_t)j * C;
+        info.tok0 = (int64_t)seq * a.fixed_len + (int64_t)j * C;
+        info.seq = seq;
+        info.len = (int32_t)(rem < C ? rem : C);
+    } else {
+        if (ci >= *a.n_chunks) return;
+        info = a.tab[ci];
+    }
+    const int h = blockIdx.y, len = info.len, H = a.H;
+    const int tid = threadIdx.x, wv = tid >> 6, w = wv & 3, hh = wv >> 2;
+    const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int t = kSub * w + li;
+    const bool ok = t < len;
+    const int64_t rs = (int64_t)H * D;
+    const int64_t row = (info.tok0 + (ok ? t : 0)) * rs + (int64_t)h * D;   // this lane's token row
+    const int64_t slot = (int64_t)h * a.max_chunks + ci;
+    auto chan = [&](int i, int r) { return kSub * (hh * NTH + i) + 4 * lg + r; };
+
+    // ---- inputs at (token t, this lane's channels); decay cumulative sum
+    float qf[CH], kf[CH], b[CH];
+#pragma unroll
+    for (int i = 0; i < NTH; ++i) {
+        const int64_t at = row + chan(i, 0);
+        uint2 rq = make_uint2(0, 0), rk = rq, rg = rq;
+        if (ok) {
+            rq = *reinterpret_cast<const uint2*>(a.q + at);
+            rk = *reinterpret_cast<const uint2*>(a.k + at);
+            rg = *reinterpret_cast<const uint2*>(a.g + at);
+        }
+        const E* eq = reinterpret_cast<const E*>(&rq);
+        const E* ek = reinterpret_cast<const E*>(&rk);
+        const E* eg = reinterpret_cast<const E*>(&rg);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            qf[4 * i + r] = (float)eq[r];
+            kf[4 * i + r] = (float)ek[r];
+            b[4 * i + r] = row_scan16((float)eg[r]);
+        }
+    }
+    const float bt = ok ? (float)a.beta[(info.tok0 + t) * H + h] : 0.f;
+    if (hh == 0 && lg == 0) sBeta[t] = bt;
+    if (li == 15) {
+#pragma unroll
+        for (int i = 0; i < NTH; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sTot[w * D + chan(i, r)] = b[4 * i + r];
+    }
+    // token rows of dO, dY, U~, dZ, Y as fragments over value columns
+    uint4 fo[KV], fy[KV], fu[KV], fz[KV];
+    float dbeta1 = 0.f;
+    {
+        const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < KV; ++m) {
+            const int64_t at = row + M::KS * m + M::KW * lg;
+            fo[m] = ok ? *reinterpret_cast<const uint4*>(a.dO + at) : z;
+            fy[m] = ok ? *reinterpret_cast<const uint4*>(a.dv + at) : z;
+            fu[m] = ok ? *reinterpret_cast<const uint4*>(a.U + at) : z;
+            fz[m] = ok ? *reinterpret_cast<const uint4*>(a.dZ + at) : z;
+            const uint4 yv = ok ? *reinterpret_cast<const uint4*>(a.Y + at) : z;
+            const bf16x8 zf = as_frag(fz[m]), yf = as_frag(yv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dbeta1 += (float)zf[e] * (float)yf[e];
+        }
+        dbeta1 += __shfl_xor(dbeta1, 16);
+        dbeta1 += __shfl_xor(dbeta1, 32);
+    }
+    // S and dS' of this chunk into LDS
+    {
+        const uint4* gS = reinterpret_cast<const uint4*>(a.ckS + slot * D * D);
+        const uint4* gD = reinterpret_cast<const uint4*>(a.ckdS + slot * D * D);
+        for (int vi = tid; vi < D * D / 8; vi += kGradThreads) {
+            const int c = vi / (D / 8), j8 = vi % (D / 8);
+            *reinterpret_cast<uint4*>(&sS[c * PSd + 8 * j8]) = gS[vi];
+            *reinterpret_cast<uint4*>(&sdS[c * PSd + 8 * j8]) = gD[vi];
+        }
+    }
+    __syncthreads();
+    for (int c = tid; c < D; c += kGradThreads) {
+        float run = 0.f;
+#pragma unroll
+        for (int R = 0; R < kNSub; ++R) {
+            sRho[R * D + c] = run;
+            run += sTot[R * D + c];
+        }
+        sRho[kNSub * D + c] = run;
+    }
+    // dgamma_c = sum_j dS'_cj S_cj
+    {
+        constexpr int TPC = kGradThreads / D;   // threads per channel
+        const int c = tid / TPC, part = tid % TPC;
+        float acc = 0.f;
+        for (int j = part * (D / TPC); j < (part + 1) * (D / TPC); ++j)
+            acc += (float)sS[c * PSd + j] * (float)sdS[c * PSd + j];
+#pragma unroll
+        for (int o = 1; o < TPC; o <<= 1) acc += __shfl_xor(acc, o);
+        if (part == 0) sDgam[c] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NTH; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) b[4 * i + r] += sRho[w * D + chan(i, r)];
+
+    // ---- products with the states: d(Q.Gamma), d(K.Gamma), dK^
+    float dq[CH], dk[CH], db[CH];
+#pragma unroll
+    for (int i = 0; i < NTH; ++i) {
+        const int n = hh * NTH + i;
+        f32x4 aq = zero4(), ak = zero4(), ah = zero4();
+#pragma unroll
+        for (int m = 0; m < KV; ++m) {
+            const F fs = M::load(&sS[(kSub * n + li) * PSd + M::KS * m + M::KW * lg]);
+            const F fd = M::load(&sdS[(kSub * n + li) * PSd + M::KS * m + M::KW * lg]);
+            aq = M::mma(fs, as_frag(fo[m]), aq);
+            ak = M::mma(fs, as_frag(fy[m]), ak);
+            ah = M::mma(fd, as_frag(fu[m]), ah);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int x = 4 * i + r, c = chan(i, r);
+            const float G = __expf(b[x]), eh = __expf(sRho[kNSub * D + c] - b[x]);
+            const float dqg = aq[r], dkg = -ak[r], dkh = ah[r];
+            dq[x] = dqg * G;
+            dk[x] = dkg * G + dkh * eh;
+            const float hk = dkh * kf[x] * eh;   // dK^ . K^
+            db[x] = (dqg * qf[x] + dkg * kf[x]) * G - hk;
+            const float cs = row_scan16(hk);          // column sum over the tile's tokens
+            if (li == 15) sCol[w * D + c] = cs;
+        }
+    }
+    // ---- dA and dGq, row block w; this half takes column blocks 2hh, 2hh+1
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int J = 2 * hh + jj;
+        f32x4 accA = zero4(), accG = zero4();
+        if (J <= w) {
+            uint4 fj[KV];
+            const int tj = kSub * J + li;
+            const bool okj = tj < len;
+            const int64_t rowj = (info.tok0 + (okj ? tj : 0)) * rs + (int64_t)h * D;
+#pragma unroll
+            for (int m = 0; m < KV; ++m)
+                fj[m] = (J == w) ? fu[m]
+                        : okj   ? *reinterpret_cast<const uint4*>(a.U + rowj + M::KS * m + M::KW * lg)
+                                : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int m = 0; m < KV; ++m) {
+                accA = M::mma(as_frag(fz[m]), as_frag(fj[m]), accA);
+                accG = M::mma(as_frag(fo[m]), as_frag(fj[m]), accG);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = kSub * w + 4 * lg + r, ii = kSub * J + li;
+            const float dA = ii < rr ? -accA[r] : 0.f;
+            const float dG = ii <= rr ? accG[r] : 0.f;
+            sdA[rr * PT + ii] = (E)dA;
+            sdGq[rr * PT + ii] = (E)dG;
+            sdGkT[ii * PT + rr] = (E)(sBeta[rr] * dA);
+            sdGqT[ii * PT + rr] = (E)dG;
+        }
+    }
+    __syncthreads();   // S and dS' are dead: region X takes the Gram operands
+
+#pragma unroll
+    for (int i = 0; i < NTH; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int x = 4 * i + r, c = chan(i, r);
+            const float r0 = sRho[w * D + c], r1 = sRho[(w + 1) * D + c];
+            sKD[c * PT + t] = (E)(kf[x] * __expf(r1 - b[x]));
+            sKr[c * PT + t] = (E)(kf[x] * __expf(b[x] - r0));
+            sQr[c * PT + t] = (E)(qf[x] * __expf(b[x] - r0));
+        }
+    __syncthreads();
+
+    // ---- Gram gradients
+    float dbeta2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NTH; ++i) {
+        const int n = hh * NTH + i, cA = kSub * n + li;   // channel of this lane's A-operand row
+        // row side: output tokens r in tile R = w; contraction over i in blocks J <= R
+        f32x4 accK = zero4(), accQ = zero4();
+        {
+            const int R = w;
+            const float rR1 = sRho[(R + 1) * D + cA];
+            for (int m = 0; m <= R / 2; ++m) {
+                const int J = 2 * m + (lg >> 1);
+                const float fac = J <= R ? __expf(rR1 - sRho[(J + 1) * D + cA]) : 1.f;
+                const F fa = load_scaled(&sKD[cA * PT + M::KS * m + M::KW * lg], fac);
+                accK = M::mma(fa, M::load(&sdA[(kSub * w + li) * PT + M::KS * m + M::KW * lg]), accK);
+                accQ = M::mma(fa, M::load(&sdGq[(kSub * w + li) * PT + M::KS * m + M::KW * lg]), accQ);
+            }
+        }
+        // column side: output tokens i in tile J = w; contraction over r in blocks R >= J
+        f32x4 accC = zero4();
+        {
+            const int J = w;
+            const float rJ = sRho[J * D + cA];
+            for (int m = J / 2; m < C / M::KS; ++m) {
+                const int R = 2 * m + (lg >> 1);
+                const float fac = R > J ? __expf(sRho[R * D + cA] - rJ) : 1.f;
+                const int at = cA * PT + M::KS * m + M::KW * lg;
+                const int bt_at = (kSub * w + li) * PT + M::KS * m + M::KW * lg;
+                accC = M::mma(load_scaled(&sKr[at], fac), M::load(&sdGkT[bt_at]), accC);
+                accC = M::mma(load_scaled(&sQr[at], fac), M::load(&sdGqT[bt_at]), accC);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int x = 4 * i + r, c = chan(i, r);
+            const float orow = __expf(b[x] - sRho[(w + 1) * D + c]);
+            const float ocol = __expf(sRho[w * D + c] - b[x]);
+            const float dkra = accK[r] * orow, dqr = accQ[r] * orow, dkc = accC[r] * ocol;
+            const float dkr = bt * dkra;
+            dq[x] += dqr;
+            dk[x] += dkr + dkc;
+            db[x] += kf[x] * (dkr - dkc) + qf[x] * dqr;
+            dbeta2 += kf[x] * dkra;
+        }
+    }
+    dbeta2 += __shfl_xor(dbeta2, 16);
+    dbeta2 += __shfl_xor(dbeta2, 32);
+    if (lg == 0) sDb2[hh * C + t] = dbeta2;
+    __syncthreads();
+
+    // ---- b_L terms on the last row, then dg = reverse cumulative sum of db
+    float rv[CH];
+#pragma unroll
+    for (int i = 0; i < NTH; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int x = 4 * i + r, c = chan(i, r);
+            if (t == C - 1) {
+                float cs = sDgam[c] * __expf(sRho[kNSub * D + c]);
+#pragma unroll
+                for (int W = 0; W < kNSub; ++W) cs += sCol[W * D + c];
+                db[x] += cs;
+            }
+            rv[x] = row_rscan16(db[x]);
+            if (li == 0) sRev[w * D + c] = rv[x];
+        }
+    __syncthreads();
+    if (!ok) return;
+#pragma unroll
+    for (int i = 0; i < NTH; ++i) {
+        bf16x4 oq, ok4, og;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int x = 4 * i + r, c = chan(i, r);
+            float dgv = rv[x];
+            for (int W = w + 1; W < kNSub; ++W) dgv += sRev[W * D + c];
+            oq[r] = (E)dq[x];
+            ok4[r] = (E)dk[x];
+            og[r] = (E)dgv;
+        }
+        const int64_t at = row + chan(i, 0);
+        *reinterpret_cast<bf16x4*>(a.dq + at) = oq;
+        *reinterpret_cast<bf16x4*>(a.dk + at) = ok4;
+        *reinterpret_cast<bf16x4*>(a.dg + at) = og;
+    }
+    if (hh == 0 && lg == 0) a.dbeta[(info.tok0 + t) * H + h] = (E)(dbeta1 + sDb2[t] + sDb2[C + t]);
+}
+
+hipError_t launch_grad(const GradArgs& a, int d, int32_t max_chunks, hipStream_t st) {
+    if (max_chunks <= 0) return hipSuccess;
+    if (d == 128)
+        hipLaunchKernelGGL(k_grad<128>, dim3(max_chunks, a.H), dim3(kGradThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_grad<64>, dim3(max_chunks, a.H), dim3(kGradThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace kda

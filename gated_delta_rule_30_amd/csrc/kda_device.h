@@ -65,6 +65,31 @@ template <typename E> __device__ inline float to_f(E x) { return static_cast<flo
 template <typename E> __device__ inline E from_f(float x) { return static_cast<E>(x); }
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
+
+// Scans along the 16 lanes of a DPP row (lanes 16g .. 16g+15), zero fill:
+// row_scan16 is the inclusive prefix sum, row_rscan16 the inclusive suffix sum.
+template <int kShift>
+__device__ inline float row_shr(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | kShift, 0xf, 0xf, true));
+}
+template <int kShift>
+__device__ inline float row_shl(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x100 | kShift, 0xf, 0xf, true));
+}
+__device__ inline float row_scan16(float x) {
+    x += row_shr<1>(x);
+    x += row_shr<2>(x);
+    x += row_shr<4>(x);
+    x += row_shr<8>(x);
+    return x;
+}
+__device__ inline float row_rscan16(float x) {
+    x += row_shl<1>(x);
+    x += row_shl<2>(x);
+    x += row_shl<4>(x);
+    x += row_shl<8>(x);
+    return x;
+}
 __device__ inline int wave_id() { return threadIdx.x >> 6; }
 
 }  // namespace kda

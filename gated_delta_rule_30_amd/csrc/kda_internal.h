@@ -36,7 +36,30 @@ struct Plan {
     void* ws_Kg;              // [H, max_chunks, 64, D] K . Gamma
     void* ws_KhT;             // [H, max_chunks, D, 64] (K . exp(b_L - b))^T
     float* ws_gam;            // [H, max_chunks, D] exp(b_L), fp32
+    // backward pass (kda_chunk_bwd); workspace regions carved when `bwd` is set
+    bool bwd;
+    const void* dO;           // [T, H, D] output gradients
+    const float* dS_T;        // [N, H, D, D] final-state gradients or NULL
+    void *dq, *dk, *dv, *dbeta, *dg;
+    float* dS0;               // [N, H, D, D] or NULL
+    float* ws_bet;            // [H, max_chunks, 64] beta per chunk, fp32
+    void* ws_ckS;             // [H, max_chunks, D, D] state entering each chunk (bf16)
+    void* ws_ckdS;            // [H, max_chunks, D, D] gradient of each chunk's outgoing state (bf16)
+    void *ws_Y, *ws_U, *ws_dZ;   // [T, H, D] bf16: Y, U~ and dZ per token
 };
+
+// Arguments of the per-chunk gradient kernel (kda_bwd.hip); bf16 tensors.
+struct GradArgs {
+    const __bf16 *q, *k, *g, *beta, *dO, *dv, *Y, *U, *dZ, *ckS, *ckdS;
+    const ChunkInfo* tab;
+    const int32_t* n_chunks;
+    int64_t fixed_len;        // > 0: equal-length sequences (chunk from the index)
+    int32_t fixed_chunks;
+    int32_t H;
+    int64_t max_chunks;
+    __bf16 *dq, *dk, *dbeta, *dg;
+};
+hipError_t launch_grad(const GradArgs& a, int d, int32_t max_chunks, hipStream_t stream);
 
 // Byte offsets of every workspace region for the given sizes; returns the
 // total size.  `base` may be NULL (size query only).
@@ -50,6 +73,11 @@ extern const char* const kStageNames[kNumStages];
 // kNumStages + 1 events; ev[i] is recorded before stage i and
 // ev[kNumStages] after the last.
 hipError_t launch(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
+
+// Backward pass (bf16): kNumBwdStages launches, events as for launch().
+constexpr int kNumBwdStages = 6;
+extern const char* const kBwdStageNames[kNumBwdStages];
+hipError_t launch_bwd(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
 
 // The forward pass with v = 0 from S0 = I and no output (bf16 only): S_T
 // receives each sequence's transition matrix (kda_chunk_transition).

@@ -167,20 +167,6 @@ struct RowSlice {
     }
 };
 
-// 16-lane inclusive prefix sum along a row of 16 lanes (DPP row_shr, zero fill).
-template <int kShift>
-__device__ inline float row_shr(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x110 | kShift, 0xf, 0xf, true));
-}
-
-__device__ inline float row_scan16(float x) {
-    x += row_shr<1>(x);
-    x += row_shr<2>(x);
-    x += row_shr<4>(x);
-    x += row_shr<8>(x);
-    return x;
-}
-
 // Chunk operands written by k_prep for k_recur, stored head-major: the
 // operands of chunk ci of head h sit at slot h * max_chunks + ci, so one
 // head's chunks are contiguous and the sequential kernel streams through
@@ -196,10 +182,17 @@ __device__ inline float row_scan16(float x) {
 // 16 * lg + li holds row li's contraction elements in k-step order (over
 // channels: lg*D/4 + i; over the chunk's tokens: KS*(i/KW) + KW*lg + i%KW).
 // One wave then loads a fragment vector as 1 KB of contiguous memory.
+//
+// The backward pass reuses the same five buffers for the transposed set its
+// state-gradient recurrence needs (k_prep with kBwd):
+//   TB  <- T^T                 Mm  <- M^T               Qg  <- K . exp(b_L - b)
+//   Kg  <- (Q . Gamma)^T       KhT <- (K . Gamma)^T      gam (unchanged)
+//   bet [64] fp32 beta of the chunk's tokens (0 past the end)
 struct ChunkOps {
     void *TB, *Mm, *Qg, *Kg, *KhT;
     float* gam;
     int64_t max_chunks;   // slots per head
+    float* bet;           // backward set only
 };
 
 // ---------------------------------------------------------------- k_prep
@@ -213,7 +206,11 @@ struct ChunkOps {
 //   exp(rho_w - rho_{J+1}) = prod_{R=J+1}^{w-1} exp(rho_{R+1} - rho_R)
 // The per-channel factors are computed once per chunk; per element only
 // exp(x), exp(-x) and exp(b_L - b) remain.
-template <typename E, int D>
+//
+// kBwd writes the backward set of operands (see ChunkOps) from the same
+// quantities: K . exp(b_L - b) row-wise, (Q . Gamma)^T and (K . Gamma)^T
+// through two transposing LDS stages, T^T and M^T, and beta.
+template <typename E, int D, bool kBwd = false>
 __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ g, const E* __restrict__ beta,
                                                    const ChunkInfo* __restrict__ tab,
@@ -245,6 +242,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     __shared__ float sCarry[(kNSub + 1) * D]; // rho_0 .. rho_3, b_L
     __shared__ __attribute__((aligned(16))) E sM[C * PM];
     __shared__ float sBeta[C];
+    __shared__ __attribute__((aligned(16))) E sQt[kBwd ? D * PK : 8];   // (Q . Gamma)^T staging (kBwd)
+    static_assert(!kBwd || sizeof(E) == 2, "backward operands: bf16 only");
     float* sA = sR1;
     float* sX = sR1 + kTri;
     E* sKt = reinterpret_cast<E*>(sR1);
@@ -288,6 +287,9 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     xg.load(g + off, ok);
     const float bet = ok ? to_f(beta[(info.tok0 + tok) * H + h]) : 0.f;
     if (lg == 0) sBeta[tok] = bet;
+    if constexpr (kBwd) {
+        if (lg == 0) ops.bet[((int64_t)h * ops.max_chunks + ci) * C + tok] = bet;
+    }
 
     // Cumulative log-decay: 16-lane row scan per sub-tile, carries between
     // sub-tiles, and the per-channel factors.
@@ -359,13 +361,21 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
                 }
                 const int cv = c % EPV;   // element within the current 16-byte vector
                 ec[cv] = from_f<E>(kv * (esub[c] * fd));
-                eq[cv] = from_f<E>(qv * gm);
-                ek[cv] = from_f<E>(kv * gm);
-                sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(kv * __expf(bl[c] - b[c]));
+                if constexpr (kBwd) {
+                    // row-wise K . exp(b_L - b) into the Qg slot; Gamma-scaled
+                    // Q and K staged for their transposes
+                    eq[cv] = from_f<E>(kv * __expf(bl[c] - b[c]));
+                    sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(kv * gm);
+                    sQt[kt_at(lg * CPL + c, tok)] = from_f<E>(qv * gm);
+                } else {
+                    eq[cv] = from_f<E>(qv * gm);
+                    ek[cv] = from_f<E>(kv * gm);
+                    sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(kv * __expf(bl[c] - b[c]));
+                }
                 if (cv == EPV - 1) {
                     const int i = c / EPV;
                     qg[(w * G::VPL + i) * 64 + lane_id()] = vq;
-                    kg[(w * G::VPL + i) * 64 + lane_id()] = vk;
+                    if constexpr (!kBwd) kg[(w * G::VPL + i) * 64 + lane_id()] = vk;
                     if (w < kNSub - 1) cbv[i] = vc;
                 }
             }
@@ -375,15 +385,24 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     }
     __syncthreads();
     {
+        // channel rows over the chunk's tokens: (K . exp(b_L - b))^T, or for
+        // kBwd (K . Gamma)^T and (Q . Gamma)^T
         uint4* kt = reinterpret_cast<uint4*>(static_cast<E*>(ops.KhT) + cbase * D * C);
+        uint4* qt = reinterpret_cast<uint4*>(static_cast<E*>(ops.Kg) + cbase * D * C);
         for (int vi = tid; vi < D * C / EPV; vi += kThreads) {
             const int ln = vi % 64, v = (vi / 64) % G::NVT, ct = vi / (64 * G::NVT);
             const int r = kSub * ct + (ln & 15), lgp = ln >> 4;
-            uint4 pk;
+            uint4 pk, pq;
             E* pe = reinterpret_cast<E*>(&pk);
+            E* pqe = reinterpret_cast<E*>(&pq);
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) pe[e] = sKt[kt_at(r, G::tok_of(v * EPV + e, lgp))];
+            for (int e = 0; e < EPV; ++e) {
+                const int at = kt_at(r, G::tok_of(v * EPV + e, lgp));
+                pe[e] = sKt[at];
+                if constexpr (kBwd) pqe[e] = sQt[at];
+            }
             kt[vi] = pk;
+            if constexpr (kBwd) qt[vi] = pq;
         }
     }
     __syncthreads();
@@ -468,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
         __syncthreads();
     }
 
-    // Stores: T diag(beta) and M, fragment-major 16-byte vectors.
+    // Stores: T diag(beta) and M (kBwd: T^T and M^T), fragment-major 16-byte vectors.
     uint4* otb = reinterpret_cast<uint4*>(static_cast<E*>(ops.TB) + cbase * C * C);
     uint4* omm = reinterpret_cast<uint4*>(static_cast<E*>(ops.Mm) + cbase * C * C);
     for (int vi = tid; vi < C * C / EPV; vi += kThreads) {
@@ -480,9 +499,16 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const int t = G::tok_of(v * EPV + e, lgp);
-            const bool upper = (t >> 4) > (r >> 4);   // blocks above the diagonal are zero
-            et[e] = from_f<E>(upper ? 0.f : sT[tri(r, upper ? r : t)] * sBeta[t]);
-            em[e] = upper ? from_f<E>(0.f) : sM[r * PM + t];
+            if constexpr (kBwd) {
+                // element (r, t) of the transpose is (t, r): zero unless t's block >= r's
+                const bool zero = (t >> 4) < (r >> 4);
+                et[e] = from_f<E>(zero ? 0.f : sT[tri(zero ? r : t, zero ? t : r)]);
+                em[e] = zero ? from_f<E>(0.f) : sM[t * PM + r];
+            } else {
+                const bool upper = (t >> 4) > (r >> 4);   // blocks above the diagonal are zero
+                et[e] = from_f<E>(upper ? 0.f : sT[tri(r, upper ? r : t)] * sBeta[t]);
+                em[e] = upper ? from_f<E>(0.f) : sM[r * PM + t];
+            }
         }
         otb[vi] = pt;
         omm[vi] = pm;
@@ -880,16 +906,44 @@ struct LdsGeo {
     static constexpr int kBufVec = kRecurWaves * kWaveVec;
 };
 
-// kTransition: the same chunk steps with v = 0 from S = I and no output, so
-// that S_T is the sequence's transition matrix prod_t (I - beta_t k_t k_t^T)
-// Diag(alpha_t) (orkas.ai "Kimi K3 architecture", §"請求書はサービング側に回ってくる":
-// a segment's final state is its transition applied to the incoming state
-// plus its zero-start state).  v, S0 and o are not accessed.
-template <int D, bool kTransition>
+// Modes of the sequential pass:
+//   kFwd   the forward pass: o and S_T.
+//   kTrans the same chunk steps with v = 0 from S = I and no output, so that
+//          S_T is the sequence's transition matrix prod_t (I - beta_t k_t k_t^T)
+//          Diag(alpha_t) (orkas.ai "Kimi K3 architecture", §"請求書はサービング側に回ってくる":
+//          a segment's final state is its transition applied to the incoming
+//          state plus its zero-start state).  v, S0 and o are not accessed.
+//   kCkpt  the forward steps without o, keeping what the backward pass needs:
+//          the state entering every chunk (aux.ck, bf16 [slot][D][D]), and the
+//          per-token Y = V - (K . Gamma) S and U~ (aux.y, aux.u, bf16, laid out
+//          as v).
+//   kBwd   the state-gradient recurrence, chunks last to first, on the
+//          backward operand set (see ChunkOps).  With dS' the gradient of a
+//          chunk's outgoing state and dO its output gradients:
+//            R  = (K . exp(b_L - b)) dS' + M^T dO        (= dU~)
+//            dZ = T^T R,  dY = diag(beta) dZ             (dY is dv)
+//            dS = Diag(Gamma_L) dS' + (Q . Gamma)^T dO - (K . Gamma)^T dY
+//          Inputs: v = dO, S0 = dS_T (may be NULL); outputs: o = dv, ST = dS0,
+//          aux.ck = dS' of every chunk (bf16 [slot][D][D]), aux.y = dZ.
+//          These are the adjoints of the kFwd step (the chain rule through
+//          U~ = T diag(beta) Y, O = (Q . Gamma) S + M U~ and
+//          S' = Diag(Gamma_L) S + K^T U~).
+enum { kFwd = 0, kTrans = 1, kCkpt = 2, kBwd = 3 };
+
+struct RecurAux {
+    __bf16* ck;        // kCkpt: S entering each chunk; kBwd: dS' of each chunk
+    __bf16* y;         // kCkpt: Y;  kBwd: dZ
+    __bf16* u;         // kCkpt: U~
+    const float* bet;  // kBwd: per-chunk beta (ChunkOps::bet)
+};
+
+template <int D, int kMode>
 __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     const __bf16* __restrict__ v, ChunkOps ops, const int32_t* __restrict__ cu, int64_t total_tokens,
     int64_t fixed_len, const int32_t* __restrict__ seq_chunk0, int32_t NH, int32_t H, const float* __restrict__ S0,
-    float* __restrict__ ST, __bf16* __restrict__ o) {
+    float* __restrict__ ST, __bf16* __restrict__ o, RecurAux aux) {
+    constexpr bool kTransition = kMode == kTrans;
+    constexpr bool kBack = kMode == kBwd;
     using E = __bf16;
     using G = Geo<E, D>;
     using L = LdsGeo<D>;
@@ -937,6 +991,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         const int64_t rem = s_len - (int64_t)j * C;
         return (int)(rem < C ? rem : C);
     };
+    // chunk processed at step s (the backward pass walks the chunks last to first)
+    auto chunk_at = [&](int s_) -> int { return kBack ? nch - 1 - s_ : s_; };
 
     if (w >= kRecurWaves) {
         // ------------------------------------------------ producer waves
@@ -951,6 +1007,9 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         const E* vv = v + (s_start * H + h) * D + col0 + 8 * (lane & 1);
         const int gi = (lane >= 32 && lane < 32 + 4 * RT) ? lane - 32 : 0;
         const float* gm = ops.gam + cb * D + 4 * gi;
+        // kBwd: lanes 48..51 bring beta of the region's 16 rows (bytes 768..831)
+        const bool is_bet = kBack && lane >= 48 && lane < 52;
+        const float* bt = kBack ? aux.bet + cb * C + kSub * cw + 4 * (is_bet ? lane - 48 : 0) : nullptr;
         auto dma = [](const void* src, uint4* lds) {
             __builtin_amdgcn_global_load_lds(src, KDA_LDS_PTR(lds), 16, 0, 0);
         };
@@ -977,7 +1036,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 row = row < len ? row : len - 1;
                 const void* misc = (lane < 32 && !kTransition)
                                        ? static_cast<const void*>(vv + ((int64_t)j * C + row) * rs)
-                                       : static_cast<const void*>(gm + (int64_t)j * D + kSub * RT * cw);
+                                   : is_bet ? static_cast<const void*>(bt + (int64_t)j * C)
+                                            : static_cast<const void*>(gm + (int64_t)j * D + kSub * RT * cw);
                 dma(misc, dst + b * 64);
             }
         };
@@ -989,7 +1049,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 block(std::integral_constant<int, b>{}, dst, j, len);
             });
         };
-        auto issue = [&](uint4* buf, int j) {
+        auto issue = [&](uint4* buf, int s_) {
+            const int j = chunk_at(s_);
             const int len = chunk_len(j);
             uint4* dst = buf + cw * L::kWaveVec;
             static_for<kProdPerWave>([&](auto p_c) {
@@ -1036,9 +1097,10 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 t_step[k] = 0;
             }
         }
-        // Loads one dword per line of chunk j + kAhead (clamped to the last chunk).
-        auto touch = [&](int j) {
-            const int jt = j + kAhead < nch ? j + kAhead : nch - 1;
+        // Loads one dword per line of the chunk kAhead steps after step s
+        // (clamped to the last step).
+        auto touch = [&](int s_) {
+            const int jt = chunk_at(s_ + kAhead < nch ? s_ + kAhead : nch - 1);
 #pragma unroll
             for (int k = 0; k < kTouch; ++k) {
                 const char* p;
@@ -1093,6 +1155,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     // ---------------------------------------------------- compute waves
     const int64_t o_off = (s_start * H + h) * D + col0 + li;
     // S[a][r] = state[channel 16*(RT*w + a) + 4*lg + r][column col0 + li]
+    // (kBwd: the state gradient)
     f32x4 S[RT];
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
 #pragma unroll
@@ -1110,10 +1173,20 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             for (int r = 0; r < 4; ++r) sSt[li * PS + kSub * (RT * w + a) + 4 * lg + r] = from_f<E>(S[a][r]);
     };
     put_state();
+    // kCkpt / kBwd: this slab's columns of the state (gradient) as chunk j
+    // starts, into slot j of aux.ck
+    auto keep_state = [&](int j) {
+        E* ck = aux.ck + (cb + j) * D * D + col0 + li;
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ck[(int64_t)(kSub * (RT * w + a) + 4 * lg + r) * D] = from_f<E>(S[a][r]);
+    };
 
     auto step = [&](const uint4* buf, int j) {
         const int len = chunk_len(j);
         const uint4* cur = buf + w * L::kWaveVec;
+        if constexpr (kMode == kCkpt) keep_state(j);
         barrier_lds();   // chunk j's operands are in `buf`; S^T of the previous step is in LDS
         const F* fr = reinterpret_cast<const F*>(cur) + lane;
         F fq[G::NKC], fk[G::NKC];
@@ -1136,7 +1209,11 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         for (int r = 0; r < 4; ++r) {
             const int t = kSub * w + 4 * lg + r;
             const float vv = kTransition ? 0.f : to_f(vrows[(4 * lg + r) * SW + li]);
-            sYt[li * PY + t] = from_f<E>(t < len ? vv - accX[r] : 0.f);
+            const E y = from_f<E>(t < len ? vv - accX[r] : 0.f);
+            sYt[li * PY + t] = y;
+            if constexpr (kMode == kCkpt) {
+                if (t < len) aux.y[o_off + ((int64_t)j * C + t) * rs] = y;
+            }
         }
         F ftb[G::NKT], fmm[G::NKT], fkt[RT][G::NKT];
 #pragma unroll
@@ -1160,7 +1237,14 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             for (int m = 0; m < G::NKT; ++m)
                 accU = M::mma(ftb[m], M::load(&sYt[li * PY + m * M::KS + lg * M::KW]), accU);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sUt[li * PY + kSub * w + 4 * lg + r] = from_f<E>(accU[r]);
+            for (int r = 0; r < 4; ++r) {
+                const int t = kSub * w + 4 * lg + r;
+                const E u = from_f<E>(accU[r]);
+                sUt[li * PY + t] = u;
+                if constexpr (kMode == kCkpt) {
+                    if (t < len) aux.u[o_off + ((int64_t)j * C + t) * rs] = u;
+                }
+            }
         }
         barrier_lds();
         // S <- Diag(Gamma_L) S + K^T U~, then O = P + M U~ (rows 16w..)
@@ -1180,7 +1264,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         // S^T is last read before the Y barrier of this step; the barrier at
         // the top of the next step publishes the new one.
         put_state();
-        if constexpr (!kTransition) {
+        if constexpr (kMode == kFwd) {
             E* oj = o + o_off + (int64_t)j * C * rs;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1190,10 +1274,104 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         }
     };
 
-    for (int j = 0; j < nch; j += 2) {
-        step(sBuf0, j);
-        if (j + 1 >= nch) break;
-        step(sBuf1, j + 1);
+    // kBwd step.  Buffer slots: kQg K . exp(b_L - b) (rows over channels),
+    // kKg (Q . Gamma)^T and kKt (K . Gamma)^T (channel tiles over tokens),
+    // kTb T^T and kMm M^T (rows over tokens); the misc block holds the dO
+    // rows, Gamma_L and beta.
+    auto step_bwd = [&](const uint4* buf, int j) {
+        const int len = chunk_len(j);
+        const uint4* cur = buf + w * L::kWaveVec;
+        keep_state(j);
+        barrier_lds();   // chunk j's operands are in `buf`; dS'^T is in LDS
+        const F* fr = reinterpret_cast<const F*>(cur) + lane;
+        F fkh[G::NKC];
+#pragma unroll
+        for (int m = 0; m < G::NKC; ++m) fkh[m] = fr[(L::kQg + m) * 64];
+        // dO as the B operand over tokens: token 32m + 8lg + e of column li
+        // sits in the value rows of region 2m + lg/2, row 8(lg & 1) + e.
+        F bo[G::NKT];
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m) {
+            const E* rows = reinterpret_cast<const E*>(buf + (2 * m + (lg >> 1)) * L::kWaveVec + L::kMisc * 64);
+#pragma unroll
+            for (int e = 0; e < M::KW; ++e) bo[m][e] = rows[(8 * (lg & 1) + e) * SW + li];
+        }
+        F fmt[G::NKT];
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m) fmt[m] = fr[(L::kMm + m) * 64];
+        // R = K^ dS' + M^T dO  (rows 16w..), transposed to LDS
+        f32x4 accR = zero4();
+#pragma unroll
+        for (int m = 0; m < G::NKC; ++m)
+            accR = M::mma(fkh[m], M::load(&sSt[li * PS + lg * CPL + m * M::KW]), accR);
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m) accR = M::mma(fmt[m], bo[m], accR);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = kSub * w + 4 * lg + r;
+            sYt[li * PY + t] = from_f<E>(t < len ? accR[r] : 0.f);
+        }
+        F ftt[G::NKT], fqt[RT][G::NKT], fkt[RT][G::NKT];
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m) ftt[m] = fr[(L::kTb + m) * 64];
+#pragma unroll
+        for (int a = 0; a < RT; ++a)
+#pragma unroll
+            for (int m = 0; m < G::NKT; ++m) {
+                fqt[a][m] = fr[(L::kKg + a * G::NKT + m) * 64];
+                fkt[a][m] = fr[(L::kKt + a * G::NKT + m) * 64];
+            }
+        f32x4 gam[RT];
+        const float* gl = reinterpret_cast<const float*>(cur + L::kMisc * 64) + 128;
+#pragma unroll
+        for (int a = 0; a < RT; ++a) gam[a] = *reinterpret_cast<const f32x4*>(gl + kSub * a + 4 * lg);
+        const f32x4 bet = *reinterpret_cast<const f32x4*>(gl + 64 + 4 * lg);   // bytes 768.. of the block
+        barrier_lds();
+        // dZ = T^T R, dY = diag(beta) dZ  (rows 16w..); -dY^T to LDS
+        {
+            f32x4 accZ = zero4();
+#pragma unroll
+            for (int m = 0; m < G::NKT; ++m)
+                accZ = M::mma(ftt[m], M::load(&sYt[li * PY + m * M::KS + lg * M::KW]), accZ);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = kSub * w + 4 * lg + r;
+                const float dy = bet[r] * accZ[r];
+                if (t < len) {
+                    const int64_t at = o_off + ((int64_t)j * C + t) * rs;
+                    o[at] = from_f<E>(dy);
+                    aux.y[at] = from_f<E>(accZ[r]);
+                }
+                sUt[li * PY + t] = from_f<E>(t < len ? -dy : 0.f);
+            }
+        }
+        barrier_lds();
+        // dS <- Diag(Gamma_L) dS' + (Q . Gamma)^T dO - (K . Gamma)^T dY
+        F bu[G::NKT];
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m) bu[m] = M::load(&sUt[li * PY + m * M::KS + lg * M::KW]);
+#pragma unroll
+        for (int a = 0; a < RT; ++a) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int m = 0; m < G::NKT; ++m) {
+                acc = M::mma(fqt[a][m], bo[m], acc);
+                acc = M::mma(fkt[a][m], bu[m], acc);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[a][r] = gam[a][r] * S[a][r] + acc[r];
+        }
+        put_state();
+    };
+
+    auto run = [&](const uint4* buf, int s_) {
+        if constexpr (kBack) step_bwd(buf, chunk_at(s_));
+        else step(buf, s_);
+    };
+    for (int s_ = 0; s_ < nch; s_ += 2) {
+        run(sBuf0, s_);
+        if (s_ + 1 >= nch) break;
+        run(sBuf1, s_ + 1);
     }
     if (ST) {
 #pragma unroll
@@ -1210,40 +1388,56 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 // `ev`, when given, holds kNumStages + 1 events: ev[i] is recorded before
 // stage i and ev[kNumStages] after the last one (a stage that does not run
 // for these sizes still gets its pair of records, with nothing between them).
-template <typename E, int D, bool kTransition = false>
+static ChunkOps chunk_ops(const Plan& p) {
+    return ChunkOps{p.ws_TB, p.ws_M, p.ws_Qg, p.ws_Kg, p.ws_KhT, p.ws_gam, p.max_chunks, p.ws_bet};
+}
+
+template <typename E, int D, bool kBwdOps>
+static void launch_prep(const Plan& p, const E* q, hipStream_t st) {
+    if (p.total_tokens <= 0) return;
+    hipLaunchKernelGGL((k_prep<E, D, kBwdOps>), dim3(p.max_chunks, p.n_heads), dim3(kThreads), 0, st, q,
+                       static_cast<const E*>(p.k), static_cast<const E*>(p.g), static_cast<const E*>(p.beta),
+                       p.ws_tab, p.ws_n_chunks, p.cu_seqlens ? (int64_t)0 : p.fixed_len,
+                       p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk)), p.n_heads,
+                       chunk_ops(p));
+}
+
+template <int D, int kMode>
+static void launch_recur_lds(const Plan& p, const void* v, const float* S0, float* ST, void* o, RecurAux aux,
+                             hipStream_t st) {
+    const int32_t NH = p.n_seqs * p.n_heads;
+    hipLaunchKernelGGL((k_recur_lds<D, kMode>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st,
+                       static_cast<const __bf16*>(v), chunk_ops(p), p.cu_seqlens, p.total_tokens, p.fixed_len,
+                       p.ws_seq_chunk0, NH, p.n_heads, S0, ST, static_cast<__bf16*>(o), aux);
+}
+
+static void launch_table(const Plan& p, hipStream_t st) {
+    hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(1024), 0, st, p.cu_seqlens, p.n_seqs, p.total_tokens,
+                       p.fixed_len, p.max_chunks, p.ws_tab, p.ws_seq_chunk0, p.ws_n_chunks);
+}
+
+template <typename E, int D, int kMode = kFwd>
 static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     auto mark = [&](int i) {
         if (ev) (void)hipEventRecord(ev[i], st);
     };
     constexpr int CT = 1;
+    constexpr bool kTransition = kMode == kTrans;
     const E* q = static_cast<const E*>(kTransition ? p.k : p.q);   // the transition does not use q
-    const E* kk = static_cast<const E*>(p.k);
-    const E* v = static_cast<const E*>(p.v);
-    const E* beta = static_cast<const E*>(p.beta);
-    const E* g = static_cast<const E*>(p.g);
-    ChunkOps ops{p.ws_TB, p.ws_M, p.ws_Qg, p.ws_Kg, p.ws_KhT, p.ws_gam, p.max_chunks};
-    const int32_t H = p.n_heads;
-    const int32_t NH = p.n_seqs * H;
-    const bool work = p.total_tokens > 0;
+    const int32_t NH = p.n_seqs * p.n_heads;
 
     mark(0);
-    hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(1024), 0, st, p.cu_seqlens, p.n_seqs, p.total_tokens,
-                       p.fixed_len, p.max_chunks, p.ws_tab, p.ws_seq_chunk0, p.ws_n_chunks);
+    launch_table(p, st);
     mark(1);
-    if (work)
-        hipLaunchKernelGGL((k_prep<E, D>), dim3(p.max_chunks, H), dim3(kThreads), 0, st, q, kk, g, beta, p.ws_tab,
-                           p.ws_n_chunks, p.cu_seqlens ? (int64_t)0 : p.fixed_len,
-                           p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk)), H, ops);
+    launch_prep<E, D, false>(p, q, st);
     mark(2);
     static_assert(!kTransition || sizeof(E) == 2, "transition pass: bf16 operands only");
     if constexpr (sizeof(E) == 2)
-        hipLaunchKernelGGL((k_recur_lds<D, kTransition>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st, v, ops,
-                           p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, H, p.S0, p.S_T,
-                           static_cast<E*>(p.o));
+        launch_recur_lds<D, kMode>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
     else
-        hipLaunchKernelGGL((k_recur<E, D, CT>), dim3(NH * (D / (kSub * CT))), dim3(kThreads), 0, st, v, ops,
-                           p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, H, p.S0, p.S_T,
-                           static_cast<E*>(p.o));
+        hipLaunchKernelGGL((k_recur<E, D, CT>), dim3(NH * (D / (kSub * CT))), dim3(kThreads), 0, st,
+                           static_cast<const E*>(p.v), chunk_ops(p), p.cu_seqlens, p.total_tokens, p.fixed_len,
+                           p.ws_seq_chunk0, NH, p.n_heads, p.S0, p.S_T, static_cast<E*>(p.o));
     mark(3);
     return hipGetLastError();
 }
@@ -1260,8 +1454,72 @@ hipError_t launch(const Plan& p, hipStream_t st, hipEvent_t* ev) {
 }
 
 hipError_t launch_transition(const Plan& p, hipStream_t st) {
-    if (p.d == 128) return launch_all<__bf16, 128, true>(p, st, nullptr);
-    return launch_all<__bf16, 64, true>(p, st, nullptr);
+    if (p.d == 128) return launch_all<__bf16, 128, kTrans>(p, st, nullptr);
+    return launch_all<__bf16, 64, kTrans>(p, st, nullptr);
+}
+
+// Backward: forward again with checkpoints, backward operands, the state-
+// gradient recurrence, then the chunk-parallel gradients (kda_bwd.hip).  The
+// backward operand set overwrites the forward one once the checkpointing pass
+// has consumed it (same stream).
+const char* const kBwdStageNames[kNumBwdStages] = {"k_chunk_table", "k_prep", "k_recur_lds<ckpt>",
+                                                   "k_prep<bwd>", "k_recur_lds<bwd>", "k_grad"};
+
+template <int D>
+static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
+    using E = __bf16;
+    auto mark = [&](int i) {
+        if (ev) (void)hipEventRecord(ev[i], st);
+    };
+    auto* ckS = static_cast<E*>(p.ws_ckS);
+    auto* ckdS = static_cast<E*>(p.ws_ckdS);
+    auto* Y = static_cast<E*>(p.ws_Y);
+    auto* U = static_cast<E*>(p.ws_U);
+    auto* dZ = static_cast<E*>(p.ws_dZ);
+    mark(0);
+    launch_table(p, st);
+    mark(1);
+    launch_prep<E, D, false>(p, static_cast<const E*>(p.q), st);
+    mark(2);
+    launch_recur_lds<D, kCkpt>(p, p.v, p.S0, nullptr, nullptr, RecurAux{ckS, Y, U, nullptr}, st);
+    mark(3);
+    launch_prep<E, D, true>(p, static_cast<const E*>(p.q), st);
+    mark(4);
+    launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, p.dv, RecurAux{ckdS, dZ, nullptr, p.ws_bet}, st);
+    mark(5);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && p.total_tokens > 0) {
+        GradArgs a{};
+        a.q = static_cast<const E*>(p.q);
+        a.k = static_cast<const E*>(p.k);
+        a.g = static_cast<const E*>(p.g);
+        a.beta = static_cast<const E*>(p.beta);
+        a.dO = static_cast<const E*>(p.dO);
+        a.dv = static_cast<const E*>(p.dv);
+        a.Y = Y;
+        a.U = U;
+        a.dZ = dZ;
+        a.ckS = ckS;
+        a.ckdS = ckdS;
+        a.tab = p.ws_tab;
+        a.n_chunks = p.ws_n_chunks;
+        a.fixed_len = p.cu_seqlens ? (int64_t)0 : p.fixed_len;
+        a.fixed_chunks = p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk));
+        a.H = p.n_heads;
+        a.max_chunks = p.max_chunks;
+        a.dq = static_cast<E*>(p.dq);
+        a.dk = static_cast<E*>(p.dk);
+        a.dbeta = static_cast<E*>(p.dbeta);
+        a.dg = static_cast<E*>(p.dg);
+        e = launch_grad(a, D, p.max_chunks, st);
+    }
+    mark(6);
+    return e == hipSuccess ? hipGetLastError() : e;
+}
+
+hipError_t launch_bwd(const Plan& p, hipStream_t st, hipEvent_t* ev) {
+    if (p.d == 128) return launch_bwd_d<128>(p, st, ev);
+    return launch_bwd_d<64>(p, st, ev);
 }
 
 }  // namespace kda

@@ -176,6 +176,63 @@ kda_status kda_validate_inputs(kda_dtype dt, int64_t total_tokens, int32_t n_seq
                                int32_t d_k, const void* beta, const void* log_alpha,
                                const int32_t* cu_seqlens, unsigned long long* counts, void* stream);
 
+/* Bytes of device workspace kda_chunk_bwd needs for these sizes (0 if the
+ * sizes are invalid or unsupported, including dt == KDA_F32).  256-byte
+ * aligned.  It holds the forward quantities the backward pass keeps: the
+ * state entering every chunk and the gradient of every chunk's outgoing state
+ * (2 * d_k * d_v bf16 each per chunk and head) and three bf16 tensors of the
+ * size of v. */
+size_t kda_chunk_bwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                                    int32_t d_k, int32_t d_v, int32_t chunk, kda_dtype dt);
+
+/* Chunkwise KDA backward: the gradients of a loss L with respect to the
+ * inputs of kda_chunk_fwd, given dO = dL/do and dS_T = dL/dS_T.  The forward
+ * pass is evaluated again inside (its outputs are not an argument); the
+ * gradients are those of the recurrence above taken token by token
+ * (ogis-ri NLP primer on Kimi K3, §3.1 "KDA": decay, probe, delta, write,
+ * read-out), computed through the chunked form with the same 16-token
+ * sub-tiling as the forward (orkas.ai "Kimi K3 architecture",
+ * §"GPU のコードパスを一本消した「下界」").
+ *   q, k, v, beta, log_alpha, S0, cu_seqlens : as for kda_chunk_fwd (read only)
+ *   dO         : [total_tokens, n_heads, d_v], dtype dt (required when total_tokens > 0)
+ *   dS_T       : [n_seqs, n_heads, d_k, d_v] float32, or NULL (zero)
+ *   dq, dk     : outputs [total_tokens, n_heads, d_k], dtype dt
+ *   dv         : output  [total_tokens, n_heads, d_v], dtype dt
+ *   dbeta      : output  [total_tokens, n_heads], dtype dt
+ *   dlog_alpha : output  [total_tokens, n_heads, d_k], dtype dt (gradient of log alpha)
+ *   dS0        : output  [n_seqs, n_heads, d_k, d_v] float32 (gradient of the
+ *                initial state, also when S0 is NULL), or NULL (not written)
+ *   workspace  : >= kda_chunk_bwd_workspace_size(...) bytes of device memory
+ * Outputs are written, not accumulated into.  Supported: dt == KDA_BF16,
+ * d_k == d_v in {64, 128}, chunk == 64 (KDA_ERR_UNSUPPORTED otherwise);
+ * other rules, alignment and errors as for kda_chunk_fwd.  Enqueued on
+ * `stream`, never synchronises. */
+kda_status kda_chunk_bwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                         int32_t d_k, int32_t d_v, int32_t chunk,
+                         const void* q, const void* k, const void* v,
+                         const void* beta, const void* log_alpha,
+                         const float* S0, const int32_t* cu_seqlens,
+                         const void* dO, const float* dS_T,
+                         void* dq, void* dk, void* dv, void* dbeta, void* dlog_alpha, float* dS0,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Measurement form of kda_chunk_bwd, as kda_chunk_fwd_profile is of
+ * kda_chunk_fwd: same arguments and results, blocks until done, and writes
+ * each launch's milliseconds to stage_ms[0 .. kda_profile_bwd_num_stages()-1]. */
+kda_status kda_chunk_bwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                                 int32_t d_k, int32_t d_v, int32_t chunk,
+                                 const void* q, const void* k, const void* v,
+                                 const void* beta, const void* log_alpha,
+                                 const float* S0, const int32_t* cu_seqlens,
+                                 const void* dO, const float* dS_T,
+                                 void* dq, void* dk, void* dv, void* dbeta, void* dlog_alpha, float* dS0,
+                                 void* workspace, size_t workspace_bytes, void* stream, float* stage_ms);
+
+/* Number of kernel launches one backward pass makes, and the name of launch i
+ * (NULL when out of range). */
+int32_t kda_profile_bwd_num_stages(void);
+const char* kda_profile_bwd_stage_name(int32_t i);
+
 /* Number of kernel launches one forward pass makes, and the name of launch i
  * (NULL when i is out of range); names match the kernel symbols a profiler
  * reports. */

@@ -210,3 +210,18 @@ def generate_torch(spec: Spec, device, block_tokens: int = 1 << 16) -> Inputs:
 def custom(name: str, dtype: str, lengths: Sequence[int], n_heads: int, d: int, **kw) -> Spec:
     """A small ad-hoc workload with the standard distributions."""
     return Spec(name, dtype, tuple(int(x) for x in lengths), n_heads, d, d, **kw)
+
+
+def generate_grads_numpy(spec: Spec, ds_std: float = 1.0, with_dS_T: bool = True):
+    """Seeded upstream gradients for a backward workload: dO ~ N(0, 1) shaped
+    like v (rounded to spec.dtype) and dS_T ~ ds_std * N(0, 1) float32 shaped
+    like the states (None when with_dS_T is False).  Drawn from its own
+    stream, PCG64(seed + 1000003), so the forward inputs are unchanged."""
+    rng = np.random.Generator(np.random.PCG64(spec.seed + 1000003))
+    T, H, dk, dv = spec.total_tokens, spec.n_heads, spec.d_k, spec.d_v
+    rnd = round_bf16 if spec.dtype == "bf16" else (lambda a: np.ascontiguousarray(a, np.float32))
+    dO = rnd(rng.standard_normal((T, H, dv), dtype=np.float32))
+    dS_T = None
+    if with_dS_T:
+        dS_T = (ds_std * rng.standard_normal((spec.n_seqs, H, dk, dv), dtype=np.float32)).astype(np.float32)
+    return dO, dS_T
