@@ -48,9 +48,14 @@ def kernel_bytes_per_token_head(name, C, D, es=2):
     }[name]
 
 
-def source_sha():
+# kernel -> the sources its code comes from (for matching committed counter summaries)
+KERNEL_SOURCES = {"k_prep": ("kda_kernels.hip", "kda_device.h"), "k_recur": ("kda_kernels.hip", "kda_device.h"),
+                  "k_chunk_table": ("kda_kernels.hip", "kda_device.h"), "k_grad": ("kda_bwd.hip", "kda_device.h")}
+
+
+def source_sha(files=("kda_kernels.hip", "kda_device.h")):
     h = hashlib.sha256()
-    for f in ("kda_kernels.hip", "kda_device.h"):
+    for f in files:
         with open(os.path.join(ROOT, "gated_delta_rule_30_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -65,9 +70,17 @@ def traffic_for(kernel, workload_key):
     with open(path) as f:
         rec = json.load(f)
     ent = rec.get(kernel + "|" + workload_key)
-    if not ent or ent.get("source_sha") != source_sha():
+    if not ent or ent.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
         return None
     return ent["bytes_per_launch"]
+
+
+def grad_bytes_per_token_head(C, D, es=2):
+    """Algorithmic bytes of the per-chunk gradient kernel per (token, head):
+    reads q, k, log_alpha, dO, dv, U~, dZ, Y (8 D) and beta, the chunk's two
+    d x d bf16 states spread over its C tokens; writes dq, dk, dlog_alpha and
+    the two float32 dbeta shares."""
+    return 8 * D * es + es + 2 * D * D * es / C + 3 * D * es + 2 * 4
 
 
 def cpu_baseline(inp, n_heads_sample):
@@ -153,6 +166,54 @@ def seqpar_measure(torch, kda, inp, ms_single, reps=3):
     return {"segments": G, "ms_per_pass": ms, "vs_single_pass": ms / ms_single,
             "compose_us": e0.elapsed_time(e1) / 10 * 1e3,
             "note": "one GPU runs every segment: Z pass + transition pass + rerun, about 3 single passes"}
+
+
+def backward_measure(torch, kda, inp, cu, spec, reps=5, profile_reps=3):
+    """The backward pass (kda_chunk_bwd) over the same workload: seeded dO ~
+    N(0,1) and dS_T ~ N(0,1); inputs, gradients and workspace resident in HBM.
+    One call evaluates the forward again with checkpoints, the state-gradient
+    recurrence and the per-chunk gradients."""
+    dev = inp.q.device
+    T, H, dk, dv, N, C = spec.total_tokens, spec.n_heads, spec.d_k, spec.d_v, spec.n_seqs, spec.chunk
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec.seed + 1000003)
+    dO = torch.randn((T, H, dv), generator=gen, device=dev, dtype=torch.float32).to(inp.q.dtype)
+    dST = torch.randn((N, H, dk, dv), generator=gen, device=dev, dtype=torch.float32)
+    ws = torch.empty(kda.bwd_workspace_size(T, N, H, dk, dv, C), dtype=torch.uint8, device=dev)
+
+    def call():
+        return kda.chunk_bwd(inp.q, inp.k, inp.v, inp.beta, inp.g, dO, S0=inp.S0, dS_T=dST, cu_seqlens=cu,
+                             n_seqs=N, workspace=ws)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    stage_ms = {}
+    for _ in range(profile_reps):
+        _, d = kda.chunk_bwd_profile(inp.q, inp.k, inp.v, inp.beta, inp.g, dO, S0=inp.S0, dS_T=dST,
+                                     cu_seqlens=cu, n_seqs=N, workspace=ws)
+        for k_, v_ in d.items():
+            stage_ms[k_] = stage_ms.get(k_, 0.0) + v_ / profile_reps
+    wkey = "%s_N%d_H%d_T%d_d%d" % (spec.dtype, N, H, T, dk)
+    kb = grad_bytes_per_token_head(C, dk) * T * H
+    roof = {"bound": "hbm", "kernel": "k_grad", "achieved": kb / (stage_ms["k_grad"] * 1e-3) / 1e9,
+            "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_for("k_grad", wkey)
+    roof["kernel_ms"] = stage_ms["k_grad"]
+    roof["algorithmic_bytes_per_launch"] = kb
+    return {"workload": "KDA chunked backward (dq, dk, dv, dbeta, dlog_alpha, dS0) of the same forward, "
+                        "dO ~ N(0,1), dS_T ~ N(0,1); forward re-evaluated inside",
+            "ms_per_pass": ms, "tokens_per_s": T / (ms * 1e-3), "vs_forward": None, "stage_ms": stage_ms,
+            "roofline": roof, "source_sha": source_sha(KERNEL_SOURCES["k_grad"])}
 
 
 def main():
@@ -255,6 +316,9 @@ def main():
         "stage_ms": stage_ms, "roofline": roof, "wall_s_timed": wall,
         "device": torch.cuda.get_device_name(dev), "source_sha": source_sha(),
     }
+    if spec.dtype == "bf16":
+        out["backward"] = backward_measure(torch, kda, inp, cu, spec)
+        out["backward"]["vs_forward"] = out["backward"]["ms_per_pass"] / ms
     out["decode"] = decode_measure(torch, kda, dev)
     if spec.dtype == "bf16" and spec.n_seqs == 1:
         out["sequence_parallel"] = seqpar_measure(torch, kda, inp, ms)

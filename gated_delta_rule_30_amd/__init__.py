@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_profile", "chunk_bwd", "chunk_bwd_profile", "bwd_stage_names", "recurrent_fwd", "validate_inputs", "chunk_transition",
+__all__ = ["chunk_fwd", "chunk_fwd_profile", "chunk_bwd", "chunk_bwd_profile", "bwd_stage_names", "bwd_workspace_size", "recurrent_fwd", "validate_inputs", "chunk_transition",
            "compose_states", "sequence_parallel_fwd", "stage_names", "workspace_size", "status_string", "lib_path",
            "KDA_F32", "KDA_BF16", "KdaError"]
 
@@ -180,6 +180,12 @@ def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = C
     if batched:
         o = o.reshape(B, -1, H, dv)
     return o, (S_T if output_final_state else None)
+
+
+def bwd_workspace_size(total_tokens: int, n_seqs: int, n_heads: int, d_k: int, d_v: int,
+                       chunk: int = CHUNK, dtype_code: int = KDA_BF16) -> int:
+    return int(_load().kda_chunk_bwd_workspace_size(int(total_tokens), int(n_seqs), int(n_heads), int(d_k),
+                                                    int(d_v), int(chunk), int(dtype_code)))
 
 
 def bwd_stage_names():

@@ -40,6 +40,7 @@ size_t carve_workspace(Plan* p, void* base) {
         p->ws_Y = take(2 * T * H * D);
         p->ws_U = take(2 * T * H * D);
         p->ws_dZ = take(2 * T * H * D);
+        p->ws_dbp = (float*)take(4 * 2 * T * H);
     }
     return off;
 }
@@ -221,6 +222,7 @@ size_t kda_chunk_bwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_
     if (dt != KDA_BF16) return 0;
     Plan p{};
     if (plan_sizes(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, true) != KDA_OK) return 0;
+    if (p.max_chunks >= (1 << 30)) return 0;
     p.bwd = true;
     return kda::carve_workspace(&p, nullptr);
 }
@@ -233,6 +235,7 @@ static kda_status prepare_bwd(Plan* p, kda_dtype dt, int64_t total_tokens, int32
     if (dt == KDA_F32) return KDA_ERR_UNSUPPORTED;
     kda_status s = plan_sizes(p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, cu_seqlens != nullptr);
     if (s != KDA_OK) return s;
+    if (p->max_chunks >= (1 << 30)) return KDA_ERR_UNSUPPORTED;   // two gradient workgroups per chunk
     p->bwd = true;
     if (total_tokens > 0 && (!q || !k || !v || !beta || !log_alpha || !dO || !dq || !dk || !dv || !dbeta ||
                              !dlog_alpha))

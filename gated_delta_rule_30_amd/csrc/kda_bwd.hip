@@ -36,19 +36,21 @@
 //   column side, i in J, r in R >= J:
 //     e^{b_r - b_i} = e^{b_r - rho_R} . e^{rho_R - rho_J} . e^{rho_J - b_i}
 //
-// Geometry: one workgroup of 8 waves per (chunk, head).  Wave v handles the
-// chunk's token tile w = v & 3 and half hh = v >> 2 of the key channels.
-// Every product is formed transposed (rows = key channels, columns =
-// tokens), so that lane 16 lg + li ends up holding token 16w + li and
-// channels 16n + 4lg + r (n in its half, r < 4) of every result: the decay
-// cumulative sum over tokens is a 16-lane row scan, and all per-element
-// terms combine in registers.
+// Geometry: two workgroups of 4 waves per (chunk, head), one per half of
+// the key channels (both halves of a chunk run on the same XCD, so the token
+// rows they both read come from one L2).  Wave w handles the chunk's token
+// tile w.  Every product is formed transposed (rows = key channels, columns
+// = tokens), so that lane 16 lg + li ends up holding token 16w + li and
+// channels 16n + 4lg + r (n among the half's tiles, r < 4) of every result:
+// the decay cumulative sum over tokens is a 16-lane row scan, and all
+// per-element terms combine in registers.  The two halves' shares of dbeta
+// meet in a float32 workspace; k_dbeta_sum adds them.
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-constexpr int kGradThreads = 512;
+constexpr int kGradThreads = 256;
 
 // 8 bf16 from LDS, each scaled by s in fp32, as an MFMA fragment
 __device__ inline bf16x8 load_scaled(const __bf16* p, float s) {
@@ -61,39 +63,44 @@ __device__ inline bf16x8 load_scaled(const __bf16* p, float s) {
 __device__ inline bf16x8 as_frag(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 template <int D>
-__global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
+__global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_grad(GradArgs a) {
     using E = __bf16;
     using M = Mma<E>;
     using F = M::frag;
     constexpr int C = kChunk;
-    constexpr int NT = D / 16;        // channel tiles
-    constexpr int NTH = NT / 2;       // channel tiles per half
+    constexpr int HALF = D / 2;       // key channels per workgroup
+    constexpr int NTH = HALF / 16;    // channel tiles per workgroup
     constexpr int CH = 4 * NTH;       // channels per lane
     constexpr int KV = D / M::KS;     // k-steps of a contraction over value columns
     constexpr int PSd = D + 8;        // pitch of the staged states (elements)
     constexpr int PT = C + 8;         // pitch of token-indexed rows
-    constexpr int kX = (2 * D * PSd > 3 * D * PT) ? 2 * D * PSd : 3 * D * PT;
-    // Region X: S and dS' ([channel][value column]); later the Gram operands
-    // ([channel][token]).
+    constexpr int kXs = 2 * HALF * PSd, kXu = C * PSd, kXg = 3 * HALF * PT;
+    constexpr int kX = kXs > kXu ? (kXs > kXg ? kXs : kXg) : (kXu > kXg ? kXu : kXg);
+    // Region X: the half's rows of S and dS' ([channel][value column]); then
+    // U~ ([token][value column]); then the Gram operands ([channel][token]).
     __shared__ __attribute__((aligned(16))) E sX[kX];
     __shared__ __attribute__((aligned(16))) E sdA[C * PT];     // dA      [r][i]
     __shared__ __attribute__((aligned(16))) E sdGq[C * PT];    // dGq     [r][i]
     __shared__ __attribute__((aligned(16))) E sdGkT[C * PT];   // beta dA [i][r]
     __shared__ __attribute__((aligned(16))) E sdGqT[C * PT];   // dGq     [i][r]
-    __shared__ float sRho[(kNSub + 1) * D];   // rho_0 .. rho_3, b_L
-    __shared__ float sTot[kNSub * D];         // sub-tile sums of log alpha
-    __shared__ float sCol[kNSub * D];         // per tile: sum over tokens of dK^ . K^
-    __shared__ float sRev[kNSub * D];         // per tile: sum of db
-    __shared__ float sDgam[D];
+    __shared__ float sRho[(kNSub + 1) * HALF];   // rho_0 .. rho_3, b_L
+    __shared__ float sTot[kNSub * HALF];         // sub-tile sums of log alpha
+    __shared__ float sCol[kNSub * HALF];         // per tile: sum over tokens of dK^ . K^
+    __shared__ float sRev[kNSub * HALF];         // per tile: sum of db
+    __shared__ float sDgam[HALF];
     __shared__ float sBeta[C];
-    __shared__ float sDb2[2 * C];
     E* sS = sX;
-    E* sdS = sX + D * PSd;
-    E* sKD = sX;               // k_i e^{rho_{J+1} - b_i}
-    E* sKr = sX + D * PT;      // k_r e^{b_r - rho_R}
-    E* sQr = sX + 2 * D * PT;  // q_r e^{b_r - rho_R}
+    E* sdS = sX + HALF * PSd;
+    E* sU = sX;
+    E* sKD = sX;                  // k_i e^{rho_{J+1} - b_i}
+    E* sKr = sX + HALF * PT;      // k_r e^{b_r - rho_R}
+    E* sQr = sX + 2 * HALF * PT;  // q_r e^{b_r - rho_R}
 
-    const int32_t ci = blockIdx.x;
+    // workgroup -> (chunk, half): the two halves of 8 consecutive chunks sit
+    // 8 workgroups apart, so that they share an XCD
+    const int32_t bid = blockIdx.x;
+    const int32_t ci = (bid & 7) + 8 * (bid >> 4);
+    const int hh = (bid >> 3) & 1;
     ChunkInfo info;
     if (a.fixed_len > 0) {
         const int32_t per = (int32_t)((a.fixed_len + C - 1) / C);
@@ -108,26 +115,27 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
         info = a.tab[ci];
     }
     const int h = blockIdx.y, len = info.len, H = a.H;
-    const int tid = threadIdx.x, wv = tid >> 6, w = wv & 3, hh = wv >> 2;
+    const int tid = threadIdx.x, w = tid >> 6;
     const int lane = tid & 63, li = lane & 15, lg = lane >> 4;
     const int t = kSub * w + li;
     const bool ok = t < len;
     const int64_t rs = (int64_t)H * D;
     const int64_t row = (info.tok0 + (ok ? t : 0)) * rs + (int64_t)h * D;   // this lane's token row
     const int64_t slot = (int64_t)h * a.max_chunks + ci;
-    auto chan = [&](int i, int r) { return kSub * (hh * NTH + i) + 4 * lg + r; };
+    // i-th channel group of this lane: local channel (within the half) and global channel
+    auto lch = [&](int i, int r) { return kSub * i + 4 * lg + r; };
+    const int c0 = hh * HALF;
 
-    // ---- inputs at (token t, this lane's channels); decay cumulative sum
+    // ---- inputs at (token t, this lane's channels)
     float qf[CH], kf[CH], b[CH];
 #pragma unroll
     for (int i = 0; i < NTH; ++i) {
-        const int64_t at = row + chan(i, 0);
-        uint2 rq = make_uint2(0, 0), rk = rq, rg = rq;
-        if (ok) {
-            rq = *reinterpret_cast<const uint2*>(a.q + at);
-            rk = *reinterpret_cast<const uint2*>(a.k + at);
-            rg = *reinterpret_cast<const uint2*>(a.g + at);
-        }
+        // rows past the chunk end load a valid row (the chunk's first) and read as zero
+        const int64_t at = row + c0 + lch(i, 0);
+        uint2 rq = *reinterpret_cast<const uint2*>(a.q + at);
+        uint2 rk = *reinterpret_cast<const uint2*>(a.k + at);
+        uint2 rg = *reinterpret_cast<const uint2*>(a.g + at);
+        if (!ok) rq = rk = rg = make_uint2(0, 0);
         const E* eq = reinterpret_cast<const E*>(&rq);
         const E* ek = reinterpret_cast<const E*>(&rk);
         const E* eg = reinterpret_cast<const E*>(&rg);
@@ -135,60 +143,71 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
         for (int r = 0; r < 4; ++r) {
             qf[4 * i + r] = (float)eq[r];
             kf[4 * i + r] = (float)ek[r];
-            b[4 * i + r] = row_scan16((float)eg[r]);
+            b[4 * i + r] = (float)eg[r];
         }
     }
-    const float bt = ok ? (float)a.beta[(info.tok0 + t) * H + h] : 0.f;
-    if (hh == 0 && lg == 0) sBeta[t] = bt;
-    if (li == 15) {
-#pragma unroll
-        for (int i = 0; i < NTH; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sTot[w * D + chan(i, r)] = b[4 * i + r];
-    }
-    // token rows of dO, dY, U~, dZ, Y as fragments over value columns
+    float bt = (float)a.beta[(info.tok0 + (ok ? t : 0)) * H + h];
+    if (!ok) bt = 0.f;
+    // token rows of dO, dY, U~, dZ as fragments over value columns
     uint4 fo[KV], fy[KV], fu[KV], fz[KV];
-    float dbeta1 = 0.f;
+    float dbeta = 0.f;
     {
         const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int m = 0; m < KV; ++m) {
             const int64_t at = row + M::KS * m + M::KW * lg;
-            fo[m] = ok ? *reinterpret_cast<const uint4*>(a.dO + at) : z;
-            fy[m] = ok ? *reinterpret_cast<const uint4*>(a.dv + at) : z;
-            fu[m] = ok ? *reinterpret_cast<const uint4*>(a.U + at) : z;
-            fz[m] = ok ? *reinterpret_cast<const uint4*>(a.dZ + at) : z;
-            const uint4 yv = ok ? *reinterpret_cast<const uint4*>(a.Y + at) : z;
-            const bf16x8 zf = as_frag(fz[m]), yf = as_frag(yv);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dbeta1 += (float)zf[e] * (float)yf[e];
+            fo[m] = *reinterpret_cast<const uint4*>(a.dO + at);
+            fy[m] = *reinterpret_cast<const uint4*>(a.dv + at);
+            fu[m] = *reinterpret_cast<const uint4*>(a.U + at);
+            fz[m] = *reinterpret_cast<const uint4*>(a.dZ + at);
+            if (!ok) fo[m] = fy[m] = fu[m] = fz[m] = z;
         }
-        dbeta1 += __shfl_xor(dbeta1, 16);
-        dbeta1 += __shfl_xor(dbeta1, 32);
+        if (hh == 0) {   // first dbeta term, sum_j dZ_tj Y_tj (the other half adds none)
+#pragma unroll
+            for (int m = 0; m < KV; ++m) {
+                uint4 yv = *reinterpret_cast<const uint4*>(a.Y + row + M::KS * m + M::KW * lg);
+                if (!ok) yv = z;
+                const bf16x8 zf = as_frag(fz[m]), yf = as_frag(yv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dbeta += (float)zf[e] * (float)yf[e];
+            }
+            dbeta += __shfl_xor(dbeta, 16);
+            dbeta += __shfl_xor(dbeta, 32);
+        }
     }
-    // S and dS' of this chunk into LDS
+    // this half's rows of S and dS' into LDS
     {
-        const uint4* gS = reinterpret_cast<const uint4*>(a.ckS + slot * D * D);
-        const uint4* gD = reinterpret_cast<const uint4*>(a.ckdS + slot * D * D);
-        for (int vi = tid; vi < D * D / 8; vi += kGradThreads) {
+        const uint4* gS = reinterpret_cast<const uint4*>(a.ckS + slot * D * D + (int64_t)c0 * D);
+        const uint4* gD = reinterpret_cast<const uint4*>(a.ckdS + slot * D * D + (int64_t)c0 * D);
+        for (int vi = tid; vi < HALF * D / 8; vi += kGradThreads) {
             const int c = vi / (D / 8), j8 = vi % (D / 8);
             *reinterpret_cast<uint4*>(&sS[c * PSd + 8 * j8]) = gS[vi];
             *reinterpret_cast<uint4*>(&sdS[c * PSd + 8 * j8]) = gD[vi];
         }
     }
+    // decay cumulative sum: 16-lane row scan, carries between token tiles
+#pragma unroll
+    for (int x = 0; x < CH; ++x) b[x] = row_scan16(b[x]);
+    if (lg == 0) sBeta[t] = bt;
+    if (li == 15) {
+#pragma unroll
+        for (int i = 0; i < NTH; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sTot[w * HALF + lch(i, r)] = b[4 * i + r];
+    }
     __syncthreads();
-    for (int c = tid; c < D; c += kGradThreads) {
+    for (int c = tid; c < HALF; c += kGradThreads) {
         float run = 0.f;
 #pragma unroll
         for (int R = 0; R < kNSub; ++R) {
-            sRho[R * D + c] = run;
-            run += sTot[R * D + c];
+            sRho[R * HALF + c] = run;
+            run += sTot[R * HALF + c];
         }
-        sRho[kNSub * D + c] = run;
+        sRho[kNSub * HALF + c] = run;
     }
     // dgamma_c = sum_j dS'_cj S_cj
     {
-        constexpr int TPC = kGradThreads / D;   // threads per channel
+        constexpr int TPC = kGradThreads / HALF;   // threads per channel
         const int c = tid / TPC, part = tid % TPC;
         float acc = 0.f;
         for (int j = part * (D / TPC); j < (part + 1) * (D / TPC); ++j)
@@ -201,54 +220,48 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
 #pragma unroll
     for (int i = 0; i < NTH; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) b[4 * i + r] += sRho[w * D + chan(i, r)];
+        for (int r = 0; r < 4; ++r) b[4 * i + r] += sRho[w * HALF + lch(i, r)];
 
     // ---- products with the states: d(Q.Gamma), d(K.Gamma), dK^
     float dq[CH], dk[CH], db[CH];
 #pragma unroll
     for (int i = 0; i < NTH; ++i) {
-        const int n = hh * NTH + i;
         f32x4 aq = zero4(), ak = zero4(), ah = zero4();
 #pragma unroll
         for (int m = 0; m < KV; ++m) {
-            const F fs = M::load(&sS[(kSub * n + li) * PSd + M::KS * m + M::KW * lg]);
-            const F fd = M::load(&sdS[(kSub * n + li) * PSd + M::KS * m + M::KW * lg]);
+            const F fs = M::load(&sS[(kSub * i + li) * PSd + M::KS * m + M::KW * lg]);
+            const F fd = M::load(&sdS[(kSub * i + li) * PSd + M::KS * m + M::KW * lg]);
             aq = M::mma(fs, as_frag(fo[m]), aq);
             ak = M::mma(fs, as_frag(fy[m]), ak);
             ah = M::mma(fd, as_frag(fu[m]), ah);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int x = 4 * i + r, c = chan(i, r);
-            const float G = __expf(b[x]), eh = __expf(sRho[kNSub * D + c] - b[x]);
+            const int x = 4 * i + r, c = lch(i, r);
+            const float G = __expf(b[x]), eh = __expf(sRho[kNSub * HALF + c] - b[x]);
             const float dqg = aq[r], dkg = -ak[r], dkh = ah[r];
             dq[x] = dqg * G;
             dk[x] = dkg * G + dkh * eh;
             const float hk = dkh * kf[x] * eh;   // dK^ . K^
             db[x] = (dqg * qf[x] + dkg * kf[x]) * G - hk;
-            const float cs = row_scan16(hk);          // column sum over the tile's tokens
-            if (li == 15) sCol[w * D + c] = cs;
+            const float cs = row_scan16(hk);      // column sum over the tile's tokens
+            if (li == 15) sCol[w * HALF + c] = cs;
         }
     }
-    // ---- dA and dGq, row block w; this half takes column blocks 2hh, 2hh+1
+    __syncthreads();   // S and dS' are dead: region X takes U~
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int J = 2 * hh + jj;
+    for (int m = 0; m < KV; ++m) *reinterpret_cast<uint4*>(&sU[t * PSd + M::KS * m + M::KW * lg]) = fu[m];
+    __syncthreads();
+    // ---- dA and dGq, row block w (blocks above the diagonal are written as zero)
+#pragma unroll
+    for (int J = 0; J < kNSub; ++J) {
         f32x4 accA = zero4(), accG = zero4();
         if (J <= w) {
-            uint4 fj[KV];
-            const int tj = kSub * J + li;
-            const bool okj = tj < len;
-            const int64_t rowj = (info.tok0 + (okj ? tj : 0)) * rs + (int64_t)h * D;
-#pragma unroll
-            for (int m = 0; m < KV; ++m)
-                fj[m] = (J == w) ? fu[m]
-                        : okj   ? *reinterpret_cast<const uint4*>(a.U + rowj + M::KS * m + M::KW * lg)
-                                : make_uint4(0, 0, 0, 0);
 #pragma unroll
             for (int m = 0; m < KV; ++m) {
-                accA = M::mma(as_frag(fz[m]), as_frag(fj[m]), accA);
-                accG = M::mma(as_frag(fo[m]), as_frag(fj[m]), accG);
+                const F fj = M::load(&sU[(kSub * J + li) * PSd + M::KS * m + M::KW * lg]);
+                accA = M::mma(as_frag(fz[m]), fj, accA);
+                accG = M::mma(as_frag(fo[m]), fj, accG);
             }
         }
 #pragma unroll
@@ -262,14 +275,13 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
             sdGqT[ii * PT + rr] = (E)dG;
         }
     }
-    __syncthreads();   // S and dS' are dead: region X takes the Gram operands
-
+    __syncthreads();   // U~ is dead: region X takes the Gram operands
 #pragma unroll
     for (int i = 0; i < NTH; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int x = 4 * i + r, c = chan(i, r);
-            const float r0 = sRho[w * D + c], r1 = sRho[(w + 1) * D + c];
+            const int x = 4 * i + r, c = lch(i, r);
+            const float r0 = sRho[w * HALF + c], r1 = sRho[(w + 1) * HALF + c];
             sKD[c * PT + t] = (E)(kf[x] * __expf(r1 - b[x]));
             sKr[c * PT + t] = (E)(kf[x] * __expf(b[x] - r0));
             sQr[c * PT + t] = (E)(qf[x] * __expf(b[x] - r0));
@@ -280,15 +292,15 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
     float dbeta2 = 0.f;
 #pragma unroll
     for (int i = 0; i < NTH; ++i) {
-        const int n = hh * NTH + i, cA = kSub * n + li;   // channel of this lane's A-operand row
+        const int cA = kSub * i + li;   // local channel of this lane's A-operand row
         // row side: output tokens r in tile R = w; contraction over i in blocks J <= R
         f32x4 accK = zero4(), accQ = zero4();
         {
             const int R = w;
-            const float rR1 = sRho[(R + 1) * D + cA];
+            const float rR1 = sRho[(R + 1) * HALF + cA];
             for (int m = 0; m <= R / 2; ++m) {
                 const int J = 2 * m + (lg >> 1);
-                const float fac = J <= R ? __expf(rR1 - sRho[(J + 1) * D + cA]) : 1.f;
+                const float fac = J <= R ? __expf(rR1 - sRho[(J + 1) * HALF + cA]) : 1.f;
                 const F fa = load_scaled(&sKD[cA * PT + M::KS * m + M::KW * lg], fac);
                 accK = M::mma(fa, M::load(&sdA[(kSub * w + li) * PT + M::KS * m + M::KW * lg]), accK);
                 accQ = M::mma(fa, M::load(&sdGq[(kSub * w + li) * PT + M::KS * m + M::KW * lg]), accQ);
@@ -298,10 +310,10 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
         f32x4 accC = zero4();
         {
             const int J = w;
-            const float rJ = sRho[J * D + cA];
+            const float rJ = sRho[J * HALF + cA];
             for (int m = J / 2; m < C / M::KS; ++m) {
                 const int R = 2 * m + (lg >> 1);
-                const float fac = R > J ? __expf(sRho[R * D + cA] - rJ) : 1.f;
+                const float fac = R > J ? __expf(sRho[R * HALF + cA] - rJ) : 1.f;
                 const int at = cA * PT + M::KS * m + M::KW * lg;
                 const int bt_at = (kSub * w + li) * PT + M::KS * m + M::KW * lg;
                 accC = M::mma(load_scaled(&sKr[at], fac), M::load(&sdGkT[bt_at]), accC);
@@ -310,9 +322,9 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int x = 4 * i + r, c = chan(i, r);
-            const float orow = __expf(b[x] - sRho[(w + 1) * D + c]);
-            const float ocol = __expf(sRho[w * D + c] - b[x]);
+            const int x = 4 * i + r, c = lch(i, r);
+            const float orow = __expf(b[x] - sRho[(w + 1) * HALF + c]);
+            const float ocol = __expf(sRho[w * HALF + c] - b[x]);
             const float dkra = accK[r] * orow, dqr = accQ[r] * orow, dkc = accC[r] * ocol;
             const float dkr = bt * dkra;
             dq[x] += dqr;
@@ -323,8 +335,7 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
     }
     dbeta2 += __shfl_xor(dbeta2, 16);
     dbeta2 += __shfl_xor(dbeta2, 32);
-    if (lg == 0) sDb2[hh * C + t] = dbeta2;
-    __syncthreads();
+    dbeta += dbeta2;
 
     // ---- b_L terms on the last row, then dg = reverse cumulative sum of db
     float rv[CH];
@@ -332,15 +343,15 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
     for (int i = 0; i < NTH; ++i)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int x = 4 * i + r, c = chan(i, r);
+            const int x = 4 * i + r, c = lch(i, r);
             if (t == C - 1) {
-                float cs = sDgam[c] * __expf(sRho[kNSub * D + c]);
+                float cs = sDgam[c] * __expf(sRho[kNSub * HALF + c]);
 #pragma unroll
-                for (int W = 0; W < kNSub; ++W) cs += sCol[W * D + c];
+                for (int W = 0; W < kNSub; ++W) cs += sCol[W * HALF + c];
                 db[x] += cs;
             }
             rv[x] = row_rscan16(db[x]);
-            if (li == 0) sRev[w * D + c] = rv[x];
+            if (li == 0) sRev[w * HALF + c] = rv[x];
         }
     __syncthreads();
     if (!ok) return;
@@ -349,27 +360,43 @@ __global__ __launch_bounds__(kGradThreads) void k_grad(GradArgs a) {
         bf16x4 oq, ok4, og;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int x = 4 * i + r, c = chan(i, r);
+            const int x = 4 * i + r, c = lch(i, r);
             float dgv = rv[x];
-            for (int W = w + 1; W < kNSub; ++W) dgv += sRev[W * D + c];
+            for (int W = w + 1; W < kNSub; ++W) dgv += sRev[W * HALF + c];
             oq[r] = (E)dq[x];
             ok4[r] = (E)dk[x];
             og[r] = (E)dgv;
         }
-        const int64_t at = row + chan(i, 0);
+        const int64_t at = row + c0 + lch(i, 0);
         *reinterpret_cast<bf16x4*>(a.dq + at) = oq;
         *reinterpret_cast<bf16x4*>(a.dk + at) = ok4;
         *reinterpret_cast<bf16x4*>(a.dg + at) = og;
     }
-    if (hh == 0 && lg == 0) a.dbeta[(info.tok0 + t) * H + h] = (E)(dbeta1 + sDb2[t] + sDb2[C + t]);
+    if (lg == 0) a.dbp[((int64_t)hh * a.total_tokens + info.tok0 + t) * H + h] = dbeta;
+}
+
+// dbeta = the two halves' float32 shares, rounded once to bf16
+__global__ __launch_bounds__(256) void k_dbeta_sum(const float* __restrict__ dbp, int64_t n, __bf16* __restrict__ dbeta) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        dbeta[i] = (__bf16)(dbp[i] + dbp[n + i]);
 }
 
 hipError_t launch_grad(const GradArgs& a, int d, int32_t max_chunks, hipStream_t st) {
     if (max_chunks <= 0) return hipSuccess;
+    // two workgroups per chunk, in groups of 16 (8 chunks x 2 halves)
+    const int32_t groups = (max_chunks + 7) / 8;
+    const dim3 grid(16 * groups, a.H);
     if (d == 128)
-        hipLaunchKernelGGL(k_grad<128>, dim3(max_chunks, a.H), dim3(kGradThreads), 0, st, a);
+        hipLaunchKernelGGL(k_grad<128>, grid, dim3(kGradThreads), 0, st, a);
     else
-        hipLaunchKernelGGL(k_grad<64>, dim3(max_chunks, a.H), dim3(kGradThreads), 0, st, a);
+        hipLaunchKernelGGL(k_grad<64>, grid, dim3(kGradThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dbeta_sum(const GradArgs& a, hipStream_t st) {
+    const int64_t n = a.total_tokens * a.H;
+    const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+    if (n > 0) hipLaunchKernelGGL(k_dbeta_sum, dim3((unsigned)blocks), dim3(256), 0, st, a.dbp, n, a.dbeta);
     return hipGetLastError();
 }
 

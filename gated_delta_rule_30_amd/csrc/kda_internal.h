@@ -46,6 +46,7 @@ struct Plan {
     void* ws_ckS;             // [H, max_chunks, D, D] state entering each chunk (bf16)
     void* ws_ckdS;            // [H, max_chunks, D, D] gradient of each chunk's outgoing state (bf16)
     void *ws_Y, *ws_U, *ws_dZ;   // [T, H, D] bf16: Y, U~ and dZ per token
+    float* ws_dbp;            // [2, T, H] float32 dbeta shares of the two channel halves
 };
 
 // Arguments of the per-chunk gradient kernel (kda_bwd.hip); bf16 tensors.
@@ -57,9 +58,12 @@ struct GradArgs {
     int32_t fixed_chunks;
     int32_t H;
     int64_t max_chunks;
+    int64_t total_tokens;
     __bf16 *dq, *dk, *dbeta, *dg;
+    float* dbp;               // [2, total_tokens, H] the halves' dbeta shares
 };
 hipError_t launch_grad(const GradArgs& a, int d, int32_t max_chunks, hipStream_t stream);
+hipError_t launch_dbeta_sum(const GradArgs& a, hipStream_t stream);
 
 // Byte offsets of every workspace region for the given sizes; returns the
 // total size.  `base` may be NULL (size query only).
@@ -75,7 +79,7 @@ extern const char* const kStageNames[kNumStages];
 hipError_t launch(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
 
 // Backward pass (bf16): kNumBwdStages launches, events as for launch().
-constexpr int kNumBwdStages = 6;
+constexpr int kNumBwdStages = 7;
 extern const char* const kBwdStageNames[kNumBwdStages];
 hipError_t launch_bwd(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
 

@@ -1463,7 +1463,7 @@ hipError_t launch_transition(const Plan& p, hipStream_t st) {
 // backward operand set overwrites the forward one once the checkpointing pass
 // has consumed it (same stream).
 const char* const kBwdStageNames[kNumBwdStages] = {"k_chunk_table", "k_prep", "k_recur_lds<ckpt>",
-                                                   "k_prep<bwd>", "k_recur_lds<bwd>", "k_grad"};
+                                                   "k_prep<bwd>", "k_recur_lds<bwd>", "k_grad", "k_dbeta_sum"};
 
 template <int D>
 static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
@@ -1488,8 +1488,8 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, p.dv, RecurAux{ckdS, dZ, nullptr, p.ws_bet}, st);
     mark(5);
     hipError_t e = hipGetLastError();
+    GradArgs a{};
     if (e == hipSuccess && p.total_tokens > 0) {
-        GradArgs a{};
         a.q = static_cast<const E*>(p.q);
         a.k = static_cast<const E*>(p.k);
         a.g = static_cast<const E*>(p.g);
@@ -1507,6 +1507,8 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         a.fixed_chunks = p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk));
         a.H = p.n_heads;
         a.max_chunks = p.max_chunks;
+        a.total_tokens = p.total_tokens;
+        a.dbp = p.ws_dbp;
         a.dq = static_cast<E*>(p.dq);
         a.dk = static_cast<E*>(p.dk);
         a.dbeta = static_cast<E*>(p.dbeta);
@@ -1514,6 +1516,8 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         e = launch_grad(a, D, p.max_chunks, st);
     }
     mark(6);
+    if (e == hipSuccess && p.total_tokens > 0) e = launch_dbeta_sum(a, st);
+    mark(7);
     return e == hipSuccess ? hipGetLastError() : e;
 }
 

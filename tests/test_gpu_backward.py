@@ -128,3 +128,33 @@ def test_backward_config1_sampled(torch_dev):
         _say("  seq %d head %d: " % (n, h) + " ".join("%s=%.2e" % (key, e[key]) for key in KEYS))
         for key in KEYS:
             assert e[key] <= TOL, "%s parity %.3e > %.0e (seq %d head %d)" % (key, e[key], TOL, n, h)
+
+
+def test_backward_headline_sampled(torch_dev):
+    """The headline workload (B=1, H=32, T=65536, d=128, S0 ~ 0.02 N(0,1)) in
+    one backward launch over all heads, with dO and dS_T drawn as the
+    benchmark draws them; head 5 checked in full against the oracle."""
+    torch, dev = torch_dev
+    import gated_delta_rule_30_amd as kda
+    spec = ki.headline_configs()[2]
+    inp = ki.generate_torch(spec, dev)
+    T, H, d, N = spec.total_tokens, spec.n_heads, spec.d_k, spec.n_seqs
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec.seed + 1000003)
+    dO = torch.randn((T, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    dST = torch.randn((N, H, d, d), generator=gen, device=dev, dtype=torch.float32)
+    _say("headline backward: B=1 H=32 T=65536 d=128")
+    out = kda.chunk_bwd(inp.q, inp.k, inp.v, inp.beta, inp.g, dO, S0=inp.S0, dS_T=dST, n_seqs=N)
+    torch.cuda.synchronize()
+    h = 5
+    host = lambda x: x[:, h:h + 1].float().cpu().numpy()
+    t0 = time.time()
+    ref = oracle.backward(host(inp.q), host(inp.k), host(inp.v), host(inp.beta), host(inp.g), host(dO),
+                          inp.S0[:, h:h + 1].cpu().numpy(), dST[:, h:h + 1].cpu().numpy())
+    e = {key: oracle.parity_error(host(out[key]), ref[key]) for key in ("dq", "dk", "dv", "dg")}
+    e["dbeta"] = oracle.parity_error(host(out["dbeta"])[:, :, None], ref["dbeta"][:, :, None])
+    e["dS0"] = oracle.parity_error(out["dS0"][:, h:h + 1].cpu().numpy(), ref["dS0"])
+    _say("  head %d: " % h + " ".join("%s=%.2e" % (key, e[key]) for key in KEYS) +
+         "  (oracle %.1fs)" % (time.time() - t0))
+    for key in KEYS:
+        assert e[key] <= TOL, "%s parity %.3e > %.0e" % (key, e[key], TOL)
