@@ -161,3 +161,51 @@ def test_transition_and_compose_reject_bad_arguments(lib):
     assert comp(Pp=None) == ERR_NULL
     assert comp(S=None) == ERR_NULL
     assert comp(Z=fake + 4) == ERR_SHAPE
+
+
+def test_backward_workspace_and_rejections(lib):
+    P = ctypes.c_void_p
+    fake = 0x7f0000000000          # never dereferenced: every case below fails validation
+    fwd = kda.workspace_size(65536, 1, 32, 128, 128, 64, kda.KDA_BF16)
+    bwd = kda.bwd_workspace_size(65536, 1, 32, 128, 128, 64, kda.KDA_BF16)
+    # the backward keeps two d x d bf16 states per chunk and head and three v-sized bf16 tensors
+    assert bwd >= fwd + 2 * 1024 * 32 * 128 * 128 * 2 + 3 * 65536 * 32 * 128 * 2
+    assert kda.bwd_workspace_size(65536, 1, 32, 128, 128, 64, kda.KDA_F32) == 0
+    assert kda.bwd_workspace_size(256, 1, 2, 96, 96, 64, kda.KDA_BF16) == 0
+    assert kda.bwd_workspace_size(0, 3, 2, 64, 64, 64, kda.KDA_BF16) > 0
+    assert kda.bwd_workspace_size(1000, 3, 4, 64, 64, 64, kda.KDA_BF16) % 256 == 0
+
+    def bw(dt=kda.KDA_BF16, T=128, N=1, H=2, d=64, C=64, ptrs=None, ws=0x100000, ws_bytes=0):
+        p = dict(q=fake, k=fake, v=fake, beta=fake, g=fake, S0=None, cu=None, dO=fake, dST=None,
+                 dq=fake, dk=fake, dv=fake, dbeta=fake, dg=fake, dS0=None)
+        if ptrs:
+            p.update(ptrs)
+        return lib.kda_chunk_bwd(dt, T, N, H, d, d, C, *(P(p[n]) for n in (
+            "q", "k", "v", "beta", "g", "S0", "cu", "dO", "dST", "dq", "dk", "dv", "dbeta", "dg", "dS0")),
+            P(ws), ws_bytes, None)
+    assert bw(dt=kda.KDA_F32) == ERR_UNSUPPORTED
+    assert bw(dt=9) == ERR_DTYPE
+    assert bw(d=96) == ERR_UNSUPPORTED
+    assert bw(C=32) == ERR_UNSUPPORTED
+    assert bw(T=100, N=3) == ERR_SHAPE
+    for name in ("q", "k", "v", "beta", "g", "dO", "dq", "dk", "dv", "dbeta", "dg"):
+        assert bw(ptrs={name: None}) == ERR_NULL, name
+    assert bw(ptrs={"dS0": fake + 4}) == ERR_SHAPE
+    assert bw(ptrs={"dST": fake + 8}) == ERR_SHAPE
+    assert bw(ws=None) == ERR_WORKSPACE
+    need = kda.bwd_workspace_size(128, 1, 2, 64, 64, 64, kda.KDA_BF16)
+    assert bw(ws_bytes=need - 1) == ERR_WORKSPACE
+    # the forward's workspace is not enough for the backward
+    assert bw(ws_bytes=kda.workspace_size(128, 1, 2, 64, 64, 64, kda.KDA_BF16)) == ERR_WORKSPACE
+    ms = (ctypes.c_float * 7)()
+    assert lib.kda_chunk_bwd_profile(kda.KDA_F32, 128, 1, 2, 64, 64, 64, *([None] * 15), None, 0, None,
+                                     ms) == ERR_UNSUPPORTED
+    assert kda.bwd_stage_names() == ["k_chunk_table", "k_prep", "k_recur_lds<ckpt>", "k_prep<bwd>",
+                                     "k_recur_lds<bwd>", "k_grad", "k_dbeta_sum"]
+
+
+def test_backward_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        kda.chunk_bwd(x, x, x, torch.zeros(4, 2, dtype=torch.bfloat16), x, x)
