@@ -216,6 +216,34 @@ def backward_measure(torch, kda, inp, cu, spec, reps=5, profile_reps=3):
             "roofline": roof, "source_sha": source_sha(KERNEL_SOURCES["k_grad"])}
 
 
+def epilogue_measure(torch, kda, o, reps=20):
+    """Output epilogue RMSNorm(o) * w * sigmoid(z) over the forward's o
+    (bf16, all token-head rows); bound by reading o and z and writing y."""
+    gen = torch.Generator(device=o.device)
+    gen.manual_seed(11)
+    z = torch.randn(o.shape, generator=gen, device=o.device, dtype=torch.float32).to(o.dtype)
+    w = torch.rand((o.shape[-1],), generator=gen, device=o.device, dtype=torch.float32) + 0.5
+    y = torch.empty_like(o)
+    for _ in range(3):
+        kda.output_gate(o, z, w, out=y)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(o.device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        kda.output_gate(o, z, w, out=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    nbytes = 3 * o.numel() * o.element_size()
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"workload": "RMSNorm(o) * w * sigmoid(z) on the forward's o, %s rows x d=%d, bf16"
+                        % (o.numel() // o.shape[-1], o.shape[-1]),
+            "us_per_call": us,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_call": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +347,7 @@ def main():
     if spec.dtype == "bf16":
         out["backward"] = backward_measure(torch, kda, inp, cu, spec)
         out["backward"]["vs_forward"] = out["backward"]["ms_per_pass"] / ms
+    out["epilogue"] = epilogue_measure(torch, kda, o)
     out["decode"] = decode_measure(torch, kda, dev)
     if spec.dtype == "bf16" and spec.n_seqs == 1:
         out["sequence_parallel"] = seqpar_measure(torch, kda, inp, ms)

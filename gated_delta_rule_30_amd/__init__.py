@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_profile", "chunk_bwd", "chunk_bwd_profile", "bwd_stage_names", "bwd_workspace_size", "recurrent_fwd", "validate_inputs", "chunk_transition",
+__all__ = ["chunk_fwd", "chunk_fwd_profile", "chunk_bwd", "chunk_bwd_profile", "output_gate", "bwd_stage_names", "bwd_workspace_size", "recurrent_fwd", "validate_inputs", "chunk_transition",
            "compose_states", "sequence_parallel_fwd", "stage_names", "workspace_size", "status_string", "lib_path",
            "KDA_F32", "KDA_BF16", "KdaError"]
 
@@ -72,6 +72,8 @@ def _load():
         lib.kda_profile_bwd_num_stages.restype = ctypes.c_int32
         lib.kda_profile_bwd_stage_name.argtypes = [ctypes.c_int32]
         lib.kda_profile_bwd_stage_name.restype = ctypes.c_char_p
+        lib.kda_output_gate.argtypes = [ctypes.c_int, I64, I32, P, P, P, ctypes.c_float, P, P]
+        lib.kda_output_gate.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -255,6 +257,40 @@ def chunk_bwd(q, k, v, beta, log_alpha, dO, S0=None, dS_T=None, cu_seqlens=None,
     if batched:
         for key, shp in (("dq", shape_q), ("dk", shape_q), ("dg", shape_q), ("dv", shape_v), ("dbeta", shape_b)):
             out[key] = out[key].reshape(shp)
+    return out
+
+
+def output_gate(o, gate, weight=None, eps: float = 1e-6, out=None):
+    """Output epilogue (kda_output_gate): RMSNorm(o) * weight * sigmoid(gate)
+    per row of the last dimension.  o, gate: same shape [..., d_v], float32 or
+    bfloat16, contiguous, on one GPU; weight: [d_v] float32 or None; out:
+    preallocated result (may be o) or None."""
+    import torch
+    lib = _load()
+    dt = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}.get(o.dtype)
+    if dt is None:
+        raise TypeError("o must be float32 or bfloat16, got %s" % o.dtype)
+    if gate.shape != o.shape or gate.dtype != o.dtype:
+        raise ValueError("gate must match o in shape and dtype")
+    dev = o.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    for name, t in (("o", o), ("gate", gate)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("%s must be contiguous on %s" % (name, dev))
+    d = o.shape[-1]
+    if weight is not None and (weight.dtype != torch.float32 or weight.shape != (d,) or weight.device != dev
+                               or not weight.is_contiguous()):
+        raise ValueError("weight must be contiguous float32 [%d] on %s" % (d, dev))
+    if out is None:
+        out = torch.empty_like(o)
+    elif out.shape != o.shape or out.dtype != o.dtype or out.device != dev or not out.is_contiguous():
+        raise ValueError("out must match o")
+    n_rows = o.numel() // d if d else 0
+    code = lib.kda_output_gate(dt, n_rows, d, _ptr(o), _ptr(gate), _ptr(weight), float(eps), _ptr(out),
+                               ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream))
+    if code != 0:
+        raise KdaError(code, lib.kda_status_string(code).decode())
     return out
 
 

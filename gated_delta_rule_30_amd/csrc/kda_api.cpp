@@ -310,6 +310,21 @@ kda_status kda_chunk_bwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_s
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+kda_status kda_output_gate(kda_dtype dt, int64_t n_rows, int32_t d_v, const void* o, const void* gate,
+                           const float* weight, float eps, void* y, void* stream) {
+    if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
+    if (n_rows < 0 || d_v < 1) return KDA_ERR_SHAPE;
+    if (d_v != 64 && d_v != 128) return KDA_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f) || eps > 1.f) return KDA_ERR_SHAPE;   // also rejects NaN
+    if (n_rows > 0 && (!o || !gate || !y)) return KDA_ERR_NULL;
+    const void* ptrs[] = {o, gate, weight, y};
+    for (const void* ptr : ptrs)
+        if (ptr && ((uintptr_t)ptr % 16) != 0) return KDA_ERR_SHAPE;
+    hipError_t e = kda::launch_output_gate(dt == KDA_BF16, n_rows, d_v, o, gate, weight, eps, y,
+                                           static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 const char* kda_status_string(kda_status s) {
     switch (s) {
         case KDA_OK: return "KDA_OK: success";

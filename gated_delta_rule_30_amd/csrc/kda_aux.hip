@@ -235,4 +235,79 @@ hipError_t launch_validate(bool bf16, int64_t total_tokens, int32_t n_seqs, int3
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- output epilogue
+// y = RMSNorm(o) * sigmoid(z) per (token, head) row of d_v channels (ogis-ri
+// NLP primer on Kimi K3, §3.1 "KDA": the read-out is normalised because its
+// magnitude varies with the state, then multiplied channel by channel by a
+// gate in (0, 1) made from the layer input; W_o follows outside).
+// RMSNorm(x) = x / sqrt(mean(x^2) + eps) * w.  16 lanes per row, D/16
+// consecutive channels per lane (one 16- or 8-byte load per operand), the
+// sum of squares reduced by a 16-lane butterfly; 16 rows per workgroup,
+// grid-stride over rows.  y may be o itself: each row is read whole before
+// any of it is written.
+template <typename E, int D>
+__global__ __launch_bounds__(256) void k_output_gate(const E* __restrict__ o, const E* __restrict__ z,
+                                                     const float* __restrict__ w, float eps, int64_t n_rows,
+                                                     E* __restrict__ y) {
+    constexpr int PER = D / 16;
+    const int sub = threadIdx.x & 15;
+    const int c0 = sub * PER;
+    float wv[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) wv[e] = w ? w[c0 + e] : 1.f;
+    for (int64_t r = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4; r < n_rows; r += (int64_t)gridDim.x * 16) {
+        const int64_t at = r * D + c0;
+        // PER consecutive elements per lane as whole 16-byte vectors (8 bytes for bf16 at D = 64)
+        constexpr int NV = (PER * (int)sizeof(E) + 15) / 16;
+        using V = typename std::conditional<PER * sizeof(E) >= 16, uint4, uint2>::type;
+        V vo[NV], vz[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            vo[i] = reinterpret_cast<const V*>(o + at)[i];
+            vz[i] = reinterpret_cast<const V*>(z + at)[i];
+        }
+        const E* eo = reinterpret_cast<const E*>(vo);
+        const E* ez = reinterpret_cast<const E*>(vz);
+        float ov[PER], zv[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            ov[e] = to_f(eo[e]);
+            zv[e] = to_f(ez[e]);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) ss += ov[e] * ov[e];
+        ss += __shfl_xor(ss, 1);
+        ss += __shfl_xor(ss, 2);
+        ss += __shfl_xor(ss, 4);
+        ss += __shfl_xor(ss, 8);
+        const float inv = rsqrtf(ss / (float)D + eps);
+        V vy[NV];
+        E* ey = reinterpret_cast<E*>(vy);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) ey[e] = from_f<E>(ov[e] * inv * wv[e] / (1.f + __expf(-zv[e])));
+#pragma unroll
+        for (int i = 0; i < NV; ++i) reinterpret_cast<V*>(y + at)[i] = vy[i];
+    }
+}
+
+hipError_t launch_output_gate(bool bf16, int64_t n_rows, int32_t d, const void* o, const void* z, const float* w,
+                              float eps, void* y, hipStream_t st) {
+    if (n_rows <= 0) return hipSuccess;
+    const int64_t want = (n_rows + 15) / 16;
+    const unsigned blocks = (unsigned)(want < 16384 ? want : 16384);
+#define KDA_GATE(E, D)                                                                                      \
+    hipLaunchKernelGGL((k_output_gate<E, D>), dim3(blocks), dim3(256), 0, st, static_cast<const E*>(o),   \
+                       static_cast<const E*>(z), w, eps, n_rows, static_cast<E*>(y))
+    if (bf16) {
+        if (d == 128) KDA_GATE(__bf16, 128);
+        else KDA_GATE(__bf16, 64);
+    } else {
+        if (d == 128) KDA_GATE(float, 128);
+        else KDA_GATE(float, 64);
+    }
+#undef KDA_GATE
+    return hipGetLastError();
+}
+
 }  // namespace kda

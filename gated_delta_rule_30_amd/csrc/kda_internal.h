@@ -103,6 +103,10 @@ struct DecodePlan {
 };
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
 
+// Output epilogue y = RMSNorm(o) * sigmoid(z) over rows of d channels (kda_output_gate).
+hipError_t launch_output_gate(bool bf16, int64_t n_rows, int32_t d, const void* o, const void* z, const float* w,
+                              float eps, void* y, hipStream_t stream);
+
 // Input validator (kda_validate_inputs): clears counts[0..2] and adds the
 // number of violations found; see the header.
 hipError_t launch_validate(bool bf16, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,

@@ -163,6 +163,24 @@ kda_status kda_recurrent_fwd(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int
                              const void* beta, const void* log_alpha,
                              const float* S_in, float* S_out, void* o, void* stream);
 
+/* Output epilogue of a KDA layer (ogis-ri NLP primer on Kimi K3, §3.1
+ * "KDA": the read-out is normalised by RMSNorm because its magnitude varies
+ * with the state, then multiplied channel by channel by a gate in (0, 1)
+ * made from the layer input; the output projection W_o follows and is not
+ * part of this call).  The printed formula was lost; this library reads it
+ * as, per row (one token of one head, d_v channels):
+ *     y = o / sqrt(mean(o^2) + eps) * w * sigmoid(gate)
+ *   o, gate, y : [n_rows, d_v] contiguous, dtype dt (n_rows = tokens x heads
+ *                for the [T, H, d_v] layout of kda_chunk_fwd's o); y may be o
+ *                (in place); gate holds the pre-activations
+ *   weight     : [d_v] float32 per-channel scale, or NULL (ones)
+ *   eps        : in [0, 1] (KDA_ERR_SHAPE otherwise, NaN included)
+ * Supported: d_v in {64, 128}, dt KDA_F32 or KDA_BF16; pointers 16-byte
+ * aligned.  n_rows == 0 is valid (nothing is done).  Needs no workspace;
+ * enqueued on `stream`, never synchronises. */
+kda_status kda_output_gate(kda_dtype dt, int64_t n_rows, int32_t d_v, const void* o, const void* gate,
+                           const float* weight, float eps, void* y, void* stream);
+
 /* Debug check of the value-range preconditions that the compute entry points
  * do not check: counts[0] receives the number of log_alpha elements outside
  * [-5, 0] or not finite, counts[1] the number of beta elements outside

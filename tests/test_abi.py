@@ -209,3 +209,21 @@ def test_backward_binding_rejects_host_tensors():
     x = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         kda.chunk_bwd(x, x, x, torch.zeros(4, 2, dtype=torch.bfloat16), x, x)
+
+
+def test_output_gate_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    fake = 0x7f0000000000
+
+    def og(dt=kda.KDA_BF16, n=10, d=128, o=fake, z=fake, w=None, eps=1e-6, y=fake):
+        return lib.kda_output_gate(dt, n, d, P(o), P(z), P(w), eps, P(y), None)
+    assert og(dt=5) == ERR_DTYPE
+    assert og(n=-1) == ERR_SHAPE
+    assert og(d=96) == ERR_UNSUPPORTED
+    assert og(eps=float("nan")) == ERR_SHAPE
+    assert og(eps=-1.0) == ERR_SHAPE
+    assert og(o=None) == ERR_NULL
+    assert og(z=None) == ERR_NULL
+    assert og(y=None) == ERR_NULL
+    assert og(w=fake + 4) == ERR_SHAPE
+    assert og(n=0, o=None, z=None, y=None) == OK      # nothing to do, nothing launched
