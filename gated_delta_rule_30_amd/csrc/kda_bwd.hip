@@ -72,12 +72,13 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
     constexpr int NTH = HALF / 16;    // channel tiles per workgroup
     constexpr int CH = 4 * NTH;       // channels per lane
     constexpr int KV = D / M::KS;     // k-steps of a contraction over value columns
-    constexpr int PSd = D + 8;        // pitch of the staged states (elements)
+    constexpr int PSd = D + 8;        // pitch of the staged U~ rows (elements)
     constexpr int PT = C + 8;         // pitch of token-indexed rows
-    constexpr int kXs = 2 * HALF * PSd, kXu = C * PSd, kXg = 3 * HALF * PT;
+    constexpr int kXs = 2 * HALF * D, kXu = C * PSd, kXg = 3 * HALF * PT;
     constexpr int kX = kXs > kXu ? (kXs > kXg ? kXs : kXg) : (kXu > kXg ? kXu : kXg);
-    // Region X: the half's rows of S and dS' ([channel][value column]); then
-    // U~ ([token][value column]); then the Gram operands ([channel][token]).
+    // Region X: the half's rows of S and dS' (state_swz layout, copied as
+    // stored); then U~ ([token][value column]); then the Gram operands
+    // ([channel][token]).
     __shared__ __attribute__((aligned(16))) E sX[kX];
     __shared__ __attribute__((aligned(16))) E sdA[C * PT];     // dA      [r][i]
     __shared__ __attribute__((aligned(16))) E sdGq[C * PT];    // dGq     [r][i]
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
     __shared__ float sDgam[HALF];
     __shared__ float sBeta[C];
     E* sS = sX;
-    E* sdS = sX + HALF * PSd;
+    E* sdS = sX + HALF * D;
     E* sU = sX;
     E* sKD = sX;                  // k_i e^{rho_{J+1} - b_i}
     E* sKr = sX + HALF * PT;      // k_r e^{b_r - rho_R}
@@ -120,70 +121,81 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
     const int t = kSub * w + li;
     const bool ok = t < len;
     const int64_t rs = (int64_t)H * D;
-    const int64_t row = (info.tok0 + (ok ? t : 0)) * rs + (int64_t)h * D;   // this lane's token row
+    // this lane's token row; rows past the chunk end read the chunk's first
+    // row (a valid address) and are zeroed in registers
+    const int64_t row = (info.tok0 + (ok ? t : 0)) * rs + (int64_t)h * D;
     const int64_t slot = (int64_t)h * a.max_chunks + ci;
-    // i-th channel group of this lane: local channel (within the half) and global channel
-    auto lch = [&](int i, int r) { return kSub * i + 4 * lg + r; };
+    auto lch = [&](int i, int r) { return kSub * i + 4 * lg + r; };   // local channel in the half
     const int c0 = hh * HALF;
 
-    // ---- inputs at (token t, this lane's channels)
+    // ---- every load is issued before any is used
+    // the half's rows of S and dS' go global -> LDS by direct loads, 1 KB per wave instruction
+    {
+        constexpr int kVec = HALF * D / 8;   // 16-byte vectors per matrix
+        const E* gS = a.ckS + slot * D * D + (int64_t)c0 * D;
+        const E* gD = a.ckdS + slot * D * D + (int64_t)c0 * D;
+#pragma unroll
+        for (int v0 = w * 64; v0 < kVec; v0 += kGradThreads) {
+            __builtin_amdgcn_global_load_lds(gS + 8 * (v0 + lane), (__attribute__((address_space(3))) void*)(sS + 8 * v0), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(gD + 8 * (v0 + lane), (__attribute__((address_space(3))) void*)(sdS + 8 * v0), 16, 0, 0);
+        }
+    }
+    uint2 rq[NTH], rk[NTH], rg[NTH];
+#pragma unroll
+    for (int i = 0; i < NTH; ++i) {
+        const int64_t at = row + c0 + lch(i, 0);
+        rq[i] = *reinterpret_cast<const uint2*>(a.q + at);
+        rk[i] = *reinterpret_cast<const uint2*>(a.k + at);
+        rg[i] = *reinterpret_cast<const uint2*>(a.g + at);
+    }
+    const E beta_raw = a.beta[(info.tok0 + (ok ? t : 0)) * H + h];
+    // token rows of dO, dY, U~, dZ (and Y) as fragments over value columns
+    uint4 fo[KV], fy[KV], fu[KV], fz[KV], fY[KV];
+#pragma unroll
+    for (int m = 0; m < KV; ++m) {
+        const int64_t at = row + M::KS * m + M::KW * lg;
+        fo[m] = *reinterpret_cast<const uint4*>(a.dO + at);
+        fy[m] = *reinterpret_cast<const uint4*>(a.dv + at);
+        fu[m] = *reinterpret_cast<const uint4*>(a.U + at);
+        fz[m] = *reinterpret_cast<const uint4*>(a.dZ + at);
+        if (hh == 0) fY[m] = *reinterpret_cast<const uint4*>(a.Y + at);
+    }
+    // ---- zero the rows past the chunk end (bit masks: no branches, so the
+    // loads above stay in flight until their first use)
+    const unsigned msk = ok ? 0xffffffffu : 0u;
+    const float okf = ok ? 1.f : 0.f;
+    auto mask4 = [&](uint4& u) { u.x &= msk; u.y &= msk; u.z &= msk; u.w &= msk; };
     float qf[CH], kf[CH], b[CH];
 #pragma unroll
     for (int i = 0; i < NTH; ++i) {
-        // rows past the chunk end load a valid row (the chunk's first) and read as zero
-        const int64_t at = row + c0 + lch(i, 0);
-        uint2 rq = *reinterpret_cast<const uint2*>(a.q + at);
-        uint2 rk = *reinterpret_cast<const uint2*>(a.k + at);
-        uint2 rg = *reinterpret_cast<const uint2*>(a.g + at);
-        if (!ok) rq = rk = rg = make_uint2(0, 0);
-        const E* eq = reinterpret_cast<const E*>(&rq);
-        const E* ek = reinterpret_cast<const E*>(&rk);
-        const E* eg = reinterpret_cast<const E*>(&rg);
+        const E* eq = reinterpret_cast<const E*>(&rq[i]);
+        const E* ek = reinterpret_cast<const E*>(&rk[i]);
+        const E* eg = reinterpret_cast<const E*>(&rg[i]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            qf[4 * i + r] = (float)eq[r];
-            kf[4 * i + r] = (float)ek[r];
-            b[4 * i + r] = (float)eg[r];
+            qf[4 * i + r] = (float)eq[r] * okf;
+            kf[4 * i + r] = (float)ek[r] * okf;
+            b[4 * i + r] = (float)eg[r] * okf;
         }
     }
-    float bt = (float)a.beta[(info.tok0 + (ok ? t : 0)) * H + h];
-    if (!ok) bt = 0.f;
-    // token rows of dO, dY, U~, dZ as fragments over value columns
-    uint4 fo[KV], fy[KV], fu[KV], fz[KV];
+    const float bt = (float)beta_raw * okf;
     float dbeta = 0.f;
-    {
-        const uint4 z = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int m = 0; m < KV; ++m) {
+        mask4(fo[m]);
+        mask4(fy[m]);
+        mask4(fu[m]);
+        mask4(fz[m]);
+    }
+    if (hh == 0) {   // first dbeta term, sum_j dZ_tj Y_tj (the other half adds none)
 #pragma unroll
         for (int m = 0; m < KV; ++m) {
-            const int64_t at = row + M::KS * m + M::KW * lg;
-            fo[m] = *reinterpret_cast<const uint4*>(a.dO + at);
-            fy[m] = *reinterpret_cast<const uint4*>(a.dv + at);
-            fu[m] = *reinterpret_cast<const uint4*>(a.U + at);
-            fz[m] = *reinterpret_cast<const uint4*>(a.dZ + at);
-            if (!ok) fo[m] = fy[m] = fu[m] = fz[m] = z;
-        }
-        if (hh == 0) {   // first dbeta term, sum_j dZ_tj Y_tj (the other half adds none)
+            const bf16x8 zf = as_frag(fz[m]), yf = as_frag(fY[m]);
 #pragma unroll
-            for (int m = 0; m < KV; ++m) {
-                uint4 yv = *reinterpret_cast<const uint4*>(a.Y + row + M::KS * m + M::KW * lg);
-                if (!ok) yv = z;
-                const bf16x8 zf = as_frag(fz[m]), yf = as_frag(yv);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dbeta += (float)zf[e] * (float)yf[e];
-            }
-            dbeta += __shfl_xor(dbeta, 16);
-            dbeta += __shfl_xor(dbeta, 32);
+            for (int e = 0; e < 8; ++e) dbeta += (float)zf[e] * (float)yf[e];
         }
-    }
-    // this half's rows of S and dS' into LDS
-    {
-        const uint4* gS = reinterpret_cast<const uint4*>(a.ckS + slot * D * D + (int64_t)c0 * D);
-        const uint4* gD = reinterpret_cast<const uint4*>(a.ckdS + slot * D * D + (int64_t)c0 * D);
-        for (int vi = tid; vi < HALF * D / 8; vi += kGradThreads) {
-            const int c = vi / (D / 8), j8 = vi % (D / 8);
-            *reinterpret_cast<uint4*>(&sS[c * PSd + 8 * j8]) = gS[vi];
-            *reinterpret_cast<uint4*>(&sdS[c * PSd + 8 * j8]) = gD[vi];
-        }
+        dbeta += __shfl_xor(dbeta, 16);
+        dbeta += __shfl_xor(dbeta, 32);
     }
     // decay cumulative sum: 16-lane row scan, carries between token tiles
 #pragma unroll
@@ -195,6 +207,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
             for (int r = 0; r < 4; ++r) sTot[w * HALF + lch(i, r)] = b[4 * i + r];
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the direct loads into LDS have landed
     __syncthreads();
     for (int c = tid; c < HALF; c += kGradThreads) {
         float run = 0.f;
@@ -205,13 +218,20 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
         }
         sRho[kNSub * HALF + c] = run;
     }
-    // dgamma_c = sum_j dS'_cj S_cj
+    // dgamma_c = sum_j dS'_cj S_cj (the row's vectors in any order: both
+    // matrices carry the same permutation)
     {
         constexpr int TPC = kGradThreads / HALF;   // threads per channel
+        constexpr int VPT = D / 8 / TPC;           // 16-byte vectors per thread
         const int c = tid / TPC, part = tid % TPC;
         float acc = 0.f;
-        for (int j = part * (D / TPC); j < (part + 1) * (D / TPC); ++j)
-            acc += (float)sS[c * PSd + j] * (float)sdS[c * PSd + j];
+#pragma unroll
+        for (int v = 0; v < VPT; ++v) {
+            const bf16x8 xs = *reinterpret_cast<const bf16x8*>(&sS[c * D + 8 * (part * VPT + v)]);
+            const bf16x8 xd = *reinterpret_cast<const bf16x8*>(&sdS[c * D + 8 * (part * VPT + v)]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc += (float)xs[e] * (float)xd[e];
+        }
 #pragma unroll
         for (int o = 1; o < TPC; o <<= 1) acc += __shfl_xor(acc, o);
         if (part == 0) sDgam[c] = acc;
@@ -229,8 +249,10 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
         f32x4 aq = zero4(), ak = zero4(), ah = zero4();
 #pragma unroll
         for (int m = 0; m < KV; ++m) {
-            const F fs = M::load(&sS[(kSub * i + li) * PSd + M::KS * m + M::KW * lg]);
-            const F fd = M::load(&sdS[(kSub * i + li) * PSd + M::KS * m + M::KW * lg]);
+            // row kSub*i + li, vector 4m + lg, permuted by the row (state_swz)
+            const int at = (kSub * i + li) * D + ((((M::KS * m + M::KW * lg) >> 3) ^ (li & (D / 8 - 1))) << 3);
+            const F fs = M::load(&sS[at]);
+            const F fd = M::load(&sdS[at]);
             aq = M::mma(fs, as_frag(fo[m]), aq);
             ak = M::mma(fs, as_frag(fy[m]), ak);
             ah = M::mma(fd, as_frag(fu[m]), ah);
@@ -264,16 +286,20 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
                 accG = M::mma(as_frag(fo[m]), fj, accG);
             }
         }
+        bf16x4 tk, tq;   // rows 4lg .. 4lg+3 of column ii: consecutive in the transposes
+        const int ii = kSub * J + li;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int rr = kSub * w + 4 * lg + r, ii = kSub * J + li;
+            const int rr = kSub * w + 4 * lg + r;
             const float dA = ii < rr ? -accA[r] : 0.f;
             const float dG = ii <= rr ? accG[r] : 0.f;
             sdA[rr * PT + ii] = (E)dA;
             sdGq[rr * PT + ii] = (E)dG;
-            sdGkT[ii * PT + rr] = (E)(sBeta[rr] * dA);
-            sdGqT[ii * PT + rr] = (E)dG;
+            tk[r] = (E)(sBeta[rr] * dA);
+            tq[r] = (E)dG;
         }
+        *reinterpret_cast<bf16x4*>(&sdGkT[ii * PT + kSub * w + 4 * lg]) = tk;
+        *reinterpret_cast<bf16x4*>(&sdGqT[ii * PT + kSub * w + 4 * lg]) = tq;
     }
     __syncthreads();   // U~ is dead: region X takes the Gram operands
 #pragma unroll

@@ -66,6 +66,16 @@ template <typename E> __device__ inline E from_f(float x) { return static_cast<E
 
 __device__ inline int lane_id() { return threadIdx.x & 63; }
 
+// Layout of a d x d bf16 state kept for the backward pass (row = key
+// channel, d = 64 or 128): row-major, with the 16-byte vectors of row c
+// permuted by XOR with c mod (d/8).  Copied linearly into LDS, the A-operand
+// reads of 16 consecutive rows at one k-step then touch 16 distinct vector
+// positions, i.e. different banks.  Element index of (c, col):
+template <int D>
+__device__ inline int state_swz(int c, int col) {
+    return c * D + ((((col >> 3) ^ (c & (D / 8 - 1)))) << 3) + (col & 7);
+}
+
 // Scans along the 16 lanes of a DPP row (lanes 16g .. 16g+15), zero fill:
 // row_scan16 is the inclusive prefix sum, row_rscan16 the inclusive suffix sum.
 template <int kShift>

@@ -1174,13 +1174,14 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     };
     put_state();
     // kCkpt / kBwd: this slab's columns of the state (gradient) as chunk j
-    // starts, into slot j of aux.ck
+    // starts, into slot j of aux.ck (state_swz layout)
     auto keep_state = [&](int j) {
-        E* ck = aux.ck + (cb + j) * D * D + col0 + li;
+        E* ck = aux.ck + (cb + j) * D * D;
 #pragma unroll
         for (int a = 0; a < RT; ++a)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ck[(int64_t)(kSub * (RT * w + a) + 4 * lg + r) * D] = from_f<E>(S[a][r]);
+            for (int r = 0; r < 4; ++r)
+                ck[state_swz<D>(kSub * (RT * w + a) + 4 * lg + r, col0 + li)] = from_f<E>(S[a][r]);
     };
 
     auto step = [&](const uint4* buf, int j) {
