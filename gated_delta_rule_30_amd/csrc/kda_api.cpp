@@ -35,6 +35,11 @@ size_t carve_workspace(Plan* p, void* base) {
     if (p->bwd) {
         const size_t T = (size_t)p->total_tokens;
         p->ws_bet = (float*)take(4 * mc * H * kChunkTokens);
+        p->ws_bTT = take(es * mc * H * kChunkTokens * kChunkTokens);
+        p->ws_bMT = take(es * mc * H * kChunkTokens * kChunkTokens);
+        p->ws_bKh = take(es * mc * H * kChunkTokens * D);
+        p->ws_bQgT = take(es * mc * H * D * kChunkTokens);
+        p->ws_bKgT = take(es * mc * H * D * kChunkTokens);
         p->ws_ckS = take(2 * mc * H * D * D);
         p->ws_ckdS = take(2 * mc * H * D * D);
         p->ws_Y = take(2 * T * H * D);

@@ -13,7 +13,7 @@
 //
 // Per chunk (b = cumsum of log alpha inside the chunk, Gamma = exp(b),
 // gamma = Gamma at the last token, K^ = K . exp(b_L - b), dY = dv):
-//   d(Q.Gamma) = dO S^T     d(K.Gamma) = -dY S^T     dK^ = U~ dS'^T
+//   d(Q.Gamma) = dO S^T     d(K.Gamma) = -dY S^T     dK^ = U~ dS'^T   (dY = diag(beta) dZ)
 //   dgamma_c = sum_j dS'_cj S_cj
 //   dA  = -tril(dZ U~^T, -1)    (= -T^T dU~ Z^T T^T with Z = diag(beta) Y)
 //   dGq =  tril(dO U~^T)
@@ -155,7 +155,6 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
     for (int m = 0; m < KV; ++m) {
         const int64_t at = row + M::KS * m + M::KW * lg;
         fo[m] = *reinterpret_cast<const uint4*>(a.dO + at);
-        fy[m] = *reinterpret_cast<const uint4*>(a.dv + at);
         fu[m] = *reinterpret_cast<const uint4*>(a.U + at);
         fz[m] = *reinterpret_cast<const uint4*>(a.dZ + at);
         if (hh == 0) fY[m] = *reinterpret_cast<const uint4*>(a.Y + at);
@@ -183,9 +182,14 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
     for (int m = 0; m < KV; ++m) {
         mask4(fo[m]);
-        mask4(fy[m]);
         mask4(fu[m]);
         mask4(fz[m]);
+        // dY = beta dZ, row by row (the recurrence wrote the same product as dv)
+        const bf16x8 zf = as_frag(fz[m]);
+        bf16x8 yf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yf[e] = (E)(bt * (float)zf[e]);
+        fy[m] = __builtin_bit_cast(uint4, yf);
     }
     if (hh == 0) {   // first dbeta term, sum_j dZ_tj Y_tj (the other half adds none)
 #pragma unroll

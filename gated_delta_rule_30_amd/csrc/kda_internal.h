@@ -43,6 +43,12 @@ struct Plan {
     void *dq, *dk, *dv, *dbeta, *dg;
     float* dS0;               // [N, H, D, D] or NULL
     float* ws_bet;            // [H, max_chunks, 64] beta per chunk, fp32
+    // the backward operand set, same shapes as the forward one:
+    void* ws_bTT;             // T^T                      [H, max_chunks, 64, 64]
+    void* ws_bMT;             // M^T                      [H, max_chunks, 64, 64]
+    void* ws_bKh;             // K . exp(b_L - b), rows    [H, max_chunks, 64, D]
+    void* ws_bQgT;            // (Q . Gamma)^T             [H, max_chunks, D, 64]
+    void* ws_bKgT;            // (K . Gamma)^T             [H, max_chunks, D, 64]
     void* ws_ckS;             // [H, max_chunks, D, D] state entering each chunk (bf16)
     void* ws_ckdS;            // [H, max_chunks, D, D] gradient of each chunk's outgoing state (bf16)
     void *ws_Y, *ws_U, *ws_dZ;   // [T, H, D] bf16: Y, U~ and dZ per token
@@ -51,7 +57,7 @@ struct Plan {
 
 // Arguments of the per-chunk gradient kernel (kda_bwd.hip); bf16 tensors.
 struct GradArgs {
-    const __bf16 *q, *k, *g, *beta, *dO, *dv, *Y, *U, *dZ, *ckS, *ckdS;
+    const __bf16 *q, *k, *g, *beta, *dO, *Y, *U, *dZ, *ckS, *ckdS;
     const ChunkInfo* tab;
     const int32_t* n_chunks;
     int64_t fixed_len;        // > 0: equal-length sequences (chunk from the index)
@@ -79,7 +85,7 @@ extern const char* const kStageNames[kNumStages];
 hipError_t launch(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
 
 // Backward pass (bf16): kNumBwdStages launches, events as for launch().
-constexpr int kNumBwdStages = 7;
+constexpr int kNumBwdStages = 6;
 extern const char* const kBwdStageNames[kNumBwdStages];
 hipError_t launch_bwd(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
 

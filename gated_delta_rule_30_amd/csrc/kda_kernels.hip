@@ -207,15 +207,17 @@ struct ChunkOps {
 // The per-channel factors are computed once per chunk; per element only
 // exp(x), exp(-x) and exp(b_L - b) remain.
 //
-// kBwd writes the backward set of operands (see ChunkOps) from the same
-// quantities: K . exp(b_L - b) row-wise, (Q . Gamma)^T and (K . Gamma)^T
-// through two transposing LDS stages, T^T and M^T, and beta.
-template <typename E, int D, bool kBwd = false>
+// kBoth also writes the backward set of operands (see ChunkOps) into `ob`
+// from the same quantities: K . exp(b_L - b) row-wise, (K . Gamma)^T and
+// (Q . Gamma)^T through the transposing LDS stages, T^T and M^T, and beta
+// (Gamma_L is shared: ob.gam is ops.gam).
+template <typename E, int D, bool kBoth = false>
 __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ g, const E* __restrict__ beta,
                                                    const ChunkInfo* __restrict__ tab,
                                                    const int32_t* __restrict__ n_chunks_p, int64_t fixed_len,
-                                                   int32_t fixed_chunks, int32_t H, ChunkOps ops) {
+                                                   int32_t fixed_chunks, int32_t H, ChunkOps ops, ChunkOps ob) {
+    constexpr bool kBwd = kBoth;
     using G = Geo<E, D>;
     using M = Mma<E>;
     constexpr int C = kChunk, CPL = G::CPL, EPV = G::EPV;
@@ -288,7 +290,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     const float bet = ok ? to_f(beta[(info.tok0 + tok) * H + h]) : 0.f;
     if (lg == 0) sBeta[tok] = bet;
     if constexpr (kBwd) {
-        if (lg == 0) ops.bet[((int64_t)h * ops.max_chunks + ci) * C + tok] = bet;
+        if (lg == 0) ob.bet[((int64_t)h * ob.max_chunks + ci) * C + tok] = bet;
     }
 
     // Cumulative log-decay: 16-lane row scan per sub-tile, carries between
@@ -334,12 +336,15 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
         const float* esub = sTot + w * D + lg * CPL;
         uint4* qg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Qg) + cbase * C * D);
         uint4* kg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Kg) + cbase * C * D);
+        uint4* kh = reinterpret_cast<uint4*>(static_cast<E*>(ob.Qg) + cbase * C * D);
         uint4* cbv = reinterpret_cast<uint4*>(sColB + (w * kSub + li) * PC + lg * CPL);
-        // Q . Gamma, K . Gamma and the column base are stored one 16-byte
-        // vector at a time, as soon as each is complete.
-        uint4 vq, vk, vc;
+        // Q . Gamma, K . Gamma (kBoth: and K . exp(b_L - b)) and the column
+        // base are stored one 16-byte vector at a time, as soon as each is
+        // complete.
+        uint4 vq, vk, vh, vc;
         E* eq = reinterpret_cast<E*>(&vq);
         E* ek = reinterpret_cast<E*>(&vk);
+        E* eh = reinterpret_cast<E*>(&vh);
         E* ec = reinterpret_cast<E*>(&vc);
 #pragma unroll
         for (int m = 0; m < G::NKC; ++m) {
@@ -361,21 +366,20 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
                 }
                 const int cv = c % EPV;   // element within the current 16-byte vector
                 ec[cv] = from_f<E>(kv * (esub[c] * fd));
+                const float kh_v = kv * __expf(bl[c] - b[c]);
+                eq[cv] = from_f<E>(qv * gm);
+                ek[cv] = from_f<E>(kv * gm);
+                sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(kh_v);
                 if constexpr (kBwd) {
-                    // row-wise K . exp(b_L - b) into the Qg slot; Gamma-scaled
-                    // Q and K staged for their transposes
-                    eq[cv] = from_f<E>(kv * __expf(bl[c] - b[c]));
-                    sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(kv * gm);
-                    sQt[kt_at(lg * CPL + c, tok)] = from_f<E>(qv * gm);
-                } else {
-                    eq[cv] = from_f<E>(qv * gm);
-                    ek[cv] = from_f<E>(kv * gm);
-                    sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(kv * __expf(bl[c] - b[c]));
+                    // row-wise K . exp(b_L - b); K . Gamma staged for its transpose
+                    eh[cv] = from_f<E>(kh_v);
+                    sQt[kt_at(lg * CPL + c, tok)] = ek[cv];
                 }
                 if (cv == EPV - 1) {
                     const int i = c / EPV;
                     qg[(w * G::VPL + i) * 64 + lane_id()] = vq;
-                    if constexpr (!kBwd) kg[(w * G::VPL + i) * 64 + lane_id()] = vk;
+                    kg[(w * G::VPL + i) * 64 + lane_id()] = vk;
+                    if constexpr (kBwd) kh[(w * G::VPL + i) * 64 + lane_id()] = vh;
                     if (w < kNSub - 1) cbv[i] = vc;
                 }
             }
@@ -384,26 +388,32 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
         }
     }
     __syncthreads();
-    {
-        // channel rows over the chunk's tokens: (K . exp(b_L - b))^T, or for
-        // kBwd (K . Gamma)^T and (Q . Gamma)^T
-        uint4* kt = reinterpret_cast<uint4*>(static_cast<E*>(ops.KhT) + cbase * D * C);
-        uint4* qt = reinterpret_cast<uint4*>(static_cast<E*>(ops.Kg) + cbase * D * C);
+    // channel rows over the chunk's tokens, fragment-major, from a staged
+    // [channel][token] tile
+    auto store_transposed = [&](const E* st, void* dst) {
+        uint4* out = reinterpret_cast<uint4*>(static_cast<E*>(dst) + cbase * D * C);
         for (int vi = tid; vi < D * C / EPV; vi += kThreads) {
             const int ln = vi % 64, v = (vi / 64) % G::NVT, ct = vi / (64 * G::NVT);
             const int r = kSub * ct + (ln & 15), lgp = ln >> 4;
-            uint4 pk, pq;
+            uint4 pk;
             E* pe = reinterpret_cast<E*>(&pk);
-            E* pqe = reinterpret_cast<E*>(&pq);
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const int at = kt_at(r, G::tok_of(v * EPV + e, lgp));
-                pe[e] = sKt[at];
-                if constexpr (kBwd) pqe[e] = sQt[at];
-            }
-            kt[vi] = pk;
-            if constexpr (kBwd) qt[vi] = pq;
+            for (int e = 0; e < EPV; ++e) pe[e] = st[kt_at(r, G::tok_of(v * EPV + e, lgp))];
+            out[vi] = pk;
         }
+    };
+    store_transposed(sKt, ops.KhT);                     // (K . exp(b_L - b))^T
+    if constexpr (kBwd) {
+        store_transposed(sQt, ob.KhT);                  // (K . Gamma)^T
+        __syncthreads();
+        // (Q . Gamma)^T through the first stage again
+        const float* rho = sCarry + w * D + lg * CPL;
+        const float* erho = sERho + w * D + lg * CPL;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+            sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(xq.get(c) * (erho[c] * __expf(b[c] - rho[c])));
+        __syncthreads();
+        store_transposed(sKt, ob.Kg);
     }
     __syncthreads();
 
@@ -487,31 +497,38 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
         __syncthreads();
     }
 
-    // Stores: T diag(beta) and M (kBwd: T^T and M^T), fragment-major 16-byte vectors.
+    // Stores: T diag(beta) and M (kBoth: also T^T and M^T), fragment-major 16-byte vectors.
     uint4* otb = reinterpret_cast<uint4*>(static_cast<E*>(ops.TB) + cbase * C * C);
     uint4* omm = reinterpret_cast<uint4*>(static_cast<E*>(ops.Mm) + cbase * C * C);
+    uint4* ott = reinterpret_cast<uint4*>(static_cast<E*>(ob.TB) + cbase * C * C);
+    uint4* omt = reinterpret_cast<uint4*>(static_cast<E*>(ob.Mm) + cbase * C * C);
     for (int vi = tid; vi < C * C / EPV; vi += kThreads) {
         const int ln = vi % 64, v = (vi / 64) % G::NVT, wr = vi / (64 * G::NVT);
         const int r = kSub * wr + (ln & 15), lgp = ln >> 4;
-        uint4 pt, pm;
+        uint4 pt, pm, ptt, pmt;
         E* et = reinterpret_cast<E*>(&pt);
         E* em = reinterpret_cast<E*>(&pm);
+        E* ett = reinterpret_cast<E*>(&ptt);
+        E* emt = reinterpret_cast<E*>(&pmt);
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const int t = G::tok_of(v * EPV + e, lgp);
+            const bool upper = (t >> 4) > (r >> 4);   // blocks above the diagonal are zero
+            et[e] = from_f<E>(upper ? 0.f : sT[tri(r, upper ? r : t)] * sBeta[t]);
+            em[e] = upper ? from_f<E>(0.f) : sM[r * PM + t];
             if constexpr (kBwd) {
-                // element (r, t) of the transpose is (t, r): zero unless t's block >= r's
+                // element (r, t) of a transpose is (t, r): zero unless t's block >= r's
                 const bool zero = (t >> 4) < (r >> 4);
-                et[e] = from_f<E>(zero ? 0.f : sT[tri(zero ? r : t, zero ? t : r)]);
-                em[e] = zero ? from_f<E>(0.f) : sM[t * PM + r];
-            } else {
-                const bool upper = (t >> 4) > (r >> 4);   // blocks above the diagonal are zero
-                et[e] = from_f<E>(upper ? 0.f : sT[tri(r, upper ? r : t)] * sBeta[t]);
-                em[e] = upper ? from_f<E>(0.f) : sM[r * PM + t];
+                ett[e] = from_f<E>(zero ? 0.f : sT[tri(zero ? r : t, zero ? t : r)]);
+                emt[e] = zero ? from_f<E>(0.f) : sM[t * PM + r];
             }
         }
         otb[vi] = pt;
         omm[vi] = pm;
+        if constexpr (kBwd) {
+            ott[vi] = ptt;
+            omt[vi] = pmt;
+        }
     }
 }
 
@@ -1390,17 +1407,21 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 // stage i and ev[kNumStages] after the last one (a stage that does not run
 // for these sizes still gets its pair of records, with nothing between them).
 static ChunkOps chunk_ops(const Plan& p) {
-    return ChunkOps{p.ws_TB, p.ws_M, p.ws_Qg, p.ws_Kg, p.ws_KhT, p.ws_gam, p.max_chunks, p.ws_bet};
+    return ChunkOps{p.ws_TB, p.ws_M, p.ws_Qg, p.ws_Kg, p.ws_KhT, p.ws_gam, p.max_chunks, nullptr};
+}
+// the backward operand set (kda_chunk_bwd only)
+static ChunkOps chunk_ops_bwd(const Plan& p) {
+    return ChunkOps{p.ws_bTT, p.ws_bMT, p.ws_bKh, p.ws_bQgT, p.ws_bKgT, p.ws_gam, p.max_chunks, p.ws_bet};
 }
 
-template <typename E, int D, bool kBwdOps>
+template <typename E, int D, bool kBoth>
 static void launch_prep(const Plan& p, const E* q, hipStream_t st) {
     if (p.total_tokens <= 0) return;
-    hipLaunchKernelGGL((k_prep<E, D, kBwdOps>), dim3(p.max_chunks, p.n_heads), dim3(kThreads), 0, st, q,
+    hipLaunchKernelGGL((k_prep<E, D, kBoth>), dim3(p.max_chunks, p.n_heads), dim3(kThreads), 0, st, q,
                        static_cast<const E*>(p.k), static_cast<const E*>(p.g), static_cast<const E*>(p.beta),
                        p.ws_tab, p.ws_n_chunks, p.cu_seqlens ? (int64_t)0 : p.fixed_len,
                        p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk)), p.n_heads,
-                       chunk_ops(p));
+                       chunk_ops(p), kBoth ? chunk_ops_bwd(p) : chunk_ops(p));
 }
 
 template <int D, int kMode>
@@ -1408,8 +1429,9 @@ static void launch_recur_lds(const Plan& p, const void* v, const float* S0, floa
                              hipStream_t st) {
     const int32_t NH = p.n_seqs * p.n_heads;
     hipLaunchKernelGGL((k_recur_lds<D, kMode>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st,
-                       static_cast<const __bf16*>(v), chunk_ops(p), p.cu_seqlens, p.total_tokens, p.fixed_len,
-                       p.ws_seq_chunk0, NH, p.n_heads, S0, ST, static_cast<__bf16*>(o), aux);
+                       static_cast<const __bf16*>(v), kMode == kBwd ? chunk_ops_bwd(p) : chunk_ops(p),
+                       p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, p.n_heads, S0, ST,
+                       static_cast<__bf16*>(o), aux);
 }
 
 static void launch_table(const Plan& p, hipStream_t st) {
@@ -1459,12 +1481,11 @@ hipError_t launch_transition(const Plan& p, hipStream_t st) {
     return launch_all<__bf16, 64, kTrans>(p, st, nullptr);
 }
 
-// Backward: forward again with checkpoints, backward operands, the state-
-// gradient recurrence, then the chunk-parallel gradients (kda_bwd.hip).  The
-// backward operand set overwrites the forward one once the checkpointing pass
-// has consumed it (same stream).
-const char* const kBwdStageNames[kNumBwdStages] = {"k_chunk_table", "k_prep", "k_recur_lds<ckpt>",
-                                                   "k_prep<bwd>", "k_recur_lds<bwd>", "k_grad", "k_dbeta_sum"};
+// Backward: both operand sets from one k_prep, forward again with
+// checkpoints, the state-gradient recurrence, then the chunk-parallel
+// gradients (kda_bwd.hip).
+const char* const kBwdStageNames[kNumBwdStages] = {"k_chunk_table", "k_prep<fwd+bwd>", "k_recur_lds<ckpt>",
+                                                   "k_recur_lds<bwd>", "k_grad", "k_dbeta_sum"};
 
 template <int D>
 static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
@@ -1480,14 +1501,12 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     mark(0);
     launch_table(p, st);
     mark(1);
-    launch_prep<E, D, false>(p, static_cast<const E*>(p.q), st);
+    launch_prep<E, D, true>(p, static_cast<const E*>(p.q), st);
     mark(2);
     launch_recur_lds<D, kCkpt>(p, p.v, p.S0, nullptr, nullptr, RecurAux{ckS, Y, U, nullptr}, st);
     mark(3);
-    launch_prep<E, D, true>(p, static_cast<const E*>(p.q), st);
-    mark(4);
     launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, p.dv, RecurAux{ckdS, dZ, nullptr, p.ws_bet}, st);
-    mark(5);
+    mark(4);
     hipError_t e = hipGetLastError();
     GradArgs a{};
     if (e == hipSuccess && p.total_tokens > 0) {
@@ -1496,7 +1515,6 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         a.g = static_cast<const E*>(p.g);
         a.beta = static_cast<const E*>(p.beta);
         a.dO = static_cast<const E*>(p.dO);
-        a.dv = static_cast<const E*>(p.dv);
         a.Y = Y;
         a.U = U;
         a.dZ = dZ;
@@ -1516,9 +1534,9 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         a.dg = static_cast<E*>(p.dg);
         e = launch_grad(a, D, p.max_chunks, st);
     }
-    mark(6);
+    mark(5);
     if (e == hipSuccess && p.total_tokens > 0) e = launch_dbeta_sum(a, st);
-    mark(7);
+    mark(6);
     return e == hipSuccess ? hipGetLastError() : e;
 }
 

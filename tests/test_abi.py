@@ -197,10 +197,10 @@ def test_backward_workspace_and_rejections(lib):
     assert bw(ws_bytes=need - 1) == ERR_WORKSPACE
     # the forward's workspace is not enough for the backward
     assert bw(ws_bytes=kda.workspace_size(128, 1, 2, 64, 64, 64, kda.KDA_BF16)) == ERR_WORKSPACE
-    ms = (ctypes.c_float * 7)()
+    ms = (ctypes.c_float * 6)()
     assert lib.kda_chunk_bwd_profile(kda.KDA_F32, 128, 1, 2, 64, 64, 64, *([None] * 15), None, 0, None,
                                      ms) == ERR_UNSUPPORTED
-    assert kda.bwd_stage_names() == ["k_chunk_table", "k_prep", "k_recur_lds<ckpt>", "k_prep<bwd>",
+    assert kda.bwd_stage_names() == ["k_chunk_table", "k_prep<fwd+bwd>", "k_recur_lds<ckpt>",
                                      "k_recur_lds<bwd>", "k_grad", "k_dbeta_sum"]
 
 
