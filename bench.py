@@ -202,6 +202,37 @@ def backward_measure(torch, kda, inp, cu, spec, reps=5, profile_reps=3):
                                      cu_seqlens=cu, n_seqs=N, workspace=ws)
         for k_, v_ in d.items():
             stage_ms[k_] = stage_ms.get(k_, 0.0) + v_ / profile_reps
+    # the training pair: forward keeping a context, backward from it
+    ctx = torch.empty(kda.train_context_size(T, N, H, dk, dv, C), dtype=torch.uint8, device=dev)
+    fws = torch.empty(kda.workspace_size(T, N, H, dk, dv, C), dtype=torch.uint8, device=dev)
+    bws = torch.empty(kda._load().kda_chunk_bwd_ctx_workspace_size(T, N, H, dk, dv, C, kda.KDA_BF16),
+                      dtype=torch.uint8, device=dev)
+    o_t = torch.empty((T, H, dv), dtype=inp.q.dtype, device=dev)
+    ST_t = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+
+    def fwd_train():
+        kda.chunk_fwd_train(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, cu_seqlens=cu, n_seqs=N,
+                            context=ctx, o=o_t, S_T=ST_t, workspace=fws)
+
+    def bwd_ctx():
+        kda.chunk_bwd(inp.q, inp.k, inp.v, inp.beta, inp.g, dO, dS_T=dST, cu_seqlens=cu, n_seqs=N,
+                      workspace=bws, context=ctx)
+
+    fwd_train()
+    bwd_ctx()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    tf = tb = 0.0
+    for _ in range(reps):
+        ev[0].record(stream)
+        fwd_train()
+        ev[1].record(stream)
+        bwd_ctx()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        tf += ev[0].elapsed_time(ev[1]) / reps
+        tb += ev[1].elapsed_time(ev[2]) / reps
+    del ctx, fws, bws
     wkey = "%s_N%d_H%d_T%d_d%d" % (spec.dtype, N, H, T, dk)
     kb = grad_bytes_per_token_head(C, dk) * T * H
     roof = {"bound": "hbm", "kernel": "k_grad", "achieved": kb / (stage_ms["k_grad"] * 1e-3) / 1e9,
@@ -213,7 +244,10 @@ def backward_measure(torch, kda, inp, cu, spec, reps=5, profile_reps=3):
     return {"workload": "KDA chunked backward (dq, dk, dv, dbeta, dlog_alpha, dS0) of the same forward, "
                         "dO ~ N(0,1), dS_T ~ N(0,1); forward re-evaluated inside",
             "ms_per_pass": ms, "tokens_per_s": T / (ms * 1e-3), "vs_forward": None, "stage_ms": stage_ms,
-            "roofline": roof, "source_sha": source_sha(KERNEL_SOURCES["k_grad"])}
+            "roofline": roof, "source_sha": source_sha(KERNEL_SOURCES["k_grad"]),
+            "training_pair": {"fwd_train_ms": tf, "bwd_ctx_ms": tb, "step_ms": tf + tb,
+                              "note": "kda_chunk_fwd_train keeps the backward's inputs in a context; "
+                                      "kda_chunk_bwd_ctx does not evaluate the forward again"}}
 
 
 def epilogue_measure(torch, kda, o, reps=20):

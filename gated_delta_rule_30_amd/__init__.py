@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_profile", "chunk_bwd", "chunk_bwd_profile", "output_gate", "bwd_stage_names", "bwd_workspace_size", "recurrent_fwd", "validate_inputs", "chunk_transition",
+__all__ = ["chunk_fwd", "chunk_fwd_profile", "chunk_bwd", "chunk_bwd_profile", "chunk_fwd_train", "train_context_size", "output_gate", "bwd_stage_names", "bwd_workspace_size", "recurrent_fwd", "validate_inputs", "chunk_transition",
            "compose_states", "sequence_parallel_fwd", "stage_names", "workspace_size", "status_string", "lib_path",
            "KDA_F32", "KDA_BF16", "KdaError"]
 
@@ -72,6 +72,16 @@ def _load():
         lib.kda_profile_bwd_num_stages.restype = ctypes.c_int32
         lib.kda_profile_bwd_stage_name.argtypes = [ctypes.c_int32]
         lib.kda_profile_bwd_stage_name.restype = ctypes.c_char_p
+        lib.kda_chunk_train_context_size.argtypes = [I64, I32, I32, I32, I32, I32, ctypes.c_int]
+        lib.kda_chunk_train_context_size.restype = SZ
+        lib.kda_chunk_bwd_ctx_workspace_size.argtypes = [I64, I32, I32, I32, I32, I32, ctypes.c_int]
+        lib.kda_chunk_bwd_ctx_workspace_size.restype = SZ
+        lib.kda_chunk_fwd_train.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, I32,
+                                            P, P, P, P, P, P, P, P, P, P, SZ, P, SZ, P]
+        lib.kda_chunk_fwd_train.restype = ctypes.c_int
+        lib.kda_chunk_bwd_ctx.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, I32,
+                                          P, P, P, P, P, P, SZ, P, P, P, P, P, P, P, P, P, SZ, P]
+        lib.kda_chunk_bwd_ctx.restype = ctypes.c_int
         lib.kda_output_gate.argtypes = [ctypes.c_int, I64, I32, P, P, P, ctypes.c_float, P, P]
         lib.kda_output_gate.restype = ctypes.c_int
         _lib = lib
@@ -203,9 +213,49 @@ def chunk_bwd_profile(*args, **kw):
     return grads, dict(zip(bwd_stage_names(), [float(x) for x in ms]))
 
 
+def train_context_size(total_tokens: int, n_seqs: int, n_heads: int, d_k: int, d_v: int,
+                       chunk: int = CHUNK, dtype_code: int = KDA_BF16) -> int:
+    return int(_load().kda_chunk_train_context_size(int(total_tokens), int(n_seqs), int(n_heads), int(d_k),
+                                                    int(d_v), int(chunk), int(dtype_code)))
+
+
+def chunk_fwd_train(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = CHUNK, n_seqs=None,
+                    context=None, o=None, S_T=None, workspace=None):
+    """Forward for training (kda_chunk_fwd_train): chunk_fwd plus a context
+    (uint8 device tensor, allocated when None) that chunk_bwd(..., context=)
+    turns into the gradients without evaluating the forward again.  bfloat16,
+    3-D packed inputs.  Returns (o, S_T, context)."""
+    import torch
+    lib = _load()
+    dt, dev = _check_common(q, k, v, beta, log_alpha)
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else (n_seqs if n_seqs is not None else 1)
+    cb = int(lib.kda_chunk_train_context_size(T, N, H, dk, dv, chunk, dt))
+    wb = int(lib.kda_chunk_fwd_workspace_size(T, N, H, dk, dv, chunk, dt))
+    if cb == 0 or wb == 0:
+        raise KdaError(4, "KDA_ERR_UNSUPPORTED: sizes or dtype not supported by the training pair")
+    if context is None:
+        context = torch.empty(cb, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=dev)
+    if o is None:
+        o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
+    if S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    code = lib.kda_chunk_fwd_train(dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                   _ptr(log_alpha), _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T), _ptr(context),
+                                   context.numel(), _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+    if code != 0:
+        raise KdaError(code, lib.kda_status_string(code).decode())
+    return o, S_T, context
+
+
 def chunk_bwd(q, k, v, beta, log_alpha, dO, S0=None, dS_T=None, cu_seqlens=None, chunk: int = CHUNK,
-              n_seqs=None, workspace=None, _stage_ms=None):
-    """KDA chunkwise backward on the GPU (kda_chunk_bwd).
+              n_seqs=None, workspace=None, context=None, _stage_ms=None):
+    """KDA chunkwise backward on the GPU (kda_chunk_bwd, or kda_chunk_bwd_ctx
+    when `context` comes from chunk_fwd_train on the same inputs).
 
     Inputs as for chunk_fwd (bfloat16, 3-D packed [T, H, d] or 4-D [B, T, H, d]);
     dO shaped like v; dS_T [N, H, d_k, d_v] float32 or None.  Returns a dict
@@ -237,7 +287,8 @@ def chunk_bwd(q, k, v, beta, log_alpha, dO, S0=None, dS_T=None, cu_seqlens=None,
         if t is not None and (t.dtype != torch.float32 or t.shape != (N, H, dk, dv) or t.device != dev
                               or not t.is_contiguous()):
             raise ValueError("%s must be contiguous float32 [%d, %d, %d, %d] on %s" % (name, N, H, dk, dv, dev))
-    ws_bytes = int(lib.kda_chunk_bwd_workspace_size(T, N, H, dk, dv, chunk, dt))
+    size_fn = lib.kda_chunk_bwd_workspace_size if context is None else lib.kda_chunk_bwd_ctx_workspace_size
+    ws_bytes = int(size_fn(T, N, H, dk, dv, chunk, dt))
     if ws_bytes == 0:
         code = lib.kda_chunk_bwd(dt, T, N, H, dk, dv, chunk, *([None] * 15), 0, None)
         raise KdaError(code, lib.kda_status_string(code).decode())
@@ -251,7 +302,16 @@ def chunk_bwd(q, k, v, beta, log_alpha, dO, S0=None, dS_T=None, cu_seqlens=None,
             _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
             _ptr(out["dbeta"]), _ptr(out["dg"]), _ptr(out["dS0"]), _ptr(workspace),
             workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
-    code = lib.kda_chunk_bwd(*args) if _stage_ms is None else lib.kda_chunk_bwd_profile(*args, _stage_ms)
+    if context is not None:
+        if _stage_ms is not None:
+            raise ValueError("the context form has no per-kernel measurement entry point")
+        code = lib.kda_chunk_bwd_ctx(dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(beta), _ptr(log_alpha),
+                                     _ptr(cu_seqlens), _ptr(context), context.numel(), _ptr(dO), _ptr(dS_T),
+                                     _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
+                                     _ptr(out["dg"]), _ptr(out["dS0"]), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    else:
+        code = lib.kda_chunk_bwd(*args) if _stage_ms is None else lib.kda_chunk_bwd_profile(*args, _stage_ms)
     if code != 0:
         raise KdaError(code, lib.kda_status_string(code).decode())
     if batched:

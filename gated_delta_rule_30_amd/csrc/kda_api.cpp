@@ -17,6 +17,8 @@ size_t carve_workspace(Plan* p, void* base) {
     const size_t es = p->bf16 ? 2 : 4;
     const size_t H = (size_t)p->n_heads, D = (size_t)p->d;
     const size_t mc = (size_t)p->max_chunks;
+    const size_t T = (size_t)p->total_tokens;
+    const int kind = p->ws_kind;
     size_t off = 0;
     auto take = [&](size_t bytes) {
         size_t at = off;
@@ -26,14 +28,15 @@ size_t carve_workspace(Plan* p, void* base) {
     p->ws_n_chunks = (int32_t*)take(sizeof(int32_t));
     p->ws_seq_chunk0 = (int32_t*)take(sizeof(int32_t) * ((size_t)p->n_seqs + 1));
     p->ws_tab = (ChunkInfo*)take(sizeof(ChunkInfo) * mc);
-    p->ws_TB = take(es * mc * H * kChunkTokens * kChunkTokens);
-    p->ws_M = take(es * mc * H * kChunkTokens * kChunkTokens);
-    p->ws_Qg = take(es * mc * H * kChunkTokens * D);
-    p->ws_Kg = take(es * mc * H * kChunkTokens * D);
-    p->ws_KhT = take(es * mc * H * D * kChunkTokens);
-    p->ws_gam = (float*)take(4 * mc * H * D);
-    if (p->bwd) {
-        const size_t T = (size_t)p->total_tokens;
+    if (kind != kWsBwdCtx) {   // the forward operand set
+        p->ws_TB = take(es * mc * H * kChunkTokens * kChunkTokens);
+        p->ws_M = take(es * mc * H * kChunkTokens * kChunkTokens);
+        p->ws_Qg = take(es * mc * H * kChunkTokens * D);
+        p->ws_Kg = take(es * mc * H * kChunkTokens * D);
+        p->ws_KhT = take(es * mc * H * D * kChunkTokens);
+    }
+    if (kind == kWsFwd || kind == kWsBwd) p->ws_gam = (float*)take(4 * mc * H * D);
+    if (kind == kWsBwd) {
         p->ws_bet = (float*)take(4 * mc * H * kChunkTokens);
         p->ws_bTT = take(es * mc * H * kChunkTokens * kChunkTokens);
         p->ws_bMT = take(es * mc * H * kChunkTokens * kChunkTokens);
@@ -41,12 +44,38 @@ size_t carve_workspace(Plan* p, void* base) {
         p->ws_bQgT = take(es * mc * H * D * kChunkTokens);
         p->ws_bKgT = take(es * mc * H * D * kChunkTokens);
         p->ws_ckS = take(2 * mc * H * D * D);
-        p->ws_ckdS = take(2 * mc * H * D * D);
         p->ws_Y = take(2 * T * H * D);
         p->ws_U = take(2 * T * H * D);
+    }
+    if (kind == kWsBwd || kind == kWsBwdCtx) {
+        p->ws_ckdS = take(2 * mc * H * D * D);
         p->ws_dZ = take(2 * T * H * D);
         p->ws_dbp = (float*)take(4 * 2 * T * H);
     }
+    return off;
+}
+
+size_t carve_context(Plan* p, void* base) {
+    const size_t es = 2;
+    const size_t H = (size_t)p->n_heads, D = (size_t)p->d;
+    const size_t mc = (size_t)p->max_chunks;
+    const size_t T = (size_t)p->total_tokens;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes);
+        return base ? (void*)((char*)base + at) : nullptr;
+    };
+    p->ws_gam = (float*)take(4 * mc * H * D);
+    p->ws_bet = (float*)take(4 * mc * H * kChunkTokens);
+    p->ws_bTT = take(es * mc * H * kChunkTokens * kChunkTokens);
+    p->ws_bMT = take(es * mc * H * kChunkTokens * kChunkTokens);
+    p->ws_bKh = take(es * mc * H * kChunkTokens * D);
+    p->ws_bQgT = take(es * mc * H * D * kChunkTokens);
+    p->ws_bKgT = take(es * mc * H * D * kChunkTokens);
+    p->ws_ckS = take(2 * mc * H * D * D);
+    p->ws_Y = take(2 * T * H * D);
+    p->ws_U = take(2 * T * H * D);
     return off;
 }
 
@@ -228,7 +257,7 @@ size_t kda_chunk_bwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_
     Plan p{};
     if (plan_sizes(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, true) != KDA_OK) return 0;
     if (p.max_chunks >= (1 << 30)) return 0;
-    p.bwd = true;
+    p.ws_kind = kda::kWsBwd;
     return kda::carve_workspace(&p, nullptr);
 }
 
@@ -236,12 +265,13 @@ static kda_status prepare_bwd(Plan* p, kda_dtype dt, int64_t total_tokens, int32
                               int32_t d_k, int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
                               const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
                               const void* dO, const float* dS_T, void* dq, void* dk, void* dv, void* dbeta,
-                              void* dlog_alpha, float* dS0, void* workspace, size_t workspace_bytes) {
+                              void* dlog_alpha, float* dS0, void* workspace, size_t workspace_bytes,
+                              int ws_kind = kda::kWsBwd) {
     if (dt == KDA_F32) return KDA_ERR_UNSUPPORTED;
     kda_status s = plan_sizes(p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, cu_seqlens != nullptr);
     if (s != KDA_OK) return s;
     if (p->max_chunks >= (1 << 30)) return KDA_ERR_UNSUPPORTED;   // two gradient workgroups per chunk
-    p->bwd = true;
+    p->ws_kind = ws_kind;
     if (total_tokens > 0 && (!q || !k || !v || !beta || !log_alpha || !dO || !dq || !dk || !dv || !dbeta ||
                              !dlog_alpha))
         return KDA_ERR_NULL;
@@ -281,6 +311,72 @@ kda_status kda_chunk_bwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int
                                workspace_bytes);
     if (s != KDA_OK) return s;
     hipError_t e = kda::launch_bwd(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+size_t kda_chunk_train_context_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                                    int32_t d_v, int32_t chunk, kda_dtype dt) {
+    if (dt != KDA_BF16) return 0;
+    Plan p{};
+    if (plan_sizes(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, true) != KDA_OK) return 0;
+    if (p.max_chunks >= (1 << 30)) return 0;
+    return kda::carve_context(&p, nullptr);
+}
+
+size_t kda_chunk_bwd_ctx_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                                        int32_t d_v, int32_t chunk, kda_dtype dt) {
+    if (dt != KDA_BF16) return 0;
+    Plan p{};
+    if (plan_sizes(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, true) != KDA_OK) return 0;
+    if (p.max_chunks >= (1 << 30)) return 0;
+    p.ws_kind = kda::kWsBwdCtx;
+    return kda::carve_workspace(&p, nullptr);
+}
+
+// the context buffer: present, aligned and large enough; carves its regions
+static kda_status take_context(Plan* p, void* context, size_t context_bytes) {
+    if (!context || (uintptr_t)context % kda::kAlign != 0) return KDA_ERR_WORKSPACE;
+    Plan sz = *p;
+    if (context_bytes < kda::carve_context(&sz, nullptr)) return KDA_ERR_WORKSPACE;
+    kda::carve_context(p, context);
+    return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_train(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                               int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
+                               const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
+                               void* o, float* S_T, void* context, size_t context_bytes, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    if (dt == KDA_F32) return KDA_ERR_UNSUPPORTED;
+    Plan p{};
+    kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
+                           cu_seqlens, o, S_T, workspace, workspace_bytes);
+    if (s != KDA_OK) return s;
+    if (p.max_chunks >= (1 << 30)) return KDA_ERR_UNSUPPORTED;
+    p.ws_kind = kda::kWsFwdTrain;
+    kda::carve_workspace(&p, workspace);
+    s = take_context(&p, context, context_bytes);
+    if (s != KDA_OK) return s;
+    hipError_t e = kda::launch_fwd_train(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunk_bwd_ctx(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                             int32_t d_v, int32_t chunk, const void* q, const void* k, const void* beta,
+                             const void* log_alpha, const int32_t* cu_seqlens, const void* context,
+                             size_t context_bytes, const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
+                             void* dbeta, void* dlog_alpha, float* dS0, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (dt == KDA_F32) return KDA_ERR_UNSUPPORTED;
+    Plan p{};
+    // v and S0 are not read: the context holds what they contributed (k stands in, sizes only)
+    kda_status s = prepare_bwd(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, k, beta, log_alpha,
+                               nullptr, cu_seqlens, dO, dS_T, dq, dk, dv, dbeta, dlog_alpha, dS0, workspace,
+                               workspace_bytes, kda::kWsBwdCtx);
+    if (s != KDA_OK) return s;
+    s = take_context(&p, const_cast<void*>(context), context_bytes);
+    if (s != KDA_OK) return s;
+    hipError_t e = kda::launch_bwd_ctx(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -36,8 +36,12 @@ struct Plan {
     void* ws_Kg;              // [H, max_chunks, 64, D] K . Gamma
     void* ws_KhT;             // [H, max_chunks, D, 64] (K . exp(b_L - b))^T
     float* ws_gam;            // [H, max_chunks, D] exp(b_L), fp32
-    // backward pass (kda_chunk_bwd); workspace regions carved when `bwd` is set
-    bool bwd;
+    // What the workspace holds (carve_workspace) -- kWsFwd: the forward pass;
+    // kWsBwd: the backward with the forward evaluated again inside;
+    // kWsFwdTrain / kWsBwdCtx: the training pair, whose shared regions (Gamma_L,
+    // beta, the backward operand set, S per chunk, Y, U~) live in a separate
+    // context buffer (carve_context).
+    int ws_kind;
     const void* dO;           // [T, H, D] output gradients
     const float* dS_T;        // [N, H, D, D] final-state gradients or NULL
     void *dq, *dk, *dv, *dbeta, *dg;
@@ -71,9 +75,13 @@ struct GradArgs {
 hipError_t launch_grad(const GradArgs& a, int d, int32_t max_chunks, hipStream_t stream);
 hipError_t launch_dbeta_sum(const GradArgs& a, hipStream_t stream);
 
-// Byte offsets of every workspace region for the given sizes; returns the
-// total size.  `base` may be NULL (size query only).
+enum { kWsFwd = 0, kWsBwd = 1, kWsFwdTrain = 2, kWsBwdCtx = 3 };
+
+// Byte offsets of every workspace region for the given sizes and p->ws_kind;
+// returns the total size.  `base` may be NULL (size query only).
 size_t carve_workspace(Plan* p, void* base);
+// The same for the training pair's context buffer.
+size_t carve_context(Plan* p, void* base);
 
 // Kernel launches of one forward pass, in order.
 constexpr int kNumStages = 3;
@@ -88,6 +96,11 @@ hipError_t launch(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
 constexpr int kNumBwdStages = 6;
 extern const char* const kBwdStageNames[kNumBwdStages];
 hipError_t launch_bwd(const Plan& p, hipStream_t stream, hipEvent_t* ev = nullptr);
+
+// Training pair (bf16): the forward keeping the backward's inputs in the
+// context regions, and the backward from them.
+hipError_t launch_fwd_train(const Plan& p, hipStream_t stream);
+hipError_t launch_bwd_ctx(const Plan& p, hipStream_t stream);
 
 // The forward pass with v = 0 from S0 = I and no output (bf16 only): S_T
 // receives each sequence's transition matrix (kda_chunk_transition).

@@ -930,10 +930,10 @@ struct LdsGeo {
 //          Diag(alpha_t) (orkas.ai "Kimi K3 architecture", §"請求書はサービング側に回ってくる":
 //          a segment's final state is its transition applied to the incoming
 //          state plus its zero-start state).  v, S0 and o are not accessed.
-//   kCkpt  the forward steps without o, keeping what the backward pass needs:
-//          the state entering every chunk (aux.ck, bf16 [slot][D][D]), and the
+//   kCkpt  the forward steps keeping what the backward pass needs: the state
+//          entering every chunk (aux.ck, bf16 [slot][D][D]), and the
 //          per-token Y = V - (K . Gamma) S and U~ (aux.y, aux.u, bf16, laid out
-//          as v).
+//          as v); o and S_T as kFwd when given (o may be NULL).
 //   kBwd   the state-gradient recurrence, chunks last to first, on the
 //          backward operand set (see ChunkOps).  With dS' the gradient of a
 //          chunk's outgoing state and dO its output gradients:
@@ -1282,7 +1282,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         // S^T is last read before the Y barrier of this step; the barrier at
         // the top of the next step publishes the new one.
         put_state();
-        if constexpr (kMode == kFwd) {
+        if (kMode == kFwd || (kMode == kCkpt && o)) {
             E* oj = o + o_off + (int64_t)j * C * rs;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1487,26 +1487,10 @@ hipError_t launch_transition(const Plan& p, hipStream_t st) {
 const char* const kBwdStageNames[kNumBwdStages] = {"k_chunk_table", "k_prep<fwd+bwd>", "k_recur_lds<ckpt>",
                                                    "k_recur_lds<bwd>", "k_grad", "k_dbeta_sum"};
 
+// The chunk-parallel gradient kernels from the kept forward quantities.
 template <int D>
-static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
+static hipError_t launch_grads(const Plan& p, hipStream_t st, hipEvent_t ev_mid) {
     using E = __bf16;
-    auto mark = [&](int i) {
-        if (ev) (void)hipEventRecord(ev[i], st);
-    };
-    auto* ckS = static_cast<E*>(p.ws_ckS);
-    auto* ckdS = static_cast<E*>(p.ws_ckdS);
-    auto* Y = static_cast<E*>(p.ws_Y);
-    auto* U = static_cast<E*>(p.ws_U);
-    auto* dZ = static_cast<E*>(p.ws_dZ);
-    mark(0);
-    launch_table(p, st);
-    mark(1);
-    launch_prep<E, D, true>(p, static_cast<const E*>(p.q), st);
-    mark(2);
-    launch_recur_lds<D, kCkpt>(p, p.v, p.S0, nullptr, nullptr, RecurAux{ckS, Y, U, nullptr}, st);
-    mark(3);
-    launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, p.dv, RecurAux{ckdS, dZ, nullptr, p.ws_bet}, st);
-    mark(4);
     hipError_t e = hipGetLastError();
     GradArgs a{};
     if (e == hipSuccess && p.total_tokens > 0) {
@@ -1515,11 +1499,11 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         a.g = static_cast<const E*>(p.g);
         a.beta = static_cast<const E*>(p.beta);
         a.dO = static_cast<const E*>(p.dO);
-        a.Y = Y;
-        a.U = U;
-        a.dZ = dZ;
-        a.ckS = ckS;
-        a.ckdS = ckdS;
+        a.Y = static_cast<const E*>(p.ws_Y);
+        a.U = static_cast<const E*>(p.ws_U);
+        a.dZ = static_cast<const E*>(p.ws_dZ);
+        a.ckS = static_cast<const E*>(p.ws_ckS);
+        a.ckdS = static_cast<const E*>(p.ws_ckdS);
         a.tab = p.ws_tab;
         a.n_chunks = p.ws_n_chunks;
         a.fixed_len = p.cu_seqlens ? (int64_t)0 : p.fixed_len;
@@ -1534,10 +1518,64 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         a.dg = static_cast<E*>(p.dg);
         e = launch_grad(a, D, p.max_chunks, st);
     }
-    mark(5);
+    if (ev_mid) (void)hipEventRecord(ev_mid, st);
     if (e == hipSuccess && p.total_tokens > 0) e = launch_dbeta_sum(a, st);
-    mark(6);
     return e == hipSuccess ? hipGetLastError() : e;
+}
+
+template <int D>
+static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
+    using E = __bf16;
+    auto mark = [&](int i) {
+        if (ev) (void)hipEventRecord(ev[i], st);
+    };
+    mark(0);
+    launch_table(p, st);
+    mark(1);
+    launch_prep<E, D, true>(p, static_cast<const E*>(p.q), st);
+    mark(2);
+    launch_recur_lds<D, kCkpt>(p, p.v, p.S0, nullptr, nullptr,
+                               RecurAux{static_cast<E*>(p.ws_ckS), static_cast<E*>(p.ws_Y),
+                                        static_cast<E*>(p.ws_U), nullptr}, st);
+    mark(3);
+    launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, p.dv,
+                              RecurAux{static_cast<E*>(p.ws_ckdS), static_cast<E*>(p.ws_dZ), nullptr, p.ws_bet}, st);
+    mark(4);
+    const hipError_t e = launch_grads<D>(p, st, ev ? ev[5] : nullptr);
+    mark(6);
+    return e;
+}
+
+// Training pair: the forward that keeps the backward's inputs in a context
+// buffer, and the backward from that context.
+template <int D>
+static hipError_t launch_fwd_train_d(const Plan& p, hipStream_t st) {
+    using E = __bf16;
+    launch_table(p, st);
+    launch_prep<E, D, true>(p, static_cast<const E*>(p.q), st);
+    launch_recur_lds<D, kCkpt>(p, p.v, p.S0, p.S_T, p.o,
+                               RecurAux{static_cast<E*>(p.ws_ckS), static_cast<E*>(p.ws_Y),
+                                        static_cast<E*>(p.ws_U), nullptr}, st);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_bwd_ctx_d(const Plan& p, hipStream_t st) {
+    using E = __bf16;
+    launch_table(p, st);
+    launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, p.dv,
+                              RecurAux{static_cast<E*>(p.ws_ckdS), static_cast<E*>(p.ws_dZ), nullptr, p.ws_bet}, st);
+    return launch_grads<D>(p, st, nullptr);
+}
+
+hipError_t launch_fwd_train(const Plan& p, hipStream_t st) {
+    if (p.d == 128) return launch_fwd_train_d<128>(p, st);
+    return launch_fwd_train_d<64>(p, st);
+}
+
+hipError_t launch_bwd_ctx(const Plan& p, hipStream_t st) {
+    if (p.d == 128) return launch_bwd_ctx_d<128>(p, st);
+    return launch_bwd_ctx_d<64>(p, st);
 }
 
 hipError_t launch_bwd(const Plan& p, hipStream_t st, hipEvent_t* ev) {

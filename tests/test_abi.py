@@ -227,3 +227,37 @@ def test_output_gate_rejects_bad_arguments(lib):
     assert og(y=None) == ERR_NULL
     assert og(w=fake + 4) == ERR_SHAPE
     assert og(n=0, o=None, z=None, y=None) == OK      # nothing to do, nothing launched
+
+
+def test_training_pair_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    fake = 0x7f0000000000
+    assert kda.train_context_size(65536, 1, 32, 128, 128) > 0
+    assert kda.train_context_size(256, 1, 2, 64, 64, 64, kda.KDA_F32) == 0
+    assert lib.kda_chunk_bwd_ctx_workspace_size(256, 1, 2, 64, 64, 64, kda.KDA_BF16) > 0
+    need_ws = kda.workspace_size(128, 1, 2, 64, 64, 64, kda.KDA_BF16)
+    need_ctx = kda.train_context_size(128, 1, 2, 64, 64)
+
+    def ft(dt=kda.KDA_BF16, ctx=0x200000, ctx_bytes=None, ws_bytes=None, o=fake):
+        return lib.kda_chunk_fwd_train(dt, 128, 1, 2, 64, 64, 64, P(fake), P(fake), P(fake), P(fake), P(fake), None,
+                                       None, P(o), None, P(ctx), need_ctx if ctx_bytes is None else ctx_bytes,
+                                       P(0x100000), need_ws if ws_bytes is None else ws_bytes, None)
+    assert ft(dt=kda.KDA_F32) == ERR_UNSUPPORTED
+    assert ft(o=None) == ERR_NULL
+    assert ft(ctx=None) == ERR_WORKSPACE
+    assert ft(ctx=0x200010) == ERR_WORKSPACE
+    assert ft(ctx_bytes=need_ctx - 1) == ERR_WORKSPACE
+    assert ft(ws_bytes=need_ws - 1) == ERR_WORKSPACE
+
+    need_bws = lib.kda_chunk_bwd_ctx_workspace_size(128, 1, 2, 64, 64, 64, kda.KDA_BF16)
+
+    def bc(dt=kda.KDA_BF16, ctx=0x200000, ctx_bytes=None, ws_bytes=None, dO=fake):
+        return lib.kda_chunk_bwd_ctx(dt, 128, 1, 2, 64, 64, 64, P(fake), P(fake), P(fake), P(fake), None, P(ctx),
+                                     need_ctx if ctx_bytes is None else ctx_bytes, P(dO), None, P(fake), P(fake),
+                                     P(fake), P(fake), P(fake), None, P(0x100000),
+                                     need_bws if ws_bytes is None else ws_bytes, None)
+    assert bc(dt=kda.KDA_F32) == ERR_UNSUPPORTED
+    assert bc(dO=None) == ERR_NULL
+    assert bc(ctx=None) == ERR_WORKSPACE
+    assert bc(ctx_bytes=16) == ERR_WORKSPACE
+    assert bc(ws_bytes=need_bws - 1) == ERR_WORKSPACE

@@ -158,3 +158,29 @@ def test_backward_headline_sampled(torch_dev):
          "  (oracle %.1fs)" % (time.time() - t0))
     for key in KEYS:
         assert e[key] <= TOL, "%s parity %.3e > %.0e" % (key, e[key], TOL)
+
+
+@pytest.mark.parametrize("lengths,H,d,varlen", [((100, 37, 1, 64, 200), 2, 64, True), ((4096,) * 2, 4, 128, False)],
+                         ids=["varlen-d64", "equal-d128"])
+def test_training_pair_matches_recompute(torch_dev, lengths, H, d, varlen):
+    """kda_chunk_fwd_train + kda_chunk_bwd_ctx give kda_chunk_fwd's o and S_T
+    and kda_chunk_bwd's gradients bit for bit (same kernels, same inputs)."""
+    torch, dev = torch_dev
+    import gated_delta_rule_30_amd as kda
+    spec = ki.Spec("pair", "bf16", tuple(lengths), H, d, d, s0_std=0.02, varlen=varlen, seed=3)
+    inp = ki.generate_numpy(spec)
+    dO, dS_T = ki.generate_grads_numpy(spec)
+    q, k, v, beta, g, dOd = (_bf(torch, dev, a) for a in (inp.q, inp.k, inp.v, inp.beta, inp.g, dO))
+    S0 = torch.from_numpy(inp.S0).to(dev)
+    dST = torch.from_numpy(dS_T).to(dev)
+    cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev) if varlen else None
+    N = spec.n_seqs
+    o_ref, ST_ref = kda.chunk_fwd(q, k, v, beta, g, S0=S0, cu_seqlens=cu, n_seqs=N)
+    ref = kda.chunk_bwd(q, k, v, beta, g, dOd, S0=S0, dS_T=dST, cu_seqlens=cu, n_seqs=N)
+    o, ST, ctx = kda.chunk_fwd_train(q, k, v, beta, g, S0=S0, cu_seqlens=cu, n_seqs=N)
+    got = kda.chunk_bwd(q, k, v, beta, g, dOd, dS_T=dST, cu_seqlens=cu, n_seqs=N, context=ctx)
+    torch.cuda.synchronize()
+    _say("training pair %s H=%d d=%d" % (lengths, H, d))
+    assert torch.equal(o, o_ref) and torch.equal(ST, ST_ref)
+    for key in KEYS:
+        assert torch.equal(got[key], ref[key]), key
