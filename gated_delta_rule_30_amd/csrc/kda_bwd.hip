@@ -44,7 +44,8 @@
 // channels 16n + 4lg + r (n among the half's tiles, r < 4) of every result:
 // the decay cumulative sum over tokens is a 16-lane row scan, and all
 // per-element terms combine in registers.  The two halves' shares of dbeta
-// meet in a float32 workspace; k_dbeta_sum adds them.
+// meet in a float32 workspace; k_dbeta_sum adds them.  The results leave
+// through LDS as whole 16-byte vectors per token row.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -74,11 +75,13 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
     constexpr int KV = D / M::KS;     // k-steps of a contraction over value columns
     constexpr int PSd = D + 8;        // pitch of the staged U~ rows (elements)
     constexpr int PT = C + 8;         // pitch of token-indexed rows
-    constexpr int kXs = 2 * HALF * D, kXu = C * PSd, kXg = 3 * HALF * PT;
-    constexpr int kX = kXs > kXu ? (kXs > kXg ? kXs : kXg) : (kXu > kXg ? kXu : kXg);
+    constexpr int PO = HALF + 8;      // pitch of the output staging rows
+    constexpr int kXs = 2 * HALF * D, kXu = C * PSd, kXg = 3 * HALF * PT, kXo = 3 * C * PO;
+    constexpr int kX01 = kXs > kXu ? kXs : kXu, kX23 = kXg > kXo ? kXg : kXo;
+    constexpr int kX = kX01 > kX23 ? kX01 : kX23;
     // Region X: the half's rows of S and dS' (state_swz layout, copied as
     // stored); then U~ ([token][value column]); then the Gram operands
-    // ([channel][token]).
+    // ([channel][token]); last the outputs ([token][channel]).
     __shared__ __attribute__((aligned(16))) E sX[kX];
     __shared__ __attribute__((aligned(16))) E sdA[C * PT];     // dA      [r][i]
     __shared__ __attribute__((aligned(16))) E sdGq[C * PT];    // dGq     [r][i]
@@ -383,8 +386,12 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
             rv[x] = row_rscan16(db[x]);
             if (li == 0) sRev[w * HALF + c] = rv[x];
         }
-    __syncthreads();
-    if (!ok) return;
+    __syncthreads();   // also: every wave is past the Gram products, so region X is free
+    // dq, dk, dlog_alpha of the half go through region X ([token][channel],
+    // pitch PO) so that each token's 64 channels leave as whole 16-byte vectors
+    E* sOq = sX;
+    E* sOk = sX + C * PO;
+    E* sOg = sX + 2 * C * PO;
 #pragma unroll
     for (int i = 0; i < NTH; ++i) {
         bf16x4 oq, ok4, og;
@@ -397,18 +404,32 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
             ok4[r] = (E)dk[x];
             og[r] = (E)dgv;
         }
-        const int64_t at = row + c0 + lch(i, 0);
-        *reinterpret_cast<bf16x4*>(a.dq + at) = oq;
-        *reinterpret_cast<bf16x4*>(a.dk + at) = ok4;
-        *reinterpret_cast<bf16x4*>(a.dg + at) = og;
+        *reinterpret_cast<bf16x4*>(&sOq[t * PO + lch(i, 0)]) = oq;
+        *reinterpret_cast<bf16x4*>(&sOk[t * PO + lch(i, 0)]) = ok4;
+        *reinterpret_cast<bf16x4*>(&sOg[t * PO + lch(i, 0)]) = og;
     }
-    if (lg == 0) a.dbp[((int64_t)hh * a.total_tokens + info.tok0 + t) * H + h] = dbeta;
+    if (lg == 0 && ok) a.dbp[((int64_t)hh * H + h) * a.total_tokens + info.tok0 + t] = dbeta;   // [2][H][T]
+    __syncthreads();
+    {
+        constexpr int VR = HALF / 8;   // 16-byte vectors per token row of the half
+        for (int vi = tid; vi < 3 * C * VR; vi += kGradThreads) {
+            const int m = vi / (C * VR), tt = (vi / VR) % C, v = vi % VR;
+            if (tt >= len) continue;
+            const E* src = (m == 0 ? sOq : m == 1 ? sOk : sOg) + tt * PO + 8 * v;
+            E* dst = (m == 0 ? a.dq : m == 1 ? a.dk : a.dg) + (info.tok0 + tt) * rs + (int64_t)h * D + c0 + 8 * v;
+            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+        }
+    }
 }
 
-// dbeta = the two halves' float32 shares, rounded once to bf16
-__global__ __launch_bounds__(256) void k_dbeta_sum(const float* __restrict__ dbp, int64_t n, __bf16* __restrict__ dbeta) {
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-        dbeta[i] = (__bf16)(dbp[i] + dbp[n + i]);
+// dbeta[t][h] = the two halves' float32 shares ([2][H][T]), rounded once to bf16
+__global__ __launch_bounds__(256) void k_dbeta_sum(const float* __restrict__ dbp, int64_t T, int32_t H,
+                                                   __bf16* __restrict__ dbeta) {
+    const int64_t n = T * H;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+        const int64_t h = i / T, t = i % T;   // i runs over the shares' layout, so their reads coalesce
+        dbeta[t * H + h] = (__bf16)(dbp[i] + dbp[n + i]);
+    }
 }
 
 hipError_t launch_grad(const GradArgs& a, int d, int32_t max_chunks, hipStream_t st) {
@@ -426,7 +447,8 @@ hipError_t launch_grad(const GradArgs& a, int d, int32_t max_chunks, hipStream_t
 hipError_t launch_dbeta_sum(const GradArgs& a, hipStream_t st) {
     const int64_t n = a.total_tokens * a.H;
     const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
-    if (n > 0) hipLaunchKernelGGL(k_dbeta_sum, dim3((unsigned)blocks), dim3(256), 0, st, a.dbp, n, a.dbeta);
+    if (n > 0) hipLaunchKernelGGL(k_dbeta_sum, dim3((unsigned)blocks), dim3(256), 0, st, a.dbp, a.total_tokens, a.H,
+                                  a.dbeta);
     return hipGetLastError();
 }
 

@@ -56,7 +56,7 @@ struct Plan {
     void* ws_ckS;             // [H, max_chunks, D, D] state entering each chunk (bf16)
     void* ws_ckdS;            // [H, max_chunks, D, D] gradient of each chunk's outgoing state (bf16)
     void *ws_Y, *ws_U, *ws_dZ;   // [T, H, D] bf16: Y, U~ and dZ per token
-    float* ws_dbp;            // [2, T, H] float32 dbeta shares of the two channel halves
+    float* ws_dbp;            // [2, H, T] float32 dbeta shares of the two channel halves
 };
 
 // Arguments of the per-chunk gradient kernel (kda_bwd.hip); bf16 tensors.
@@ -70,7 +70,7 @@ struct GradArgs {
     int64_t max_chunks;
     int64_t total_tokens;
     __bf16 *dq, *dk, *dbeta, *dg;
-    float* dbp;               // [2, total_tokens, H] the halves' dbeta shares
+    float* dbp;               // [2, H, total_tokens] the halves' dbeta shares
 };
 hipError_t launch_grad(const GradArgs& a, int d, int32_t max_chunks, hipStream_t stream);
 hipError_t launch_dbeta_sum(const GradArgs& a, hipStream_t stream);
