@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     __shared__ float sERho[kNSub * D];        // exp(rho_R)
     __shared__ float sCarry[(kNSub + 1) * D]; // rho_0 .. rho_3, b_L
     __shared__ __attribute__((aligned(16))) E sM[C * PM];
-    __shared__ float sBeta[C];
+    __shared__ __attribute__((aligned(16))) float sBeta[C];
     __shared__ __attribute__((aligned(16))) E sQt[kBwd ? D * PK : 8];   // (Q . Gamma)^T staging (kBwd)
     static_assert(!kBwd || sizeof(E) == 2, "backward operands: bf16 only");
     float* sA = sR1;
@@ -389,17 +389,24 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     }
     __syncthreads();
     // channel rows over the chunk's tokens, fragment-major, from a staged
-    // [channel][token] tile
+    // [channel][token] tile.  With bf16 a lane's 8 tokens of one k-step are
+    // consecutive (the rotation moves whole groups of 16), so each vector is
+    // one 16-byte LDS read; eight lanes of consecutive channels then cover
+    // all banks once (row pitch 144 bytes).
     auto store_transposed = [&](const E* st, void* dst) {
         uint4* out = reinterpret_cast<uint4*>(static_cast<E*>(dst) + cbase * D * C);
         for (int vi = tid; vi < D * C / EPV; vi += kThreads) {
             const int ln = vi % 64, v = (vi / 64) % G::NVT, ct = vi / (64 * G::NVT);
             const int r = kSub * ct + (ln & 15), lgp = ln >> 4;
-            uint4 pk;
-            E* pe = reinterpret_cast<E*>(&pk);
+            if constexpr (M::KW == EPV) {
+                out[vi] = *reinterpret_cast<const uint4*>(st + kt_at(r, G::tok_of(v * EPV, lgp)));
+            } else {
+                uint4 pk;
+                E* pe = reinterpret_cast<E*>(&pk);
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) pe[e] = st[kt_at(r, G::tok_of(v * EPV + e, lgp))];
-            out[vi] = pk;
+                for (int e = 0; e < EPV; ++e) pe[e] = st[kt_at(r, G::tok_of(v * EPV + e, lgp))];
+                out[vi] = pk;
+            }
         }
     };
     store_transposed(sKt, ops.KhT);                     // (K . exp(b_L - b))^T
@@ -510,12 +517,30 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
         E* em = reinterpret_cast<E*>(&pm);
         E* ett = reinterpret_cast<E*>(&ptt);
         E* emt = reinterpret_cast<E*>(&pmt);
+        if constexpr (M::KW == EPV) {
+            // bf16: the vector's 8 tokens are consecutive and in one 16-token
+            // block, so T, beta and M come as whole 16-byte LDS reads
+            const int t0 = G::tok_of(v * EPV, lgp);
+            const bool upper = (t0 >> 4) > (r >> 4);            // blocks above the diagonal are zero
+            const int tc = upper ? ((r >> 4) << 4) | (t0 & 15) : t0;   // an address inside the stored blocks
+            const f32x4* tp = reinterpret_cast<const f32x4*>(sT + tri(r, tc));
+            const f32x4* bp = reinterpret_cast<const f32x4*>(sBeta + t0);
+            const f32x4 t_lo = tp[0], t_hi = tp[1], b_lo = bp[0], b_hi = bp[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                et[e] = from_f<E>(upper ? 0.f : t_lo[e] * b_lo[e]);
+                et[e + 4] = from_f<E>(upper ? 0.f : t_hi[e] * b_hi[e]);
+            }
+            pm = upper ? uint4{0u, 0u, 0u, 0u} : *reinterpret_cast<const uint4*>(sM + r * PM + tc);
+        }
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
             const int t = G::tok_of(v * EPV + e, lgp);
-            const bool upper = (t >> 4) > (r >> 4);   // blocks above the diagonal are zero
-            et[e] = from_f<E>(upper ? 0.f : sT[tri(r, upper ? r : t)] * sBeta[t]);
-            em[e] = upper ? from_f<E>(0.f) : sM[r * PM + t];
+            if constexpr (M::KW != EPV) {
+                const bool upper = (t >> 4) > (r >> 4);   // blocks above the diagonal are zero
+                et[e] = from_f<E>(upper ? 0.f : sT[tri(r, upper ? r : t)] * sBeta[t]);
+                em[e] = upper ? from_f<E>(0.f) : sM[r * PM + t];
+            }
             if constexpr (kBwd) {
                 // element (r, t) of a transpose is (t, r): zero unless t's block >= r's
                 const bool zero = (t >> 4) < (r >> 4);
