@@ -1083,22 +1083,32 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 dma(misc, dst + b * 64);
             }
         };
-        auto issue_part = [&](auto part_c, uint4* dst, int j, int len) {
+        // Loads [lo, hi) of this producer's kDma loads for a chunk.
+        auto issue_part = [&](auto part_c, auto lo_c, auto hi_c, uint4* dst, int j, int len) {
             constexpr int pt = decltype(part_c)::value;
             static_for<kDma>([&](auto i_c) {
-                constexpr int b0 = pt + kProdPerWave * decltype(i_c)::value;
-                constexpr int b = b0 < L::kBlocks ? b0 : b0 - kProdPerWave;
-                block(std::integral_constant<int, b>{}, dst, j, len);
+                constexpr int i = decltype(i_c)::value;
+                if constexpr (i >= decltype(lo_c)::value && i < decltype(hi_c)::value) {
+                    constexpr int b0 = pt + kProdPerWave * i;
+                    constexpr int b = b0 < L::kBlocks ? b0 : b0 - kProdPerWave;
+                    block(std::integral_constant<int, b>{}, dst, j, len);
+                }
             });
         };
-        auto issue = [&](uint4* buf, int s_) {
+        auto issue = [&](uint4* buf, int s_, auto lo_c, auto hi_c) {
             const int j = chunk_at(s_);
             const int len = chunk_len(j);
             uint4* dst = buf + cw * L::kWaveVec;
             static_for<kProdPerWave>([&](auto p_c) {
-                if (part == decltype(p_c)::value) issue_part(p_c, dst, j, len);
+                if (part == decltype(p_c)::value) issue_part(p_c, lo_c, hi_c, dst, j, len);
             });
         };
+        using All0 = std::integral_constant<int, 0>;
+        using AllN = std::integral_constant<int, kDma>;
+        // loads issued before the compute waves' second inner barrier: 6 of 17
+        // (at d = 128, 32 heads x 65536 tokens: 3, 6, 9, 12, 15 of 17 gave
+        // 1.10, 1.10, 1.11, 1.12, 1.12 ms; all 17 there, 1.15 ms)
+        using Cut = std::integral_constant<int, (kDma * 6 + 8) / 17>;
 
         // Warm-up lines of this slab: kTouch per producer lane, over one
         // chunk's operands, Gamma_L and the head's value rows.
@@ -1156,25 +1166,32 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             }
         };
         // One step j: open it; after the compute waves' first inner barrier
-        // refill chunk j's buffer with chunk j+2 and warm up chunk j+kAhead;
-        // after the second, wait until chunk j+1 has landed (the loads issued
-        // after it -- the previous step's warm-up, this step's fill and
-        // warm-up -- may stay in flight).
+        // (chunk j's operands are in their registers) refill chunk j's buffer
+        // with chunk j+2, part of the loads before their second inner barrier
+        // and the rest after it, then warm up chunk j+kAhead and wait until
+        // chunk j+1 has landed (the loads issued after it -- the previous
+        // step's warm-up, this step's fill and warm-up -- may stay in
+        // flight).  A wave needs about 80 clocks to issue each 1 KB direct
+        // load, so the whole fill takes longer than the compute waves' work
+        // between two barriers; split in two, it overlaps both stretches
+        // that follow the first inner barrier instead of holding up the
+        // second.
         auto pstep = [&](uint4* buf, int j) {
             barrier_lds();
             barrier_lds();
             const bool fill = j + 2 < nch;
-            if (fill) issue(buf, j + 2);
-            touch(j);
+            if (fill) issue(buf, j + 2, All0{}, Cut{});
             barrier_lds();
+            if (fill) issue(buf, j + 2, Cut{}, AllN{});
+            touch(j);
             if (fill)
                 wait_counts<2 * kTouch + kDma, 15>();
             else
                 wait_counts<2 * kTouch, 15>();
         };
         if (nch > 0) {
-            issue(sBuf0, 0);
-            if (nch > 1) issue(sBuf1, 1);
+            issue(sBuf0, 0, All0{}, AllN{});
+            if (nch > 1) issue(sBuf1, 1, All0{}, AllN{});
             touch(-2);
             touch(-1);
             if (nch > 1)   // chunk 0 has landed
