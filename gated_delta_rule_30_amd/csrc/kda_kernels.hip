@@ -1105,10 +1105,13 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         };
         using All0 = std::integral_constant<int, 0>;
         using AllN = std::integral_constant<int, kDma>;
-        // loads issued before the compute waves' second inner barrier: 6 of 17
-        // (at d = 128, 32 heads x 65536 tokens: 3, 6, 9, 12, 15 of 17 gave
-        // 1.10, 1.10, 1.11, 1.12, 1.12 ms; all 17 there, 1.15 ms)
-        using Cut = std::integral_constant<int, (kDma * 6 + 8) / 17>;
+        // loads issued before the compute waves' second inner barrier, in
+        // 17ths of the fill, measured at d = 128, 32 heads x 65536 tokens:
+        // forward 6 (3, 6, 9, 12, 15, 17: 1.10, 1.10, 1.11, 1.12, 1.12,
+        // 1.15 ms); kCkpt and kBwd 12 (3, 6, 9, 12, 17: 1.45 / 1.49,
+        // 1.47 / 1.52, 1.46 / 1.46, 1.45 / 1.44, 1.51 / 1.47 ms)
+        constexpr int kCut17 = (kMode == kCkpt || kMode == kBwd) ? 12 : 6;
+        using Cut = std::integral_constant<int, (kDma * kCut17 + 8) / 17>;
 
         // Warm-up lines of this slab: kTouch per producer lane, over one
         // chunk's operands, Gamma_L and the head's value rows.
