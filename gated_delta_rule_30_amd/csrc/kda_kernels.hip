@@ -212,7 +212,7 @@ struct ChunkOps {
 // (Q . Gamma)^T through the transposing LDS stages, T^T and M^T, and beta
 // (Gamma_L is shared: ob.gam is ops.gam).
 template <typename E, int D, bool kBoth = false>
-__global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ g, const E* __restrict__ beta,
                                                    const ChunkInfo* __restrict__ tab,
                                                    const int32_t* __restrict__ n_chunks_p, int64_t fixed_len,
@@ -242,6 +242,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     __shared__ float sP30[D];                 // exp(rho_3 - rho_1)
     __shared__ float sERho[kNSub * D];        // exp(rho_R)
     __shared__ float sCarry[(kNSub + 1) * D]; // rho_0 .. rho_3, b_L
+    __shared__ float sELr[kNSub * D];         // exp(b_L - rho_{R+1})
     __shared__ __attribute__((aligned(16))) E sM[C * PM];
     __shared__ __attribute__((aligned(16))) float sBeta[C];
     __shared__ __attribute__((aligned(16))) E sQt[kBwd ? D * PK : 8];   // (Q . Gamma)^T staging (kBwd)
@@ -314,6 +315,8 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
             run += t;
         }
         sCarry[kNSub * D + c] = run;
+#pragma unroll
+        for (int r = 0; r < kNSub; ++r) sELr[r * D + c] = __expf(run - sCarry[(r + 1) * D + c]);
         sP30[c] = sTot[1 * D + c] * sTot[2 * D + c];
         ops.gam[cbase * D + c] = __expf(run);
     }
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
     {
         const float* rho = sCarry + w * D + lg * CPL;
         const float* erho = sERho + w * D + lg * CPL;
-        const float* bl = sCarry + kNSub * D + lg * CPL;
+        const float* elr = sELr + w * D + lg * CPL;
         const float* esub = sTot + w * D + lg * CPL;
         uint4* qg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Qg) + cbase * C * D);
         uint4* kg = reinterpret_cast<uint4*>(static_cast<E*>(ops.Kg) + cbase * C * D);
@@ -365,8 +368,10 @@ __global__ __launch_bounds__(kThreads) void k_prep(const E* __restrict__ q, cons
                     cd[j] = from_f<E>(kv * fd);
                 }
                 const int cv = c % EPV;   // element within the current 16-byte vector
-                ec[cv] = from_f<E>(kv * (esub[c] * fd));
-                const float kh_v = kv * __expf(bl[c] - b[c]);
+                // exp(rho_{w+1} - b) <= 1, and exp(b_L - b) is that times exp(b_L - rho_{w+1}) <= 1
+                const float ew = esub[c] * fd;
+                ec[cv] = from_f<E>(kv * ew);
+                const float kh_v = kv * (elr[c] * ew);
                 eq[cv] = from_f<E>(qv * gm);
                 ek[cv] = from_f<E>(kv * gm);
                 sKt[kt_at(lg * CPL + c, tok)] = from_f<E>(kh_v);
