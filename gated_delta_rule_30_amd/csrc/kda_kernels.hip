@@ -68,6 +68,21 @@ __device__ inline void seq_range(const int32_t* __restrict__ cu, int32_t n, int6
     }
 }
 
+// Chunks c0 .. c0 + nch - 1 of sequence n of length s_len.  Equal lengths
+// (cu == NULL) list sequence n's chunks from n * ceil(len / 64) on, which is
+// what the chunk table holds for them, so no table is read; otherwise the
+// table's first chunk of each sequence, clamped to its slots.
+__device__ inline void seq_chunks(const int32_t* __restrict__ cu, const int32_t* __restrict__ seq_chunk0, int32_t n,
+                                  int64_t fixed_len, int64_t s_len, int32_t& c0, int32_t& nch) {
+    nch = (int32_t)((s_len + kChunk - 1) / kChunk);
+    if (!cu) {
+        c0 = n * (int32_t)((fixed_len + kChunk - 1) / kChunk);
+        return;
+    }
+    c0 = seq_chunk0[n];
+    if (nch > seq_chunk0[n + 1] - c0) nch = seq_chunk0[n + 1] - c0;
+}
+
 // ---------------------------------------------------------------- chunk table
 // One workgroup.  Sequence n contributes ceil(len_n / 64) chunks; chunks are
 // aligned to each sequence's first token and the last one may be partial.
@@ -693,9 +708,8 @@ __global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, Chu
     // Chunks of this sequence: c0 .. c0 + nch - 1 (the same list k_prep walked).
     int64_t s_start, s_len;
     seq_range(cu, n, total_tokens, fixed_len, s_start, s_len);
-    const int32_t c0 = seq_chunk0[n];
-    int32_t nch = (int32_t)((s_len + C - 1) / C);
-    if (nch > seq_chunk0[n + 1] - c0) nch = seq_chunk0[n + 1] - c0;
+    int32_t c0, nch;
+    seq_chunks(cu, seq_chunk0, n, fixed_len, s_len, c0, nch);
 
     RecurPtrs<E, D> P;
     {
@@ -1030,9 +1044,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 
     int64_t s_start, s_len;
     seq_range(cu, n, total_tokens, fixed_len, s_start, s_len);
-    const int32_t c0 = seq_chunk0[n];
-    int32_t nch = (int32_t)((s_len + C - 1) / C);
-    if (nch > seq_chunk0[n + 1] - c0) nch = seq_chunk0[n + 1] - c0;
+    int32_t c0, nch;
+    seq_chunks(cu, seq_chunk0, n, fixed_len, s_len, c0, nch);
     const int64_t cb = (int64_t)h * ops.max_chunks + c0;   // head-major operand slot of chunk 0
     auto chunk_len = [&](int j) -> int {
         const int64_t rem = s_len - (int64_t)j * C;
@@ -1500,7 +1513,7 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     const int32_t NH = p.n_seqs * p.n_heads;
 
     mark(0);
-    launch_table(p, st);
+    if (p.cu_seqlens) launch_table(p, st);   // equal lengths: every kernel derives the chunks itself
     mark(1);
     launch_prep<E, D, false>(p, q, st);
     mark(2);
