@@ -227,7 +227,7 @@ struct ChunkOps {
 // (Q . Gamma)^T through the transposing LDS stages, T^T and M^T, and beta
 // (Gamma_L is shared: ob.gam is ops.gam).
 template <typename E, int D, bool kBoth = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth && sizeof(E) == 2 ? 3 : 1))) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ g, const E* __restrict__ beta,
                                                    const ChunkInfo* __restrict__ tab,
                                                    const int32_t* __restrict__ n_chunks_p, int64_t fixed_len,
