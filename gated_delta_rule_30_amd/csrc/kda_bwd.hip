@@ -417,7 +417,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
             if (tt >= len) continue;
             const E* src = (m == 0 ? sOq : m == 1 ? sOk : sOg) + tt * PO + 8 * v;
             E* dst = (m == 0 ? a.dq : m == 1 ? a.dk : a.dg) + (info.tok0 + tt) * rs + (int64_t)h * D + c0 + 8 * v;
-            *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+            store_nt(dst, *reinterpret_cast<const uint4*>(src));   // streamed: read next by the caller
         }
     }
 }

@@ -61,6 +61,16 @@ __device__ inline f32x4 mma_f32(float a, float b, f32x4 c) {
 
 __device__ inline f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// 16-byte store / load with the non-temporal hint, for data that this kernel
+// touches once (the next reader is another kernel).
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ inline void store_nt(void* p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_nt, v), static_cast<u32x4_nt*>(p));
+}
+__device__ inline uint4 load_nt(const void* p) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(static_cast<const u32x4_nt*>(p)));
+}
+
 template <typename E> __device__ inline float to_f(E x) { return static_cast<float>(x); }
 template <typename E> __device__ inline E from_f(float x) { return static_cast<E>(x); }
 

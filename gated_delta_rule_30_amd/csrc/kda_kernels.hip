@@ -397,9 +397,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
                 }
                 if (cv == EPV - 1) {
                     const int i = c / EPV;
-                    qg[(w * G::VPL + i) * 64 + lane_id()] = vq;
-                    kg[(w * G::VPL + i) * 64 + lane_id()] = vk;
-                    if constexpr (kBwd) kh[(w * G::VPL + i) * 64 + lane_id()] = vh;
+                    store_nt(&qg[(w * G::VPL + i) * 64 + lane_id()], vq);
+                    store_nt(&kg[(w * G::VPL + i) * 64 + lane_id()], vk);
+                    if constexpr (kBwd) store_nt(&kh[(w * G::VPL + i) * 64 + lane_id()], vh);
                     if (w < kNSub - 1) cbv[i] = vc;
                 }
             }
@@ -419,13 +419,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
             const int ln = vi % 64, v = (vi / 64) % G::NVT, ct = vi / (64 * G::NVT);
             const int r = kSub * ct + (ln & 15), lgp = ln >> 4;
             if constexpr (M::KW == EPV) {
-                out[vi] = *reinterpret_cast<const uint4*>(st + kt_at(r, G::tok_of(v * EPV, lgp)));
+                store_nt(&out[vi], *reinterpret_cast<const uint4*>(st + kt_at(r, G::tok_of(v * EPV, lgp))));
             } else {
                 uint4 pk;
                 E* pe = reinterpret_cast<E*>(&pk);
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) pe[e] = st[kt_at(r, G::tok_of(v * EPV + e, lgp))];
-                out[vi] = pk;
+                store_nt(&out[vi], pk);
             }
         }
     };
@@ -568,11 +568,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
                 emt[e] = zero ? from_f<E>(0.f) : sM[t * PM + r];
             }
         }
-        otb[vi] = pt;
-        omm[vi] = pm;
+        store_nt(&otb[vi], pt);
+        store_nt(&omm[vi], pm);
         if constexpr (kBwd) {
-            ott[vi] = ptt;
-            omt[vi] = pmt;
+            store_nt(&ott[vi], ptt);
+            store_nt(&omt[vi], pmt);
         }
     }
 }
