@@ -38,7 +38,9 @@ def _err(y, ref):
 @pytest.mark.parametrize("dtype,T,H,d,with_w,eps,inplace", [
     ("bf16", 1000, 3, 128, True, 1e-6, False), ("bf16", 77, 2, 64, False, 1e-5, True),
     ("f32", 513, 2, 64, True, 1e-6, False), ("f32", 300, 4, 128, False, 0.0, True),
-    ("bf16", 1, 1, 128, True, 1e-6, False)])
+    ("bf16", 1, 1, 128, True, 1e-6, False),
+    # 1,120,016 rows: more than one pass of the grid-stride loop (16384 workgroups x 64 rows), ragged tail
+    ("bf16", 70001, 16, 64, True, 1e-6, False)])
 def test_output_gate_matches_oracle(torch_dev, dtype, T, H, d, with_w, eps, inplace):
     torch, dev = torch_dev
     import gated_delta_rule_30_amd as kda
