@@ -68,12 +68,13 @@ CASES = [
     ((256, 256), 3, 128, 0.0, 0.0, False, False, False),
     ((130, 77, 0, 200), 2, 64, 0.02, 0.0, True, True, True),
     ((1000,), 1, 128, 0.02, 0.25, True, True, True),
+    ((100, 100, 100), 2, 64, 0.02, 0.0, False, True, False),
 ]
 
 
 @pytest.mark.parametrize("lengths,H,d,s0,pin,varlen,with_dst,weak", CASES,
                          ids=["varlen-d64", "one-seq-d128-pinned", "equal-d128-no-state", "varlen-d64-weak",
-                              "long-d128-weak"])
+                              "long-d128-weak", "equal-ragged-d64"])
 def test_backward_matches_oracle(torch_dev, lengths, H, d, s0, pin, varlen, with_dst, weak):
     torch, dev = torch_dev
     spec = ki.Spec("bwd", "bf16", tuple(lengths), H, d, d, s0_std=s0, pin_frac=pin, varlen=varlen, seed=7)

@@ -121,6 +121,18 @@ def test_edge_cases(torch_dev, dtype, lengths, H, d, special):
     _check(inp, o, ST, what="edge %s %s %s" % (dtype, lengths, special))
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_equal_ragged_lengths_without_cu_seqlens(torch_dev, dtype, d):
+    """Three sequences of 100 tokens passed as equal lengths (cu_seqlens NULL):
+    each sequence's chunks (64 + 36 tokens) are derived from the index."""
+    torch, dev = torch_dev
+    spec = ki.custom("equal ragged", dtype, [100, 100, 100], 2, d, s0_std=0.3, varlen=False, seed=9)
+    inp = ki.generate_numpy(spec)
+    _say("equal ragged lengths 3 x 100 %s d=%d, cu_seqlens NULL" % (dtype, d))
+    o, ST = _run_numpy_inputs(torch, dev, inp)
+    _check(inp, o, ST, what="equal ragged %s" % dtype)
+
+
 def test_many_sequences(torch_dev):
     """2100 sequences (three 1024-sequence batches of the chunk table), lengths
     0..70 with empty ones, so chunk records straddle batch boundaries."""
