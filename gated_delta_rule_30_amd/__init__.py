@@ -84,6 +84,11 @@ def _load():
         lib.kda_chunk_bwd_ctx.restype = ctypes.c_int
         lib.kda_output_gate.argtypes = [ctypes.c_int, I64, I32, P, P, P, ctypes.c_float, P, P]
         lib.kda_output_gate.restype = ctypes.c_int
+        lib.kda_chunk_ckpt_size.argtypes = [I64, I32, I32, I32, I32]
+        lib.kda_chunk_ckpt_size.restype = SZ
+        lib.kda_chunk_fwd_ckpt.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, I32,
+                                           P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]
+        lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -116,7 +121,8 @@ def chunk_fwd_profile(*args, **kw):
 
 
 def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = CHUNK,
-              output_final_state: bool = True, o=None, S_T=None, workspace=None, n_seqs=None, _stage_ms=None):
+              output_final_state: bool = True, o=None, S_T=None, workspace=None, n_seqs=None, _stage_ms=None,
+              _ckpt=None):
     """KDA chunkwise forward on the GPU.
 
     q, k, log_alpha: [T_total, H, d_k] or [B, T, H, d_k]; v: [..., H, d_v];
@@ -183,7 +189,10 @@ def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = C
     args = (dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
             _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T), _ptr(workspace),
             workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
-    if _stage_ms is None:
+    if _ckpt is not None:
+        every, S_ckpt = _ckpt
+        code = lib.kda_chunk_fwd_ckpt(*args[:16], int(every), _ptr(S_ckpt), *args[16:])
+    elif _stage_ms is None:
         code = lib.kda_chunk_fwd(*args)
     else:
         code = lib.kda_chunk_fwd_profile(*args, _stage_ms)
@@ -192,6 +201,41 @@ def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = C
     if batched:
         o = o.reshape(B, -1, H, dv)
     return o, (S_T if output_final_state else None)
+
+
+def ckpt_slots(lengths, every: int, chunk: int = CHUNK):
+    """Where chunk_fwd_ckpt puts each sequence's checkpoints: for sequence n a
+    list of (tokens, slot) -- the state after its first `tokens` tokens is
+    S_ckpt[slot].  `lengths` are the sequence lengths (host integers)."""
+    out, c0 = [], 0
+    for L in lengths:
+        nch = (int(L) + chunk - 1) // chunk
+        out.append([(min((j + 1) * chunk, int(L)), c0 + j) for j in range(nch) if (j + 1) % every == 0])
+        c0 += nch
+    return out
+
+
+def chunk_fwd_ckpt(q, k, v, beta, log_alpha, every: int, S_ckpt=None, **kw):
+    """chunk_fwd that also writes the state after every `every`-th chunk of each
+    sequence (prefix-cache checkpoints) into S_ckpt, float32 [slots, H, d_k,
+    d_v] (allocated when None; see ckpt_slots for the slot of each).  bf16
+    only.  Returns (o, S_T, S_ckpt)."""
+    import torch
+    lib = _load()
+    T, H, dk = (q.reshape(-1, *q.shape[-2:]).shape if q.dim() == 4 else q.shape)
+    dv = v.shape[-1]
+    cu = kw.get("cu_seqlens")
+    N = cu.numel() - 1 if cu is not None else kw.get("n_seqs") or (q.shape[0] if q.dim() == 4 else 1)
+    nbytes = int(lib.kda_chunk_ckpt_size(T, N, H, dk, dv))
+    if S_ckpt is None:
+        if nbytes == 0:
+            raise KdaError(4, "unsupported sizes for checkpoints")
+        S_ckpt = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device).view(-1, H, dk, dv)
+    elif (S_ckpt.dtype != torch.float32 or S_ckpt.numel() * 4 < nbytes or not S_ckpt.is_contiguous()
+          or S_ckpt.device != q.device):
+        raise ValueError("S_ckpt must be contiguous float32 with at least %d bytes on %s" % (nbytes, q.device))
+    o, S_T = chunk_fwd(q, k, v, beta, log_alpha, _ckpt=(every, S_ckpt), **kw)
+    return o, S_T, S_ckpt
 
 
 def bwd_workspace_size(total_tokens: int, n_seqs: int, n_heads: int, d_k: int, d_v: int,

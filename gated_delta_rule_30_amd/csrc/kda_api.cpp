@@ -153,6 +153,31 @@ kda_status kda_chunk_fwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+size_t kda_chunk_ckpt_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k, int32_t d_v) {
+    Plan p{};
+    if (plan_sizes(&p, KDA_BF16, total_tokens, n_seqs, n_heads, d_k, d_v, kda::kChunkTokens, true) != KDA_OK) return 0;
+    return (size_t)p.max_chunks * (size_t)n_heads * (size_t)d_k * (size_t)d_v * sizeof(float);
+}
+
+kda_status kda_chunk_fwd_ckpt(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                              int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
+                              const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
+                              void* o, float* S_T, int32_t every, float* S_ckpt, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+    if (dt == KDA_F32) return KDA_ERR_UNSUPPORTED;
+    if (every < 1) return KDA_ERR_SHAPE;
+    if (!S_ckpt) return KDA_ERR_NULL;
+    if ((uintptr_t)S_ckpt % 16 != 0) return KDA_ERR_SHAPE;
+    Plan p{};
+    kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
+                           cu_seqlens, o, S_T, workspace, workspace_bytes);
+    if (s != KDA_OK) return s;
+    p.S_ckpt = S_ckpt;
+    p.ck_every = every;
+    hipError_t e = kda::launch(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 int32_t kda_profile_num_stages(void) { return kda::kNumStages; }
 
 const char* kda_profile_stage_name(int32_t i) {

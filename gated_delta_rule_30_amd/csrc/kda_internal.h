@@ -25,6 +25,8 @@ struct Plan {
     const int32_t* cu_seqlens;
     void* o;
     float* S_T;
+    float* S_ckpt;            // [slots, H, D, D] fp32 states at chosen chunk ends, or NULL
+    int32_t ck_every;         // a state after every ck_every-th chunk of a sequence
     // workspace carve-up
     int32_t* ws_n_chunks;
     int32_t* ws_seq_chunk0;

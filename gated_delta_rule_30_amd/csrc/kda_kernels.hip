@@ -989,13 +989,19 @@ struct LdsGeo {
 //          These are the adjoints of the kFwd step (the chain rule through
 //          U~ = T diag(beta) Y, O = (Q . Gamma) S + M U~ and
 //          S' = Diag(Gamma_L) S + K^T U~).
-enum { kFwd = 0, kTrans = 1, kCkpt = 2, kBwd = 3 };
+//   kFwdCk kFwd that also writes the fp32 state after every aux.every-th
+//          chunk of a sequence to aux.sck (slot = the chunk's global index):
+//          the prefix-cache checkpoints.  A mode of its own, so that the plain
+//          forward carries no test for it.
+enum { kFwd = 0, kTrans = 1, kCkpt = 2, kBwd = 3, kFwdCk = 4 };
 
 struct RecurAux {
     __bf16* ck;        // kCkpt: S entering each chunk; kBwd: dS' of each chunk
     __bf16* y;         // kCkpt: Y;  kBwd: dZ
     __bf16* u;         // kCkpt: U~
     const float* bet;  // kBwd: per-chunk beta (ChunkOps::bet)
+    float* sck;        // kFwdCk: fp32 state after every `every`-th chunk, slot = global chunk index
+    int32_t every;
 };
 
 template <int D, int kMode>
@@ -1340,12 +1346,22 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[a][r] = gam[a][r] * S[a][r] + acc[r];
         }
+        // kFwdCk: the state after this chunk, when it is a chosen checkpoint
+        if constexpr (kMode == kFwdCk) {
+            if ((j + 1) % aux.every == 0) {
+                float* dst = aux.sck + ((int64_t)(c0 + j) * H + h) * D * D + col0 + li;
+#pragma unroll
+                for (int a = 0; a < RT; ++a)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(int64_t)(kSub * (RT * w + a) + 4 * lg + r) * D] = S[a][r];
+            }
+        }
 #pragma unroll
         for (int m = 0; m < G::NKT; ++m) accO = M::mma(fmm[m], bu[m], accO);
         // S^T is last read before the Y barrier of this step; the barrier at
         // the top of the next step publishes the new one.
         put_state();
-        if (kMode == kFwd || (kMode == kCkpt && o)) {
+        if (kMode == kFwd || kMode == kFwdCk || (kMode == kCkpt && o)) {
             E* oj = o + o_off + (int64_t)j * C * rs;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -1518,8 +1534,13 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     launch_prep<E, D, false>(p, q, st);
     mark(2);
     static_assert(!kTransition || sizeof(E) == 2, "transition pass: bf16 operands only");
-    if constexpr (sizeof(E) == 2)
-        launch_recur_lds<D, kMode>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
+    if constexpr (sizeof(E) == 2) {
+        if (kMode == kFwd && p.S_ckpt)
+            launch_recur_lds<D, kFwdCk>(p, p.v, p.S0, p.S_T, p.o,
+                                        RecurAux{nullptr, nullptr, nullptr, nullptr, p.S_ckpt, p.ck_every}, st);
+        else
+            launch_recur_lds<D, kMode>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
+    }
     else
         hipLaunchKernelGGL((k_recur<E, D, CT>), dim3(NH * (D / (kSub * CT))), dim3(kThreads), 0, st,
                            static_cast<const E*>(p.v), chunk_ops(p), p.cu_seqlens, p.total_tokens, p.fixed_len,

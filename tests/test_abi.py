@@ -261,3 +261,36 @@ def test_training_pair_rejects_bad_arguments(lib):
     assert bc(ctx=None) == ERR_WORKSPACE
     assert bc(ctx_bytes=16) == ERR_WORKSPACE
     assert bc(ws_bytes=need_bws - 1) == ERR_WORKSPACE
+
+
+def test_checkpoint_size_and_rejections(lib):
+    P = ctypes.c_void_p
+    # slots = total_tokens / 64 + n_seqs, each n_heads x d_k x d_v float32
+    assert lib.kda_chunk_ckpt_size(65536, 1, 32, 128, 128) == (65536 // 64 + 1) * 32 * 128 * 128 * 4
+    assert lib.kda_chunk_ckpt_size(100, 3, 2, 64, 64) == (100 // 64 + 3) * 2 * 64 * 64 * 4
+    assert lib.kda_chunk_ckpt_size(100, 3, 2, 96, 96) == 0
+    assert lib.kda_chunk_ckpt_size(-1, 3, 2, 64, 64) == 0
+    buf = (ctypes.c_byte * 4096)()
+    a = ctypes.addressof(buf)
+    a16 = P(a + (-a) % 16)
+
+    def call(dt=kda.KDA_BF16, every=2, sck=a16, ws=a16, ws_bytes=1 << 40):
+        return lib.kda_chunk_fwd_ckpt(dt, 128, 1, 2, 64, 64, 64, a16, a16, a16, a16, a16, None, None,
+                                      a16, None, every, sck, ws, ws_bytes, None)
+    assert call(dt=kda.KDA_F32) == ERR_UNSUPPORTED
+    assert call(every=0) == ERR_SHAPE
+    assert call(every=-3) == ERR_SHAPE
+    assert call(sck=None) == ERR_NULL
+    assert call(sck=P(a16.value + 4)) == ERR_SHAPE
+    assert call(ws=None) == ERR_WORKSPACE
+
+
+def test_checkpoint_slots_helper():
+    got = kda.ckpt_slots([700, 64, 1100, 0, 513], 2)
+    # sequence 0: 11 chunks, checkpoints after chunks 1, 3, 5, 7, 9; sequence 2 starts at slot 12 and its
+    # last (partial) chunk 17 ends at token 1100
+    assert got[0] == [(128, 1), (256, 3), (384, 5), (512, 7), (640, 9)]
+    assert got[1] == [] and got[3] == []
+    assert got[2][0] == (128, 13) and got[2][-1] == (1100, 29)
+    assert got[4] == [(128, 31), (256, 33), (384, 35), (512, 37)]
+    assert kda.ckpt_slots([512], 8) == [[(512, 7)]]
