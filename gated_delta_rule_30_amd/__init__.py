@@ -56,6 +56,8 @@ def _load():
         lib.kda_profile_stage_name.restype = ctypes.c_char_p
         lib.kda_recurrent_fwd.argtypes = [ctypes.c_int, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P]
         lib.kda_recurrent_fwd.restype = ctypes.c_int
+        lib.kda_recurrent_commit.argtypes = [ctypes.c_int, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P, P, P]
+        lib.kda_recurrent_commit.restype = ctypes.c_int
         lib.kda_validate_inputs.argtypes = [ctypes.c_int, I64, I32, I32, I32, P, P, P, P, P]
         lib.kda_validate_inputs.restype = ctypes.c_int
         lib.kda_chunk_transition.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]
@@ -415,7 +417,8 @@ def _check_common(q, k, v, beta, log_alpha):
     return dt, dev
 
 
-def recurrent_fwd(q, k, v, beta, log_alpha, S_in=None, S_out=None, n_seqs=None, o=None):
+def recurrent_fwd(q, k, v, beta, log_alpha, S_in=None, S_out=None, n_seqs=None, o=None, n_accept=None,
+                  want_o=True):
     """Token-by-token KDA update for decoding (kda_recurrent_fwd).
 
     q, k, log_alpha: [N*n, H, d_k] or [N, n, H, d_k]; v: [..., H, d_v];
@@ -423,6 +426,11 @@ def recurrent_fwd(q, k, v, beta, log_alpha, S_in=None, S_out=None, n_seqs=None, 
     or `n_seqs`, default 1).  S_in: [N, H, d_k, d_v] float32 or None (zeros).
     S_out: preallocated output state (may be S_in itself for an in-place
     update) or None (allocated).  Returns (o, S_out).
+
+    With n_accept (int32 [N] on the device) the call goes to
+    kda_recurrent_commit: sequence i takes only its first n_accept[i] token
+    slots (clamped to [0, n]); o rows of the other slots are left as they
+    were, and with want_o=False no o is written at all (returned as None).
     """
     import torch
     lib = _load()
@@ -444,18 +452,28 @@ def recurrent_fwd(q, k, v, beta, log_alpha, S_in=None, S_out=None, n_seqs=None, 
         if t is not None and (t.dtype != torch.float32 or t.shape != (N, H, dk, dv) or t.device != dev
                               or not t.is_contiguous()):
             raise ValueError("%s must be contiguous float32 [%d, %d, %d, %d] on %s" % (name, N, H, dk, dv, dev))
+    if n_accept is not None and (n_accept.dtype != torch.int32 or n_accept.shape != (N,) or n_accept.device != dev
+                                 or not n_accept.is_contiguous()):
+        raise ValueError("n_accept must be contiguous int32 [%d] on %s" % (N, dev))
+    if not want_o and n_accept is None:
+        raise ValueError("want_o=False needs n_accept")
     if S_out is None:
         S_out = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    if o is None:
+    if not want_o:
+        o = None
+    elif o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
     elif o.shape != (T, H, dv) or o.dtype != q.dtype or o.device != dev or not o.is_contiguous():
         raise ValueError("o must be contiguous %s [%d, %d, %d] on %s" % (q.dtype, T, H, dv, dev))
-    stream = torch.cuda.current_stream(dev).cuda_stream
-    code = lib.kda_recurrent_fwd(dt, N, T // N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
-                                 _ptr(S_in), _ptr(S_out), _ptr(o), ctypes.c_void_p(stream))
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    args = (dt, N, T // N, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha))
+    if n_accept is None:
+        code = lib.kda_recurrent_fwd(*args, _ptr(S_in), _ptr(S_out), _ptr(o), stream)
+    else:
+        code = lib.kda_recurrent_commit(*args, _ptr(n_accept), _ptr(S_in), _ptr(S_out), _ptr(o), stream)
     if code != 0:
         raise KdaError(code, lib.kda_status_string(code).decode())
-    if batched:
+    if batched and o is not None:
         o = o.reshape(N, -1, H, dv)
     return o, S_out
 

@@ -234,18 +234,21 @@ kda_status kda_compose_states(int32_t n_segments, int32_t n_heads, int32_t d, co
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
-kda_status kda_recurrent_fwd(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t d_k,
-                             int32_t d_v, const void* q, const void* k, const void* v, const void* beta,
-                             const void* log_alpha, const float* S_in, float* S_out, void* o, void* stream) {
+static kda_status recurrent(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t d_k,
+                            int32_t d_v, const void* q, const void* k, const void* v, const void* beta,
+                            const void* log_alpha, bool commit, const int32_t* n_apply, const float* S_in,
+                            float* S_out, void* o, void* stream) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
     if (n_seqs < 1 || n_tokens < 1 || n_heads < 1 || d_k < 1 || d_v < 1) return KDA_ERR_SHAPE;
     if (d_k != d_v || (d_k != 64 && d_k != 128)) return KDA_ERR_UNSUPPORTED;
     if ((int64_t)n_seqs * n_tokens >= ((int64_t)1 << 31) || (int64_t)n_seqs * n_heads * (d_k / 64) >= ((int64_t)1 << 31))
         return KDA_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !beta || !log_alpha || !S_out || !o) return KDA_ERR_NULL;
+    if (!q || !k || !v || !beta || !log_alpha || !S_out || (!commit && !o) || (commit && !n_apply))
+        return KDA_ERR_NULL;
     const void* ptrs[] = {q, k, v, beta, log_alpha, S_in, S_out, o};
     for (const void* ptr : ptrs)
         if (ptr && ((uintptr_t)ptr % 16) != 0) return KDA_ERR_SHAPE;
+    if ((uintptr_t)n_apply % 4 != 0) return KDA_ERR_SHAPE;
     kda::DecodePlan p{};
     p.bf16 = dt == KDA_BF16;
     p.d = d_k;
@@ -260,8 +263,24 @@ kda_status kda_recurrent_fwd(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int
     p.S_in = S_in;
     p.S_out = S_out;
     p.o = o;
+    p.n_apply = n_apply;
     hipError_t e = kda::launch_decode(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_recurrent_fwd(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t d_k,
+                             int32_t d_v, const void* q, const void* k, const void* v, const void* beta,
+                             const void* log_alpha, const float* S_in, float* S_out, void* o, void* stream) {
+    return recurrent(dt, n_seqs, n_tokens, n_heads, d_k, d_v, q, k, v, beta, log_alpha, false, nullptr, S_in, S_out,
+                     o, stream);
+}
+
+kda_status kda_recurrent_commit(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int32_t n_heads, int32_t d_k,
+                                int32_t d_v, const void* q, const void* k, const void* v, const void* beta,
+                                const void* log_alpha, const int32_t* n_accept, const float* S_in, float* S_out,
+                                void* o, void* stream) {
+    return recurrent(dt, n_seqs, n_tokens, n_heads, d_k, d_v, q, k, v, beta, log_alpha, true, n_accept, S_in, S_out,
+                     o, stream);
 }
 
 kda_status kda_validate_inputs(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,

@@ -18,12 +18,15 @@ namespace kda {
 // (rg, col) = (tid / 64, tid % 64) holds rows [rg*D/4, (rg+1)*D/4) of column
 // col0 + col; a wave therefore reads and writes whole 256-byte row segments.
 // The two contractions over key channels (S^T k and S^T q) sum per thread,
-// then across the four row groups through LDS.
+// then across the four row groups through LDS.  With n_apply given, sequence
+// n takes only its first n_apply[n] (clamped to [0, n_tokens]) of the
+// n_tokens token slots it owns; o may then be NULL (state only).
 template <typename E, int D>
 __global__ __launch_bounds__(256) void k_decode(const E* __restrict__ q, const E* __restrict__ k,
                                                 const E* __restrict__ v, const E* __restrict__ beta,
                                                 const E* __restrict__ g, const float* S_in, float* S_out,
-                                                E* __restrict__ o, int32_t n_tokens, int32_t H) {
+                                                E* __restrict__ o, int32_t n_tokens, int32_t H,
+                                                const int32_t* __restrict__ n_apply) {
     constexpr int RPT = D / 4;          // rows per thread
     constexpr int NCB = D / 64;         // column blocks per state
     __shared__ float sQ[D], sK[D], sA[D];
@@ -39,7 +42,9 @@ __global__ __launch_bounds__(256) void k_decode(const E* __restrict__ q, const E
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S[r] = S_in ? S_in[sbase + (int64_t)(rg * RPT + r) * D + c] : 0.f;
 
-    for (int t = 0; t < n_tokens; ++t) {
+    int n_run = n_tokens;
+    if (n_apply) n_run = min(max(n_apply[n], 0), n_tokens);
+    for (int t = 0; t < n_run; ++t) {
         const int64_t tok = n * n_tokens + t;
         const int64_t row = (tok * H + h) * D;
         __syncthreads();   // the previous token's LDS reads are done
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(256) void k_decode(const E* __restrict__ q, const E
         __syncthreads();   // everyone has read sPart
         sPart[rg][col] = y;
         __syncthreads();
-        if (rg == 0) o[row + c] = from_f<E>(sPart[0][col] + sPart[1][col] + sPart[2][col] + sPart[3][col]);
+        if (rg == 0 && o) o[row + c] = from_f<E>(sPart[0][col] + sPart[1][col] + sPart[2][col] + sPart[3][col]);
     }
 #pragma unroll
     for (int r = 0; r < RPT; ++r) S_out[sbase + (int64_t)(rg * RPT + r) * D + c] = S[r];
@@ -85,7 +90,7 @@ static hipError_t launch_decode_t(const DecodePlan& p, hipStream_t st) {
     hipLaunchKernelGGL((k_decode<E, D>), dim3((unsigned)grid), dim3(256), 0, st, static_cast<const E*>(p.q),
                        static_cast<const E*>(p.k), static_cast<const E*>(p.v), static_cast<const E*>(p.beta),
                        static_cast<const E*>(p.g), p.S_in, p.S_out, static_cast<E*>(p.o), p.n_tokens,
-                       p.n_heads);
+                       p.n_heads, p.n_apply);
     return hipGetLastError();
 }
 

@@ -120,7 +120,8 @@ struct DecodePlan {
     const void *q, *k, *v, *beta, *g;
     const float* S_in;        // may be NULL (zeros); may equal S_out
     float* S_out;
-    void* o;
+    void* o;                  // may be NULL when n_apply is set
+    const int32_t* n_apply;   // device [n_seqs] tokens to take per sequence, or NULL (all)
 };
 hipError_t launch_decode(const DecodePlan& p, hipStream_t stream);
 

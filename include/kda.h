@@ -193,6 +193,29 @@ kda_status kda_recurrent_fwd(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int
                              const void* beta, const void* log_alpha,
                              const float* S_in, float* S_out, void* o, void* stream);
 
+/* Speculative-decoding commit (orkas.ai "Kimi K3 architecture",
+ * §"請求書はサービング側に回ってくる", speculative decoding: the state is
+ * updated in place, so a rejected draft cannot be undone; only the much
+ * smaller projected inputs are cached and the state is rebuilt on chip).
+ * Same as kda_recurrent_fwd over n_tokens cached draft token slots per
+ * sequence, except that sequence n takes only its first n_accept[n] of them:
+ *   n_accept : device int32 [n_seqs] (4-byte aligned, required); each value
+ *              is clamped to [0, n_tokens], so 0 leaves the state as S_in
+ *              (copied to S_out when they differ)
+ *   o        : as for kda_recurrent_fwd, or NULL (state only); only the rows
+ *              of taken tokens are written, the others are left untouched
+ * The usual flow keeps S_in, runs the draft with kda_recurrent_fwd into a
+ * separate S_out, and once the verifier has fixed n_accept calls this with
+ * S_out == S_in and o == NULL.  The state it leaves equals, bit for bit,
+ * the one kda_recurrent_fwd reaches over the same accepted tokens.  Sizes,
+ * dtypes, alignment and errors as for kda_recurrent_fwd.  Enqueued on
+ * `stream`, never synchronises. */
+kda_status kda_recurrent_commit(kda_dtype dt, int32_t n_seqs, int32_t n_tokens, int32_t n_heads,
+                                int32_t d_k, int32_t d_v,
+                                const void* q, const void* k, const void* v,
+                                const void* beta, const void* log_alpha, const int32_t* n_accept,
+                                const float* S_in, float* S_out, void* o, void* stream);
+
 /* Output epilogue of a KDA layer (ogis-ri NLP primer on Kimi K3, §3.1
  * "KDA": the read-out is normalised by RMSNorm because its magnitude varies
  * with the state, then multiplied channel by channel by a gate in (0, 1)

@@ -127,6 +127,22 @@ def test_recurrent_rejects_bad_arguments(lib):
     assert call(S_in=fake + 8) == ERR_SHAPE
 
 
+def test_recurrent_commit_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p
+    fake = 0x7f0000000000          # never dereferenced: every case fails validation
+
+    def call(dt=kda.KDA_BF16, N=2, n=3, H=2, dk=64, dv=64, acc=fake, S_out=fake, o=None):
+        return lib.kda_recurrent_commit(dt, N, n, H, dk, dv, P(fake), P(fake), P(fake), P(fake), P(fake),
+                                        P(acc), None, P(S_out), P(o), None)
+    assert call(dt=7) == ERR_DTYPE
+    assert call(n=0) == ERR_SHAPE
+    assert call(dk=32, dv=32) == ERR_UNSUPPORTED
+    assert call(acc=None) == ERR_NULL          # the accepted counts are required
+    assert call(S_out=None) == ERR_NULL
+    assert call(acc=fake + 2) == ERR_SHAPE     # int32 alignment
+    assert call(o=fake + 4) == ERR_SHAPE
+
+
 def test_validate_rejects_bad_arguments(lib):
     P = ctypes.c_void_p
     fake = 0x7f0000000000

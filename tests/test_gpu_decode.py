@@ -133,3 +133,74 @@ def test_validate_inputs_counts(torch_dev):
     bad_cu = torch.tensor([0, 120, 100, 200], dtype=torch.int32, device=dev)   # decreasing, wrong end
     assert kda.validate_inputs(beta, g, bad_cu) == {"log_alpha": 3, "beta": 3, "cu_seqlens": 2}
     assert kda.validate_inputs(beta, g, None, n_seqs=1) == {"log_alpha": 3, "beta": 3, "cu_seqlens": 0}
+
+
+COMMIT = [("bf16", 128, (0, 1, 4, 2, 9, -3)), ("f32", 64, (3, 0, 4, 1))]
+
+
+@pytest.mark.parametrize("dtype,d,accept", COMMIT, ids=["bf16-d128", "f32-d64"])
+def test_commit_matches_prefix_oracle(torch_dev, dtype, d, accept):
+    """kda_recurrent_commit over n = 4 cached draft slots per sequence takes
+    each sequence's first n_accept tokens (clamped to [0, n]: 9 -> 4,
+    -3 -> 0): states and the taken rows of o match the oracle run over just
+    those prefixes; the other o rows keep their NaN fill."""
+    import gated_delta_rule_30_amd as kda
+    torch, dev = torch_dev
+    N, n, H = len(accept), 4, 2
+    spec = ki.custom("commit", dtype, [n] * N, H, d, s0_std=0.3, varlen=True, seed=11)
+    inp = ki.generate_numpy(spec)
+    _say("commit %s d=%d accept %s" % (dtype, d, accept))
+    t = [_dev(torch, dev, getattr(inp, name), dtype) for name in ("q", "k", "v", "beta", "g")]
+    S_in = torch.from_numpy(inp.S0).to(dev)
+    acc = torch.tensor(accept, dtype=torch.int32, device=dev)
+    o = torch.full((N * n, H, d), float("nan"), dtype=t[0].dtype, device=dev)
+    _, S_out = kda.recurrent_fwd(*t, S_in=S_in, n_seqs=N, o=o, n_accept=acc)
+    torch.cuda.synchronize()
+    taken = [min(max(a, 0), n) for a in accept]
+    rows = np.concatenate([np.arange(i * n, i * n + a) for i, a in enumerate(taken)]).astype(np.int64)
+    cu = np.concatenate([[0], np.cumsum(taken)])
+    sub = [np.ascontiguousarray(getattr(inp, name)[rows]) for name in ("q", "k", "v", "beta", "g")]
+    o_ref, S_ref = oracle.forward(*sub, inp.S0, cu)
+    og = o.float().cpu().numpy()
+    eo = oracle.parity_error(og[rows], o_ref, cu)
+    es = oracle.parity_error(S_out.cpu().numpy(), S_ref)
+    skipped = np.setdiff1d(np.arange(N * n), rows)
+    _say("  o err %.3e  S err %.3e (tol %.0e); %d skipped rows" % (eo, es, TOL[dtype], skipped.size))
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+    assert np.isnan(og[skipped]).all()
+    for i, a in enumerate(taken):
+        if a == 0:
+            assert torch.equal(S_out[i], S_in[i])
+
+
+def test_speculative_verify_then_commit(torch_dev):
+    """The serving flow: verify a draft of 5 tokens from the kept state into a
+    scratch state, then commit each sequence's accepted prefix in place with
+    no output.  The committed state equals, bit for bit, what
+    kda_recurrent_fwd reaches over just the accepted tokens, and the draft's
+    outputs for accepted tokens are the committed run's outputs."""
+    import gated_delta_rule_30_amd as kda
+    torch, dev = torch_dev
+    N, n, H, d = 4, 5, 3, 128
+    accept = (5, 2, 0, 3)
+    spec = ki.custom("spec", "bf16", [n] * N, H, d, s0_std=0.3, varlen=True, seed=12)
+    inp = ki.generate_numpy(spec)
+    t = [_dev(torch, dev, getattr(inp, name), "bf16") for name in ("q", "k", "v", "beta", "g")]
+    S = torch.from_numpy(inp.S0).to(dev)
+    S_keep = S.clone()
+    o_draft, S_draft = kda.recurrent_fwd(*t, S_in=S, n_seqs=N)
+    acc = torch.tensor(accept, dtype=torch.int32, device=dev)
+    o_none, S_after = kda.recurrent_fwd(*t, S_in=S, S_out=S, n_seqs=N, n_accept=acc, want_o=False)
+    torch.cuda.synchronize()
+    assert o_none is None and S_after is S
+    assert torch.equal(S[2], S_keep[2])              # nothing accepted: the kept state
+    for i, a in enumerate(accept):
+        if a == 0:
+            continue
+        sl = [x.reshape(N, n, *x.shape[1:])[i, :a].clone() for x in t]   # fresh, aligned buffers
+        o_i, S_i = kda.recurrent_fwd(*sl, S_in=S_keep[i:i + 1].clone(), n_seqs=1)
+        torch.cuda.synchronize()
+        assert torch.equal(S[i], S_i[0]), "sequence %d" % i
+        assert torch.equal(o_draft.reshape(N, n, H, d)[i, :a], o_i)
+        if a == n:
+            assert torch.equal(S[i], S_draft[i])
