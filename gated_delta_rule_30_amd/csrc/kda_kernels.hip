@@ -568,11 +568,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
                 emt[e] = zero ? from_f<E>(0.f) : sM[t * PM + r];
             }
         }
-        store_nt(&otb[vi], pt);
-        store_nt(&omm[vi], pm);
+        // bf16: the 32-token halves that are zero by structure (row tiles 0
+        // and 1 over tokens 32..63; of the transposes, row tiles 2 and 3 over
+        // tokens 0..31) are not stored: the bf16 recurrence never reads them.
+        // (The fp32 recurrence reads whole tiles.)  A wave's 64 vectors are
+        // one (row tile, half) block, so the skip is wave-uniform.
+        constexpr bool kSkipZero = M::KW == EPV && G::NVT == 2;
+        if (!(kSkipZero && wr < 2 && v == 1)) {
+            store_nt(&otb[vi], pt);
+            store_nt(&omm[vi], pm);
+        }
         if constexpr (kBwd) {
-            store_nt(&ott[vi], ptt);
-            store_nt(&omt[vi], pmt);
+            if (!(kSkipZero && wr >= 2 && v == 0)) {
+                store_nt(&ott[vi], ptt);
+                store_nt(&omt[vi], pmt);
+            }
         }
     }
 }
@@ -1004,6 +1014,18 @@ struct RecurAux {
     int32_t every;
 };
 
+// The two triangular tiles of a region (T diag(beta) and M in the forward
+// modes, T^T and M^T in kBwd) have a 32-token half that is zero by structure:
+// row tiles 0 and 1 of the lower-triangular forms over tokens 32..63, row
+// tiles 2 and 3 of the transposes over tokens 0..31 (T continues as the
+// identity past a chunk's end, so this holds for short chunks too).  Those
+// halves are neither loaded nor read; the fragments are zero in registers.
+template <int kMode>
+struct ZeroHalf {
+    static constexpr int kHalf = kMode == kBwd ? 0 : 1;   // which 32-token half is zero
+    __device__ static bool zero(int region) { return kMode == kBwd ? region >= 2 : region < 2; }
+};
+
 template <int D, int kMode>
 __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     const __bf16* __restrict__ v, ChunkOps ops, const int32_t* __restrict__ cu, int64_t total_tokens,
@@ -1016,8 +1038,10 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     using L = LdsGeo<D>;
     using M = Mma<E>;
     using F = typename M::frag;
+    using Z = ZeroHalf<kMode>;
     static_assert(G::VPL == G::NKC && G::NVT == G::NKT, "one 16-byte vector per bf16 fragment");
     static_assert(kRecurWaves == kNSub, "one compute wave per 16-token row tile");
+    static_assert(G::NKT == 2, "the zero halves are the two 32-token halves of a 64-token chunk");
     constexpr int C = kChunk, CPL = G::CPL, RT = L::RT;
     constexpr int SW = kSub;           // slab width (value columns)
     constexpr int NS = D / SW;         // slabs per head
@@ -1107,7 +1131,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 dma(misc, dst + b * 64);
             }
         };
-        // Loads [lo, hi) of this producer's kDma loads for a chunk.
+        // Loads [lo, hi) of this producer's kDma loads for a chunk.  Blocks
+        // that are zero for this region (ZeroHalf) are not loaded.
         auto issue_part = [&](auto part_c, auto lo_c, auto hi_c, uint4* dst, int j, int len) {
             constexpr int pt = decltype(part_c)::value;
             static_for<kDma>([&](auto i_c) {
@@ -1115,7 +1140,11 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 if constexpr (i >= decltype(lo_c)::value && i < decltype(hi_c)::value) {
                     constexpr int b0 = pt + kProdPerWave * i;
                     constexpr int b = b0 < L::kBlocks ? b0 : b0 - kProdPerWave;
-                    block(std::integral_constant<int, b>{}, dst, j, len);
+                    if constexpr (b == L::kTb + Z::kHalf || b == L::kMm + Z::kHalf) {
+                        if (!Z::zero(cw)) block(std::integral_constant<int, b>{}, dst, j, len);
+                    } else {
+                        block(std::integral_constant<int, b>{}, dst, j, len);
+                    }
                 }
             });
         };
@@ -1141,7 +1170,16 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         // chunk's operands, Gamma_L and the head's value rows.
         constexpr int kAhead = 4;
         constexpr int64_t kBq = (int64_t)C * D * 2, kBs = (int64_t)C * C * 2;   // bytes per chunk slot
-        constexpr int kOpsLines = (int)((3 * kBq + 2 * kBs) / 128);
+        constexpr int kQLines = (int)(kBq / 128);
+        constexpr int kTriLines = (int)(kBs / 128) - 2 * 8;   // the two zero 1 KB halves skipped
+        constexpr int kOpsLines = 3 * kQLines + 2 * kTriLines;
+        // byte offset of line t of a triangular tile's loaded blocks (tile
+        // block 2 w + half; the zero ones are 1, 3 or, in kBwd, 4, 6)
+        auto tri_off = [](int t) -> int64_t {
+            const int k = t / 8;
+            const int b = kMode == kBwd ? (k < 4 ? k : 2 * k - 3) : (k == 0 ? 0 : k == 1 ? 2 : k + 2);
+            return (int64_t)b * 1024 + (t % 8) * 128;
+        };
         constexpr int kGamLines = D * 4 / 128;
         constexpr int kVRowLines = D * 2 / 128;
         constexpr int kLines = kOpsLines + kGamLines + kChunk * kVRowLines;
@@ -1161,9 +1199,13 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             if (off < kBq) { t_base[k] = (const char*)ops.Qg + cb * kBq + off; t_step[k] = kBq; }
             else if (off < 2 * kBq) { t_base[k] = (const char*)ops.Kg + cb * kBq + off - kBq; t_step[k] = kBq; }
             else if (off < 3 * kBq) { t_base[k] = (const char*)ops.KhT + cb * kBq + off - 2 * kBq; t_step[k] = kBq; }
-            else if (off < 3 * kBq + kBs) { t_base[k] = (const char*)ops.TB + cb * kBs + off - 3 * kBq; t_step[k] = kBs; }
-            else if (line < kOpsLines) { t_base[k] = (const char*)ops.Mm + cb * kBs + off - 3 * kBq - kBs; t_step[k] = kBs; }
-            else if (line < kOpsLines + kGamLines) {
+            else if (line < 3 * kQLines + kTriLines) {
+                t_base[k] = (const char*)ops.TB + cb * kBs + tri_off(line - 3 * kQLines);
+                t_step[k] = kBs;
+            } else if (line < kOpsLines) {
+                t_base[k] = (const char*)ops.Mm + cb * kBs + tri_off(line - 3 * kQLines - kTriLines);
+                t_step[k] = kBs;
+            } else if (line < kOpsLines + kGamLines) {
                 t_base[k] = (const char*)(ops.gam + cb * D) + (int64_t)(line - kOpsLines) * 128;
                 t_step[k] = (int64_t)D * 4;
             } else if (kTransition) {   // no value rows: warm Gamma_L again instead
@@ -1192,6 +1234,13 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 __builtin_amdgcn_global_load_lds(p, KDA_LDS_PTR(sTouch + pw * 64), 4, 0, 0);
             }
         };
+        // Loads per chunk fill of this producer: kDma, or kDma - 2 when its
+        // region skips the zero halves of the two triangular tiles.
+        const bool lean = Z::zero(cw);
+        auto wait_fill = [&]() {
+            if (lean) wait_counts<2 * kTouch + kDma - 2, 15>();
+            else wait_counts<2 * kTouch + kDma, 15>();
+        };
         // One step j: open it; after the compute waves' first inner barrier
         // (chunk j's operands are in their registers) refill chunk j's buffer
         // with chunk j+2, part of the loads before their second inner barrier
@@ -1212,7 +1261,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             if (fill) issue(buf, j + 2, Cut{}, AllN{});
             touch(j);
             if (fill)
-                wait_counts<2 * kTouch + kDma, 15>();
+                wait_fill();
             else
                 wait_counts<2 * kTouch, 15>();
         };
@@ -1222,7 +1271,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             touch(-2);
             touch(-1);
             if (nch > 1)   // chunk 0 has landed
-                wait_counts<2 * kTouch + kDma, 15>();
+                wait_fill();
             else
                 wait_counts<2 * kTouch, 15>();
             for (int j = 0; j < nch; j += 2) {
@@ -1303,10 +1352,16 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             }
         }
         F ftb[G::NKT], fmm[G::NKT], fkt[RT][G::NKT];
+        const bool zh = Z::zero(w);
 #pragma unroll
         for (int m = 0; m < G::NKT; ++m) {
-            ftb[m] = fr[(L::kTb + m) * 64];
-            fmm[m] = fr[(L::kMm + m) * 64];
+            if (m == Z::kHalf && zh) {
+                ftb[m] = F{};
+                fmm[m] = F{};
+            } else {
+                ftb[m] = fr[(L::kTb + m) * 64];
+                fmm[m] = fr[(L::kMm + m) * 64];
+            }
         }
 #pragma unroll
         for (int a = 0; a < RT; ++a)
@@ -1395,7 +1450,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         }
         F fmt[G::NKT];
 #pragma unroll
-        for (int m = 0; m < G::NKT; ++m) fmt[m] = fr[(L::kMm + m) * 64];
+        for (int m = 0; m < G::NKT; ++m) fmt[m] = (m == Z::kHalf && Z::zero(w)) ? F{} : fr[(L::kMm + m) * 64];
         // R = K^ dS' + M^T dO  (rows 16w..), transposed to LDS
         f32x4 accR = zero4();
 #pragma unroll
@@ -1410,7 +1465,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         }
         F ftt[G::NKT], fqt[RT][G::NKT], fkt[RT][G::NKT];
 #pragma unroll
-        for (int m = 0; m < G::NKT; ++m) ftt[m] = fr[(L::kTb + m) * 64];
+        for (int m = 0; m < G::NKT; ++m) ftt[m] = (m == Z::kHalf && Z::zero(w)) ? F{} : fr[(L::kTb + m) * 64];
 #pragma unroll
         for (int a = 0; a < RT; ++a)
 #pragma unroll

@@ -10,7 +10,8 @@ found from the published workspace sizes and the library's documented carve
 order, and the fragment-major tiles are decoded here.  Every stage is
 compared per chunk as max|gpu - ref| / max|ref| <= 1e-2 (bf16 storage),
 and the triangular inverse is checked directly: (I + A) T diag(beta) =
-diag(beta) with A from the model.
+diag(beta) with A from the model.  The halves of the triangular tiles that
+are zero by structure are not stored and are left out of the comparison.
 """
 import sys
 
@@ -168,6 +169,16 @@ def test_stages_match_chunked_model(torch_dev, lengths, H, d):
             ref["Y"] = Vv - (Kv * Gam) @ r["S_in"]
             got["Ut"] = Ug[c0:c1, h]
             ref["Ut"] = r["Ut"]
+            # bf16 tiles: the 32-token halves that are zero by structure are
+            # not stored (rows 0..31 x tokens 32..63 of the lower-triangular
+            # T diag(beta) and M; rows 32..63 x tokens 0..31 of T^T and M^T);
+            # the reference is zero there, so the unwritten bytes are left out
+            for key in ("TB", "M"):
+                got[key][:32, 32:] = 0.0
+                assert not np.any(ref[key][:32, 32:])
+            for key in ("bTT", "bMT"):
+                got[key][32:, :32] = 0.0
+                assert not np.any(ref[key][32:, :32])
             for key in ref:
                 worst[key] = max(worst.get(key, 0.0), _err(got[key], ref[key]))
             # the inverse itself: (I + A) (T diag(beta)) = diag(beta)
