@@ -40,7 +40,10 @@ def kernel_bytes_per_token_head(name, C, D, es=2):
     """Algorithmic bytes each kernel of this design moves per (token, head):
     its inputs read once and its outputs written once (the value-column slabs
     of one head re-read the chunk operands through L2; that is not counted)."""
-    ops = 3 * es * D + 2 * es * C + 4 * D / C     # Q.Gamma, K.Gamma, K^T, T diag(beta), M, Gamma_L
+    # the two C x C triangular tiles: bf16 moves them without the 32-token
+    # halves that are zero by structure (3/4 of each at C = 64), fp32 whole
+    tri = 2 * es * C * (0.75 if es == 2 and C == 64 else 1.0)
+    ops = 3 * es * D + tri + 4 * D / C            # Q.Gamma, K.Gamma, K^T, T diag(beta), M, Gamma_L
     return {
         "k_prep": (3 * es * D + es) + ops,        # q, k, g, beta -> chunk operands
         "k_recur": ops + es * D + es * D,         # chunk operands, v -> o
