@@ -52,6 +52,8 @@ size_t carve_workspace(Plan* p, void* base) {
         p->ws_dZ = take(2 * T * H * D);
         p->ws_dbp = (float*)take(4 * 2 * T * H);
     }
+    // last, so that the regions above keep their offsets
+    p->ws_prog = (int32_t*)take(4 * (size_t)p->n_seqs * H * (D / 16));
     return off;
 }
 

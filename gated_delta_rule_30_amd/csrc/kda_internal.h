@@ -59,6 +59,7 @@ struct Plan {
     void* ws_ckdS;            // [H, max_chunks, D, D] gradient of each chunk's outgoing state (bf16)
     void *ws_Y, *ws_U, *ws_dZ;   // [T, H, D] bf16: Y, U~ and dZ per token
     float* ws_dbp;            // [2, H, T] float32 dbeta shares of the two channel halves
+    int32_t* ws_prog;         // [n_seqs * H, d_v / 16] steps done per recurrence workgroup (pacing)
 };
 
 // Arguments of the per-chunk gradient kernel (kda_bwd.hip); bf16 tensors.

@@ -952,7 +952,8 @@ __device__ inline void static_for(Fn&& f) {
 constexpr int kRecurWaves = 4;                              // compute waves
 constexpr int kProdPerWave = 1;                             // producer waves per compute wave
 constexpr int kProducers = kRecurWaves * kProdPerWave;
-constexpr int kRecurLdsThreads = (kRecurWaves + kProducers) * 64;
+constexpr int kPacerWave = kRecurWaves + kProducers;        // the pacing wave (see k_recur_lds)
+constexpr int kRecurLdsThreads = (kRecurWaves + kProducers + 1) * 64;
 
 // Buffer layout: one region per compute wave w, in 1 KB blocks (64 lanes x
 // 16 bytes: the fragment-major tiles of k_prep copied as they are):
@@ -1012,6 +1013,7 @@ struct RecurAux {
     const float* bet;  // kBwd: per-chunk beta (ChunkOps::bet)
     float* sck;        // kFwdCk: fp32 state after every `every`-th chunk, slot = global chunk index
     int32_t every;
+    int32_t* prog;     // pacing: steps done per (sequence*head, slab), or NULL (no pacing)
 };
 
 // The two triangular tiles of a region (T diag(beta) and M in the forward
@@ -1084,6 +1086,65 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     // chunk processed at step s (the backward pass walks the chunks last to first)
     auto chunk_at = [&](int s_) -> int { return kBack ? nch - 1 - s_ : s_; };
 
+    if (w == kPacerWave) {
+        // ------------------------------------------------ pacing wave
+        // The slab workgroups of a head share their chunk operands through
+        // L2: each warms only its share of the lines ahead of use.  One that
+        // falls further behind than L2 holds those lines loses that support,
+        // misses on the other shares and falls further behind, so over a long
+        // sequence the drift, not the step, sets the kernel time.  This wave
+        // passes the same three barriers per step as the others (so it is at
+        // the workgroup's step), and every kPaceEvery steps compares its
+        // step count with its siblings' published counts, sleeps while it is
+        // more than kPaceLag steps ahead of the slowest (which holds the
+        // whole workgroup at the next barrier), then publishes its own.  Every wait ends: at most
+        // kPaceBudget sleeps per workgroup.  Counts outside 0..nch (the
+        // sentinel written at the end of a call, or memory never written)
+        // are ignored.
+        // Drift needs thousands of steps to build up; shorter sequences are
+        // not paced at all (this wave then only passes the barriers).
+        constexpr int kPaceEvery = 8, kPaceLead = 4, kPaceLag = 16, kPaceBudget = 1024, kPaceMinChunks = 2048;
+        int32_t* const pg = (aux.prog && nch >= kPaceMinChunks) ? aux.prog + (int64_t)nh * NS : nullptr;
+        auto post = [&](int v) {
+            if (pg && lane == 0) __hip_atomic_store(pg + sl, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        auto load = [&]() {
+            return lane < NS ? __hip_atomic_load(pg + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : 0x7fffffff;
+        };
+        auto slowest = [&](int v) {
+            v = (v < 0 || v > nch) ? 0x7fffffff : v;
+            v = min(v, __shfl_xor(v, 1));
+            v = min(v, __shfl_xor(v, 2));
+            v = min(v, __shfl_xor(v, 4));
+            return __builtin_amdgcn_readfirstlane(v);
+        };
+        // The counts are read kPaceLead steps before they are used, and this
+        // wave's own count is published right after each check, so that the
+        // wait for a load never covers a recent store (both are device-scope
+        // accesses, with a long latency).  The counts seen are then up to
+        // kPaceEvery + kPaceLead - 1 steps old, which kPaceLag allows for.
+        int left = kPaceBudget;
+        int seen = 0;
+        post(0);
+        for (int s_ = 0; s_ < nch; ++s_) {
+            const bool on = pg && s_ + 1 < nch;
+            barrier_lds();
+            if (on && (s_ % kPaceEvery) == kPaceEvery - 1 - kPaceLead) seen = load();
+            barrier_lds();
+            barrier_lds();
+            if (on && (s_ % kPaceEvery) == kPaceEvery - 1) {
+                // sleep in proportion to the excess lead (about 0.4 us per
+                // step), rather than until the slowest sibling publishes again
+                const int excess = s_ + 1 - kPaceLag - slowest(seen);
+                for (int n = excess > 0 ? min(2 * excess, 40) : 0; n > 0 && left > 0; --n, --left)
+                    __builtin_amdgcn_s_sleep(8);
+                post(s_ + 1);
+            }
+        }
+        post(0x7fffffff);
+        return;
+    }
     if (w >= kRecurWaves) {
         // ------------------------------------------------ producer waves
         const int pw = w - kRecurWaves;
@@ -1562,6 +1623,7 @@ template <int D, int kMode>
 static void launch_recur_lds(const Plan& p, const void* v, const float* S0, float* ST, void* o, RecurAux aux,
                              hipStream_t st) {
     const int32_t NH = p.n_seqs * p.n_heads;
+    aux.prog = p.ws_prog;
     hipLaunchKernelGGL((k_recur_lds<D, kMode>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st,
                        static_cast<const __bf16*>(v), kMode == kBwd ? chunk_ops_bwd(p) : chunk_ops(p),
                        p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, p.n_heads, S0, ST,
