@@ -920,6 +920,9 @@ __global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, Chu
 // workgroups of a head take disjoint shares, so the direct loads of every
 // slab later hit L2 rather than HBM.  Landing in LDS, these loads hold no
 // registers and nothing waits for them except the counted waits below.
+// Because of that sharing the slabs of a head have to stay within a few
+// steps of each other; on long sequences a ninth wave per workgroup (the
+// pacing wave) holds back a workgroup that runs too far ahead.
 #define KDA_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
