@@ -13,6 +13,7 @@ on), and the fp64 CPU oracle timed on a bounded sample of the same inputs.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -57,10 +58,16 @@ KERNEL_SOURCES = {"k_prep": ("kda_kernels.hip", "kda_device.h"), "k_recur": ("kd
 
 
 def source_sha(files=("kda_kernels.hip", "kda_device.h")):
+    """Hash of the kernels' code: comments and blank lines are left out, so
+    that a comment edit does not invalidate counters taken on the same code."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "gated_delta_rule_30_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "gated_delta_rule_30_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        lines = [ln.rstrip() for ln in text.splitlines() if ln.strip()]
+        h.update("\n".join(lines).encode())
     return h.hexdigest()[:16]
 
 
