@@ -217,3 +217,38 @@ def test_backward_config3_sampled(torch_dev):
             _say("  seq %d (len %d) head %d: " % (n, b - a, h) + " ".join("%s=%.2e" % (key, e[key]) for key in KEYS))
             for key in KEYS:
                 assert e[key] <= TOL, "%s parity %.3e > %.0e (seq %d head %d)" % (key, e[key], TOL, n, h)
+
+
+def test_long_sequence_paced_sampled(torch_dev):
+    """One 131,072-token sequence: 2048 chunks, so the recurrence's slab
+    workgroups pace each other (in the forward, the checkpointing forward and
+    the state-gradient pass).  H=4, d=64, S0 ~ 0.02 N(0,1); the forward and
+    the backward run over all heads, head 2 is checked in full against the
+    oracle (o and S_T, and every gradient)."""
+    torch, dev = torch_dev
+    import gated_delta_rule_30_amd as kda
+    spec = ki.custom("paced", "bf16", [131072], 4, 64, s0_std=0.02, varlen=False, seed=9)
+    inp = ki.generate_torch(spec, dev)
+    T, H, d, N = spec.total_tokens, spec.n_heads, spec.d_k, spec.n_seqs
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(spec.seed + 77)
+    dO = torch.randn((T, H, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    dST = torch.randn((N, H, d, d), generator=gen, device=dev, dtype=torch.float32)
+    _say("paced long sequence: T=131072 H=4 d=64")
+    o, S_T = kda.chunk_fwd(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, n_seqs=N)
+    out = kda.chunk_bwd(inp.q, inp.k, inp.v, inp.beta, inp.g, dO, S0=inp.S0, dS_T=dST, n_seqs=N)
+    torch.cuda.synchronize()
+    h = 2
+    host = lambda x: x[:, h:h + 1].float().cpu().numpy()
+    S0h = inp.S0[:, h:h + 1].cpu().numpy()
+    t0 = time.time()
+    o_ref, S_ref = oracle.forward(host(inp.q), host(inp.k), host(inp.v), host(inp.beta), host(inp.g), S0h)
+    ref = oracle.backward(host(inp.q), host(inp.k), host(inp.v), host(inp.beta), host(inp.g), host(dO), S0h,
+                          dST[:, h:h + 1].cpu().numpy())
+    e = {"o": oracle.parity_error(host(o), o_ref), "S_T": oracle.parity_error(S_T[:, h:h + 1].cpu().numpy(), S_ref)}
+    e.update({key: oracle.parity_error(host(out[key]), ref[key]) for key in ("dq", "dk", "dv", "dg")})
+    e["dbeta"] = oracle.parity_error(host(out["dbeta"])[:, :, None], ref["dbeta"][:, :, None])
+    e["dS0"] = oracle.parity_error(out["dS0"][:, h:h + 1].cpu().numpy(), ref["dS0"])
+    _say("  head %d: " % h + " ".join("%s=%.2e" % kv for kv in e.items()) + "  (oracle %.1fs)" % (time.time() - t0))
+    for key, err in e.items():
+        assert err <= TOL, "%s parity %.3e > %.0e" % (key, err, TOL)
