@@ -297,6 +297,8 @@ def main():
     ap.add_argument("--profile-reps", type=int, default=10)
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time only the forward pass (no backward, epilogue, decode or sequence-parallel legs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES bytes 3 times (yardstick for the "
                          "profiler's HBM byte counters) and exit")
@@ -388,12 +390,13 @@ def main():
         "stage_ms": stage_ms, "roofline": roof, "wall_s_timed": wall,
         "device": torch.cuda.get_device_name(dev), "source_sha": source_sha(),
     }
-    if spec.dtype == "bf16":
+    if spec.dtype == "bf16" and not args.forward_only:
         out["backward"] = backward_measure(torch, kda, inp, cu, spec)
         out["backward"]["vs_forward"] = out["backward"]["ms_per_pass"] / ms
-    out["epilogue"] = epilogue_measure(torch, kda, o)
-    out["decode"] = decode_measure(torch, kda, dev)
-    if spec.dtype == "bf16" and spec.n_seqs == 1:
+    if not args.forward_only:
+        out["epilogue"] = epilogue_measure(torch, kda, o)
+        out["decode"] = decode_measure(torch, kda, dev)
+    if spec.dtype == "bf16" and spec.n_seqs == 1 and not args.forward_only:
         out["sequence_parallel"] = seqpar_measure(torch, kda, inp, ms)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_heads, H))
