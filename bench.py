@@ -140,11 +140,34 @@ def decode_measure(torch, kda, dev, reps=50):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / reps * 1e3
     nbytes = N * H * (2 * d * d * 4 + n * (4 * d * 2 + 2 + d * 2))
-    return {"workload": "decode, bf16, N=%d sequences x %d token, H=%d, d=%d, fp32 state in place" % (N, n, H, d),
-            "us_per_call": us, "tokens_per_s": N * n / (us * 1e-6),
-            "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                         "algorithmic_bytes_per_call": nbytes}}
+    out = {"workload": "decode, bf16, N=%d sequences x %d token, H=%d, d=%d, fp32 state in place" % (N, n, H, d),
+           "us_per_call": us, "tokens_per_s": N * n / (us * 1e-6),
+           "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                        "algorithmic_bytes_per_call": nbytes}}
+    # speculative decoding: verify a 4-token draft from the kept state into a
+    # scratch state, then commit each sequence's accepted prefix in place
+    nd = 4
+    qd, kd, vd, bd, ld = (x.repeat(nd, *([1] * (x.dim() - 1))) for x in (q, k, v, beta, la))
+    od = torch.empty_like(vd)
+    S_draft = torch.empty_like(S)
+    acc = torch.randint(0, nd + 1, (N,), generator=g, device=dev, dtype=torch.int32)
+    def spec_step():
+        kda.recurrent_fwd(qd, kd, vd, bd, ld, S_in=S, S_out=S_draft, n_seqs=N, o=od)
+        kda.recurrent_fwd(qd, kd, vd, bd, ld, S_in=S, S_out=S, n_seqs=N, n_accept=acc, want_o=False)
+    for _ in range(3):
+        spec_step()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        spec_step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    out["speculative"] = {"workload": "verify a %d-token draft into a scratch state, then commit each sequence's "
+                                      "accepted prefix (0..%d, drawn once) in place; N=%d, H=%d, d=%d" % (nd, nd, N, H, d),
+                          "us_per_verify_and_commit": e0.elapsed_time(e1) / reps * 1e3,
+                          "mean_accepted": float(acc.float().mean().item())}
+    return out
 
 
 def seqpar_measure(torch, kda, inp, ms_single, reps=3):
