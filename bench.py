@@ -71,10 +71,10 @@ def source_sha(files=("kda_kernels.hip", "kda_device.h")):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel, workload_key):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+def _profile_record(fname, kernel, workload_key):
+    """Entry `kernel|workload_key` of a committed counter summary under
+    profiles/ when it was taken on the current kernel source, else None."""
+    path = os.path.join(ROOT, "profiles", fname)
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -82,7 +82,26 @@ def traffic_for(kernel, workload_key):
     ent = rec.get(kernel + "|" + workload_key)
     if not ent or ent.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
         return None
-    return ent["bytes_per_launch"]
+    return ent
+
+
+def traffic_for(kernel, workload_key):
+    """HBM bytes per launch (rocprofv3 FETCH_SIZE and WRITE_SIZE, scaled by a
+    plain copy's readings) from profiles/traffic.json, if they were taken on
+    the current kernel source; else None."""
+    ent = _profile_record("traffic.json", kernel, workload_key)
+    return None if ent is None else ent["bytes_per_launch"]
+
+
+def mfma_counters_for(kernel, workload_key):
+    """Counter-based MFMA figures of one launch from profiles/mfma.json (taken
+    on the current kernel source, else None): executed MFMA FLOP
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 + _F32, x 512 each) and the busy fraction
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs)."""
+    ent = _profile_record("mfma.json", kernel, workload_key)
+    if ent is None:
+        return None
+    return {k: ent[k] for k in ("mfma_flop_executed", "mfma_busy_frac", "gui_active_cycles", "note") if k in ent}
 
 
 def grad_bytes_per_token_head(C, D, es=2):
@@ -112,11 +131,14 @@ def cpu_baseline(inp, n_heads_sample):
             "seconds": dt}
 
 
-def decode_measure(torch, kda, dev, reps=50):
-    """Serving decode step: 64 sequences x 32 heads, d=128, bf16, one token per
+def decode_measure(torch, kda, dev, reps=50, N=64):
+    """Serving decode step: N sequences x 32 heads, d=128, bf16, one token per
     sequence per call, state updated in place.  Bound by moving the fp32 state
-    (read + write 2 d^2 4 B per sequence and head)."""
-    N, H, d, n = 64, 32, 128, 1
+    (read + write 2 d^2 4 B per sequence and head).  At N = 64 the state is
+    128 MiB and stays in the GPU's 256 MB last-level (Infinity) cache across
+    repeated calls, so that leg is a cache-resident rate, not an HBM one; at
+    N = 256 (512 MiB) every call streams the state from HBM."""
+    H, d, n = 32, 128, 1
     g = torch.Generator(device=dev)
     g.manual_seed(1)
     def rnd(*shape):
@@ -140,11 +162,20 @@ def decode_measure(torch, kda, dev, reps=50):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / reps * 1e3
     nbytes = N * H * (2 * d * d * 4 + n * (4 * d * 2 + 2 + d * 2))
-    out = {"workload": "decode, bf16, N=%d sequences x %d token, H=%d, d=%d, fp32 state in place" % (N, n, H, d),
+    state_mib = N * H * d * d * 4 / 2 ** 20
+    resident = state_mib < 256 * 1e6 / 2 ** 20
+    out = {"workload": "decode, bf16, N=%d sequences x %d token, H=%d, d=%d, fp32 state in place (%d MiB)"
+                       % (N, n, H, d, state_mib),
            "us_per_call": us, "tokens_per_s": N * n / (us * 1e-6),
-           "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
+           "roofline": {"bound": "last-level cache (state resident across calls)" if resident else "hbm",
+                        "achieved": nbytes / (us * 1e-6) / 1e9, "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
-                        "algorithmic_bytes_per_call": nbytes}}
+                        "algorithmic_bytes_per_call": nbytes,
+                        "note": ("the %d MiB state fits the 256 MB Infinity Cache, so repeated calls may be served "
+                                 "from it: this frac is against the HBM peak but is not an HBM stream" % state_mib)
+                                if resident else "state larger than the 256 MB Infinity Cache: streamed from HBM"}}
+    if N != 64:
+        return out
     # speculative decoding: verify a 4-token draft from the kept state into a
     # scratch state, then commit each sequence's accepted prefix in place
     nd = 4
@@ -267,17 +298,22 @@ def backward_measure(torch, kda, inp, cu, spec, reps=5, profile_reps=3):
         tb += ev[1].elapsed_time(ev[2]) / reps
     del ctx, fws, bws
     wkey = "%s_N%d_H%d_T%d_d%d" % (spec.dtype, N, H, T, dk)
-    kb = grad_bytes_per_token_head(C, dk) * T * H
-    roof = {"bound": "hbm", "kernel": "k_grad", "achieved": kb / (stage_ms["k_grad"] * 1e-3) / 1e9,
-            "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    # the method's minimum per (token, head): read q, k, log_alpha, v, beta,
+    # dO; write dq, dk, dlog_alpha, dv, dbeta (bf16)
+    min_b = 2 * (3 * dk + 2 * dv + 1) + 2 * (3 * dk + dv + 1)
+    roof = {"bound": "hbm", "kernel": "kda_chunk_bwd pass (" + " + ".join(stage_ms) + ")",
+            "achieved": min_b * T * H / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_for("k_grad", wkey)
-    roof["kernel_ms"] = stage_ms["k_grad"]
-    roof["algorithmic_bytes_per_launch"] = kb
+    roof["traffic"] = None
+    roof["algorithmic_bytes_per_launch"] = min_b * T * H
+    roof["bytes_per_token_head"] = min_b
+    kb = grad_bytes_per_token_head(C, dk) * T * H
+    k_grad = {"ms": stage_ms["k_grad"], "design_bytes_per_token_head": grad_bytes_per_token_head(C, dk),
+              "design_gbs": kb / (stage_ms["k_grad"] * 1e-3) / 1e9, "hbm_bytes_counted": traffic_for("k_grad", wkey)}
     return {"workload": "KDA chunked backward (dq, dk, dv, dbeta, dlog_alpha, dS0) of the same forward, "
                         "dO ~ N(0,1), dS_T ~ N(0,1); forward re-evaluated inside",
             "ms_per_pass": ms, "tokens_per_s": T / (ms * 1e-3), "vs_forward": None, "stage_ms": stage_ms,
-            "roofline": roof, "source_sha": source_sha(KERNEL_SOURCES["k_grad"]),
+            "roofline": roof, "k_grad": k_grad, "source_sha": source_sha(KERNEL_SOURCES["k_grad"]),
             "training_pair": {"fwd_train_ms": tf, "bwd_ctx_ms": tb, "step_ms": tf + tb,
                               "note": "kda_chunk_fwd_train keeps the backward's inputs in a context; "
                                       "kda_chunk_bwd_ctx does not evaluate the forward again"}}
@@ -387,18 +423,44 @@ def main():
     F = flop_per_token_head(C, dk, dv)
     tflops = token_heads * F / (ms * 1e-3) / 1e12
     tokens_s = T / (ms * 1e-3)
-    pass_bytes = token_heads * min_bytes_per_token_head(dk, dv, 2 if spec.dtype == "bf16" else 4)
+    es = 2 if spec.dtype == "bf16" else 4
+    bpth = min_bytes_per_token_head(dk, dv, es)
+    pass_bytes = token_heads * bpth
     workload = ("KDA chunked forward, %s inputs / fp32 state, N=%d H=%d T_total=%d d_k=d_v=%d, chunk %d "
                 "(16-token sub-tiles), %s" % (spec.dtype, spec.n_seqs, H, T, dk, C,
                                               "S0 ~ 0.02 N(0,1)" if spec.s0_std else "zero S0"))
     wkey = "%s_N%d_H%d_T%d_d%d" % (spec.dtype, spec.n_seqs, H, T, dk)
-    kb = kernel_bytes_per_token_head(dom, C, dk, 2 if spec.dtype == "bf16" else 4) * token_heads
-    roof = {"bound": "hbm", "kernel": dom, "achieved": kb / (stage_ms[dom] * 1e-3) / 1e9,
-            "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    # The roofline of the whole pass (one kda_chunk_fwd call = k_chunk_table
+    # when cu_seqlens is given, k_prep, k_recur, all on this stream): the
+    # minimum bytes of the method per (token, head) -- read q, k, log_alpha,
+    # v, beta, write o -- over the measured time per pass.
+    kernels = [k_ for k_ in ("k_chunk_table", "k_prep", "k_recur") if k_ in stage_ms]
+    traffic = [traffic_for(k_, wkey) for k_ in ("k_prep", "k_recur")]
+    roof = {"bound": "hbm", "kernel": "kda_chunk_fwd pass (" + " + ".join(kernels) + ")",
+            "achieved": pass_bytes / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = traffic_for(dom, wkey)
-    roof["kernel_ms"] = stage_ms[dom]
-    roof["algorithmic_bytes_per_launch"] = kb
+    roof["traffic"] = None if any(t is None for t in traffic) else sum(traffic)
+    roof["algorithmic_bytes_per_launch"] = pass_bytes
+    roof["bytes_per_token_head"] = bpth
+    roof["pass_ms"] = ms
+    # Per kernel: HIP-event time, the bytes this design moves per (token,
+    # head) (k_prep writes the chunk operands that k_recur reads back; these
+    # are not the method's minimum), and counter-based MFMA figures.
+    per_kernel = {}
+    n_chunk_steps = -(-(T // spec.n_seqs) // C)
+    for k_ in kernels:
+        ent = {"ms": stage_ms[k_]}
+        if k_ != "k_chunk_table":
+            db = kernel_bytes_per_token_head(k_, C, dk, es)
+            ent["design_bytes_per_token_head"] = db
+            ent["design_gbs"] = db * token_heads / (stage_ms[k_] * 1e-3) / 1e9
+            ent["hbm_bytes_counted"] = traffic_for(k_, wkey)
+            ent["mfma_counters"] = mfma_counters_for(k_, wkey)
+        if k_ == "k_recur":
+            ent["limiter"] = "the serial chain: %d chunk steps per (sequence, head), each fed its chunk's " \
+                             "operands from L2 into every 16-column slab workgroup" % n_chunk_steps
+            ent["us_per_chunk_step"] = stage_ms[k_] * 1e3 / n_chunk_steps
+        per_kernel[k_] = ent
 
     out = {
         "metric": METRIC, "value": tokens_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -408,9 +470,7 @@ def main():
                    "d_k": dk, "d_v": dv, "chunk": C, "parallelism": "single GPU"},
         "tflops": tflops, "mfma_peak_tflops": PEAK_BF16_TFLOPS, "mfma_frac": tflops / PEAK_BF16_TFLOPS,
         "flop_per_token_head": F,
-        "pass_hbm_gbs_algorithmic": pass_bytes / (ms * 1e-3) / 1e9,
-        "pass_hbm_frac": pass_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-        "stage_ms": stage_ms, "roofline": roof, "wall_s_timed": wall,
+        "stage_ms": stage_ms, "roofline": roof, "kernels": per_kernel, "wall_s_timed": wall,
         "device": torch.cuda.get_device_name(dev), "source_sha": source_sha(),
     }
     if spec.dtype == "bf16" and not args.forward_only:
@@ -419,6 +479,7 @@ def main():
     if not args.forward_only:
         out["epilogue"] = epilogue_measure(torch, kda, o)
         out["decode"] = decode_measure(torch, kda, dev)
+        out["decode_hbm"] = decode_measure(torch, kda, dev, N=256)
     if spec.dtype == "bf16" and spec.n_seqs == 1 and not args.forward_only:
         out["sequence_parallel"] = seqpar_measure(torch, kda, inp, ms)
     if not args.no_cpu_baseline:

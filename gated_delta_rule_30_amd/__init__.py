@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["chunk_fwd", "chunk_fwd_profile", "chunk_bwd", "chunk_bwd_profile", "chunk_fwd_train", "train_context_size", "output_gate", "bwd_stage_names", "bwd_workspace_size", "recurrent_fwd", "validate_inputs", "chunk_transition",
+__all__ = ["chunk_fwd", "chunk_fwd_profile", "chunk_fwd_ckpt", "ckpt_slots", "ckpt_size", "chunk_bwd", "chunk_bwd_profile", "chunk_fwd_train", "train_context_size", "output_gate", "bwd_stage_names", "bwd_workspace_size", "recurrent_fwd", "validate_inputs", "chunk_transition",
            "compose_states", "sequence_parallel_fwd", "stage_names", "workspace_size", "status_string", "lib_path",
            "KDA_F32", "KDA_BF16", "KdaError"]
 
@@ -86,10 +86,10 @@ def _load():
         lib.kda_chunk_bwd_ctx.restype = ctypes.c_int
         lib.kda_output_gate.argtypes = [ctypes.c_int, I64, I32, P, P, P, ctypes.c_float, P, P]
         lib.kda_output_gate.restype = ctypes.c_int
-        lib.kda_chunk_ckpt_size.argtypes = [I64, I32, I32, I32, I32]
+        lib.kda_chunk_ckpt_size.argtypes = [I64, I32, I32, I32, I32, I32]
         lib.kda_chunk_ckpt_size.restype = SZ
         lib.kda_chunk_fwd_ckpt.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, I32,
-                                           P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P]
+                                           P, P, P, P, P, P, P, P, P, I32, P, SZ, P, SZ, P]
         lib.kda_chunk_fwd_ckpt.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -112,6 +112,76 @@ def _ptr(t):
 def stage_names():
     lib = _load()
     return [lib.kda_profile_stage_name(i).decode() for i in range(lib.kda_profile_num_stages())]
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _fwd_problem(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, n_seqs=None, dtypes=None):
+    """Checks the forward-shaped arguments every entry point shares, before
+    anything is launched: one float dtype (in `dtypes` when given); q, k,
+    log_alpha [T, H, d_k] and v [T, H, d_v], beta [T, H] (or the same with a
+    leading batch axis B); cu_seqlens a contiguous 1-D int32 tensor of N + 1
+    offsets; S0 contiguous float32 [N, H, d_k, d_v]; everything contiguous
+    on one GPU.  The C ABI sees only pointers, so an extent it cannot check
+    would become an out-of-bounds access on the device.  Extents and dtypes
+    are checked before devices.  Returns a namespace with the flattened 3-D
+    tensors, dt, dev, T, H, dk, dv, N, batched and B."""
+    import torch
+    from types import SimpleNamespace
+    dt = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}.get(q.dtype)
+    if dt is None or (dtypes is not None and q.dtype not in dtypes):
+        raise TypeError("q has unsupported dtype %s" % q.dtype)
+    for name, t in (("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha)):
+        if t.dtype != q.dtype:
+            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
+    if q.dim() not in (3, 4):
+        raise ValueError("q must be [T, H, d_k] or [B, T, H, d_k], got shape %s" % (tuple(q.shape),))
+    batched = q.dim() == 4
+    B = q.shape[0] if batched else 1
+    if batched:
+        if v.dim() != 4 or beta.dim() != 3 or k.dim() != 4 or log_alpha.dim() != 4:
+            raise ValueError("4-D q needs 4-D k, v, log_alpha and 3-D beta (shape)")
+        q, k, v, log_alpha = (t.reshape(-1, *t.shape[2:]) for t in (q, k, v, log_alpha))
+        beta = beta.reshape(-1, beta.shape[-1])
+    T, H, dk = q.shape
+    if v.dim() != 3:
+        raise ValueError("v must have as many axes as q (shape %s)" % (tuple(v.shape),))
+    dv = v.shape[-1]
+    if k.shape != (T, H, dk) or log_alpha.shape != (T, H, dk) or v.shape != (T, H, dv) or beta.shape != (T, H):
+        raise ValueError("inconsistent shapes q%s k%s v%s beta%s log_alpha%s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(beta.shape),
+                            tuple(log_alpha.shape)))
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_contiguous() \
+                or cu_seqlens.numel() < 2:
+            raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor of N + 1 >= 2 offsets")
+        N = cu_seqlens.numel() - 1
+    else:
+        N = int(n_seqs) if n_seqs is not None else B
+    if S0 is not None and (S0.dtype != torch.float32 or S0.shape != (N, H, dk, dv) or not S0.is_contiguous()):
+        raise ValueError("S0 must be contiguous float32 [%d, %d, %d, %d]" % (N, H, dk, dv))
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be on a GPU device")
+    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha),
+                    ("cu_seqlens", cu_seqlens), ("S0", S0)):
+        if t is not None and (t.device != dev or not t.is_contiguous()):
+            raise ValueError("%s must be contiguous on %s" % (name, dev))
+    return SimpleNamespace(q=q, k=k, v=v, beta=beta, log_alpha=log_alpha, dt=dt, dev=dev, T=T, H=H, dk=dk,
+                           dv=dv, N=N, batched=batched, B=B)
+
+
+def _check_out(name, t, shape, dtype, dev):
+    if t is not None and (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev
+                          or not t.is_contiguous()):
+        raise ValueError("%s must be contiguous %s %s on %s" % (name, dtype, list(shape), dev))
+
+
+def _check_buffer(name, t, nbytes, dev):
+    if t is not None and (t.device != dev or not t.is_contiguous() or _nbytes(t) < nbytes):
+        raise ValueError("%s must be a contiguous tensor of at least %d bytes on %s" % (name, nbytes, dev))
 
 
 def chunk_fwd_profile(*args, **kw):
@@ -137,63 +207,30 @@ def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = C
     """
     import torch
     lib = _load()
-    dt = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}.get(q.dtype)
-    if dt is None:
-        raise TypeError("q must be float32 or bfloat16, got %s" % q.dtype)
-    for name, t in (("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha)):
-        if t.dtype != q.dtype:
-            raise TypeError("%s has dtype %s, expected %s" % (name, t.dtype, q.dtype))
-    batched = q.dim() == 4
-    if batched:
-        B = q.shape[0]
-        q, k, v, log_alpha = (t.reshape(-1, *t.shape[2:]) for t in (q, k, v, log_alpha))
-        beta = beta.reshape(-1, beta.shape[-1])
-    T, H, dk = q.shape
-    dv = v.shape[-1]
-    if k.shape != (T, H, dk) or log_alpha.shape != (T, H, dk) or v.shape != (T, H, dv) or beta.shape != (T, H):
-        raise ValueError("inconsistent shapes q%s k%s v%s beta%s log_alpha%s"
-                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(beta.shape),
-                            tuple(log_alpha.shape)))
-    dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("inputs must be on a GPU device")
-    for name, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("log_alpha", log_alpha)):
-        if t.device != dev or not t.is_contiguous():
-            raise ValueError("%s must be contiguous on %s" % (name, dev))
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
-            raise ValueError("cu_seqlens must be a 1-D int32 tensor on %s" % dev)
-        N = cu_seqlens.numel() - 1
-    else:
-        N = n_seqs if n_seqs is not None else (B if batched else 1)
-    if S0 is not None:
-        if S0.dtype != torch.float32 or S0.shape != (N, H, dk, dv) or S0.device != dev or not S0.is_contiguous():
-            raise ValueError("S0 must be contiguous float32 [%d, %d, %d, %d] on %s" % (N, H, dk, dv, dev))
+    P = _fwd_problem(q, k, v, beta, log_alpha, S0, cu_seqlens, n_seqs)
+    q, k, v, beta, log_alpha = P.q, P.k, P.v, P.beta, P.log_alpha
+    dt, dev, T, H, dk, dv, N, batched, B = P.dt, P.dev, P.T, P.H, P.dk, P.dv, P.N, P.batched, P.B
     ws_bytes = int(lib.kda_chunk_fwd_workspace_size(T, N, H, dk, dv, chunk, dt))
     if ws_bytes == 0:
         code = lib.kda_chunk_fwd(dt, T, N, H, dk, dv, chunk, None, None, None, None, None, None, None,
                                  None, None, None, 0, None)
         raise KdaError(code, lib.kda_status_string(code).decode())
+    _check_buffer("workspace", workspace, ws_bytes, dev)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    elif workspace.device != dev or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on %s" % dev)
+    _check_out("o", o, (T, H, dv), q.dtype, dev)
     if o is None:
         o = torch.empty((T, H, dv), dtype=q.dtype, device=dev)
-    elif o.shape != (T, H, dv) or o.dtype != q.dtype or o.device != dev or not o.is_contiguous():
-        raise ValueError("o must be contiguous %s [%d, %d, %d] on %s" % (q.dtype, T, H, dv, dev))
+    _check_out("S_T", S_T, (N, H, dk, dv), torch.float32, dev)
     if output_final_state and S_T is None:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    elif S_T is not None and (S_T.shape != (N, H, dk, dv) or S_T.dtype != torch.float32 or S_T.device != dev
-                              or not S_T.is_contiguous()):
-        raise ValueError("S_T must be contiguous float32 [%d, %d, %d, %d] on %s" % (N, H, dk, dv, dev))
     stream = torch.cuda.current_stream(dev).cuda_stream
     args = (dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha),
             _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+            _nbytes(workspace), ctypes.c_void_p(stream))
     if _ckpt is not None:
         every, S_ckpt = _ckpt
-        code = lib.kda_chunk_fwd_ckpt(*args[:16], int(every), _ptr(S_ckpt), *args[16:])
+        code = lib.kda_chunk_fwd_ckpt(*args[:16], int(every), _ptr(S_ckpt), _nbytes(S_ckpt), *args[16:])
     elif _stage_ms is None:
         code = lib.kda_chunk_fwd(*args)
     else:
@@ -208,13 +245,25 @@ def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = C
 def ckpt_slots(lengths, every: int, chunk: int = CHUNK):
     """Where chunk_fwd_ckpt puts each sequence's checkpoints: for sequence n a
     list of (tokens, slot) -- the state after its first `tokens` tokens is
-    S_ckpt[slot].  `lengths` are the sequence lengths (host integers)."""
-    out, c0 = [], 0
+    S_ckpt[slot].  The checkpoints are packed in sequence order.  `lengths`
+    are the sequence lengths (host integers)."""
+    out, slot = [], 0
     for L in lengths:
         nch = (int(L) + chunk - 1) // chunk
-        out.append([(min((j + 1) * chunk, int(L)), c0 + j) for j in range(nch) if (j + 1) % every == 0])
-        c0 += nch
+        lst = []
+        for j in range(nch):
+            if (j + 1) % every == 0:
+                lst.append((min((j + 1) * chunk, int(L)), slot))
+                slot += 1
+        out.append(lst)
     return out
+
+
+def ckpt_size(total_tokens: int, n_seqs: int, n_heads: int, d_k: int, d_v: int, every: int) -> int:
+    """Bytes of the checkpoint buffer for kda_chunk_fwd_ckpt (an upper bound
+    over all splits of total_tokens into n_seqs sequences)."""
+    return int(_load().kda_chunk_ckpt_size(int(total_tokens), int(n_seqs), int(n_heads), int(d_k), int(d_v),
+                                           int(every)))
 
 
 def chunk_fwd_ckpt(q, k, v, beta, log_alpha, every: int, S_ckpt=None, **kw):
@@ -223,19 +272,17 @@ def chunk_fwd_ckpt(q, k, v, beta, log_alpha, every: int, S_ckpt=None, **kw):
     d_v] (allocated when None; see ckpt_slots for the slot of each).  bf16
     only.  Returns (o, S_T, S_ckpt)."""
     import torch
-    lib = _load()
-    T, H, dk = (q.reshape(-1, *q.shape[-2:]).shape if q.dim() == 4 else q.shape)
-    dv = v.shape[-1]
-    cu = kw.get("cu_seqlens")
-    N = cu.numel() - 1 if cu is not None else kw.get("n_seqs") or (q.shape[0] if q.dim() == 4 else 1)
-    nbytes = int(lib.kda_chunk_ckpt_size(T, N, H, dk, dv))
+    P = _fwd_problem(q, k, v, beta, log_alpha, kw.get("S0"), kw.get("cu_seqlens"), kw.get("n_seqs"))
+    if int(every) < 1:
+        raise ValueError("every must be >= 1")
+    nbytes = ckpt_size(P.T, P.N, P.H, P.dk, P.dv, every)
+    if nbytes == 0:
+        raise KdaError(4, "unsupported sizes for checkpoints")
     if S_ckpt is None:
-        if nbytes == 0:
-            raise KdaError(4, "unsupported sizes for checkpoints")
-        S_ckpt = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device).view(-1, H, dk, dv)
-    elif (S_ckpt.dtype != torch.float32 or S_ckpt.numel() * 4 < nbytes or not S_ckpt.is_contiguous()
-          or S_ckpt.device != q.device):
-        raise ValueError("S_ckpt must be contiguous float32 with at least %d bytes on %s" % (nbytes, q.device))
+        S_ckpt = torch.empty(nbytes // 4, dtype=torch.float32, device=P.dev).view(-1, P.H, P.dk, P.dv)
+    elif (S_ckpt.dtype != torch.float32 or _nbytes(S_ckpt) < nbytes or not S_ckpt.is_contiguous()
+          or S_ckpt.device != P.dev):
+        raise ValueError("S_ckpt must be contiguous float32 with at least %d bytes on %s" % (nbytes, P.dev))
     o, S_T = chunk_fwd(q, k, v, beta, log_alpha, _ckpt=(every, S_ckpt), **kw)
     return o, S_T, S_ckpt
 
@@ -273,14 +320,18 @@ def chunk_fwd_train(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: i
     3-D packed inputs.  Returns (o, S_T, context)."""
     import torch
     lib = _load()
-    dt, dev = _check_common(q, k, v, beta, log_alpha)
-    T, H, dk = q.shape
-    dv = v.shape[-1]
-    N = (cu_seqlens.numel() - 1) if cu_seqlens is not None else (n_seqs if n_seqs is not None else 1)
+    if q.dim() != 3:
+        raise ValueError("chunk_fwd_train takes 3-D packed inputs [T, H, d], got shape %s" % (tuple(q.shape),))
+    P = _fwd_problem(q, k, v, beta, log_alpha, S0, cu_seqlens, n_seqs, dtypes=(torch.bfloat16,))
+    dt, dev, T, H, dk, dv, N = P.dt, P.dev, P.T, P.H, P.dk, P.dv, P.N
     cb = int(lib.kda_chunk_train_context_size(T, N, H, dk, dv, chunk, dt))
     wb = int(lib.kda_chunk_fwd_workspace_size(T, N, H, dk, dv, chunk, dt))
     if cb == 0 or wb == 0:
         raise KdaError(4, "KDA_ERR_UNSUPPORTED: sizes or dtype not supported by the training pair")
+    _check_buffer("context", context, cb, dev)
+    _check_buffer("workspace", workspace, wb, dev)
+    _check_out("o", o, (T, H, dv), q.dtype, dev)
+    _check_out("S_T", S_T, (N, H, dk, dv), torch.float32, dev)
     if context is None:
         context = torch.empty(cb, dtype=torch.uint8, device=dev)
     if workspace is None:
@@ -292,7 +343,7 @@ def chunk_fwd_train(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: i
     stream = torch.cuda.current_stream(dev).cuda_stream
     code = lib.kda_chunk_fwd_train(dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
                                    _ptr(log_alpha), _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T), _ptr(context),
-                                   context.numel(), _ptr(workspace), workspace.numel(), ctypes.c_void_p(stream))
+                                   _nbytes(context), _ptr(workspace), _nbytes(workspace), ctypes.c_void_p(stream))
     if code != 0:
         raise KdaError(code, lib.kda_status_string(code).decode())
     return o, S_T, context
@@ -309,35 +360,23 @@ def chunk_bwd(q, k, v, beta, log_alpha, dO, S0=None, dS_T=None, cu_seqlens=None,
     inputs) and dS0 ([N, H, d_k, d_v] float32)."""
     import torch
     lib = _load()
-    dt, dev = _check_common(q, k, v, beta, log_alpha)
-    batched = q.dim() == 4
     shape_q, shape_v, shape_b = q.shape, v.shape, beta.shape
+    P = _fwd_problem(q, k, v, beta, log_alpha, S0, cu_seqlens, n_seqs, dtypes=(torch.bfloat16,))
+    q, k, v, beta, log_alpha = P.q, P.k, P.v, P.beta, P.log_alpha
+    dt, dev, T, H, dk, dv, N, batched = P.dt, P.dev, P.T, P.H, P.dk, P.dv, P.N, P.batched
     if batched:
-        B = q.shape[0]
-        q, k, v, log_alpha, dO = (t.reshape(-1, *t.shape[2:]) for t in (q, k, v, log_alpha, dO))
-        beta = beta.reshape(-1, beta.shape[-1])
-    T, H, dk = q.shape
-    dv = v.shape[-1]
-    if (k.shape != (T, H, dk) or log_alpha.shape != (T, H, dk) or v.shape != (T, H, dv)
-            or beta.shape != (T, H) or dO.shape != (T, H, dv)):
-        raise ValueError("inconsistent shapes")
-    if dO.dtype != q.dtype or dO.device != dev or not dO.is_contiguous():
-        raise ValueError("dO must be contiguous %s on %s" % (q.dtype, dev))
-    if cu_seqlens is not None:
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
-            raise ValueError("cu_seqlens must be a 1-D int32 tensor on %s" % dev)
-        N = cu_seqlens.numel() - 1
-    else:
-        N = n_seqs if n_seqs is not None else (B if batched else 1)
-    for name, t in (("S0", S0), ("dS_T", dS_T)):
-        if t is not None and (t.dtype != torch.float32 or t.shape != (N, H, dk, dv) or t.device != dev
-                              or not t.is_contiguous()):
-            raise ValueError("%s must be contiguous float32 [%d, %d, %d, %d] on %s" % (name, N, H, dk, dv, dev))
+        dO = dO.reshape(-1, *dO.shape[2:])
+    if dO.shape != (T, H, dv) or dO.dtype != q.dtype or dO.device != dev or not dO.is_contiguous():
+        raise ValueError("dO must be contiguous %s shaped like v on %s" % (q.dtype, dev))
+    _check_out("dS_T", dS_T, (N, H, dk, dv), torch.float32, dev)
     size_fn = lib.kda_chunk_bwd_workspace_size if context is None else lib.kda_chunk_bwd_ctx_workspace_size
     ws_bytes = int(size_fn(T, N, H, dk, dv, chunk, dt))
     if ws_bytes == 0:
         code = lib.kda_chunk_bwd(dt, T, N, H, dk, dv, chunk, *([None] * 15), 0, None)
         raise KdaError(code, lib.kda_status_string(code).decode())
+    _check_buffer("workspace", workspace, ws_bytes, dev)
+    if context is not None:
+        _check_buffer("context", context, int(lib.kda_chunk_train_context_size(T, N, H, dk, dv, chunk, dt)), dev)
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
@@ -347,15 +386,15 @@ def chunk_bwd(q, k, v, beta, log_alpha, dO, S0=None, dS_T=None, cu_seqlens=None,
     args = (dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(log_alpha), _ptr(S0),
             _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
             _ptr(out["dbeta"]), _ptr(out["dg"]), _ptr(out["dS0"]), _ptr(workspace),
-            workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+            _nbytes(workspace), ctypes.c_void_p(stream))
     if context is not None:
         if _stage_ms is not None:
             raise ValueError("the context form has no per-kernel measurement entry point")
         code = lib.kda_chunk_bwd_ctx(dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(beta), _ptr(log_alpha),
-                                     _ptr(cu_seqlens), _ptr(context), context.numel(), _ptr(dO), _ptr(dS_T),
+                                     _ptr(cu_seqlens), _ptr(context), _nbytes(context), _ptr(dO), _ptr(dS_T),
                                      _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
                                      _ptr(out["dg"]), _ptr(out["dS0"]), _ptr(workspace),
-                                     workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+                                     _nbytes(workspace), ctypes.c_void_p(stream))
     else:
         code = lib.kda_chunk_bwd(*args) if _stage_ms is None else lib.kda_chunk_bwd_profile(*args, _stage_ms)
     if code != 0:
@@ -513,31 +552,21 @@ def chunk_transition(k, beta, log_alpha, cu_seqlens=None, n_seqs=None, workspace
     sequence maps an incoming state S to P S + Z (Z its zero-start state)."""
     import torch
     lib = _load()
-    if k.dtype != torch.bfloat16 or beta.dtype != k.dtype or log_alpha.dtype != k.dtype:
+    if k.dtype != torch.bfloat16:
         raise TypeError("chunk_transition takes bfloat16 k, beta, log_alpha")
-    if k.dim() == 4:
-        B = k.shape[0]
-        k, log_alpha = (t.reshape(-1, *t.shape[2:]) for t in (k, log_alpha))
-        beta = beta.reshape(-1, beta.shape[-1])
-    else:
-        B = 1
-    T, H, d = k.shape
-    dev = k.device
-    for name, t in (("k", k), ("beta", beta), ("log_alpha", log_alpha)):
-        if t.device != dev or not t.is_contiguous():
-            raise ValueError("%s must be contiguous on %s" % (name, dev))
-    if cu_seqlens is not None:
-        N = cu_seqlens.numel() - 1
-    else:
-        N = n_seqs if n_seqs is not None else B
+    # k stands in for q and v in the shared checks (the transition reads neither)
+    P = _fwd_problem(k, k, k, beta, log_alpha, None, cu_seqlens, n_seqs, dtypes=(torch.bfloat16,))
+    k, beta, log_alpha = P.k, P.beta, P.log_alpha
+    T, H, d, N, dev = P.T, P.H, P.dk, P.N, P.dev
     ws_bytes = int(lib.kda_chunk_fwd_workspace_size(T, N, H, d, d, CHUNK, KDA_BF16))
+    _check_buffer("workspace", workspace, ws_bytes, dev)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     P_out = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev).cuda_stream
     code = lib.kda_chunk_transition(KDA_BF16, T, N, H, d, CHUNK, _ptr(k), _ptr(beta), _ptr(log_alpha),
                                     _ptr(cu_seqlens), _ptr(P_out), _ptr(workspace),
-                                    0 if workspace is None else workspace.numel(), ctypes.c_void_p(stream))
+                                    0 if workspace is None else _nbytes(workspace), ctypes.c_void_p(stream))
     if code != 0:
         raise KdaError(code, lib.kda_status_string(code).decode())
     return P_out

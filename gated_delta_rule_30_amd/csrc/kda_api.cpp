@@ -36,6 +36,7 @@ size_t carve_workspace(Plan* p, void* base) {
         p->ws_KhT = take(es * mc * H * D * kChunkTokens);
     }
     if (kind == kWsFwd || kind == kWsBwd) p->ws_gam = (float*)take(4 * mc * H * D);
+    if (kind == kWsFwd) p->ws_state2 = (float*)take(4 * 2 * (size_t)p->n_seqs * H * D * D);
     if (kind == kWsBwd) {
         p->ws_bet = (float*)take(4 * mc * H * kChunkTokens);
         p->ws_bTT = take(es * mc * H * kChunkTokens * kChunkTokens);
@@ -52,6 +53,8 @@ size_t carve_workspace(Plan* p, void* base) {
         p->ws_dZ = take(2 * T * H * D);
         p->ws_dbp = (float*)take(4 * 2 * T * H);
     }
+    // first checkpoint slot of each sequence (kda_chunk_fwd_ckpt with cu_seqlens)
+    p->ws_ck0 = (int32_t*)take(sizeof(int32_t) * ((size_t)p->n_seqs + 1));
     // last, so that the regions above keep their offsets
     p->ws_prog = (int32_t*)take(4 * (size_t)p->n_seqs * H * (D / 16));
     return off;
@@ -147,25 +150,24 @@ kda_status kda_chunk_fwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int
                          int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
                          const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
                          void* o, float* S_T, void* workspace, size_t workspace_bytes, void* stream) {
-    Plan p{};
-    kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
-                           cu_seqlens, o, S_T, workspace, workspace_bytes);
-    if (s != KDA_OK) return s;
-    hipError_t e = kda::launch(p, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return kda::chunk_fwd_entry(dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
+                                cu_seqlens, o, S_T, workspace, workspace_bytes, stream, true);
 }
 
-size_t kda_chunk_ckpt_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k, int32_t d_v) {
+size_t kda_chunk_ckpt_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k, int32_t d_v,
+                           int32_t every) {
     Plan p{};
+    if (every < 1) return 0;
     if (plan_sizes(&p, KDA_BF16, total_tokens, n_seqs, n_heads, d_k, d_v, kda::kChunkTokens, true) != KDA_OK) return 0;
-    return (size_t)p.max_chunks * (size_t)n_heads * (size_t)d_k * (size_t)d_v * sizeof(float);
+    const int64_t slots = (total_tokens / kda::kChunkTokens + n_seqs) / every;
+    return (size_t)slots * (size_t)n_heads * (size_t)d_k * (size_t)d_v * sizeof(float);
 }
 
 kda_status kda_chunk_fwd_ckpt(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
                               int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
                               const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
-                              void* o, float* S_T, int32_t every, float* S_ckpt, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              void* o, float* S_T, int32_t every, float* S_ckpt, size_t S_ckpt_bytes,
+                              void* workspace, size_t workspace_bytes, void* stream) {
     if (dt == KDA_F32) return KDA_ERR_UNSUPPORTED;
     if (every < 1) return KDA_ERR_SHAPE;
     if (!S_ckpt) return KDA_ERR_NULL;
@@ -174,8 +176,10 @@ kda_status kda_chunk_fwd_ckpt(kda_dtype dt, int64_t total_tokens, int32_t n_seqs
     kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
                            cu_seqlens, o, S_T, workspace, workspace_bytes);
     if (s != KDA_OK) return s;
+    if (S_ckpt_bytes < kda_chunk_ckpt_size(total_tokens, n_seqs, n_heads, d_k, d_v, every)) return KDA_ERR_WORKSPACE;
     p.S_ckpt = S_ckpt;
     p.ck_every = every;
+    p.ck_slots = (int32_t)((total_tokens / kda::kChunkTokens + n_seqs) / every);
     hipError_t e = kda::launch(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -488,3 +492,17 @@ const char* kda_status_string(kda_status s) {
 const char* kda_version(void) { return "0.1.0"; }
 
 }  // extern "C"
+
+kda_status kda::chunk_fwd_entry(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                                int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
+                                const void* beta, const void* log_alpha, const float* S0,
+                                const int32_t* cu_seqlens, void* o, float* S_T, void* workspace,
+                                size_t workspace_bytes, void* stream, bool pipeline) {
+    Plan p{};
+    kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
+                           cu_seqlens, o, S_T, workspace, workspace_bytes);
+    if (s != KDA_OK) return s;
+    p.no_pipeline = !pipeline;
+    hipError_t e = kda::launch(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}

@@ -261,9 +261,10 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 
 template <typename E, int D>
-__global__ __launch_bounds__(256) void k_output_gate(const E* __restrict__ o, const E* __restrict__ z,
+// y may be o itself (in place), so neither pointer is declared restrict.
+__global__ __launch_bounds__(256) void k_output_gate(const E* o, const E* __restrict__ z,
                                                      const float* __restrict__ w, float eps, int64_t n_rows,
-                                                     E* __restrict__ y) {
+                                                     E* y) {
     constexpr int PER = D / 16;                            // channels per lane
     constexpr int NV = (PER * (int)sizeof(E) + 15) / 16;   // vectors per lane per row
     using V = typename std::conditional<PER * sizeof(E) >= 16, uint4, uint2>::type;

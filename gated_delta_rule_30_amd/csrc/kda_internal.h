@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/kda.h"
+
 namespace kda {
 
 struct ChunkInfo {
@@ -27,6 +29,8 @@ struct Plan {
     float* S_T;
     float* S_ckpt;            // [slots, H, D, D] fp32 states at chosen chunk ends, or NULL
     int32_t ck_every;         // a state after every ck_every-th chunk of a sequence
+    int32_t ck_slots;         // slots of S_ckpt
+    bool no_pipeline;         // never split the forward into token blocks on a side stream
     // workspace carve-up
     int32_t* ws_n_chunks;
     int32_t* ws_seq_chunk0;
@@ -38,6 +42,7 @@ struct Plan {
     void* ws_Kg;              // [H, max_chunks, 64, D] K . Gamma
     void* ws_KhT;             // [H, max_chunks, D, 64] (K . exp(b_L - b))^T
     float* ws_gam;            // [H, max_chunks, D] exp(b_L), fp32
+    float* ws_state2;         // [2, N, H, D, D] fp32: states between the blocks of a pipelined forward
     // What the workspace holds (carve_workspace) -- kWsFwd: the forward pass;
     // kWsBwd: the backward with the forward evaluated again inside;
     // kWsFwdTrain / kWsBwdCtx: the training pair, whose shared regions (Gamma_L,
@@ -59,6 +64,7 @@ struct Plan {
     void* ws_ckdS;            // [H, max_chunks, D, D] gradient of each chunk's outgoing state (bf16)
     void *ws_Y, *ws_U, *ws_dZ;   // [T, H, D] bf16: Y, U~ and dZ per token
     float* ws_dbp;            // [2, H, T] float32 dbeta shares of the two channel halves
+    int32_t* ws_ck0;          // [n_seqs + 1] first checkpoint slot of each sequence (varlen checkpoints)
     int32_t* ws_prog;         // [n_seqs * H, d_v / 16] steps done per recurrence workgroup (pacing)
 };
 
@@ -85,6 +91,13 @@ enum { kWsFwd = 0, kWsBwd = 1, kWsFwdTrain = 2, kWsBwdCtx = 3 };
 size_t carve_workspace(Plan* p, void* base);
 // The same for the training pair's context buffer.
 size_t carve_context(Plan* p, void* base);
+
+// kda_chunk_fwd with its checks; `pipeline` = false keeps every launch on
+// `stream` (no side stream is created or used).
+kda_status chunk_fwd_entry(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
+                           int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v, const void* beta,
+                           const void* log_alpha, const float* S0, const int32_t* cu_seqlens, void* o, float* S_T,
+                           void* workspace, size_t workspace_bytes, void* stream, bool pipeline);
 
 // Kernel launches of one forward pass, in order.
 constexpr int kNumStages = 3;

@@ -45,6 +45,8 @@
 // also the B-operand fragment of column block w, so the diagonal sub-tile
 // products need no data exchange.  The per-channel cumulative sum over
 // tokens is a 16-lane row scan (DPP row shifts) plus carries between waves.
+#include <mutex>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -89,37 +91,51 @@ __device__ inline void seq_chunks(const int32_t* __restrict__ cu, const int32_t*
 // Sequences are taken 1024 at a time: a prefix sum of their chunk counts
 // gives each one's first chunk, then the whole workgroup writes the batch's
 // chunk records, finding each chunk's sequence by binary search in the sums.
+//
+// With every > 0 it also writes ck0[n] = sum over m < n of floor(chunks_m /
+// every), the first state-checkpoint slot of each sequence (ck0[n_seqs] is
+// the total).
 __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict__ cu, int32_t n_seqs,
                                                       int64_t total_tokens, int64_t fixed_len,
                                                       int32_t max_chunks, ChunkInfo* __restrict__ tab,
                                                       int32_t* __restrict__ seq_chunk0,
-                                                      int32_t* __restrict__ n_chunks_out) {
+                                                      int32_t* __restrict__ n_chunks_out, int32_t every,
+                                                      int32_t* __restrict__ ck0) {
     __shared__ int32_t s_scan[1024];     // inclusive prefix sum of chunk counts in the batch
+    __shared__ int32_t s_ck[1024];       // the same for checkpoint counts (every > 0)
     __shared__ int64_t s_start[1024];
     __shared__ int64_t s_len[1024];
-    __shared__ int32_t s_carry;
+    __shared__ int32_t s_carry, s_ck_carry;
     const int tid = threadIdx.x;
-    if (tid == 0) s_carry = 0;
+    if (tid == 0) {
+        s_carry = 0;
+        s_ck_carry = 0;
+    }
     __syncthreads();
     for (int32_t base = 0; base < n_seqs; base += 1024) {
         const int32_t n = base + tid;
         int64_t start = 0, len = 0;
         if (n < n_seqs) seq_range(cu, n, total_tokens, fixed_len, start, len);
         const int32_t cnt = (int32_t)((len + kChunk - 1) / kChunk);
+        const int32_t ckc = every > 0 ? cnt / every : 0;
         s_scan[tid] = cnt;
+        s_ck[tid] = ckc;
         s_start[tid] = start;
         s_len[tid] = len;
         __syncthreads();
         for (int off = 1; off < 1024; off <<= 1) {
-            int32_t add = tid >= off ? s_scan[tid - off] : 0;
+            const int32_t add = tid >= off ? s_scan[tid - off] : 0;
+            const int32_t add_ck = tid >= off ? s_ck[tid - off] : 0;
             __syncthreads();
             s_scan[tid] += add;
+            s_ck[tid] += add_ck;
             __syncthreads();
         }
         const int32_t carry = s_carry;
         if (n < n_seqs) {
             const int32_t first = carry + s_scan[tid] - cnt;
             seq_chunk0[n] = first < max_chunks ? first : max_chunks;
+            if (every > 0) ck0[n] = s_ck_carry + s_ck[tid] - ckc;
         }
         const int32_t batch = s_scan[1023];
         for (int32_t c = tid; c < batch; c += 1024) {
@@ -139,13 +155,17 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
             tab[cg] = ci;
         }
         __syncthreads();
-        if (tid == 1023) s_carry = carry + batch;
+        if (tid == 1023) {
+            s_carry = carry + batch;
+            s_ck_carry += s_ck[1023];
+        }
         __syncthreads();
     }
     if (tid == 0) {
         const int32_t total = s_carry < max_chunks ? s_carry : max_chunks;
         seq_chunk0[n_seqs] = total;
         *n_chunks_out = total;
+        if (every > 0) ck0[n_seqs] = s_ck_carry;
     }
 }
 
@@ -231,7 +251,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
                                                    const E* __restrict__ g, const E* __restrict__ beta,
                                                    const ChunkInfo* __restrict__ tab,
                                                    const int32_t* __restrict__ n_chunks_p, int64_t fixed_len,
-                                                   int32_t fixed_chunks, int32_t H, ChunkOps ops, ChunkOps ob) {
+                                                   int32_t fixed_chunks, int32_t H, ChunkOps ops, ChunkOps ob,
+                                                   int32_t blk_j0, int32_t blk_nj) {
     constexpr bool kBwd = kBoth;
     using G = Geo<E, D>;
     using M = Mma<E>;
@@ -277,10 +298,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
     // Chunk ci: for equal-length sequences (fixed_len > 0) it follows from
     // the index (fixed_chunks chunks per sequence, in sequence order, as the
     // chunk table lists them); otherwise it is read from the chunk table.
-    const int32_t ci = blockIdx.x;
+    // With blk_nj > 0 (equal lengths only) the grid covers chunks
+    // blk_j0 .. blk_j0 + blk_nj - 1 of every sequence.
+    int32_t ci = blockIdx.x;
     ChunkInfo info;
     if (fixed_len > 0) {
         const int32_t per = (int32_t)((fixed_len + kChunk - 1) / kChunk);
+        if (blk_nj > 0) {
+            const int32_t jj = blk_j0 + ci % blk_nj;
+            if (jj >= per) return;
+            ci = (ci / blk_nj) * per + jj;
+        }
         if (ci >= fixed_chunks) return;
         const int32_t seq = ci / per, j = ci % per;
         const int64_t rem = fixed_len - (int64_t)j * kChunk;
@@ -1014,8 +1042,10 @@ struct RecurAux {
     __bf16* y;         // kCkpt: Y;  kBwd: dZ
     __bf16* u;         // kCkpt: U~
     const float* bet;  // kBwd: per-chunk beta (ChunkOps::bet)
-    float* sck;        // kFwdCk: fp32 state after every `every`-th chunk, slot = global chunk index
+    float* sck;        // kFwdCk: fp32 state after every `every`-th chunk of a sequence
     int32_t every;
+    int32_t n_slots;   // kFwdCk: slots of sck
+    const int32_t* ck0;   // kFwdCk with cu_seqlens: first slot of each sequence (k_chunk_table)
     int32_t* prog;     // pacing: steps done per (sequence*head, slab), or NULL (no pacing)
 };
 
@@ -1035,7 +1065,7 @@ template <int D, int kMode>
 __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     const __bf16* __restrict__ v, ChunkOps ops, const int32_t* __restrict__ cu, int64_t total_tokens,
     int64_t fixed_len, const int32_t* __restrict__ seq_chunk0, int32_t NH, int32_t H, const float* __restrict__ S0,
-    float* __restrict__ ST, __bf16* __restrict__ o, RecurAux aux) {
+    float* __restrict__ ST, __bf16* __restrict__ o, RecurAux aux, int32_t jb, int32_t je) {
     constexpr bool kTransition = kMode == kTrans;
     constexpr bool kBack = kMode == kBwd;
     using E = __bf16;
@@ -1081,13 +1111,18 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     seq_range(cu, n, total_tokens, fixed_len, s_start, s_len);
     int32_t c0, nch;
     seq_chunks(cu, seq_chunk0, n, fixed_len, s_len, c0, nch);
+    // This launch takes chunks [j_lo, j_lo + ns) of the sequence (all of
+    // them when [jb, je) covers it): S0 is the state entering chunk j_lo and
+    // ST the state after the last one.
+    const int32_t j_lo = jb < nch ? jb : nch;
+    const int32_t ns = (je < nch ? je : nch) > j_lo ? (je < nch ? je : nch) - j_lo : 0;
     const int64_t cb = (int64_t)h * ops.max_chunks + c0;   // head-major operand slot of chunk 0
     auto chunk_len = [&](int j) -> int {
         const int64_t rem = s_len - (int64_t)j * C;
         return (int)(rem < C ? rem : C);
     };
     // chunk processed at step s (the backward pass walks the chunks last to first)
-    auto chunk_at = [&](int s_) -> int { return kBack ? nch - 1 - s_ : s_; };
+    auto chunk_at = [&](int s_) -> int { return kBack ? j_lo + ns - 1 - s_ : j_lo + s_; };
 
     if (w == kPacerWave) {
         // ------------------------------------------------ pacing wave
@@ -1101,13 +1136,13 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         // step count with its siblings' published counts, sleeps while it is
         // more than kPaceLag steps ahead of the slowest (which holds the
         // whole workgroup at the next barrier), then publishes its own.  Every wait ends: at most
-        // kPaceBudget sleeps per workgroup.  Counts outside 0..nch (the
+        // kPaceBudget sleeps per workgroup.  Counts outside 0..ns (the
         // sentinel written at the end of a call, or memory never written)
         // are ignored.
         // Drift needs thousands of steps to build up; shorter sequences are
         // not paced at all (this wave then only passes the barriers).
         constexpr int kPaceEvery = 8, kPaceLead = 4, kPaceLag = 16, kPaceBudget = 1024, kPaceMinChunks = 2048;
-        int32_t* const pg = (aux.prog && nch >= kPaceMinChunks) ? aux.prog + (int64_t)nh * NS : nullptr;
+        int32_t* const pg = (aux.prog && ns >= kPaceMinChunks) ? aux.prog + (int64_t)nh * NS : nullptr;
         auto post = [&](int v) {
             if (pg && lane == 0) __hip_atomic_store(pg + sl, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         };
@@ -1116,7 +1151,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                              : 0x7fffffff;
         };
         auto slowest = [&](int v) {
-            v = (v < 0 || v > nch) ? 0x7fffffff : v;
+            v = (v < 0 || v > ns) ? 0x7fffffff : v;
             v = min(v, __shfl_xor(v, 1));
             v = min(v, __shfl_xor(v, 2));
             v = min(v, __shfl_xor(v, 4));
@@ -1130,8 +1165,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         int left = kPaceBudget;
         int seen = 0;
         post(0);
-        for (int s_ = 0; s_ < nch; ++s_) {
-            const bool on = pg && s_ + 1 < nch;
+        for (int s_ = 0; s_ < ns; ++s_) {
+            const bool on = pg && s_ + 1 < ns;
             barrier_lds();
             if (on && (s_ % kPaceEvery) == kPaceEvery - 1 - kPaceLead) seen = load();
             barrier_lds();
@@ -1285,7 +1320,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         // Loads one dword per line of the chunk kAhead steps after step s
         // (clamped to the last step).
         auto touch = [&](int s_) {
-            const int jt = chunk_at(s_ + kAhead < nch ? s_ + kAhead : nch - 1);
+            const int jt = chunk_at(s_ + kAhead < ns ? s_ + kAhead : ns - 1);
 #pragma unroll
             for (int k = 0; k < kTouch; ++k) {
                 const char* p;
@@ -1319,7 +1354,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         auto pstep = [&](uint4* buf, int j) {
             barrier_lds();
             barrier_lds();
-            const bool fill = j + 2 < nch;
+            const bool fill = j + 2 < ns;
             if (fill) issue(buf, j + 2, All0{}, Cut{});
             barrier_lds();
             if (fill) issue(buf, j + 2, Cut{}, AllN{});
@@ -1329,18 +1364,18 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             else
                 wait_counts<2 * kTouch, 15>();
         };
-        if (nch > 0) {
+        if (ns > 0) {
             issue(sBuf0, 0, All0{}, AllN{});
-            if (nch > 1) issue(sBuf1, 1, All0{}, AllN{});
+            if (ns > 1) issue(sBuf1, 1, All0{}, AllN{});
             touch(-2);
             touch(-1);
-            if (nch > 1)   // chunk 0 has landed
+            if (ns > 1)   // chunk 0 has landed
                 wait_fill();
             else
                 wait_counts<2 * kTouch, 15>();
-            for (int j = 0; j < nch; j += 2) {
+            for (int j = 0; j < ns; j += 2) {
                 pstep(sBuf0, j);
-                if (j + 1 >= nch) break;
+                if (j + 1 >= ns) break;
                 pstep(sBuf1, j + 1);
             }
         }
@@ -1353,6 +1388,9 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 
     // ---------------------------------------------------- compute waves
     const int64_t o_off = (s_start * H + h) * D + col0 + li;
+    // kFwdCk: slot of this sequence's first checkpoint
+    int32_t ck_first = 0;
+    if constexpr (kMode == kFwdCk) ck_first = cu ? aux.ck0[n] : n * (nch / aux.every);
     // S[a][r] = state[channel 16*(RT*w + a) + 4*lg + r][column col0 + li]
     // (kBwd: the state gradient)
     f32x4 S[RT];
@@ -1465,10 +1503,12 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[a][r] = gam[a][r] * S[a][r] + acc[r];
         }
-        // kFwdCk: the state after this chunk, when it is a chosen checkpoint
+        // kFwdCk: the state after this chunk, when it is a chosen checkpoint;
+        // the checkpoints are packed, sequence after sequence
         if constexpr (kMode == kFwdCk) {
-            if ((j + 1) % aux.every == 0) {
-                float* dst = aux.sck + ((int64_t)(c0 + j) * H + h) * D * D + col0 + li;
+            const int32_t slot = ck_first + (j + 1) / aux.every - 1;
+            if ((j + 1) % aux.every == 0 && slot < aux.n_slots) {
+                float* dst = aux.sck + ((int64_t)slot * H + h) * D * D + col0 + li;
 #pragma unroll
                 for (int a = 0; a < RT; ++a)
 #pragma unroll
@@ -1582,11 +1622,11 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 
     auto run = [&](const uint4* buf, int s_) {
         if constexpr (kBack) step_bwd(buf, chunk_at(s_));
-        else step(buf, s_);
+        else step(buf, chunk_at(s_));
     };
-    for (int s_ = 0; s_ < nch; s_ += 2) {
+    for (int s_ = 0; s_ < ns; s_ += 2) {
         run(sBuf0, s_);
-        if (s_ + 1 >= nch) break;
+        if (s_ + 1 >= ns) break;
         run(sBuf1, s_ + 1);
     }
     if (ST) {
@@ -1612,30 +1652,121 @@ static ChunkOps chunk_ops_bwd(const Plan& p) {
     return ChunkOps{p.ws_bTT, p.ws_bMT, p.ws_bKh, p.ws_bQgT, p.ws_bKgT, p.ws_gam, p.max_chunks, p.ws_bet};
 }
 
+// All chunks, or (equal lengths, nj > 0) chunks [j0, j0 + nj) of every sequence.
 template <typename E, int D, bool kBoth>
-static void launch_prep(const Plan& p, const E* q, hipStream_t st) {
+static void launch_prep(const Plan& p, const E* q, hipStream_t st, int32_t j0 = 0, int32_t nj = 0) {
     if (p.total_tokens <= 0) return;
-    hipLaunchKernelGGL((k_prep<E, D, kBoth>), dim3(p.max_chunks, p.n_heads), dim3(kThreads), 0, st, q,
+    const int32_t grid = nj > 0 ? p.n_seqs * nj : p.max_chunks;
+    hipLaunchKernelGGL((k_prep<E, D, kBoth>), dim3(grid, p.n_heads), dim3(kThreads), 0, st, q,
                        static_cast<const E*>(p.k), static_cast<const E*>(p.g), static_cast<const E*>(p.beta),
                        p.ws_tab, p.ws_n_chunks, p.cu_seqlens ? (int64_t)0 : p.fixed_len,
                        p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk)), p.n_heads,
-                       chunk_ops(p), kBoth ? chunk_ops_bwd(p) : chunk_ops(p));
+                       chunk_ops(p), kBoth ? chunk_ops_bwd(p) : chunk_ops(p), j0, nj);
 }
 
+// Chunks [jb, je) of every sequence (default: all of them).
 template <int D, int kMode>
 static void launch_recur_lds(const Plan& p, const void* v, const float* S0, float* ST, void* o, RecurAux aux,
-                             hipStream_t st) {
+                             hipStream_t st, int32_t jb = 0, int32_t je = 0x7fffffff) {
     const int32_t NH = p.n_seqs * p.n_heads;
     aux.prog = p.ws_prog;
     hipLaunchKernelGGL((k_recur_lds<D, kMode>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st,
                        static_cast<const __bf16*>(v), kMode == kBwd ? chunk_ops_bwd(p) : chunk_ops(p),
                        p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, p.n_heads, S0, ST,
-                       static_cast<__bf16*>(o), aux);
+                       static_cast<__bf16*>(o), aux, jb, je);
 }
 
 static void launch_table(const Plan& p, hipStream_t st) {
     hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(1024), 0, st, p.cu_seqlens, p.n_seqs, p.total_tokens,
-                       p.fixed_len, p.max_chunks, p.ws_tab, p.ws_seq_chunk0, p.ws_n_chunks);
+                       p.fixed_len, p.max_chunks, p.ws_tab, p.ws_seq_chunk0, p.ws_n_chunks,
+                       p.S_ckpt ? p.ck_every : 0, p.ws_ck0);
+}
+
+// ---------------------------------------------------------------- pipelined forward
+// When the sequences have equal lengths and the recurrence's workgroups
+// (one per sequence, head and 16-column slab) fill at most half of the CUs,
+// the chunk-parallel k_prep of a token block runs on the idle CUs while the
+// recurrence works on the block before it.  Block b's k_prep goes on a side
+// stream that the library keeps per device; block b's recurrence waits for it
+// on the caller's stream, takes its incoming state from the previous block
+// (ws_state2, two fp32 buffers used in turn) and hands its final state on.
+// k_prep of block b + 1 also waits for the recurrence of block b - 1, so
+// that only one block of k_prep shares the GPU with a recurrence.
+constexpr int kSideEvents = 96;
+constexpr int kMaxDevices = 64;
+constexpr int32_t kPipeMinChunks = 2048;   // per sequence
+constexpr int32_t kPipeFirst = 256;        // chunks in the first block (its k_prep runs alone)
+constexpr int32_t kPipeBlock = 1024;       // chunks in the later blocks
+
+struct SideStream {
+    bool tried = false, ok = false;
+    hipStream_t s = nullptr;
+    hipEvent_t ev[kSideEvents] = {};
+    int cus = 0;
+};
+static std::mutex g_side_mu;
+static SideStream g_side[kMaxDevices];
+
+// The current device's side stream (created on first use, default priority).
+// Called with g_side_mu held.
+static SideStream* side_stream() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream& ss = g_side[dev];
+    if (!ss.tried) {
+        ss.tried = true;
+        bool ok = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) == hipSuccess;
+        for (int i = 0; ok && i < kSideEvents; ++i)
+            ok = hipEventCreateWithFlags(&ss.ev[i], hipEventDisableTiming) == hipSuccess;
+        ok = ok && hipDeviceGetAttribute(&ss.cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess;
+        ss.ok = ok;
+    }
+    return ss.ok ? &ss : nullptr;
+}
+
+// Block boundaries (in chunks of each sequence) for `per` chunks per sequence.
+static int pipe_blocks(int32_t per, int32_t* j0, int max_blocks) {
+    int32_t blk = kPipeBlock;
+    while ((per - kPipeFirst + blk - 1) / blk + 1 > max_blocks) blk *= 2;
+    int nb = 0;
+    for (int32_t j = 0; j < per; j += (nb == 1 ? kPipeFirst : blk)) j0[nb++] = j;
+    j0[nb] = per;
+    return nb;
+}
+
+template <int D>
+static bool launch_pipelined(const Plan& p, hipStream_t st) {
+    constexpr int NS = D / kSub;
+    if (p.no_pipeline || p.cu_seqlens || p.S_ckpt || !p.bf16 || p.total_tokens <= 0) return false;
+    const int32_t per = (int32_t)((p.fixed_len + kChunk - 1) / kChunk);
+    if (per < kPipeMinChunks) return false;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* ss = side_stream();
+    if (!ss || (int64_t)p.n_seqs * p.n_heads * NS * 2 > ss->cus) return false;
+    constexpr int kMaxBlocks = (kSideEvents - 1) / 2;
+    int32_t j0[kMaxBlocks + 2];
+    const int nb = pipe_blocks(per, j0, kMaxBlocks);
+    hipEvent_t* evp = ss->ev + 1;            // k_prep of block b done
+    hipEvent_t* evr = ss->ev + 1 + nb;       // recurrence of block b done
+    const __bf16* q = static_cast<const __bf16*>(p.q);
+    const size_t state = (size_t)p.n_seqs * p.n_heads * D * D;
+    if (hipEventRecord(ss->ev[0], st) != hipSuccess || hipStreamWaitEvent(ss->s, ss->ev[0], 0) != hipSuccess)
+        return false;
+    launch_prep<__bf16, D, false>(p, q, ss->s, j0[0], j0[1] - j0[0]);
+    (void)hipEventRecord(evp[0], ss->s);
+    for (int b = 0; b < nb; ++b) {
+        if (b + 1 < nb) {
+            if (b >= 1) (void)hipStreamWaitEvent(ss->s, evr[b - 1], 0);
+            launch_prep<__bf16, D, false>(p, q, ss->s, j0[b + 1], j0[b + 2] - j0[b + 1]);
+            (void)hipEventRecord(evp[b + 1], ss->s);
+        }
+        (void)hipStreamWaitEvent(st, evp[b], 0);
+        const float* s_in = b == 0 ? p.S0 : p.ws_state2 + (size_t)((b - 1) & 1) * state;
+        float* s_out = b == nb - 1 ? p.S_T : p.ws_state2 + (size_t)(b & 1) * state;
+        launch_recur_lds<D, kFwd>(p, p.v, s_in, s_out, p.o, RecurAux{}, st, j0[b], j0[b + 1]);
+        (void)hipEventRecord(evr[b], st);
+    }
+    return true;
 }
 
 template <typename E, int D, int kMode = kFwd>
@@ -1648,6 +1779,10 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     const E* q = static_cast<const E*>(kTransition ? p.k : p.q);   // the transition does not use q
     const int32_t NH = p.n_seqs * p.n_heads;
 
+    if constexpr (kMode == kFwd && sizeof(E) == 2) {
+        // the measurement entry point (ev) times the kernels one after another
+        if (!ev && launch_pipelined<D>(p, st)) return hipGetLastError();
+    }
     mark(0);
     if (p.cu_seqlens) launch_table(p, st);   // equal lengths: every kernel derives the chunks itself
     mark(1);
@@ -1657,7 +1792,8 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     if constexpr (sizeof(E) == 2) {
         if (kMode == kFwd && p.S_ckpt)
             launch_recur_lds<D, kFwdCk>(p, p.v, p.S0, p.S_T, p.o,
-                                        RecurAux{nullptr, nullptr, nullptr, nullptr, p.S_ckpt, p.ck_every}, st);
+                                        RecurAux{nullptr, nullptr, nullptr, nullptr, p.S_ckpt, p.ck_every,
+                                                 p.ck_slots, p.ws_ck0}, st);
         else
             launch_recur_lds<D, kMode>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
     }

@@ -91,10 +91,13 @@ kda_status kda_chunk_fwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int
                          void* o, float* S_T,
                          void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of the state-checkpoint buffer kda_chunk_fwd_ckpt writes into:
- * (total_tokens / 64 + n_seqs) slots x n_heads x d_k x d_v float32 (0 if the
- * sizes are invalid). */
-size_t kda_chunk_ckpt_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k, int32_t d_v);
+/* Bytes of the state-checkpoint buffer kda_chunk_fwd_ckpt writes into for a
+ * given `every`: floor((floor(total_tokens / 64) + n_seqs) / every) slots x
+ * n_heads x d_k x d_v float32 -- an upper bound on the checkpoints any
+ * split of total_tokens into n_seqs sequences produces (0 if the sizes are
+ * invalid or every < 1). */
+size_t kda_chunk_ckpt_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k, int32_t d_v,
+                           int32_t every);
 
 /* kda_chunk_fwd that also emits the recurrent state at chosen chunk
  * boundaries, the prefix-cache checkpoints of the serving side (orkas.ai
@@ -102,23 +105,29 @@ size_t kda_chunk_ckpt_size(int64_t total_tokens, int32_t n_seqs, int32_t n_heads
  * hashed in 512-token units and the recurrent state is checkpointed only at a
  * sparse subset of those ends).  Same arguments, results and errors as
  * kda_chunk_fwd, plus:
- *   every  : >= 1; after chunk j of a sequence (0-based, 64 tokens each, the
- *            last one possibly partial) with (j + 1) % every == 0 -- i.e. after
- *            its first min(64 (j + 1), len) tokens -- the state is written
- *            (every = 8: every 512 tokens)
- *   S_ckpt : device float32 [slots][n_heads][d_k][d_v], at least
- *            kda_chunk_ckpt_size(...) bytes; the state after chunk j of
- *            sequence n goes to slot c0(n) + j, where c0(n) is the sum of
- *            ceil(len_m / 64) over the sequences m < n; no other slot is
- *            written.  The same values as kda_chunk_fwd's S_T of that prefix.
- * KDA_ERR_SHAPE if every < 1, KDA_ERR_NULL if S_ckpt is NULL, and
- * KDA_ERR_UNSUPPORTED for KDA_F32. */
+ *   every        : >= 1; after chunk j of a sequence (0-based, 64 tokens
+ *                  each, the last one possibly partial) with (j + 1) % every
+ *                  == 0 -- i.e. after its first min(64 (j + 1), len) tokens
+ *                  -- the state is written (every = 8: every 512 tokens)
+ *   S_ckpt       : device float32 [slots][n_heads][d_k][d_v]; the state after
+ *                  chunk j of sequence n goes to slot ck0(n) + (j + 1) / every
+ *                  - 1, where ck0(n) is the sum of floor(ceil(len_m / 64) /
+ *                  every) over the sequences m < n (the checkpoints are
+ *                  packed: slot i holds the i-th checkpoint in sequence
+ *                  order); slots past the last checkpoint are not written.
+ *                  The same values as kda_chunk_fwd's S_T of that prefix.
+ *   S_ckpt_bytes : size of S_ckpt; at least
+ *                  kda_chunk_ckpt_size(total_tokens, n_seqs, n_heads, d_k,
+ *                  d_v, every).
+ * KDA_ERR_SHAPE if every < 1, KDA_ERR_NULL if S_ckpt is NULL,
+ * KDA_ERR_WORKSPACE if S_ckpt_bytes is too small, and KDA_ERR_UNSUPPORTED
+ * for KDA_F32. */
 kda_status kda_chunk_fwd_ckpt(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
                               int32_t d_k, int32_t d_v, int32_t chunk,
                               const void* q, const void* k, const void* v,
                               const void* beta, const void* log_alpha,
                               const float* S0, const int32_t* cu_seqlens,
-                              void* o, float* S_T, int32_t every, float* S_ckpt,
+                              void* o, float* S_T, int32_t every, float* S_ckpt, size_t S_ckpt_bytes,
                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Measurement entry point: the same work as kda_chunk_fwd (same arguments,

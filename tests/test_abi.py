@@ -281,32 +281,99 @@ def test_training_pair_rejects_bad_arguments(lib):
 
 def test_checkpoint_size_and_rejections(lib):
     P = ctypes.c_void_p
-    # slots = total_tokens / 64 + n_seqs, each n_heads x d_k x d_v float32
-    assert lib.kda_chunk_ckpt_size(65536, 1, 32, 128, 128) == (65536 // 64 + 1) * 32 * 128 * 128 * 4
-    assert lib.kda_chunk_ckpt_size(100, 3, 2, 64, 64) == (100 // 64 + 3) * 2 * 64 * 64 * 4
-    assert lib.kda_chunk_ckpt_size(100, 3, 2, 96, 96) == 0
-    assert lib.kda_chunk_ckpt_size(-1, 3, 2, 64, 64) == 0
+    # slots = (total_tokens / 64 + n_seqs) / every, each n_heads x d_k x d_v float32
+    assert lib.kda_chunk_ckpt_size(65536, 1, 32, 128, 128, 1) == (65536 // 64 + 1) * 32 * 128 * 128 * 4
+    assert lib.kda_chunk_ckpt_size(65536, 1, 32, 128, 128, 8) == (1025 // 8) * 32 * 128 * 128 * 4
+    assert lib.kda_chunk_ckpt_size(100, 3, 2, 64, 64, 1) == (100 // 64 + 3) * 2 * 64 * 64 * 4
+    assert lib.kda_chunk_ckpt_size(100, 3, 2, 64, 64, 3) == 1 * 2 * 64 * 64 * 4
+    assert lib.kda_chunk_ckpt_size(100, 3, 2, 96, 96, 1) == 0
+    assert lib.kda_chunk_ckpt_size(-1, 3, 2, 64, 64, 1) == 0
+    assert lib.kda_chunk_ckpt_size(100, 3, 2, 64, 64, 0) == 0
     buf = (ctypes.c_byte * 4096)()
     a = ctypes.addressof(buf)
     a16 = P(a + (-a) % 16)
+    need = lib.kda_chunk_ckpt_size(128, 1, 2, 64, 64, 2)
 
-    def call(dt=kda.KDA_BF16, every=2, sck=a16, ws=a16, ws_bytes=1 << 40):
+    def call(dt=kda.KDA_BF16, every=2, sck=a16, sck_bytes=need, ws=a16, ws_bytes=1 << 40):
         return lib.kda_chunk_fwd_ckpt(dt, 128, 1, 2, 64, 64, 64, a16, a16, a16, a16, a16, None, None,
-                                      a16, None, every, sck, ws, ws_bytes, None)
+                                      a16, None, every, sck, sck_bytes, ws, ws_bytes, None)
     assert call(dt=kda.KDA_F32) == ERR_UNSUPPORTED
     assert call(every=0) == ERR_SHAPE
     assert call(every=-3) == ERR_SHAPE
     assert call(sck=None) == ERR_NULL
     assert call(sck=P(a16.value + 4)) == ERR_SHAPE
     assert call(ws=None) == ERR_WORKSPACE
+    assert call(sck_bytes=need - 1) == ERR_WORKSPACE
 
 
 def test_checkpoint_slots_helper():
     got = kda.ckpt_slots([700, 64, 1100, 0, 513], 2)
-    # sequence 0: 11 chunks, checkpoints after chunks 1, 3, 5, 7, 9; sequence 2 starts at slot 12 and its
-    # last (partial) chunk 17 ends at token 1100
-    assert got[0] == [(128, 1), (256, 3), (384, 5), (512, 7), (640, 9)]
+    # packed in sequence order: sequence 0 (11 chunks) has checkpoints after
+    # chunks 1, 3, 5, 7, 9 in slots 0-4; sequence 1 (one chunk) none;
+    # sequence 2 (18 chunks, the last partial, ending at token 1100) 9 in
+    # slots 5-13; sequence 4 (9 chunks) 4 in slots 14-17
+    assert got[0] == [(128, 0), (256, 1), (384, 2), (512, 3), (640, 4)]
     assert got[1] == [] and got[3] == []
-    assert got[2][0] == (128, 13) and got[2][-1] == (1100, 29)
-    assert got[4] == [(128, 31), (256, 33), (384, 35), (512, 37)]
-    assert kda.ckpt_slots([512], 8) == [[(512, 7)]]
+    assert got[2][0] == (128, 5) and got[2][-1] == (1100, 13) and len(got[2]) == 9
+    assert got[4] == [(128, 14), (256, 15), (384, 16), (512, 17)]
+    assert kda.ckpt_slots([512], 8) == [[(512, 0)]]
+    # every split fits the size the library reports
+    for lengths, every in (([700, 64, 1100, 0, 513], 2), ([63] * 7, 1), ([65] * 5, 2), ([512], 8)):
+        n = sum(len(x) for x in got) if lengths == [700, 64, 1100, 0, 513] else \
+            sum(len(x) for x in kda.ckpt_slots(lengths, every))
+        assert n <= (sum(lengths) // 64 + len(lengths)) // every
+
+
+def _cpu(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+@pytest.mark.parametrize("entry", ["chunk_fwd", "chunk_fwd_train", "chunk_bwd", "chunk_fwd_ckpt"])
+def test_bad_shapes_rejected_before_launch(entry):
+    """The binding checks every shape the C ABI cannot see (it takes only
+    pointers) before anything is launched: a wrong extent raises ValueError
+    (these CPU tensors never reach the device)."""
+    import torch
+    T, H, d = 70, 2, 64
+    good = dict(q=_cpu(T, H, d), k=_cpu(T, H, d), v=_cpu(T, H, d), beta=_cpu(T, H), log_alpha=_cpu(T, H, d))
+    bad = [dict(good, beta=_cpu(T)), dict(good, beta=_cpu(T, H + 1)), dict(good, k=_cpu(T, H, d + 1)),
+           dict(good, log_alpha=_cpu(T - 1, H, d)), dict(good, v=_cpu(T, H + 1, d)), dict(good, q=_cpu(T, d))]
+
+    def call(a, **kw):
+        if entry == "chunk_fwd":
+            return kda.chunk_fwd(**a, **kw)
+        if entry == "chunk_fwd_train":
+            return kda.chunk_fwd_train(**a, **kw)
+        if entry == "chunk_fwd_ckpt":
+            return kda.chunk_fwd_ckpt(**a, every=2, **kw)
+        return kda.chunk_bwd(**a, dO=_cpu(T, H, d), **kw)
+    for a in bad:
+        with pytest.raises(ValueError, match="shape|must be"):
+            call(a)
+    # well-shaped CPU tensors get as far as the device check
+    with pytest.raises(ValueError, match="GPU"):
+        call(good)
+
+
+def test_bad_state_and_offsets_rejected():
+    """S0 of the wrong dtype or extent, and cu_seqlens of the wrong dtype or
+    rank, are rejected by the shared check before its device check (so CPU
+    tensors show it)."""
+    import torch
+    T, H, d = 70, 2, 64
+    good = dict(q=_cpu(T, H, d), k=_cpu(T, H, d), v=_cpu(T, H, d), beta=_cpu(T, H), log_alpha=_cpu(T, H, d))
+    with pytest.raises(ValueError, match="GPU"):
+        kda._fwd_problem(**good, S0=_cpu(1, H, d, d, dtype=torch.float32),
+                         cu_seqlens=torch.tensor([0, 70], dtype=torch.int32))
+    for kw in (dict(S0=_cpu(1, H, d, d)),                                   # bf16 state
+               dict(S0=_cpu(2, H, d, d, dtype=torch.float32)),              # wrong N
+               dict(cu_seqlens=torch.tensor([0, 30, 70], dtype=torch.int64)),
+               dict(cu_seqlens=torch.tensor([[0, 70]], dtype=torch.int32)),
+               dict(cu_seqlens=torch.tensor([0], dtype=torch.int32))):
+        with pytest.raises(ValueError):
+            try:
+                kda._fwd_problem(**good, **kw)
+            except ValueError as e:
+                assert "GPU" not in str(e), "the device check came first: %s" % e
+                raise

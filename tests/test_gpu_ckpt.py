@@ -1,6 +1,7 @@
 """Prefix-cache checkpoints (kda_chunk_fwd_ckpt): the state after every
 `every`-th chunk of each sequence, against the fp64 oracle run on that
-prefix; o and S_T unchanged from kda_chunk_fwd; no other slot written."""
+prefix; o and S_T unchanged from kda_chunk_fwd; the checkpoints packed in
+sequence order and no slot past the last one written."""
 import sys
 
 import numpy as np
@@ -31,7 +32,8 @@ def torch_dev():
     ((700, 64, 1100, 0, 513), 2, 128, 2, True),
     ((700, 64, 1100, 0, 513), 2, 64, 8, True),
     ((600, 600), 3, 128, 3, False),
-], ids=["varlen-d128-every2", "varlen-d64-every8", "equal-d128-every3"])
+    ((64, 63, 65, 1, 200, 128), 2, 64, 1, True),
+], ids=["varlen-d128-every2", "varlen-d64-every8", "equal-d128-every3", "varlen-d64-every1"])
 def test_checkpoints_match_prefix_oracle(torch_dev, lengths, H, d, every, varlen):
     torch, dev = torch_dev
     import gated_delta_rule_30_amd as kda
@@ -42,7 +44,7 @@ def test_checkpoints_match_prefix_oracle(torch_dev, lengths, H, d, every, varlen
     S0 = torch.from_numpy(inp.S0).to(dev)
     cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev) if varlen else None
     N = len(lengths)
-    nbytes = kda._load().kda_chunk_ckpt_size(spec.total_tokens, N, H, d, d)
+    nbytes = kda.ckpt_size(spec.total_tokens, N, H, d, d, every)
     S_ckpt = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device=dev).view(-1, H, d, d)
     o, ST, _ = kda.chunk_fwd_ckpt(q, k, v, beta, g, every, S_ckpt=S_ckpt, S0=S0, cu_seqlens=cu, n_seqs=N)
     o_ref, ST_ref = kda.chunk_fwd(q, k, v, beta, g, S0=S0, cu_seqlens=cu, n_seqs=N)
@@ -66,5 +68,6 @@ def test_checkpoints_match_prefix_oracle(torch_dev, lengths, H, d, every, varlen
     _say("%s H=%d d=%d every=%d: %d checkpoints, worst %.2e" % (lengths, H, d, every, len(written), worst))
     assert written, "no checkpoint in this case"
     assert worst <= TOL
-    untouched = [s for s in range(ck.shape[0]) if s not in written]
-    assert np.all(np.isnan(ck[untouched])), "a slot that is no checkpoint was written"
+    assert written == set(range(len(written))), "checkpoints are not packed from slot 0"
+    assert len(written) <= ck.shape[0]
+    assert np.all(np.isnan(ck[len(written):])), "a slot past the last checkpoint was written"

@@ -288,3 +288,25 @@ def test_config4_1m_full(torch_dev):
     _full_check(torch, inp, o, ST, "config 4", [[0]], [list(range(h, h + 4)) for h in range(0, 16, 4)])
     del inp, o, ST
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("lengths,H,d,s0", [((135000, 135000), 2, 128, 0.02), ((140000,), 3, 64, 0.0)],
+                         ids=["2seq-d128-S0", "1seq-d64-zeroS0"])
+def test_pipelined_forward(torch_dev, lengths, H, d, s0):
+    """Equal-length sequences of more than 2048 chunks whose recurrence fills
+    at most half of the CUs take the pipelined path (k_prep of the next token
+    block on a side stream while the recurrence works on this one, state
+    handed between blocks in fp32): every (sequence, head) slice against the
+    oracle, and bit for bit equal to the same kernels run one after another
+    (the measurement entry point does not pipeline)."""
+    torch, dev = torch_dev
+    import gated_delta_rule_30_amd as kda
+    spec = ki.custom("pipe", "bf16", list(lengths), H, d, s0_std=s0, varlen=False, seed=21)
+    inp = ki.generate_torch(spec, dev)
+    N = spec.n_seqs
+    _say("pipelined forward: %s H=%d d=%d" % (lengths, H, d))
+    o, ST = kda.chunk_fwd(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, n_seqs=N)
+    o2, ST2, _ = kda.chunk_fwd_profile(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, n_seqs=N)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(ST, ST2), "pipelined and sequential launches differ"
+    _full_check(torch, inp, o, ST, "pipelined", [[n] for n in range(N)], [list(range(H))])

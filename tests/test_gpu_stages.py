@@ -109,10 +109,12 @@ def test_stages_match_chunked_model(torch_dev, lengths, H, d):
     S0 = torch.from_numpy(inp.S0).to(dev)
     cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
     mc = T // C + N
-    # forward workspace: n_chunks, seq_chunk0, chunk table, TB, M, Qg, Kg, KhT, Gamma_L, and last the
-    # recurrence's per-workgroup step counts
+    # forward workspace: n_chunks, seq_chunk0, chunk table, TB, M, Qg, Kg, KhT, Gamma_L, the two states
+    # between pipelined blocks, the first checkpoint slot per sequence, and last the recurrence's
+    # per-workgroup step counts
     sizes = [4, 4 * (N + 1), 16 * mc, 2 * mc * H * C * C, 2 * mc * H * C * C, 2 * mc * H * C * d,
-             2 * mc * H * C * d, 2 * mc * H * d * C, 4 * mc * H * d, 4 * N * H * (d // 16)]
+             2 * mc * H * C * d, 2 * mc * H * d * C, 4 * mc * H * d, 4 * 2 * N * H * d * d, 4 * (N + 1),
+             4 * N * H * (d // 16)]
     offs, total = _carve(sizes)
     assert total == kda.workspace_size(T, N, H, d, d)
     ws = torch.zeros(total, dtype=torch.uint8, device=dev)
