@@ -91,6 +91,33 @@ kda_status kda_chunk_fwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int
                          void* o, float* S_T,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Size of the device array that kda_chunk_fwd_noalloc uses as its workspace
+ * (64 MiB: about 60,000 (token, head) pairs at d_k = d_v = 128, e.g. 3,584
+ * tokens x 16 heads). */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* kda_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, kernels and results, minus the workspace, which is a
+ * fixed device array of KDA_NOALLOC_SCRATCH_BYTES inside this library (one
+ * per GPU, held until the process ends; its address is looked up once per
+ * GPU, with that GPU current, on the first call there).  The call allocates
+ * nothing and never uses a second stream.
+ * Errors: as kda_chunk_fwd; KDA_ERR_WORKSPACE when
+ * kda_chunk_fwd_workspace_size(...) exceeds KDA_NOALLOC_SCRATCH_BYTES;
+ * KDA_ERR_HIP if the array's address cannot be found.
+ * All calls on one GPU share the array: calls that overlap in time on one
+ * GPU (on different streams, or from several threads without ordering)
+ * race and give wrong results.  Calls on one stream are ordered and safe.
+ * Nothing in the array needs to start at zero (each call writes every
+ * region it later reads). */
+kda_status kda_chunk_fwd_noalloc(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
+                                 int32_t d_k, int32_t d_v, int32_t chunk,
+                                 const void* q, const void* k, const void* v,
+                                 const void* beta, const void* log_alpha,
+                                 const float* S0, const int32_t* cu_seqlens,
+                                 void* o, float* S_T, void* stream);
+
 /* Bytes of the state-checkpoint buffer kda_chunk_fwd_ckpt writes into for a
  * given `every`: floor((floor(total_tokens / 64) + n_seqs) / every) slots x
  * n_heads x d_k x d_v float32 -- an upper bound on the checkpoints any
