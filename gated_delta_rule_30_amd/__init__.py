@@ -203,6 +203,9 @@ def chunk_fwd(q, k, v, beta, log_alpha, S0=None, cu_seqlens=None, chunk: int = C
     [N+1] (packed variable-length batch) or None (B equal sequences for 4-D
     inputs, one sequence for 3-D inputs; `n_seqs` overrides).  Optional
     preallocated `o`, `S_T` and `workspace` (uint8) tensors are used as given.
+    `chunk`: 16, 32, 64 or 128 tokens; d_k, d_v: 64 or 128.  Chunk 64 with
+    d_k == d_v (bf16 at 64 or 128, fp32 at 64) runs the tuned kernels, every
+    other supported size the generic fp32 ones (same results to rounding).
     Returns (o, S_T) with o shaped like v and S_T None unless requested.
     """
     import torch

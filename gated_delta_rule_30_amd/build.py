@@ -12,6 +12,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkda.so")
 SOURCES = [os.path.join(CSRC, "kda_kernels.hip"), os.path.join(CSRC, "kda_aux.hip"),
            os.path.join(CSRC, "kda_bwd.hip"), os.path.join(CSRC, "kda_noalloc.hip"),
+           os.path.join(CSRC, "kda_generic.hip"),
            os.path.join(CSRC, "kda_api.cpp")]
 
 # Device flags: gfx950 only; packed-fp32 instructions are turned off (the

@@ -28,6 +28,16 @@ size_t carve_workspace(Plan* p, void* base) {
     p->ws_n_chunks = (int32_t*)take(sizeof(int32_t));
     p->ws_seq_chunk0 = (int32_t*)take(sizeof(int32_t) * ((size_t)p->n_seqs + 1));
     p->ws_tab = (ChunkInfo*)take(sizeof(ChunkInfo) * mc);
+    if (p->generic) {   // fp32 operands of the generic kernels (kda_generic.hip)
+        const size_t C = (size_t)p->chunk, DK = (size_t)p->d_k;
+        p->ws_Qg = take(4 * mc * H * C * DK);
+        p->ws_Kg = take(4 * mc * H * C * DK);
+        p->ws_KhT = take(4 * mc * H * C * DK);
+        p->ws_TB = take(4 * mc * H * C * C);
+        p->ws_M = take(4 * mc * H * C * C);
+        p->ws_gam = (float*)take(4 * mc * H * DK);
+        return off;
+    }
     if (kind != kWsBwdCtx) {   // the forward operand set
         p->ws_TB = take(es * mc * H * kChunkTokens * kChunkTokens);
         p->ws_M = take(es * mc * H * kChunkTokens * kChunkTokens);
@@ -88,19 +98,33 @@ size_t carve_context(Plan* p, void* base) {
 
 using kda::Plan;
 
+// The sizes the tuned kernels cover: chunk 64, d_k = d_v, bf16 at 64 or 128, fp32 at 64.
+static bool tuned_sizes(kda_dtype dt, int32_t d_k, int32_t d_v, int32_t chunk) {
+    return chunk == kda::kChunkTokens && d_k == d_v && (d_k == 64 || (d_k == 128 && dt == KDA_BF16));
+}
+
+// `generic_ok`: the forward, which runs every other supported size (chunk
+// 16, 32, 64 or 128; d_k, d_v in {64, 128}; either dtype) on the generic
+// kernels; every other entry point takes the tuned sizes only.
 static kda_status plan_sizes(Plan* p, kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
-                             int32_t d_k, int32_t d_v, int32_t chunk, bool varlen) {
+                             int32_t d_k, int32_t d_v, int32_t chunk, bool varlen, bool generic_ok = false) {
     if (dt != KDA_F32 && dt != KDA_BF16) return KDA_ERR_DTYPE;
     if (total_tokens < 0 || n_seqs < 1 || n_heads < 1 || d_k < 1 || d_v < 1 || chunk < 1) return KDA_ERR_SHAPE;
     if (!varlen && total_tokens % n_seqs != 0) return KDA_ERR_SHAPE;
-    if (d_k != d_v || (d_k != 64 && d_k != 128) || chunk != kda::kChunkTokens) return KDA_ERR_UNSUPPORTED;
-    if (dt == KDA_F32 && d_k != 64) return KDA_ERR_UNSUPPORTED;
+    if ((d_k != 64 && d_k != 128) || (d_v != 64 && d_v != 128)) return KDA_ERR_UNSUPPORTED;
+    if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128) return KDA_ERR_UNSUPPORTED;
+    const bool tuned = tuned_sizes(dt, d_k, d_v, chunk);
+    if (!tuned && !generic_ok) return KDA_ERR_UNSUPPORTED;
     if (total_tokens >= ((int64_t)1 << 31) || n_heads > 65535) return KDA_ERR_UNSUPPORTED;
-    const int64_t max_chunks = total_tokens / kda::kChunkTokens + n_seqs;
+    const int64_t max_chunks = total_tokens / chunk + n_seqs;
     if (max_chunks >= ((int64_t)1 << 31) || (int64_t)n_seqs * n_heads * (d_v / 16) >= ((int64_t)1 << 31))
         return KDA_ERR_UNSUPPORTED;
     p->bf16 = dt == KDA_BF16;
     p->d = d_k;
+    p->generic = !tuned;
+    p->chunk = chunk;
+    p->d_k = d_k;
+    p->d_v = d_v;
     p->total_tokens = total_tokens;
     p->n_seqs = n_seqs;
     p->n_heads = n_heads;
@@ -115,15 +139,17 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_
                                     int32_t d_v, int32_t chunk, kda_dtype dt) {
     Plan p{};
     // Size for the variable-length case: it never needs less than equal lengths.
-    if (plan_sizes(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, true) != KDA_OK) return 0;
+    if (plan_sizes(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, true, true) != KDA_OK) return 0;
     return kda::carve_workspace(&p, nullptr);
 }
 
 static kda_status prepare(Plan* p, kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
                           int32_t d_k, int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
                           const void* beta, const void* log_alpha, const float* S0, const int32_t* cu_seqlens,
-                          void* o, float* S_T, void* workspace, size_t workspace_bytes, bool no_output = false) {
-    kda_status s = plan_sizes(p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, cu_seqlens != nullptr);
+                          void* o, float* S_T, void* workspace, size_t workspace_bytes, bool no_output = false,
+                          bool generic_ok = false) {
+    kda_status s = plan_sizes(p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, cu_seqlens != nullptr,
+                              generic_ok);
     if (s != KDA_OK) return s;
     if (total_tokens > 0 && (!q || !k || !v || !beta || !log_alpha || (!o && !no_output))) return KDA_ERR_NULL;
     const void* ptrs[] = {q, k, v, beta, log_alpha, S0, cu_seqlens, o, S_T};
@@ -198,7 +224,7 @@ kda_status kda_chunk_fwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_s
     if (!stage_ms) return KDA_ERR_NULL;
     Plan p{};
     kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
-                           cu_seqlens, o, S_T, workspace, workspace_bytes);
+                           cu_seqlens, o, S_T, workspace, workspace_bytes, false, true);
     if (s != KDA_OK) return s;
     hipEvent_t ev[kda::kNumStages + 1];
     int made = 0;
@@ -500,7 +526,7 @@ kda_status kda::chunk_fwd_entry(kda_dtype dt, int64_t total_tokens, int32_t n_se
                                 size_t workspace_bytes, void* stream, bool pipeline) {
     Plan p{};
     kda_status s = prepare(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha, S0,
-                           cu_seqlens, o, S_T, workspace, workspace_bytes);
+                           cu_seqlens, o, S_T, workspace, workspace_bytes, false, true);
     if (s != KDA_OK) return s;
     p.no_pipeline = !pipeline;
     hipError_t e = kda::launch(p, static_cast<hipStream_t>(stream));

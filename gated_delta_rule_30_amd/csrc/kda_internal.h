@@ -17,7 +17,14 @@ struct ChunkInfo {
 
 struct Plan {
     bool bf16;
-    int d;                    // d_k == d_v
+    int d;                    // d_k == d_v (the tuned kernels); d_k for the generic ones
+    // The generic kernels (kda_generic.hip): any chunk size and d_k, d_v the
+    // tuned ones do not cover.  Their workspace reuses the operand fields
+    // below as fp32 arrays: ws_Qg, ws_Kg, ws_KhT (K . exp(b_L - b), rows)
+    // [H, max_chunks, chunk, d_k], ws_TB and ws_M [H, max_chunks, chunk,
+    // chunk], ws_gam [H, max_chunks, d_k].
+    bool generic;
+    int32_t chunk, d_k, d_v;     // chunk tokens and head dims (all plans)
     int64_t total_tokens;
     int32_t n_seqs, n_heads;
     int64_t fixed_len;        // tokens per sequence when cu_seqlens is NULL
@@ -98,6 +105,12 @@ kda_status chunk_fwd_entry(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, i
                            int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v, const void* beta,
                            const void* log_alpha, const float* S0, const int32_t* cu_seqlens, void* o, float* S_T,
                            void* workspace, size_t workspace_bytes, void* stream, bool pipeline);
+
+// The chunk table for chunks of `chunk` tokens (k_chunk_table).
+void launch_chunk_table(const Plan& p, int32_t chunk, hipStream_t stream);
+
+// The forward pass with the generic kernels (p.generic), same events as launch().
+hipError_t launch_generic(const Plan& p, hipStream_t stream, hipEvent_t* ev);
 
 // Kernel launches of one forward pass, in order.
 constexpr int kNumStages = 3;

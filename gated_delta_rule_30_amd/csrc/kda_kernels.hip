@@ -86,7 +86,7 @@ __device__ inline void seq_chunks(const int32_t* __restrict__ cu, const int32_t*
 }
 
 // ---------------------------------------------------------------- chunk table
-// One workgroup.  Sequence n contributes ceil(len_n / 64) chunks; chunks are
+// One workgroup.  Sequence n contributes ceil(len_n / C) chunks; chunks are
 // aligned to each sequence's first token and the last one may be partial.
 // Sequences are taken 1024 at a time: a prefix sum of their chunk counts
 // gives each one's first chunk, then the whole workgroup writes the batch's
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
                                                       int32_t max_chunks, ChunkInfo* __restrict__ tab,
                                                       int32_t* __restrict__ seq_chunk0,
                                                       int32_t* __restrict__ n_chunks_out, int32_t every,
-                                                      int32_t* __restrict__ ck0) {
+                                                      int32_t* __restrict__ ck0, int32_t C) {
     __shared__ int32_t s_scan[1024];     // inclusive prefix sum of chunk counts in the batch
     __shared__ int32_t s_ck[1024];       // the same for checkpoint counts (every > 0)
     __shared__ int64_t s_start[1024];
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
         const int32_t n = base + tid;
         int64_t start = 0, len = 0;
         if (n < n_seqs) seq_range(cu, n, total_tokens, fixed_len, start, len);
-        const int32_t cnt = (int32_t)((len + kChunk - 1) / kChunk);
+        const int32_t cnt = (int32_t)((len + C - 1) / C);
         const int32_t ckc = every > 0 ? cnt / every : 0;
         s_scan[tid] = cnt;
         s_ck[tid] = ckc;
@@ -148,10 +148,10 @@ __global__ __launch_bounds__(1024) void k_chunk_table(const int32_t* __restrict_
             }
             const int32_t j = c - (lo > 0 ? s_scan[lo - 1] : 0);
             ChunkInfo ci;
-            ci.tok0 = s_start[lo] + (int64_t)j * kChunk;
+            ci.tok0 = s_start[lo] + (int64_t)j * C;
             ci.seq = base + lo;
-            const int64_t rem = s_len[lo] - (int64_t)j * kChunk;
-            ci.len = (int32_t)(rem < kChunk ? rem : kChunk);
+            const int64_t rem = s_len[lo] - (int64_t)j * C;
+            ci.len = (int32_t)(rem < C ? rem : C);
             tab[cg] = ci;
         }
         __syncthreads();
@@ -1676,11 +1676,13 @@ static void launch_recur_lds(const Plan& p, const void* v, const float* S0, floa
                        static_cast<__bf16*>(o), aux, jb, je);
 }
 
-static void launch_table(const Plan& p, hipStream_t st) {
+void launch_chunk_table(const Plan& p, int32_t chunk, hipStream_t st) {
     hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(1024), 0, st, p.cu_seqlens, p.n_seqs, p.total_tokens,
                        p.fixed_len, p.max_chunks, p.ws_tab, p.ws_seq_chunk0, p.ws_n_chunks,
-                       p.S_ckpt ? p.ck_every : 0, p.ws_ck0);
+                       p.S_ckpt ? p.ck_every : 0, p.ws_ck0, chunk);
 }
+
+static void launch_table(const Plan& p, hipStream_t st) { launch_chunk_table(p, kChunk, st); }
 
 // ---------------------------------------------------------------- pipelined forward
 // When the sequences have equal lengths and the recurrence's workgroups
@@ -1808,6 +1810,7 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
 const char* const kStageNames[kNumStages] = {"k_chunk_table", "k_prep", "k_recur"};
 
 hipError_t launch(const Plan& p, hipStream_t st, hipEvent_t* ev) {
+    if (p.generic) return launch_generic(p, st, ev);
     if (p.bf16) {
         if (p.d == 128) return launch_all<__bf16, 128>(p, st, ev);
         return launch_all<__bf16, 64>(p, st, ev);

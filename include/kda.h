@@ -39,9 +39,13 @@
  *     access outside the buffers described here).  Device-side cu_seqlens
  *     that break the rules above give unspecified results but every access
  *     stays inside the buffers.
- *   - Supported: dt == KDA_BF16 with d_k == d_v in {64, 128}, or
- *     dt == KDA_F32 with d_k == d_v == 64; chunk == 64; total_tokens < 2^31;
- *     n_heads <= 65535.  Anything else returns KDA_ERR_UNSUPPORTED.
+ *   - Supported by every entry point (the tuned sizes): chunk == 64 and
+ *     d_k == d_v, with dt == KDA_BF16 at d in {64, 128} or dt == KDA_F32 at
+ *     d == 64; total_tokens < 2^31; n_heads <= 65535.  kda_chunk_fwd,
+ *     kda_chunk_fwd_profile and kda_chunk_fwd_noalloc also take chunk in
+ *     {16, 32, 64, 128} with any d_k, d_v in {64, 128} and either dtype; the
+ *     sizes outside the tuned ones run untuned fp32 kernels (see
+ *     kda_chunk_fwd).  Anything else returns KDA_ERR_UNSUPPORTED.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -82,7 +86,16 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_
  *   stream     : HIP stream (hipStream_t) the work is queued on; NULL = default
  * total_tokens == 0 is valid: o is empty and S_T (if given) receives S0
  * (or zeros).  Every tensor pointer must be 16-byte aligned (KDA_ERR_SHAPE
- * otherwise). */
+ * otherwise).
+ * Chunk size and head dims: the result does not depend on the chunk size
+ * (up to rounding: the chunked form is an exact regrouping of the
+ * recurrence).  Chunk 64 with d_k == d_v (bf16 at 64 or 128, fp32 at 64)
+ * runs the tuned kernels (bf16 MFMA operands at bf16, fp32 at fp32); every
+ * other supported size -- chunk 16, 32 or 128, d_k != d_v, fp32 at 128 --
+ * runs generic kernels in fp32 arithmetic (no MFMA; the decay ratio of
+ * each token pair and channel formed directly), correct to the same bars but
+ * not tuned for speed.  Their workspace is fp32: about
+ * 4 (3 d_k + 2 chunk + d_k / chunk) bytes per (token, head). */
 kda_status kda_chunk_fwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
                          int32_t d_k, int32_t d_v, int32_t chunk,
                          const void* q, const void* k, const void* v,
@@ -163,7 +176,9 @@ kda_status kda_chunk_fwd_ckpt(kda_dtype dt, int64_t total_tokens, int32_t n_seqs
  * (it synchronises on its last event), then writes each launch's duration in
  * milliseconds to stage_ms[0 .. kda_profile_num_stages()-1] (host memory,
  * required).  It creates and destroys its events; it allocates no device
- * memory.  Errors as for kda_chunk_fwd; KDA_ERR_NULL if stage_ms is NULL. */
+ * memory.  Errors as for kda_chunk_fwd; KDA_ERR_NULL if stage_ms is NULL.
+ * On the generic sizes stage 1 ("k_prep") times the two chunk-parallel
+ * kernels together and stage 2 ("k_recur") the sequential one. */
 kda_status kda_chunk_fwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
                                  int32_t d_k, int32_t d_v, int32_t chunk,
                                  const void* q, const void* k, const void* v,

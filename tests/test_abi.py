@@ -47,10 +47,14 @@ def test_status_strings(lib):
 def test_workspace_size():
     a = kda.workspace_size(65536, 1, 32, 128, 128, 64, kda.KDA_BF16)
     b = kda.workspace_size(65536, 1, 32, 128, 128, 64, kda.KDA_F32)
-    assert a > 0 and b == 0                    # fp32 operands only at d = 64
+    assert a > 0 and b > 0                     # fp32 at d = 128: the generic kernels
     assert kda.workspace_size(256, 1, 2, 64, 64, 64, kda.KDA_F32) > 0
     assert kda.workspace_size(256, 1, 2, 96, 96, 64, kda.KDA_BF16) == 0
-    assert kda.workspace_size(256, 1, 2, 64, 64, 32, kda.KDA_BF16) == 0
+    assert kda.workspace_size(256, 1, 2, 64, 96, 64, kda.KDA_BF16) == 0
+    for C in (16, 32, 128):
+        assert kda.workspace_size(256, 1, 2, 64, 64, C, kda.KDA_BF16) > 0
+    for C in (0, 8, 48, 96, 256):
+        assert kda.workspace_size(256, 1, 2, 64, 64, C, kda.KDA_BF16) == 0
     assert kda.workspace_size(-1, 1, 2, 64, 64, 64, kda.KDA_BF16) == 0
     assert kda.workspace_size(1 << 31, 1, 2, 64, 64, 64, kda.KDA_BF16) == 0
     # monotone in tokens and heads; 256-byte granularity
@@ -59,6 +63,22 @@ def test_workspace_size():
     s3 = kda.workspace_size(1000, 3, 8, 64, 64, 64, kda.KDA_BF16)
     assert s1 < s2 and s1 < s3 and s1 % 256 == 0
     assert kda.workspace_size(0, 2, 4, 128, 128, 64, kda.KDA_BF16) > 0
+
+
+@pytest.mark.parametrize("T,N,H,dk,dv,C,dt", [(1000, 3, 4, 64, 128, 32, kda.KDA_BF16),
+                                              (65536, 1, 32, 128, 128, 128, kda.KDA_BF16),
+                                              (4096, 2, 2, 128, 64, 16, kda.KDA_F32),
+                                              (777, 5, 3, 128, 128, 64, kda.KDA_F32)])
+def test_generic_workspace_size(T, N, H, dk, dv, C, dt):
+    """The sizes outside the tuned ones take fp32 operands: per chunk slot
+    and head, Q.e^b, K.e^b, K.e^{b_L-b} (C x d_k each), T diag(beta) and M
+    (C x C each) and e^{b_L} (d_k), plus the chunk table; every region
+    rounded up to 256 bytes."""
+    mc = T // C + N
+    up = lambda x: (x + 255) // 256 * 256
+    expect = up(4) + up(4 * (N + 1)) + up(16 * mc)
+    expect += 3 * up(4 * mc * H * C * dk) + 2 * up(4 * mc * H * C * C) + up(4 * mc * H * dk)
+    assert kda.workspace_size(T, N, H, dk, dv, C, dt) == expect
 
 
 def _call(lib, dt=kda.KDA_BF16, T=128, N=1, H=2, dk=64, dv=64, C=64, ptrs=None, S0=None, cu=None,
@@ -80,10 +100,15 @@ def test_rejects_bad_arguments(lib):
     assert _call(lib, N=0) == ERR_SHAPE
     assert _call(lib, H=0) == ERR_SHAPE
     assert _call(lib, T=100, N=3) == ERR_SHAPE              # equal lengths must divide
-    assert _call(lib, dk=64, dv=128) == ERR_UNSUPPORTED
     assert _call(lib, dk=96, dv=96) == ERR_UNSUPPORTED
-    assert _call(lib, C=128) == ERR_UNSUPPORTED
-    assert _call(lib, dt=kda.KDA_F32, dk=128, dv=128) == ERR_UNSUPPORTED
+    assert _call(lib, dk=64, dv=32) == ERR_UNSUPPORTED
+    for C in (0, 8, 48, 256):
+        assert _call(lib, C=C) == (ERR_SHAPE if C == 0 else ERR_UNSUPPORTED), C
+    # the generic sizes are accepted (and fail here on the missing workspace)
+    assert _call(lib, dk=64, dv=128) == ERR_WORKSPACE
+    assert _call(lib, C=128) == ERR_WORKSPACE
+    assert _call(lib, C=16, dk=128) == ERR_WORKSPACE
+    assert _call(lib, dt=kda.KDA_F32, dk=128, dv=128) == ERR_WORKSPACE
     assert _call(lib, T=1 << 31) == ERR_UNSUPPORTED
     assert _call(lib, H=70000) == ERR_UNSUPPORTED
     for name in ("q", "k", "v", "beta", "g", "o"):
@@ -298,6 +323,11 @@ def test_checkpoint_size_and_rejections(lib):
         return lib.kda_chunk_fwd_ckpt(dt, 128, 1, 2, 64, 64, 64, a16, a16, a16, a16, a16, None, None,
                                       a16, None, every, sck, sck_bytes, ws, ws_bytes, None)
     assert call(dt=kda.KDA_F32) == ERR_UNSUPPORTED
+    for C in (16, 32, 128):   # the generic sizes are the plain forward's only
+        assert lib.kda_chunk_fwd_ckpt(kda.KDA_BF16, 128, 1, 2, 64, 64, C, a16, a16, a16, a16, a16, None, None,
+                                      a16, None, 2, a16, need, a16, 1 << 40, None) == ERR_UNSUPPORTED
+        assert kda.bwd_workspace_size(128, 1, 2, 64, 64, C, kda.KDA_BF16) == 0
+    assert kda.bwd_workspace_size(128, 1, 2, 64, 128, 64, kda.KDA_BF16) == 0
     assert call(every=0) == ERR_SHAPE
     assert call(every=-3) == ERR_SHAPE
     assert call(sck=None) == ERR_NULL

@@ -184,16 +184,19 @@ def _slice_errors(x, ref):
     return err
 
 
-def _full_check(torch, inp, o_dev, ST_dev, what, seq_groups, head_groups):
+def _full_check(torch, inp, o_dev, ST_dev, what, seq_groups, head_groups, extra=()):
     """Every (sequence, head) slice of o (within the workload's output
     window) and of S_T against the oracle, run group by group on the exact
-    values the kernels read (copied back from the device).  Prints the worst
-    slice and the slices whose element offsets pass 2^31; returns the worst
-    errors."""
+    values the kernels read (copied back from the device).  `extra` holds
+    more (label, o, S_T) results of the same inputs (other chunk sizes),
+    checked against the same oracle output.  Prints the worst slice of each
+    and the slices whose element offsets pass 2^31; returns the first run's
+    worst errors and that slice count."""
     cu = inp.cu_seqlens
     lo_w, hi_w = inp.window
     H, d = inp.q.shape[1], inp.q.shape[2]
-    worst = {"o": (0.0, None), "S_T": (0.0, None)}
+    runs = [(what, o_dev, ST_dev)] + list(extra)
+    worst = {name: {"o": (0.0, None), "S_T": (0.0, None)} for name, _, _ in runs}
     big_slices = 0
     for seqs in seq_groups:
         a, b = int(cu[seqs[0]]), int(cu[seqs[-1] + 1])
@@ -207,39 +210,48 @@ def _full_check(torch, inp, o_dev, ST_dev, what, seq_groups, head_groups):
             t0 = time.time()
             o_ref, S_ref = oracle.forward(q, k, v, beta, g, S0, lcu,
                                           out_range=(max(wlo - a, 0), max(whi - a, 0)))
-            o_gpu = o_dev[max(wlo, a):max(whi, a), hs].float().cpu().numpy()
-            S_gpu = ST_dev[seqs[0]:seqs[-1] + 1, hs].cpu().numpy()
-            assert o_gpu.shape == o_ref.shape and S_gpu.shape == S_ref.shape, (o_gpu.shape, o_ref.shape)
-            g_o = g_s = 0.0
-            for i, n in enumerate(seqs):
-                sa, sb = int(cu[n]), int(cu[n + 1])
-                oa, ob = max(sa, wlo), min(sb, whi)
-                if ob > oa:
-                    e = _slice_errors(o_gpu[oa - wlo:ob - wlo], o_ref[oa - wlo:ob - wlo])
-                    h = int(np.argmax(e))
-                    g_o = max(g_o, float(e[h]))
-                    if e[h] > worst["o"][0] or worst["o"][1] is None:
-                        worst["o"] = (float(e[h]), (n, heads[0] + h))
-                es = _slice_errors(S_gpu[i:i + 1].transpose(1, 0, 2, 3), S_ref[i:i + 1].transpose(1, 0, 2, 3))
-                h = int(np.argmax(es))
-                g_s = max(g_s, float(es[h]))
-                if es[h] > worst["S_T"][0] or worst["S_T"][1] is None:
-                    worst["S_T"] = (float(es[h]), (n, heads[0] + h))
-                if (int(cu[n + 1]) * H * d) > 2 ** 31:
-                    big_slices += len(heads)
-            _say("%s seqs %d..%d (tokens %d..%d) heads %d..%d: o %.3e S_T %.3e (oracle %.1fs)"
-                 % (what, seqs[0], seqs[-1], a, b, heads[0], heads[-1], g_o, g_s, time.time() - t0))
-    _say("%s worst slice: o %.3e at (seq, head) %s; S_T %.3e at %s; %d slices reach element offsets past 2^31"
-         % (what, worst["o"][0], worst["o"][1], worst["S_T"][0], worst["S_T"][1], big_slices))
-    assert worst["o"][0] <= TOL["bf16"] and worst["S_T"][0] <= TOL["bf16"], worst
-    return worst, big_slices
+            t_or = time.time() - t0
+            for name, o_d, ST_d in runs:
+                w = worst[name]
+                o_gpu = o_d[max(wlo, a):max(whi, a), hs].float().cpu().numpy()
+                S_gpu = ST_d[seqs[0]:seqs[-1] + 1, hs].cpu().numpy()
+                assert o_gpu.shape == o_ref.shape and S_gpu.shape == S_ref.shape, (o_gpu.shape, o_ref.shape)
+                g_o = g_s = 0.0
+                for i, n in enumerate(seqs):
+                    sa, sb = int(cu[n]), int(cu[n + 1])
+                    oa, ob = max(sa, wlo), min(sb, whi)
+                    if ob > oa:
+                        e = _slice_errors(o_gpu[oa - wlo:ob - wlo], o_ref[oa - wlo:ob - wlo])
+                        h = int(np.argmax(e))
+                        g_o = max(g_o, float(e[h]))
+                        if e[h] > w["o"][0] or w["o"][1] is None:
+                            w["o"] = (float(e[h]), (n, heads[0] + h))
+                    es = _slice_errors(S_gpu[i:i + 1].transpose(1, 0, 2, 3), S_ref[i:i + 1].transpose(1, 0, 2, 3))
+                    h = int(np.argmax(es))
+                    g_s = max(g_s, float(es[h]))
+                    if es[h] > w["S_T"][0] or w["S_T"][1] is None:
+                        w["S_T"] = (float(es[h]), (n, heads[0] + h))
+                    if name == what and (int(cu[n + 1]) * H * d) > 2 ** 31:
+                        big_slices += len(heads)
+                _say("%s seqs %d..%d (tokens %d..%d) heads %d..%d: o %.3e S_T %.3e (oracle %.1fs)"
+                     % (name, seqs[0], seqs[-1], a, b, heads[0], heads[-1], g_o, g_s, t_or))
+    for name, _, _ in runs:
+        w = worst[name]
+        _say("%s worst slice: o %.3e at (seq, head) %s; S_T %.3e at %s"
+             % (name, w["o"][0], w["o"][1], w["S_T"][0], w["S_T"][1]))
+    _say("%s: %d slices reach element offsets past 2^31" % (what, big_slices))
+    for name, _, _ in runs:
+        w = worst[name]
+        assert w["o"][0] <= TOL["bf16"] and w["S_T"][0] <= TOL["bf16"], (name, w)
+    return worst[what], big_slices
 
 
-def _run_torch_inputs(torch, inp):
+def _run_torch_inputs(torch, inp, chunk=64):
     import gated_delta_rule_30_amd as kda
     s = inp.spec
     cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(inp.q.device) if s.varlen else None
-    o, ST = kda.chunk_fwd(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, cu_seqlens=cu, n_seqs=s.n_seqs)
+    o, ST = kda.chunk_fwd(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, cu_seqlens=cu, n_seqs=s.n_seqs,
+                          chunk=chunk)
     torch.cuda.synchronize()
     return o, ST
 
@@ -247,46 +259,55 @@ def _run_torch_inputs(torch, inp):
 @pytest.mark.timeout(900)
 def test_config2_headline_full(torch_dev):
     """B=1, H=32, T=65536, d=128, S0 ~ 0.02 N(0,1), launched as the
-    benchmark launches it: all 32 heads of o and S_T against the oracle."""
+    benchmark launches it: all 32 heads of o and S_T against the oracle; the
+    same at chunk 128 (the generic kernels) against the same oracle run."""
     torch, dev = torch_dev
     spec = ki.headline_configs()[2]
     _say("config 2 generate (torch, on device)")
     inp = ki.generate_torch(spec, dev)
     o, ST = _run_torch_inputs(torch, inp)
-    _full_check(torch, inp, o, ST, "config 2", [[0]], [list(range(0, 16)), list(range(16, 32))])
-    del inp, o, ST
+    o128, ST128 = _run_torch_inputs(torch, inp, chunk=128)
+    _full_check(torch, inp, o, ST, "config 2", [[0]], [list(range(0, 16)), list(range(16, 32))],
+                extra=[("config 2 chunk 128", o128, ST128)])
+    del inp, o, ST, o128, ST128
     torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)
 def test_config3_varlen_full(torch_dev):
     """64 packed sequences (L ~ U[512, 16384], 550,809 tokens), H=32, d=128,
-    25 % of channels at g = -5: every (sequence, head) slice of o and S_T.
-    Sequences 60-63 sit at element offsets past 2^31 (from token 524,288)."""
+    25 % of channels at g = -5: every (sequence, head) slice of o and S_T,
+    at chunk 64 and at chunk 128.  Sequences 60-63 sit at element offsets
+    past 2^31 (from token 524,288)."""
     torch, dev = torch_dev
     spec = ki.headline_configs()[3]
     _say("config 3 generate (torch, on device), T_total=%d" % spec.total_tokens)
     inp = ki.generate_torch(spec, dev)
     o, ST = _run_torch_inputs(torch, inp)
+    o128, ST128 = _run_torch_inputs(torch, inp, chunk=128)
     groups = [list(range(i, min(i + 8, spec.n_seqs))) for i in range(0, spec.n_seqs, 8)]
-    _, big = _full_check(torch, inp, o, ST, "config 3", groups, [list(range(32))])
+    _, big = _full_check(torch, inp, o, ST, "config 3", groups, [list(range(32))],
+                         extra=[("config 3 chunk 128", o128, ST128)])
     assert big >= 4 * 32, "the slices past 2^31 element offsets must be among those compared"
-    del inp, o, ST
+    del inp, o, ST, o128, ST128
     torch.cuda.empty_cache()
 
 
 @pytest.mark.timeout(900)
 def test_config4_1m_full(torch_dev):
     """B=1, H=16, T=1,048,576, d=128, S0 ~ 0.02 N(0,1): all 16 heads, o on
-    the seeded 8192-token window and S_T (the oracle runs all 1M tokens)."""
+    the seeded 8192-token window and S_T (the oracle runs all 1M tokens), at
+    chunk 64 and at chunk 128."""
     torch, dev = torch_dev
     spec = ki.headline_configs()[4]
     _say("config 4 generate (torch, on device)")
     inp = ki.generate_torch(spec, dev)
     o, ST = _run_torch_inputs(torch, inp)
+    o128, ST128 = _run_torch_inputs(torch, inp, chunk=128)
     _say("config 4 window %s" % (inp.window,))
-    _full_check(torch, inp, o, ST, "config 4", [[0]], [list(range(h, h + 4)) for h in range(0, 16, 4)])
-    del inp, o, ST
+    _full_check(torch, inp, o, ST, "config 4", [[0]], [list(range(h, h + 4)) for h in range(0, 16, 4)],
+                extra=[("config 4 chunk 128", o128, ST128)])
+    del inp, o, ST, o128, ST128
     torch.cuda.empty_cache()
 
 
