@@ -52,6 +52,17 @@ def kernel_bytes_per_token_head(name, C, D, es=2):
     }[name]
 
 
+def generic_bytes_per_token_head(name, C, D, es=2):
+    """The same for the generic kernels (chunk sizes other than 64): the
+    chunk-parallel stage reads q, k, g, beta and writes fp32 Q.e^b, K.e^b,
+    K.e^{b_L-b}, T diag(beta), M and e^{b_L} (A is written and read back
+    once more in between); the sequential stage reads those and v and
+    writes o."""
+    ops = 4 * (3 * D + 2 * C + D / C)
+    return {"k_prep": 3 * es * D + es + ops + 2 * 4 * C, "k_recur": ops + 2 * es * D,
+            "k_chunk_table": 0.0}[name]
+
+
 # kernel -> the sources its code comes from (for matching committed counter summaries)
 KERNEL_SOURCES = {"k_prep": ("kda_kernels.hip", "kda_device.h"), "k_recur": ("kda_kernels.hip", "kda_device.h"),
                   "k_chunk_table": ("kda_kernels.hip", "kda_device.h"), "k_grad": ("kda_bwd.hip", "kda_device.h")}
@@ -347,6 +358,34 @@ def epilogue_measure(torch, kda, o, reps=20):
                          "frac": gbs / PEAK_HBM_GBS, "algorithmic_bytes_per_call": nbytes}}
 
 
+def chunk_measure(torch, kda, inp, cu, spec, chunks=(16, 32, 128), reps=2):
+    """The same workload at other chunk sizes: those run the generic fp32
+    kernels (kg_gram + kg_solve as the chunk-parallel stage, kg_recur as the
+    sequential one; correct to the same bars, not tuned).  Per chunk size:
+    ms per pass and per stage (HIP events, the measurement entry point) and
+    the sequential kernel's time per chunk step."""
+    T, H, dk, dv = spec.total_tokens, spec.n_heads, spec.d_k, spec.d_v
+    res = {}
+    for C in chunks:
+        dt_code = kda.KDA_BF16 if spec.dtype == "bf16" else kda.KDA_F32
+        ws = torch.empty(kda.workspace_size(T, spec.n_seqs, H, dk, dv, C, dt_code), dtype=torch.uint8,
+                         device=inp.q.device)
+        stage = {}
+        for r in range(reps + 1):   # the first call warms up
+            _, _, d = kda.chunk_fwd_profile(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, cu_seqlens=cu,
+                                            n_seqs=spec.n_seqs, chunk=C, workspace=ws)
+            if r:
+                for k_, v_ in d.items():
+                    stage[k_] = stage.get(k_, 0.0) + v_ / reps
+        steps = -(-(T // spec.n_seqs) // C)
+        res[str(C)] = {"kernels": "kg_gram + kg_solve, kg_recur (generic fp32)", "ms_per_pass": sum(stage.values()),
+                       "stage_ms": stage, "us_per_chunk_step": stage.get("k_recur", 0.0) * 1e3 / steps,
+                       "workspace_bytes": ws.numel()}
+        del ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +395,9 @@ def main():
     ap.add_argument("--profile-reps", type=int, default=10)
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--chunk", type=int, default=0,
+                    help="chunk size of the timed pass (default: the workload's, 64); other sizes run the "
+                         "generic kernels")
     ap.add_argument("--forward-only", action="store_true",
                     help="time only the forward pass (no backward, epilogue, decode or sequence-parallel legs)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -385,7 +427,7 @@ def main():
     dev = torch.device("cuda:0")
     spec = ki.headline_configs()[args.config]
     inp = ki.generate_torch(spec, dev)
-    T, H, dk, dv, C = spec.total_tokens, spec.n_heads, spec.d_k, spec.d_v, spec.chunk
+    T, H, dk, dv, C = spec.total_tokens, spec.n_heads, spec.d_k, spec.d_v, args.chunk or spec.chunk
     dt_code = kda.KDA_BF16 if spec.dtype == "bf16" else kda.KDA_F32
     ws = torch.empty(kda.workspace_size(T, spec.n_seqs, H, dk, dv, C, dt_code), dtype=torch.uint8, device=dev)
     o = torch.empty((T, H, dv), dtype=inp.q.dtype, device=dev)
@@ -394,7 +436,7 @@ def main():
 
     def step():
         kda.chunk_fwd(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, cu_seqlens=cu, n_seqs=spec.n_seqs,
-                      o=o, S_T=ST, workspace=ws)
+                      o=o, S_T=ST, workspace=ws, chunk=C)
 
     for _ in range(args.warmup):
         step()
@@ -414,7 +456,7 @@ def main():
     stage_ms = {}
     for _ in range(args.profile_reps):
         _, _, d = kda.chunk_fwd_profile(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, cu_seqlens=cu,
-                                        n_seqs=spec.n_seqs, o=o, S_T=ST, workspace=ws)
+                                        n_seqs=spec.n_seqs, o=o, S_T=ST, workspace=ws, chunk=C)
         for k_, v_ in d.items():
             stage_ms[k_] = stage_ms.get(k_, 0.0) + v_ / args.profile_reps
     dom = max(stage_ms, key=stage_ms.get)
@@ -429,7 +471,8 @@ def main():
     workload = ("KDA chunked forward, %s inputs / fp32 state, N=%d H=%d T_total=%d d_k=d_v=%d, chunk %d "
                 "(16-token sub-tiles), %s" % (spec.dtype, spec.n_seqs, H, T, dk, C,
                                               "S0 ~ 0.02 N(0,1)" if spec.s0_std else "zero S0"))
-    wkey = "%s_N%d_H%d_T%d_d%d" % (spec.dtype, spec.n_seqs, H, T, dk)
+    wkey = "%s_N%d_H%d_T%d_d%d" % (spec.dtype, spec.n_seqs, H, T, dk) + ("" if C == 64 else "_C%d" % C)
+    generic = C != 64 or dk != dv or (spec.dtype == "f32" and dk != 64)
     # The roofline of the whole pass (one kda_chunk_fwd call = k_chunk_table
     # when cu_seqlens is given, k_prep, k_recur, all on this stream): the
     # minimum bytes of the method per (token, head) -- read q, k, log_alpha,
@@ -451,7 +494,7 @@ def main():
     for k_ in kernels:
         ent = {"ms": stage_ms[k_]}
         if k_ != "k_chunk_table":
-            db = kernel_bytes_per_token_head(k_, C, dk, es)
+            db = (generic_bytes_per_token_head if generic else kernel_bytes_per_token_head)(k_, C, dk, es)
             ent["design_bytes_per_token_head"] = db
             ent["design_gbs"] = db * token_heads / (stage_ms[k_] * 1e-3) / 1e9
             ent["hbm_bytes_counted"] = traffic_for(k_, wkey)
@@ -477,6 +520,7 @@ def main():
         out["backward"] = backward_measure(torch, kda, inp, cu, spec)
         out["backward"]["vs_forward"] = out["backward"]["ms_per_pass"] / ms
     if not args.forward_only:
+        out["other_chunk_sizes"] = chunk_measure(torch, kda, inp, cu, spec)
         out["epilogue"] = epilogue_measure(torch, kda, o)
         out["decode"] = decode_measure(torch, kda, dev)
         out["decode_hbm"] = decode_measure(torch, kda, dev, N=256)
