@@ -72,13 +72,27 @@ __device__ inline float ldf(const void* p, int64_t i) {
     return to_f(static_cast<const E*>(p)[i]);
 }
 
+__device__ inline float dot4(float4 x, float4 y) { return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w; }
+
+__device__ inline float4 fma4(float s, float4 x, float4 acc) {
+    return make_float4(acc.x + s * x.x, acc.y + s * x.y, acc.z + s * x.z, acc.w + s * x.w);
+}
+
 // ------------------------------------------------------------------ kg_gram
+// Rows r0 .. r0+15 (one 16-token sub-tile) of A and M.  With rho = b at
+// row r0, e^{b_r - b_i} = e^{b_r - rho} e^{rho - b_i}: for r in the
+// sub-tile the first factor lies in [e^-80, 1]; the second is <= 1 for
+// i < r0 and <= e^80 for i in the sub-tile (16 tokens at log alpha >= -5),
+// which fp32 holds.  So each entry is a plain dot product over channels of
+// the rows scaled once, k_r e^{b_r - rho} (or q_r ...) and k_i e^{rho - b_i}:
+// one exponential per (row, channel) instead of one per (pair, channel).
 template <typename E>
 __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
-    constexpr int P = kGenMaxD + 1;   // row pitch (floats): lanes reading different rows hit different banks
-    __shared__ float sB[kGenMaxC * P];          // b, [token][channel]
-    __shared__ float sK[kGenMaxC * P];          // k, [token][channel]
-    __shared__ float sQ[kGenRows * P];          // q rows of this block
+    constexpr int P = kGenMaxD + 4;   // row pitch (floats): 16-byte rows, lanes of consecutive rows on distinct banks
+    __shared__ __attribute__((aligned(16))) float sKi[kGenMaxC * P];   // g, then b, then k_i e^{rho - b_i}
+    __shared__ __attribute__((aligned(16))) float sKr[kGenRows * P];   // k_r e^{b_r - rho}, rows of this block
+    __shared__ __attribute__((aligned(16))) float sQr[kGenRows * P];   // q_r e^{b_r - rho}
+    __shared__ float sRho[kGenMaxD];
     __shared__ float sBeta[kGenRows];
     const int32_t ci = blockIdx.x;
     const int h = blockIdx.y, r0 = kGenRows * blockIdx.z;
@@ -86,65 +100,82 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
     int len;
     if (!gen_chunk(a, ci, tok0, len)) return;
     const int C = a.C, DK = a.DK, tid = threadIdx.x;
+    const int nrow = r0 + kGenRows;   // columns i <= r for the block's rows r
     const int64_t rs = (int64_t)a.H * DK;
     const int64_t base = tok0 * rs + (int64_t)h * DK;
-    // b: per-channel running sum over the chunk (tokens past its end add 0)
-    for (int c = tid; c < DK; c += 256) {
-        float run = 0.f;
-        for (int t = 0; t < C; ++t) {
-            run += t < len ? ldf<E>(a.g, base + t * rs + c) : 0.f;
-            sB[t * P + c] = run;
-        }
-    }
+    const int64_t slot = (int64_t)h * a.max_chunks + ci;
     for (int x = tid; x < C * DK; x += 256) {
         const int t = x / DK, c = x % DK;
-        sK[t * P + c] = t < len ? ldf<E>(a.k, base + t * rs + c) : 0.f;
-    }
-    for (int x = tid; x < kGenRows * DK; x += 256) {
-        const int t = r0 + x / DK, c = x % DK;
-        sQ[(x / DK) * P + c] = t < len ? ldf<E>(a.q, base + t * rs + c) : 0.f;
+        sKi[t * P + c] = t < len ? ldf<E>(a.g, base + t * rs + c) : 0.f;
     }
     if (tid < kGenRows) {
         const int t = r0 + tid;
         sBeta[tid] = t < len ? ldf<E>(a.beta, (tok0 + t) * a.H + h) : 0.f;
     }
     __syncthreads();
-    const int64_t slot = (int64_t)h * a.max_chunks + ci;
-    // rows r0 .. r0+15 of A and M, every column (zero above the diagonal)
-    for (int x = tid; x < kGenRows * C; x += 256) {
-        const int rr = x / C, r = r0 + rr, i = x % C;
-        float sa = 0.f, sm = 0.f;
-        if (i <= r) {
-            const float *br = sB + r * P, *bi = sB + i * P, *kr = sK + r * P, *ki = sK + i * P;
-            const float* qr = sQ + rr * P;
-            for (int c = 0; c < DK; ++c) {
-                const float e = __expf(br[c] - bi[c]) * ki[c];
-                sa += kr[c] * e;
-                sm += qr[c] * e;
-            }
+    // b: per-channel running sum over the chunk (tokens past its end add 0)
+    for (int c = tid; c < DK; c += 256) {
+        float run = 0.f;
+        for (int t = 0; t < C; ++t) {
+            run += sKi[t * P + c];
+            sKi[t * P + c] = run;
         }
-        a.TB[(slot * C + r) * C + i] = i < r ? sBeta[rr] * sa : 0.f;
-        a.M[(slot * C + r) * C + i] = sm;
+        sRho[c] = sKi[r0 * P + c];
     }
-    // rows r0 .. r0+15 of Q.e^b, K.e^b and K.e^{b_L - b}; b_L is the running
-    // sum at the last slot (tokens past the end added nothing)
+    __syncthreads();
+    // the block's rows: scaled operands, and Q.e^b, K.e^b, K.e^{b_L - b}
     for (int x = tid; x < kGenRows * DK; x += 256) {
         const int rr = x / DK, r = r0 + rr, c = x % DK;
-        const float b = sB[r * P + c], bl = sB[(C - 1) * P + c];
-        const float eb = __expf(b), kv = sK[r * P + c];
+        const float bv = sKi[r * P + c], bl = sKi[(C - 1) * P + c];
+        const float kv = r < len ? ldf<E>(a.k, base + r * rs + c) : 0.f;
+        const float qv = r < len ? ldf<E>(a.q, base + r * rs + c) : 0.f;
+        const float er = __expf(bv - sRho[c]), eb = __expf(bv);
+        sKr[rr * P + c] = kv * er;
+        sQr[rr * P + c] = qv * er;
         const int64_t at = (slot * C + r) * DK + c;
-        a.Qg[at] = sQ[rr * P + c] * eb;
+        a.Qg[at] = qv * eb;
         a.Kg[at] = kv * eb;
-        a.Kh[at] = kv * __expf(bl - b);
+        a.Kh[at] = kv * __expf(bl - bv);
     }
     if (blockIdx.z == 0)
-        for (int c = tid; c < DK; c += 256) a.gam[slot * DK + c] = __expf(sB[(C - 1) * P + c]);
+        for (int c = tid; c < DK; c += 256) a.gam[slot * DK + c] = __expf(sKi[(C - 1) * P + c]);
+    __syncthreads();   // every read of b is done
+    for (int x = tid; x < nrow * DK; x += 256) {
+        const int i = x / DK, c = x % DK;
+        const float kv = i < len ? ldf<E>(a.k, base + i * rs + c) : 0.f;
+        sKi[i * P + c] = kv * __expf(sRho[c] - sKi[i * P + c]);
+    }
+    __syncthreads();
+    // column i = tid % 128 against rows 8 * (tid / 128) .. +7 of the block
+    const int i = tid % 128, rb = 8 * (tid / 128);
+    if (i >= C) return;
+    float accA[8], accM[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) accA[m] = accM[m] = 0.f;
+    if (i < nrow) {
+        for (int c = 0; c < DK; c += 4) {
+            const float4 ki = *reinterpret_cast<const float4*>(&sKi[i * P + c]);
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                accA[m] += dot4(*reinterpret_cast<const float4*>(&sKr[(rb + m) * P + c]), ki);
+                accM[m] += dot4(*reinterpret_cast<const float4*>(&sQr[(rb + m) * P + c]), ki);
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const int r = r0 + rb + m;
+        a.TB[(slot * C + r) * C + i] = i < r ? sBeta[rb + m] * accA[m] : 0.f;
+        a.M[(slot * C + r) * C + i] = i <= r ? accM[m] : 0.f;
+    }
 }
 
 // ------------------------------------------------------------------ kg_solve
-// T = (I + A)^-1 for the strictly lower A of one chunk, then T diag(beta),
-// written over A.  Row r of T is e_r - sum_{i<r} A[r][i] T[i]; one thread per
-// column walks the rows.
+// T = (I + A)^-1 for the strictly lower A of one chunk, by right-looking
+// elimination: T starts as I; once row i of T is final, every later row r
+// takes away A[r][i] times it (T[r][j] = delta_rj - sum_{i<r} A[r][i] T[i][j]).
+// Each step updates all (r > i, j <= i) pairs in parallel.  Then T diag(beta)
+// is written over A.
 template <typename E>
 __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
     constexpr int P = kGenMaxC + 1;
@@ -158,39 +189,49 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
     const int C = a.C, tid = threadIdx.x;
     const int64_t slot = (int64_t)h * a.max_chunks + ci;
     float* A = a.TB + slot * C * C;
-    for (int x = tid; x < C * C; x += 256) sA[(x / C) * P + x % C] = A[x];
-    __syncthreads();
-    if (tid < C) {
-        const int j = tid;
-        for (int r = 0; r < C; ++r) {
-            float s = r == j ? 1.f : 0.f;
-            for (int i = j; i < r; ++i) s -= sA[r * P + i] * sT[i * P + j];
-            sT[r * P + j] = r >= j ? s : 0.f;   // each thread reads only its own column of T
-        }
-    }
-    __syncthreads();
     for (int x = tid; x < C * C; x += 256) {
         const int r = x / C, j = x % C;
-        const float bj = j < len ? ldf<E>(a.beta, (tok0 + j) * a.H + h) : 0.f;
-        A[x] = sT[r * P + j] * bj;
+        sA[r * P + j] = A[x];
+        sT[r * P + j] = r == j ? 1.f : 0.f;
+    }
+    __syncthreads();
+    const int j = tid % C, g = tid / C, ng = 256 / C;   // column j; rows r = g (mod ng)
+    for (int i = 0; i < C - 1; ++i) {
+        if (j <= i) {
+            const float ti = sT[i * P + j];
+            int r = i + 1 + ((g - (i + 1)) % ng + ng) % ng;
+            for (; r < C; r += ng) sT[r * P + j] -= sA[r * P + i] * ti;
+        }
+        __syncthreads();
+    }
+    for (int x = tid; x < C * C; x += 256) {
+        const int r = x / C, jj = x % C;
+        const float bj = jj < len ? ldf<E>(a.beta, (tok0 + jj) * a.H + h) : 0.f;
+        A[x] = sT[r * P + jj] * bj;
     }
 }
 
 // ------------------------------------------------------------------ kg_recur
+// One workgroup per (sequence, head, 16 value columns), sequential over the
+// sequence's chunks.  A thread owns 4 columns (4 cq .. 4 cq + 3) of up to two
+// rows (t = tr and tr + 64) of each C x 16 product, or of two channels of
+// the state update, and reads 16-byte vectors from LDS.
 template <typename E>
 __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
-    constexpr int PO = (kGenMaxC > kGenMaxD ? kGenMaxC : kGenMaxD) + 1;
+    constexpr int PO = kGenMaxD + 4;   // pitch of the staged operands (kGenMaxC == kGenMaxD)
     constexpr int W = kGenCols;
-    __shared__ float sOp[kGenMaxC * PO];   // the operand of the current phase, [token][channel or token]
-    __shared__ float sS[kGenMaxD * W];     // the state's 16 columns, [channel][column]
-    __shared__ float sY[kGenMaxC * W];
-    __shared__ float sU[kGenMaxC * W];
+    static_assert(kGenMaxC == kGenMaxD, "one pitch for [token][channel], [token][token] and [channel][token]");
+    __shared__ __attribute__((aligned(16))) float bufA[kGenMaxC * PO];   // K.e^b, then T diag(beta), then (K.e^{b_L-b})^T
+    __shared__ __attribute__((aligned(16))) float bufB[kGenMaxC * PO];   // Q.e^b, then M
+    __shared__ __attribute__((aligned(16))) float sS[kGenMaxD * W];      // the state's 16 columns, [channel][column]
+    __shared__ __attribute__((aligned(16))) float sY[kGenMaxC * W];
+    __shared__ __attribute__((aligned(16))) float sU[kGenMaxC * W];
     const int C = a.C, DK = a.DK, DV = a.DV, tid = threadIdx.x;
     const int slabs = DV / W;
     const int32_t wg = blockIdx.x;
     const int32_t n = wg / (a.H * slabs);
     const int h = (wg / slabs) % a.H, col0 = W * (wg % slabs);
-    const int col = tid % W, row = tid / W;   // 16 rows of 16 columns per pass
+    const int cq = tid % 4, tr = tid / 4;
     int64_t s_start, s_len;
     if (a.cu) {
         int64_t b0 = a.cu[n], b1 = a.cu[n + 1];
@@ -211,85 +252,142 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
     }
     const int64_t sbase = ((int64_t)n * a.H + h) * DK * DV;
     for (int x = tid; x < DK * W; x += 256) {
-        const int c = x / W, j = x % W;
-        sS[x] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + j] : 0.f;
+        const int c = x / W, jj = x % W;
+        sS[x] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
     }
     const int64_t vrs = (int64_t)a.H * DV;
-    // copies an R x K fp32 matrix (row-major, K a multiple of 4) into sOp
-    auto stage = [&](const float* src, int R, int K) {
-        __syncthreads();
-        const int kv = K / 4;
-        for (int x = tid; x < R * kv; x += 256) {
-            const int r = x / kv, c4 = x % kv;
-            const float4 f = reinterpret_cast<const float4*>(src + (int64_t)r * K)[c4];
-            float* d = sOp + r * PO + 4 * c4;
-            d[0] = f.x;
-            d[1] = f.y;
-            d[2] = f.z;
-            d[3] = f.w;
+    // an R x K fp32 matrix (row-major, K a multiple of 4) into dst, as rows
+    // (transposed = false) or as columns (dst[k][r])
+    auto stage = [&](float* dst, const float* src, int R, int K, bool transposed) {
+        const int kv = K / 4, n4 = R * kv;
+        constexpr int kMax = kGenMaxC * kGenMaxD / 4 / 256;
+#pragma unroll
+        for (int u = 0; u < kMax; u += 4) {
+            float4 f[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int x = tid + 256 * (u + v);
+                f[v] = x < n4 ? reinterpret_cast<const float4*>(src)[x] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int x = tid + 256 * (u + v);
+                if (x >= n4) continue;
+                const int r = x / kv, c4 = 4 * (x % kv);
+                if (transposed) {
+                    dst[(c4 + 0) * PO + r] = f[v].x;
+                    dst[(c4 + 1) * PO + r] = f[v].y;
+                    dst[(c4 + 2) * PO + r] = f[v].z;
+                    dst[(c4 + 3) * PO + r] = f[v].w;
+                } else {
+                    *reinterpret_cast<float4*>(&dst[r * PO + c4]) = f[v];
+                }
+            }
         }
-        __syncthreads();
     };
+    // acc[m] += rows t_m of `op` (16-byte vectors along the contraction, up
+    // to `kend` rounded up to 4; entries past a row's end must be zero in
+    // `op`) times the 4 columns of `rhs` ([k][16] in LDS)
+    auto rows_times = [&](const float* op, const float* rhs, int kend0, bool tri, float4 acc[2]) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = tr + 64 * m;
+            if (t >= C) continue;
+            const int kend = tri ? ((t + 4) & ~3) : kend0;
+            float4 s = acc[m];
+            for (int k = 0; k < kend; k += 4) {
+                const float4 o4 = *reinterpret_cast<const float4*>(&op[t * PO + k]);
+                s = fma4(o4.x, *reinterpret_cast<const float4*>(&rhs[(k + 0) * W + 4 * cq]), s);
+                s = fma4(o4.y, *reinterpret_cast<const float4*>(&rhs[(k + 1) * W + 4 * cq]), s);
+                s = fma4(o4.z, *reinterpret_cast<const float4*>(&rhs[(k + 2) * W + 4 * cq]), s);
+                s = fma4(o4.w, *reinterpret_cast<const float4*>(&rhs[(k + 3) * W + 4 * cq]), s);
+            }
+            acc[m] = s;
+        }
+    };
+    if (nch > 0) {
+        const int64_t slot0 = (int64_t)h * a.max_chunks + c0;
+        stage(bufA, a.Kg + slot0 * C * DK, C, DK, false);
+        stage(bufB, a.Qg + slot0 * C * DK, C, DK, false);
+    }
     for (int j = 0; j < nch; ++j) {
         const int64_t slot = (int64_t)h * a.max_chunks + c0 + j;
         const int64_t tok0 = s_start + (int64_t)j * C;
         const int len = (int)(s_len - (int64_t)j * C < C ? s_len - (int64_t)j * C : C);
-        // Y = V - (K . e^b) S
-        stage(a.Kg + slot * C * DK, C, DK);
-        for (int t = row; t < C; t += 256 / W) {
-            float x = 0.f;
-            for (int c = 0; c < DK; ++c) x += sOp[t * PO + c] * sS[c * W + col];
-            const float vv = t < len ? ldf<E>(a.v, (tok0 + t) * vrs + (int64_t)h * DV + col0 + col) : 0.f;
-            sY[t * W + col] = t < len ? vv - x : 0.f;
-        }
-        // U~ = T diag(beta) Y (lower triangular)
-        stage(a.TB + slot * C * C, C, C);
-        for (int t = row; t < C; t += 256 / W) {
-            float u = 0.f;
-            for (int i = 0; i <= t; ++i) u += sOp[t * PO + i] * sY[i * W + col];
-            sU[t * W + col] = u;
-        }
-        // O = (Q . e^b) S + M U~
-        // (a fixed number of rows per thread, so that the partial sums stay in registers)
-        constexpr int kRowsPer = kGenMaxC / (256 / W);
-        float acc[kRowsPer];
-        stage(a.Qg + slot * C * DK, C, DK);
+        __syncthreads();   // K.e^b, Q.e^b and the state are in LDS
+        // X = (K.e^b) S, P = (Q.e^b) S; Y = V - X
+        float4 accX[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+        float4 accP[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+        rows_times(bufA, sS, DK, false, accX);
+        rows_times(bufB, sS, DK, false, accP);
 #pragma unroll
-        for (int m = 0; m < kRowsPer; ++m) {
-            const int t = row + m * (256 / W);
-            float x = 0.f;
-            if (t < C)
-                for (int c = 0; c < DK; ++c) x += sOp[t * PO + c] * sS[c * W + col];
-            acc[m] = x;
-        }
-        stage(a.M + slot * C * C, C, C);
-#pragma unroll
-        for (int m = 0; m < kRowsPer; ++m) {
-            const int t = row + m * (256 / W);
+        for (int m = 0; m < 2; ++m) {
+            const int t = tr + 64 * m;
             if (t >= C) continue;
-            float x = acc[m];
-            for (int i = 0; i <= t; ++i) x += sOp[t * PO + i] * sU[i * W + col];
-            if (t < len) static_cast<E*>(a.o)[(tok0 + t) * vrs + (int64_t)h * DV + col0 + col] = from_f<E>(x);
-        }
-        // S <- Diag(e^{b_L}) S + (K . e^{b_L - b})^T U~
-        stage(a.Kh + slot * C * DK, C, DK);
-        constexpr int kChPer = kGenMaxD / (256 / W);
-        float ns[kChPer];
-#pragma unroll
-        for (int m = 0; m < kChPer; ++m) {
-            const int c = row + m * (256 / W);
-            float x = 0.f;
-            if (c < DK) {
-                x = a.gam[slot * DK + c] * sS[c * W + col];
-                for (int t = 0; t < C; ++t) x += sOp[t * PO + c] * sU[t * W + col];
+            float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (t < len) {
+                const int64_t vo = (tok0 + t) * vrs + (int64_t)h * DV + col0 + 4 * cq;
+                y = make_float4(ldf<E>(a.v, vo) - accX[m].x, ldf<E>(a.v, vo + 1) - accX[m].y,
+                                ldf<E>(a.v, vo + 2) - accX[m].z, ldf<E>(a.v, vo + 3) - accX[m].w);
             }
-            ns[m] = x;
+            *reinterpret_cast<float4*>(&sY[t * W + 4 * cq]) = y;
         }
-        __syncthreads();   // every read of the old state is done
+        __syncthreads();   // K.e^b and Q.e^b are dead
+        stage(bufA, a.TB + slot * C * C, C, C, false);
+        stage(bufB, a.M + slot * C * C, C, C, false);
+        __syncthreads();
+        // U~ = T diag(beta) Y (lower triangular)
+        {
+            float4 accU[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+            rows_times(bufA, sY, 0, true, accU);
 #pragma unroll
-        for (int m = 0; m < kChPer; ++m) {
-            const int c = row + m * (256 / W);
-            if (c < DK) sS[c * W + col] = ns[m];
+            for (int m = 0; m < 2; ++m) {
+                const int t = tr + 64 * m;
+                if (t < C) *reinterpret_cast<float4*>(&sU[t * W + 4 * cq]) = accU[m];
+            }
+        }
+        __syncthreads();   // U~ is in LDS; T diag(beta) is dead
+        // O = P + M U~
+        rows_times(bufB, sU, 0, true, accP);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = tr + 64 * m;
+            if (t >= len) continue;
+            E* op = static_cast<E*>(a.o) + (tok0 + t) * vrs + (int64_t)h * DV + col0 + 4 * cq;
+            op[0] = from_f<E>(accP[m].x);
+            op[1] = from_f<E>(accP[m].y);
+            op[2] = from_f<E>(accP[m].z);
+            op[3] = from_f<E>(accP[m].w);
+        }
+        stage(bufA, a.Kh + slot * C * DK, C, DK, true);
+        __syncthreads();
+        // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~: channels c = tr, tr + 64
+        float4 ns[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int c = tr + 64 * m;
+            if (c >= DK) continue;
+            const float gm = a.gam[slot * DK + c];
+            const float4 s0 = *reinterpret_cast<const float4*>(&sS[c * W + 4 * cq]);
+            float4 acc = make_float4(gm * s0.x, gm * s0.y, gm * s0.z, gm * s0.w);
+            for (int t = 0; t < C; t += 4) {
+                const float4 k4 = *reinterpret_cast<const float4*>(&bufA[c * PO + t]);
+                acc = fma4(k4.x, *reinterpret_cast<const float4*>(&sU[(t + 0) * W + 4 * cq]), acc);
+                acc = fma4(k4.y, *reinterpret_cast<const float4*>(&sU[(t + 1) * W + 4 * cq]), acc);
+                acc = fma4(k4.z, *reinterpret_cast<const float4*>(&sU[(t + 2) * W + 4 * cq]), acc);
+                acc = fma4(k4.w, *reinterpret_cast<const float4*>(&sU[(t + 3) * W + 4 * cq]), acc);
+            }
+            ns[m] = acc;
+        }
+        __syncthreads();   // every read of the old state and of M, (K.e^{b_L-b})^T is done
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int c = tr + 64 * m;
+            if (c < DK) *reinterpret_cast<float4*>(&sS[c * W + 4 * cq]) = ns[m];
+        }
+        if (j + 1 < nch) {
+            stage(bufA, a.Kg + (slot + 1) * C * DK, C, DK, false);
+            stage(bufB, a.Qg + (slot + 1) * C * DK, C, DK, false);
         }
     }
     __syncthreads();
