@@ -15,13 +15,15 @@
 //   Y  = V - (K . e^b) S,   U~ = T diag(beta) Y
 //   O  = (Q . e^b) S + M U~
 //   S' = Diag(e^{b_L}) S + (K . e^{b_L - b})^T U~
-// Every exponent is <= 0 when log alpha <= 0 (r >= i), so in fp32 the decay
-// ratios are formed directly for each token pair and channel: a long chunk
-// only underflows terms that are negligible anyway.
+// The decay ratios of A and M factor through b at the first row of each
+// 16-token sub-tile (orkas.ai "Kimi K3 architecture", §"GPU のコードパスを
+// 一本消した「下界」": with log alpha >= -5 a sub-tile spans at most 80 in
+// log-decay), so every entry is a dot product of rows scaled once; factors
+// that underflow over a long chunk belong to negligible terms.
 //
 //   kg_gram  (chunks, H, C/16)  16 rows of A and M per workgroup, and those
 //                               rows of Q.e^b, K.e^b, K.e^{b_L-b}
-//   kg_solve (chunks, H)        T diag(beta) in LDS by forward substitution
+//   kg_solve (chunks, H)        T diag(beta) in LDS by right-looking elimination
 //   kg_recur (N*H*d_v/16)       sequential over one sequence's chunks for one
 //                               head and 16 value columns of the state
 #include "kda_device.h"

@@ -35,7 +35,8 @@
  *   - Argument errors are detected on the host before anything is enqueued;
  *     on error nothing is written.  Value ranges are not checked: log_alpha
  *     must lie in [-5, 0] and beta in [0, 1] for the documented accuracy
- *     (values outside give finite but unspecified results, never a memory
+ *     (values outside give unspecified results, possibly inf or NaN: below
+ *     -5 the in-chunk decay factors can overflow; never a memory
  *     access outside the buffers described here).  Device-side cu_seqlens
  *     that break the rules above give unspecified results but every access
  *     stays inside the buffers.
