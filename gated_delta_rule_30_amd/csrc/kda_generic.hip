@@ -80,6 +80,28 @@ __device__ inline float4 fma4(float s, float4 x, float4 acc) {
     return make_float4(acc.x + s * x.x, acc.y + s * x.y, acc.z + s * x.z, acc.w + s * x.w);
 }
 
+// 16 bytes of E from element `i` of p, widened to fp32: 8 (bf16) or 4 (fp32)
+// values.  Callers keep i a multiple of the count (every row starts on
+// 16 bytes: d_k and d_v are multiples of 8, the tensors 16-byte aligned).
+template <typename E>
+struct Vec16 {
+    static constexpr int N = 16 / (int)sizeof(E);
+    __device__ static inline void load(const void* p, int64_t i, float* out) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const E*>(p) + i);
+        if constexpr (sizeof(E) == 2) {
+            const bf16x8 v = __builtin_bit_cast(bf16x8, u);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
+        } else {
+            const float4 f = __builtin_bit_cast(float4, u);
+            out[0] = f.x;
+            out[1] = f.y;
+            out[2] = f.z;
+            out[3] = f.w;
+        }
+    }
+};
+
 // ------------------------------------------------------------------ kg_gram
 // Rows r0 .. r0+15 (one 16-token sub-tile) of A and M.  With rho = b at
 // row r0, e^{b_r - b_i} = e^{b_r - rho} e^{rho - b_i}: for r in the
@@ -88,9 +110,13 @@ __device__ inline float4 fma4(float s, float4 x, float4 acc) {
 // which fp32 holds.  So each entry is a plain dot product over channels of
 // the rows scaled once, k_r e^{b_r - rho} (or q_r ...) and k_i e^{rho - b_i}:
 // one exponential per (row, channel) instead of one per (pair, channel).
+// Every global load is a 16-byte vector, and a thread issues all of its
+// loads of a tile before it uses any.
 template <typename E>
 __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
     constexpr int P = kGenMaxD + 4;   // row pitch (floats): 16-byte rows, lanes of consecutive rows on distinct banks
+    constexpr int NV = Vec16<E>::N;
+    constexpr int kTileVec = kGenMaxC * kGenMaxD / NV / 256;   // 16-byte vectors per thread of a full tile
     __shared__ __attribute__((aligned(16))) float sKi[kGenMaxC * P];   // g, then b, then k_i e^{rho - b_i}
     __shared__ __attribute__((aligned(16))) float sKr[kGenRows * P];   // k_r e^{b_r - rho}, rows of this block
     __shared__ __attribute__((aligned(16))) float sQr[kGenRows * P];   // q_r e^{b_r - rho}
@@ -106,46 +132,90 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
     const int64_t rs = (int64_t)a.H * DK;
     const int64_t base = tok0 * rs + (int64_t)h * DK;
     const int64_t slot = (int64_t)h * a.max_chunks + ci;
-    for (int x = tid; x < C * DK; x += 256) {
-        const int t = x / DK, c = x % DK;
-        sKi[t * P + c] = t < len ? ldf<E>(a.g, base + t * rs + c) : 0.f;
+    const int vpr = DK / NV;          // vectors per row
+    // g of every row (b_L needs the whole chunk) and k of rows < nrow, in
+    // registers; rows past the chunk end are zero
+    float gv[kTileVec * NV], kv[kTileVec * NV];
+#pragma unroll
+    for (int u = 0; u < kTileVec; ++u) {
+        const int x = tid + 256 * u, t = x / vpr, c = (x % vpr) * NV;
+        const bool in = x < C * vpr && t < len;
+        if (in) Vec16<E>::load(a.g, base + t * rs + c, &gv[u * NV]);
+        if (in && t < nrow) Vec16<E>::load(a.k, base + t * rs + c, &kv[u * NV]);
+#pragma unroll
+        for (int e = 0; e < NV; ++e) {
+            if (!in) gv[u * NV + e] = 0.f;
+            if (!in || t >= nrow) kv[u * NV + e] = 0.f;
+        }
     }
     if (tid < kGenRows) {
         const int t = r0 + tid;
         sBeta[tid] = t < len ? ldf<E>(a.beta, (tok0 + t) * a.H + h) : 0.f;
     }
+#pragma unroll
+    for (int u = 0; u < kTileVec; ++u) {
+        const int x = tid + 256 * u, t = x / vpr, c = (x % vpr) * NV;
+        if (x < C * vpr)
+#pragma unroll
+            for (int e = 0; e < NV; ++e) sKi[t * P + c + e] = gv[u * NV + e];
+    }
     __syncthreads();
-    // b: per-channel running sum over the chunk (tokens past its end add 0)
+    // b: per-channel running sum over the chunk, eight rows read at a time
     for (int c = tid; c < DK; c += 256) {
         float run = 0.f;
-        for (int t = 0; t < C; ++t) {
-            run += sKi[t * P + c];
-            sKi[t * P + c] = run;
+        for (int t0 = 0; t0 < C; t0 += 8) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = sKi[(t0 + e) * P + c];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                run += x[e];
+                sKi[(t0 + e) * P + c] = run;
+            }
         }
         sRho[c] = sKi[r0 * P + c];
     }
     __syncthreads();
     // the block's rows: scaled operands, and Q.e^b, K.e^b, K.e^{b_L - b}
-    for (int x = tid; x < kGenRows * DK; x += 256) {
-        const int rr = x / DK, r = r0 + rr, c = x % DK;
-        const float bv = sKi[r * P + c], bl = sKi[(C - 1) * P + c];
-        const float kv = r < len ? ldf<E>(a.k, base + r * rs + c) : 0.f;
-        const float qv = r < len ? ldf<E>(a.q, base + r * rs + c) : 0.f;
-        const float er = __expf(bv - sRho[c]), eb = __expf(bv);
-        sKr[rr * P + c] = kv * er;
-        sQr[rr * P + c] = qv * er;
+    for (int x = tid; x < kGenRows * vpr; x += 256) {
+        const int rr = x / vpr, r = r0 + rr, c = (x % vpr) * NV;
+        float kr[NV], qr[NV];
+        if (r < len) {
+            Vec16<E>::load(a.k, base + r * rs + c, kr);
+            Vec16<E>::load(a.q, base + r * rs + c, qr);
+        } else {
+#pragma unroll
+            for (int e = 0; e < NV; ++e) kr[e] = qr[e] = 0.f;
+        }
         const int64_t at = (slot * C + r) * DK + c;
-        a.Qg[at] = qv * eb;
-        a.Kg[at] = kv * eb;
-        a.Kh[at] = kv * __expf(bl - bv);
+#pragma unroll
+        for (int e4 = 0; e4 < NV; e4 += 4) {
+            float4 oq, ok, oh;
+#pragma unroll
+            for (int e = e4; e < e4 + 4; ++e) {
+                const float bv = sKi[r * P + c + e], bl = sKi[(C - 1) * P + c + e];
+                const float er = __expf(bv - sRho[c + e]), eb = __expf(bv);
+                sKr[rr * P + c + e] = kr[e] * er;
+                sQr[rr * P + c + e] = qr[e] * er;
+                (&oq.x)[e - e4] = qr[e] * eb;
+                (&ok.x)[e - e4] = kr[e] * eb;
+                (&oh.x)[e - e4] = kr[e] * __expf(bl - bv);
+            }
+            *reinterpret_cast<float4*>(a.Qg + at + e4) = oq;
+            *reinterpret_cast<float4*>(a.Kg + at + e4) = ok;
+            *reinterpret_cast<float4*>(a.Kh + at + e4) = oh;
+        }
     }
     if (blockIdx.z == 0)
         for (int c = tid; c < DK; c += 256) a.gam[slot * DK + c] = __expf(sKi[(C - 1) * P + c]);
-    __syncthreads();   // every read of b is done
-    for (int x = tid; x < nrow * DK; x += 256) {
-        const int i = x / DK, c = x % DK;
-        const float kv = i < len ? ldf<E>(a.k, base + i * rs + c) : 0.f;
-        sKi[i * P + c] = kv * __expf(sRho[c] - sKi[i * P + c]);
+    __syncthreads();   // every read of b outside each thread's own elements is done
+#pragma unroll
+    for (int u = 0; u < kTileVec; ++u) {
+        const int x = tid + 256 * u, t = x / vpr, c = (x % vpr) * NV;
+        if (x < C * vpr && t < nrow)
+#pragma unroll
+            for (int e = 0; e < NV; ++e)
+                sKi[t * P + c + e] = kv[u * NV + e] * __expf(sRho[c + e] - sKi[t * P + c + e]);
     }
     __syncthreads();
     // column i = tid % 128 against rows 8 * (tid / 128) .. +7 of the block
