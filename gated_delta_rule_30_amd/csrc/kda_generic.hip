@@ -23,7 +23,7 @@
 //
 //   kg_gram  (chunks, H, C/16)  16 rows of A and M per workgroup, and those
 //                               rows of Q.e^b, K.e^b, K.e^{b_L-b}
-//   kg_solve (chunks, H)        T diag(beta) in LDS by right-looking elimination
+//   kg_solve (chunks, H)        T diag(beta) in LDS, by 16 x 16 blocks
 //   kg_recur (N*H*d_v/16)       sequential over one sequence's chunks for one
 //                               head and 16 value columns of the state
 #include "kda_device.h"
@@ -243,14 +243,16 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
 }
 
 // ------------------------------------------------------------------ kg_solve
-// T = (I + A)^-1 for the strictly lower A of one chunk, by right-looking
-// elimination: T starts as I; once row i of T is final, every later row r
-// takes away A[r][i] times it (T[r][j] = delta_rj - sum_{i<r} A[r][i] T[i][j]).
-// Each step updates all (r > i, j <= i) pairs in parallel.  Then T diag(beta)
-// is written over A.
+// T = (I + A)^-1 for the strictly lower A of one chunk, by 16 x 16 blocks.
+// The diagonal blocks first, all at once, by right-looking elimination
+// inside each block (T_KK starts as I; once row i is final every later row
+// r takes away A[r][i] times it).  Then block row by block row,
+//   T_KL = -T_KK sum_{L <= M < K} A_KM T_ML     (L < K),
+// which only needs block rows above K.  T diag(beta) is written over A.
 template <typename E>
 __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
     constexpr int P = kGenMaxC + 1;
+    constexpr int B = 16;
     __shared__ float sA[kGenMaxC * P];
     __shared__ float sT[kGenMaxC * P];
     const int32_t ci = blockIdx.x;
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
     int64_t tok0;
     int len;
     if (!gen_chunk(a, ci, tok0, len)) return;
-    const int C = a.C, tid = threadIdx.x;
+    const int C = a.C, tid = threadIdx.x, NB = C / B;
     const int64_t slot = (int64_t)h * a.max_chunks + ci;
     float* A = a.TB + slot * C * C;
     for (int x = tid; x < C * C; x += 256) {
@@ -267,19 +269,52 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
         sT[r * P + j] = r == j ? 1.f : 0.f;
     }
     __syncthreads();
-    const int j = tid % C, g = tid / C, ng = 256 / C;   // column j; rows r = g (mod ng)
-    for (int i = 0; i < C - 1; ++i) {
-        if (j <= i) {
-            const float ti = sT[i * P + j];
-            int r = i + 1 + ((g - (i + 1)) % ng + ng) % ng;
-            for (; r < C; r += ng) sT[r * P + j] -= sA[r * P + i] * ti;
+    // diagonal blocks: thread -> block K = tid / 32, column j, rows of parity g
+    {
+        const int K = tid / 32, j = tid % B, g = (tid / B) % 2, o = B * K;
+        for (int i = 0; i < B - 1; ++i) {
+            if (K < NB && j <= i) {
+                const float ti = sT[(o + i) * P + o + j];
+                for (int r = i + 1 + ((g - (i + 1)) % 2 + 2) % 2; r < B; r += 2)
+                    sT[(o + r) * P + o + j] -= sA[(o + r) * P + o + i] * ti;
+            }
+            __syncthreads();
         }
+    }
+    // block row K: X_KL = sum_M A_KM T_ML for every L < K (thread -> element
+    // (r, j) of the block, looping over L), then T_KL = -T_KK X_KL
+    const int r = tid / B, j = tid % B;
+    for (int K = 1; K < NB; ++K) {
+        float x[kGenMaxC / B];
+#pragma unroll
+        for (int L = 0; L < kGenMaxC / B; ++L) {
+            float acc = 0.f;
+            if (L < K)
+                for (int m = B * L; m < B * K; ++m) acc += sA[(B * K + r) * P + m] * sT[m * P + B * L + j];
+            x[L] = acc;
+        }
+        __syncthreads();   // X is in registers; the block row's T entries are written below
+#pragma unroll
+        for (int L = 0; L < kGenMaxC / B; ++L)
+            if (L < K) sT[(B * K + r) * P + B * L + j] = x[L];
+        __syncthreads();
+#pragma unroll
+        for (int L = 0; L < kGenMaxC / B; ++L) {
+            if (L >= K) continue;
+            float acc = 0.f;
+            for (int m = 0; m <= r; ++m) acc += sT[(B * K + r) * P + B * K + m] * sT[(B * K + m) * P + B * L + j];
+            x[L] = -acc;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int L = 0; L < kGenMaxC / B; ++L)
+            if (L < K) sT[(B * K + r) * P + B * L + j] = x[L];
         __syncthreads();
     }
     for (int x = tid; x < C * C; x += 256) {
-        const int r = x / C, jj = x % C;
+        const int rr = x / C, jj = x % C;
         const float bj = jj < len ? ldf<E>(a.beta, (tok0 + jj) * a.H + h) : 0.f;
-        A[x] = sT[r * P + jj] * bj;
+        A[x] = sT[rr * P + jj] * bj;
     }
 }
 
