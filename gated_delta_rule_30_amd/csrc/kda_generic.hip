@@ -363,32 +363,37 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         sS[x] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
     }
     const int64_t vrs = (int64_t)a.H * DV;
-    // an R x K fp32 matrix (row-major, K a multiple of 4) into dst, as rows
-    // (transposed = false) or as columns (dst[k][r])
-    auto stage = [&](float* dst, const float* src, int R, int K, bool transposed) {
+    // An R x K fp32 matrix (row-major, K a multiple of 4) is staged in two
+    // halves: `fetch` issues its 16-byte loads into registers, `put` writes
+    // them to dst as rows (transposed = false) or as columns (dst[k][r]).
+    // Each operand is fetched one phase before it is put, so that the loads'
+    // latency overlaps the phase in between.
+    constexpr int kMaxV = kGenMaxC * kGenMaxD / 4 / 256;
+    struct Fetched {
+        float4 f[kMaxV];
+    };
+    auto fetch = [&](Fetched& pr, const float* src, int R, int K) {
+        const int n4 = R * (K / 4);
+#pragma unroll
+        for (int u = 0; u < kMaxV; ++u) {
+            const int x = tid + 256 * u;
+            pr.f[u] = x < n4 ? reinterpret_cast<const float4*>(src)[x] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto put = [&](float* dst, const Fetched& pr, int R, int K, bool transposed) {
         const int kv = K / 4, n4 = R * kv;
-        constexpr int kMax = kGenMaxC * kGenMaxD / 4 / 256;
 #pragma unroll
-        for (int u = 0; u < kMax; u += 4) {
-            float4 f[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int x = tid + 256 * (u + v);
-                f[v] = x < n4 ? reinterpret_cast<const float4*>(src)[x] : make_float4(0.f, 0.f, 0.f, 0.f);
-            }
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int x = tid + 256 * (u + v);
-                if (x >= n4) continue;
-                const int r = x / kv, c4 = 4 * (x % kv);
-                if (transposed) {
-                    dst[(c4 + 0) * PO + r] = f[v].x;
-                    dst[(c4 + 1) * PO + r] = f[v].y;
-                    dst[(c4 + 2) * PO + r] = f[v].z;
-                    dst[(c4 + 3) * PO + r] = f[v].w;
-                } else {
-                    *reinterpret_cast<float4*>(&dst[r * PO + c4]) = f[v];
-                }
+        for (int u = 0; u < kMaxV; ++u) {
+            const int x = tid + 256 * u;
+            if (x >= n4) continue;
+            const int r = x / kv, c4 = 4 * (x % kv);
+            if (transposed) {
+                dst[(c4 + 0) * PO + r] = pr.f[u].x;
+                dst[(c4 + 1) * PO + r] = pr.f[u].y;
+                dst[(c4 + 2) * PO + r] = pr.f[u].z;
+                dst[(c4 + 3) * PO + r] = pr.f[u].w;
+            } else {
+                *reinterpret_cast<float4*>(&dst[r * PO + c4]) = pr.f[u];
             }
         }
     };
@@ -412,16 +417,36 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
             acc[m] = s;
         }
     };
+    Fetched fa, fb;
     if (nch > 0) {
         const int64_t slot0 = (int64_t)h * a.max_chunks + c0;
-        stage(bufA, a.Kg + slot0 * C * DK, C, DK, false);
-        stage(bufB, a.Qg + slot0 * C * DK, C, DK, false);
+        fetch(fa, a.Kg + slot0 * C * DK, C, DK);
+        fetch(fb, a.Qg + slot0 * C * DK, C, DK);
+        put(bufA, fa, C, DK, false);
+        put(bufB, fb, C, DK, false);
     }
     for (int j = 0; j < nch; ++j) {
         const int64_t slot = (int64_t)h * a.max_chunks + c0 + j;
         const int64_t tok0 = s_start + (int64_t)j * C;
         const int len = (int)(s_len - (int64_t)j * C < C ? s_len - (int64_t)j * C : C);
         __syncthreads();   // K.e^b, Q.e^b and the state are in LDS
+        // this step's T diag(beta), M, value rows and e^{b_L}, ahead of use
+        fetch(fa, a.TB + slot * C * C, C, C);
+        fetch(fb, a.M + slot * C * C, C, C);
+        float vr[2][4], gm[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = tr + 64 * m, c = tr + 64 * m;
+            if (t < len) {
+                const int64_t vo = (tok0 + t) * vrs + (int64_t)h * DV + col0 + 4 * cq;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vr[m][e] = ldf<E>(a.v, vo + e);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) vr[m][e] = 0.f;
+            }
+            gm[m] = c < DK ? a.gam[slot * DK + c] : 0.f;
+        }
         // X = (K.e^b) S, P = (Q.e^b) S; Y = V - X
         float4 accX[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
         float4 accP[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
@@ -431,18 +456,16 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         for (int m = 0; m < 2; ++m) {
             const int t = tr + 64 * m;
             if (t >= C) continue;
-            float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (t < len) {
-                const int64_t vo = (tok0 + t) * vrs + (int64_t)h * DV + col0 + 4 * cq;
-                y = make_float4(ldf<E>(a.v, vo) - accX[m].x, ldf<E>(a.v, vo + 1) - accX[m].y,
-                                ldf<E>(a.v, vo + 2) - accX[m].z, ldf<E>(a.v, vo + 3) - accX[m].w);
-            }
+            const float4 y = t < len ? make_float4(vr[m][0] - accX[m].x, vr[m][1] - accX[m].y,
+                                                   vr[m][2] - accX[m].z, vr[m][3] - accX[m].w)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
             *reinterpret_cast<float4*>(&sY[t * W + 4 * cq]) = y;
         }
         __syncthreads();   // K.e^b and Q.e^b are dead
-        stage(bufA, a.TB + slot * C * C, C, C, false);
-        stage(bufB, a.M + slot * C * C, C, C, false);
+        put(bufA, fa, C, C, false);
+        put(bufB, fb, C, C, false);
         __syncthreads();
+        fetch(fa, a.Kh + slot * C * DK, C, DK);
         // U~ = T diag(beta) Y (lower triangular)
         {
             float4 accU[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
@@ -454,6 +477,11 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
             }
         }
         __syncthreads();   // U~ is in LDS; T diag(beta) is dead
+        put(bufA, fa, C, DK, true);
+        if (j + 1 < nch) {   // the next chunk's K.e^b and Q.e^b, put after the state update
+            fetch(fa, a.Kg + (slot + 1) * C * DK, C, DK);
+            fetch(fb, a.Qg + (slot + 1) * C * DK, C, DK);
+        }
         // O = P + M U~
         rows_times(bufB, sU, 0, true, accP);
 #pragma unroll
@@ -466,17 +494,15 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
             op[2] = from_f<E>(accP[m].z);
             op[3] = from_f<E>(accP[m].w);
         }
-        stage(bufA, a.Kh + slot * C * DK, C, DK, true);
-        __syncthreads();
+        __syncthreads();   // (K.e^{b_L-b})^T is in LDS
         // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~: channels c = tr, tr + 64
         float4 ns[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int c = tr + 64 * m;
             if (c >= DK) continue;
-            const float gm = a.gam[slot * DK + c];
             const float4 s0 = *reinterpret_cast<const float4*>(&sS[c * W + 4 * cq]);
-            float4 acc = make_float4(gm * s0.x, gm * s0.y, gm * s0.z, gm * s0.w);
+            float4 acc = make_float4(gm[m] * s0.x, gm[m] * s0.y, gm[m] * s0.z, gm[m] * s0.w);
             for (int t = 0; t < C; t += 4) {
                 const float4 k4 = *reinterpret_cast<const float4*>(&bufA[c * PO + t]);
                 acc = fma4(k4.x, *reinterpret_cast<const float4*>(&sU[(t + 0) * W + 4 * cq]), acc);
@@ -486,15 +512,15 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
             }
             ns[m] = acc;
         }
-        __syncthreads();   // every read of the old state and of M, (K.e^{b_L-b})^T is done
+        __syncthreads();   // every read of the old state, of M and of (K.e^{b_L-b})^T is done
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
             const int c = tr + 64 * m;
             if (c < DK) *reinterpret_cast<float4*>(&sS[c * W + 4 * cq]) = ns[m];
         }
         if (j + 1 < nch) {
-            stage(bufA, a.Kg + (slot + 1) * C * DK, C, DK, false);
-            stage(bufB, a.Qg + (slot + 1) * C * DK, C, DK, false);
+            put(bufA, fa, C, DK, false);
+            put(bufB, fb, C, DK, false);
         }
     }
     __syncthreads();
