@@ -244,9 +244,10 @@ def test_backward_config3_full_heads(torch_dev):
 
 
 def test_long_sequence_paced_sampled(torch_dev):
-    """One 131,072-token sequence: 2048 chunks, so the recurrence's slab
-    workgroups pace each other (in the forward, the checkpointing forward and
-    the state-gradient pass).  H=4, d=64, S0 ~ 0.02 N(0,1); the forward and
+    """One 131,072-token sequence: 2048 chunks, so the backward's recurrence
+    workgroups pace each other (the checkpointing forward and the
+    state-gradient pass; the plain forward runs pipelined in token blocks
+    below the pacing threshold).  H=4, d=64, S0 ~ 0.02 N(0,1); the forward and
     the backward run over all heads, head 2 is checked in full against the
     oracle (o and S_T, and every gradient)."""
     torch, dev = torch_dev
