@@ -161,6 +161,22 @@ def test_s0_null_equals_zeros(torch_dev):
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
+@pytest.mark.parametrize("dtype,d,chunk", [("bf16", 128, 64), ("f32", 64, 64), ("bf16", 64, 32)])
+def test_without_final_state(torch_dev, dtype, d, chunk):
+    """S_T omitted (NULL through the C ABI): o is the same, bit for bit, as
+    with S_T requested (tuned kernels, and the generic ones at chunk 32)."""
+    torch, dev = torch_dev
+    import gated_delta_rule_30_amd as kda
+    inp = ki.generate_numpy(ki.custom("nost", dtype, [300, 45, 0, 129], 2, d, s0_std=0.3, varlen=True, seed=4))
+    q, k, v, beta, g = (_to_dev(torch, dev, a, dtype) for a in (inp.q, inp.k, inp.v, inp.beta, inp.g))
+    S0 = torch.from_numpy(inp.S0).to(dev)
+    cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
+    o1, S1 = kda.chunk_fwd(q, k, v, beta, g, S0=S0, cu_seqlens=cu, chunk=chunk)
+    o2, S2 = kda.chunk_fwd(q, k, v, beta, g, S0=S0, cu_seqlens=cu, chunk=chunk, output_final_state=False)
+    torch.cuda.synchronize()
+    assert S2 is None and torch.equal(o1, o2)
+
+
 def test_deterministic(torch_dev):
     torch, dev = torch_dev
     inp = ki.generate_numpy(ki.custom("det", "bf16", [4096, 1000, 3000], 8, 128, s0_std=0.02, varlen=True))
@@ -328,6 +344,9 @@ def test_pipelined_forward(torch_dev, lengths, H, d, s0):
     _say("pipelined forward: %s H=%d d=%d" % (lengths, H, d))
     o, ST = kda.chunk_fwd(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, n_seqs=N)
     o2, ST2, _ = kda.chunk_fwd_profile(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, n_seqs=N)
+    o3, _ = kda.chunk_fwd(inp.q, inp.k, inp.v, inp.beta, inp.g, S0=inp.S0, n_seqs=N, output_final_state=False)
     torch.cuda.synchronize()
     assert torch.equal(o, o2) and torch.equal(ST, ST2), "pipelined and sequential launches differ"
+    assert torch.equal(o, o3), "the pipelined forward without S_T differs"
+    del o2, ST2, o3
     _full_check(torch, inp, o, ST, "pipelined", [[n] for n in range(N)], [list(range(H))])
