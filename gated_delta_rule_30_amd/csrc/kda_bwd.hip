@@ -92,6 +92,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
     __shared__ float sCol[kNSub * HALF];         // per tile: sum over tokens of dK^ . K^
     __shared__ float sRev[kNSub * HALF];         // per tile: sum of db
     __shared__ float sDgam[HALF];
+    __shared__ float sCs[HALF];                  // the b_L terms of the chunk's last row, per channel
     __shared__ float sBeta[C];
     E* sS = sX;
     E* sdS = sX + HALF * D;
@@ -309,6 +310,14 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
         *reinterpret_cast<bf16x4*>(&sdGqT[ii * PT + kSub * w + 4 * lg]) = tq;
     }
     __syncthreads();   // U~ is dead: region X takes the Gram operands
+    // the b_L terms of the last row (sDgam and every tile's sCol are final):
+    // one thread per channel, so that the last row's lane only adds them
+    for (int c = tid; c < HALF; c += kGradThreads) {
+        float cs = sDgam[c] * __expf(sRho[kNSub * HALF + c]);
+#pragma unroll
+        for (int W = 0; W < kNSub; ++W) cs += sCol[W * HALF + c];
+        sCs[c] = cs;
+    }
 #pragma unroll
     for (int i = 0; i < NTH; ++i)
 #pragma unroll
@@ -377,12 +386,7 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int x = 4 * i + r, c = lch(i, r);
-            if (t == C - 1) {
-                float cs = sDgam[c] * __expf(sRho[kNSub * HALF + c]);
-#pragma unroll
-                for (int W = 0; W < kNSub; ++W) cs += sCol[W * HALF + c];
-                db[x] += cs;
-            }
+            if (t == C - 1) db[x] += sCs[c];
             rv[x] = row_rscan16(db[x]);
             if (li == 0) sRev[w * HALF + c] = rv[x];
         }
@@ -399,7 +403,10 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
         for (int r = 0; r < 4; ++r) {
             const int x = 4 * i + r, c = lch(i, r);
             float dgv = rv[x];
-            for (int W = w + 1; W < kNSub; ++W) dgv += sRev[W * HALF + c];
+            // the later token tiles' totals (a fixed-length loop: every wave
+            // issues the same loads at once, whatever its tile)
+#pragma unroll
+            for (int W = 1; W < kNSub; ++W) dgv += W > w ? sRev[W * HALF + c] : 0.f;
             oq[r] = (E)dq[x];
             ok4[r] = (E)dk[x];
             og[r] = (E)dgv;
