@@ -360,8 +360,9 @@ def epilogue_measure(torch, kda, o, reps=20):
 
 def chunk_measure(torch, kda, inp, cu, spec, chunks=(16, 32, 128), reps=2):
     """The same workload at other chunk sizes: those run the generic fp32
-    kernels (kg_gram + kg_solve as the chunk-parallel stage, kg_recur as the
-    sequential one; correct to the same bars, not tuned).  Per chunk size:
+    kernels (kg_gram + kg_solve as the chunk-parallel stage, kg_recur_res for
+    chunks of at most 64 tokens or kg_recur as the sequential one; correct to
+    the same bars, not tuned).  Per chunk size:
     ms per pass and per stage (HIP events, the measurement entry point) and
     the sequential kernel's time per chunk step."""
     T, H, dk, dv = spec.total_tokens, spec.n_heads, spec.d_k, spec.d_v
@@ -378,7 +379,7 @@ def chunk_measure(torch, kda, inp, cu, spec, chunks=(16, 32, 128), reps=2):
                 for k_, v_ in d.items():
                     stage[k_] = stage.get(k_, 0.0) + v_ / reps
         steps = -(-(T // spec.n_seqs) // C)
-        res[str(C)] = {"kernels": "kg_gram + kg_solve, kg_recur (generic fp32)", "ms_per_pass": sum(stage.values()),
+        res[str(C)] = {"kernels": "kg_gram + kg_solve, %s (generic fp32)" % ("kg_recur_res" if C <= 64 else "kg_recur"), "ms_per_pass": sum(stage.values()),
                        "stage_ms": stage, "us_per_chunk_step": stage.get("k_recur", 0.0) * 1e3 / steps,
                        "workspace_bytes": ws.numel()}
         del ws

@@ -26,6 +26,7 @@
 //   kg_solve (chunks, H)        T diag(beta) in LDS, by 16 x 16 blocks
 //   kg_recur (N*H*d_v/16)       sequential over one sequence's chunks for one
 //                               head and 16 value columns of the state
+//                               (kg_recur_res for chunks of at most 64 tokens)
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -531,6 +532,202 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         }
 }
 
+// ------------------------------------------------------------------ kg_recur_res
+// kg_recur for chunks of at most CM tokens (CM = 32 or 64), where all five
+// operands of a chunk fit in LDS together: each step issues every load of
+// the next chunk (operands, value rows, e^{b_L}) into registers at its start
+// and puts them to LDS at its end, so one round of global loads per step
+// overlaps the whole step instead of each operand waiting for its own.
+template <typename E, int CM>
+__global__ __launch_bounds__(256) void kg_recur_res(GenArgs a) {
+    constexpr int W = kGenCols;
+    constexpr int PD = kGenMaxD + 4;          // pitch of [token][channel] rows
+    constexpr int PC = CM + 4;                // pitch of [token][token] and [channel][token] rows
+    constexpr int kRowV = CM * kGenMaxD / 4 / 256;   // 16-byte vectors per thread of a [CM][d_k] operand
+    constexpr int kTriV = (CM * CM / 4 + 255) / 256;   // ... of a [CM][CM] operand
+    static_assert(CM <= 64, "one row of each product per thread");
+    __shared__ __attribute__((aligned(16))) float sKg[CM * PD];
+    __shared__ __attribute__((aligned(16))) float sQg[CM * PD];
+    __shared__ __attribute__((aligned(16))) float sKhT[kGenMaxD * PC];
+    __shared__ __attribute__((aligned(16))) float sTB[CM * PC];
+    __shared__ __attribute__((aligned(16))) float sM[CM * PC];
+    __shared__ __attribute__((aligned(16))) float sS[kGenMaxD * W];
+    __shared__ __attribute__((aligned(16))) float sY[CM * W];
+    __shared__ __attribute__((aligned(16))) float sU[CM * W];
+    const int C = a.C, DK = a.DK, DV = a.DV, tid = threadIdx.x;
+    const int slabs = DV / W;
+    const int32_t wg = blockIdx.x;
+    const int32_t n = wg / (a.H * slabs);
+    const int h = (wg / slabs) % a.H, col0 = W * (wg % slabs);
+    const int cq = tid % 4, tr = tid / 4;   // 4 columns of token row tr (or of channels tr, tr + 64)
+    int64_t s_start, s_len;
+    if (a.cu) {
+        int64_t b0 = a.cu[n], b1 = a.cu[n + 1];
+        b0 = b0 < 0 ? 0 : (b0 > a.total_tokens ? a.total_tokens : b0);
+        b1 = b1 < b0 ? b0 : (b1 > a.total_tokens ? a.total_tokens : b1);
+        s_start = b0;
+        s_len = b1 - b0;
+    } else {
+        s_start = (int64_t)n * a.fixed_len;
+        s_len = a.fixed_len;
+    }
+    int32_t c0, nch = (int32_t)((s_len + C - 1) / C);
+    if (a.cu) {
+        c0 = a.seq_chunk0[n];
+        if (nch > a.seq_chunk0[n + 1] - c0) nch = a.seq_chunk0[n + 1] - c0;
+    } else {
+        c0 = n * nch;
+    }
+    const int64_t sbase = ((int64_t)n * a.H + h) * DK * DV;
+    for (int x = tid; x < DK * W; x += 256) {
+        const int c = x / W, jj = x % W;
+        sS[x] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
+    }
+    const int64_t vrs = (int64_t)a.H * DV;
+    // the next chunk's loads, in registers between fetch and put
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    v4 nKg[kRowV], nQg[kRowV], nKh[kRowV], nTB[kTriV], nM[kTriV];
+    float nv[4], ng[2];
+    auto fetch = [&](int j) __attribute__((always_inline)) {
+        const int64_t slot = (int64_t)h * a.max_chunks + c0 + j;
+        const int64_t tok0 = s_start + (int64_t)j * C;
+        const int len = (int)(s_len - (int64_t)j * C < C ? s_len - (int64_t)j * C : C);
+        const int nr = C * DK / 4, nt = C * C / 4;
+        const v4* kg = reinterpret_cast<const v4*>(a.Kg + slot * C * DK);
+        const v4* qg = reinterpret_cast<const v4*>(a.Qg + slot * C * DK);
+        const v4* kh = reinterpret_cast<const v4*>(a.Kh + slot * C * DK);
+        const v4* tb = reinterpret_cast<const v4*>(a.TB + slot * C * C);
+        const v4* mm = reinterpret_cast<const v4*>(a.M + slot * C * C);
+#pragma unroll
+        for (int u = 0; u < kRowV; ++u) {
+            const int x = tid + 256 * u;
+            if (x < nr) {
+                nKg[u] = kg[x];
+                nQg[u] = qg[x];
+                nKh[u] = kh[x];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kTriV; ++u) {
+            const int x = tid + 256 * u;
+            if (x < nt) {
+                nTB[u] = tb[x];
+                nM[u] = mm[x];
+            }
+        }
+        const int64_t vo = (tok0 + tr) * vrs + (int64_t)h * DV + col0 + 4 * cq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nv[e] = tr < len ? ldf<E>(a.v, vo + e) : 0.f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int c = tr + 64 * m;
+            ng[m] = c < DK ? a.gam[slot * DK + c] : 0.f;
+        }
+    };
+    auto put = [&]() __attribute__((always_inline)) {
+        const int kv = DK / 4, nr = C * kv, tv = C / 4, nt = C * tv;
+#pragma unroll
+        for (int u = 0; u < kRowV; ++u) {
+            const int x = tid + 256 * u;
+            if (x >= nr) continue;
+            const int r = x / kv, c4 = 4 * (x % kv);
+            *reinterpret_cast<v4*>(&sKg[r * PD + c4]) = nKg[u];
+            *reinterpret_cast<v4*>(&sQg[r * PD + c4]) = nQg[u];
+            sKhT[(c4 + 0) * PC + r] = nKh[u].x;
+            sKhT[(c4 + 1) * PC + r] = nKh[u].y;
+            sKhT[(c4 + 2) * PC + r] = nKh[u].z;
+            sKhT[(c4 + 3) * PC + r] = nKh[u].w;
+        }
+#pragma unroll
+        for (int u = 0; u < kTriV; ++u) {
+            const int x = tid + 256 * u;
+            if (x >= nt) continue;
+            const int r = x / tv, c4 = 4 * (x % tv);
+            *reinterpret_cast<v4*>(&sTB[r * PC + c4]) = nTB[u];
+            *reinterpret_cast<v4*>(&sM[r * PC + c4]) = nM[u];
+        }
+    };
+    // acc += row t of `op` (pitch P, entries past the row's end zero) times
+    // the 4 columns of `rhs` ([k][16]), over k < kend (a multiple of 4)
+    auto row_times = [&](const float* op, int P, int t, const float* rhs, int kend, float4 acc) __attribute__((always_inline)) {
+        for (int k = 0; k < kend; k += 4) {
+            const float4 o4 = *reinterpret_cast<const float4*>(&op[t * P + k]);
+            acc = fma4(o4.x, *reinterpret_cast<const float4*>(&rhs[(k + 0) * W + 4 * cq]), acc);
+            acc = fma4(o4.y, *reinterpret_cast<const float4*>(&rhs[(k + 1) * W + 4 * cq]), acc);
+            acc = fma4(o4.z, *reinterpret_cast<const float4*>(&rhs[(k + 2) * W + 4 * cq]), acc);
+            acc = fma4(o4.w, *reinterpret_cast<const float4*>(&rhs[(k + 3) * W + 4 * cq]), acc);
+        }
+        return acc;
+    };
+    float vr[4] = {0.f, 0.f, 0.f, 0.f}, gm[2] = {0.f, 0.f};
+    if (nch > 0) {
+        fetch(0);
+        put();
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vr[e] = nv[e];
+        gm[0] = ng[0];
+        gm[1] = ng[1];
+    }
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < nch; ++j) {
+        const int64_t tok0 = s_start + (int64_t)j * C;
+        const int len = (int)(s_len - (int64_t)j * C < C ? s_len - (int64_t)j * C : C);
+        __syncthreads();   // chunk j's operands and the state are in LDS
+        if (j + 1 < nch) fetch(j + 1);
+        // X = (K.e^b) S, P = (Q.e^b) S; Y = V - X
+        float4 accP = z4;
+        if (tr < C) {
+            const float4 x = row_times(sKg, PD, tr, sS, DK, z4);
+            accP = row_times(sQg, PD, tr, sS, DK, z4);
+            const float4 y = tr < len ? make_float4(vr[0] - x.x, vr[1] - x.y, vr[2] - x.z, vr[3] - x.w) : z4;
+            *reinterpret_cast<float4*>(&sY[tr * W + 4 * cq]) = y;
+        }
+        __syncthreads();
+        // U~ = T diag(beta) Y (lower triangular: row t needs k <= t)
+        if (tr < C) *reinterpret_cast<float4*>(&sU[tr * W + 4 * cq]) = row_times(sTB, PC, tr, sY, (tr + 4) & ~3, z4);
+        __syncthreads();
+        // O = P + M U~
+        if (tr < len) {
+            const float4 ov = row_times(sM, PC, tr, sU, (tr + 4) & ~3, accP);
+            E* op = static_cast<E*>(a.o) + (tok0 + tr) * vrs + (int64_t)h * DV + col0 + 4 * cq;
+            op[0] = from_f<E>(ov.x);
+            op[1] = from_f<E>(ov.y);
+            op[2] = from_f<E>(ov.z);
+            op[3] = from_f<E>(ov.w);
+        }
+        // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~: channels tr, tr + 64
+        float4 ns[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int c = tr + 64 * m;
+            ns[m] = z4;
+            if (c < DK) {
+                const float4 s0 = *reinterpret_cast<const float4*>(&sS[c * W + 4 * cq]);
+                ns[m] = row_times(sKhT, PC, c, sU, C, make_float4(gm[m] * s0.x, gm[m] * s0.y, gm[m] * s0.z, gm[m] * s0.w));
+            }
+        }
+        __syncthreads();   // every read of chunk j's operands and of the old state is done
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int c = tr + 64 * m;
+            if (c < DK) *reinterpret_cast<float4*>(&sS[c * W + 4 * cq]) = ns[m];
+        }
+        if (j + 1 < nch) {
+            put();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vr[e] = nv[e];
+            gm[0] = ng[0];
+            gm[1] = ng[1];
+        }
+    }
+    __syncthreads();
+    if (a.S_T)
+        for (int x = tid; x < DK * W; x += 256) {
+            const int c = x / W, jj = x % W;
+            a.S_T[sbase + (int64_t)c * DV + col0 + jj] = sS[x];
+        }
+}
+
 // ------------------------------------------------------------------ launch
 template <typename E>
 static hipError_t launch_gen(const Plan& p, hipStream_t st, hipEvent_t* ev) {
@@ -572,7 +769,13 @@ static hipError_t launch_gen(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         hipLaunchKernelGGL(kg_solve<E>, dim3(p.max_chunks, p.n_heads), dim3(256), 0, st, a);
     }
     mark(2);
-    hipLaunchKernelGGL(kg_recur<E>, dim3(p.n_seqs * p.n_heads * (p.d_v / kGenCols)), dim3(256), 0, st, a);
+    const dim3 rgrid(p.n_seqs * p.n_heads * (p.d_v / kGenCols));
+    if (p.chunk <= 32)
+        hipLaunchKernelGGL((kg_recur_res<E, 32>), rgrid, dim3(256), 0, st, a);
+    else if (p.chunk <= 64)
+        hipLaunchKernelGGL((kg_recur_res<E, 64>), rgrid, dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL(kg_recur<E>, rgrid, dim3(256), 0, st, a);
     mark(3);
     return hipGetLastError();
 }
