@@ -35,6 +35,11 @@ namespace kda {
 constexpr int kGenMaxC = 128, kGenMaxD = 128;
 constexpr int kGenRows = 16;    // A and M rows per kg_gram workgroup
 constexpr int kGenCols = 16;    // value columns per kg_recur workgroup
+constexpr int kGenRecurThreads = 512;   // kg_recur and kg_recur_res threads
+
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt unconstrained
+// (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr unsigned kWaitVmcnt0 = 0x0F70;
 
 struct GenArgs {
     const void *q, *k, *v, *beta, *g;
@@ -68,6 +73,25 @@ __device__ inline bool gen_chunk(const GenArgs& a, int32_t ci, int64_t& tok0, in
     tok0 = info.tok0;
     len = info.len;
     return true;
+}
+
+// Recurrence workgroup -> (sequence n, head h, first value column col0).
+// When the (sequence, head) count is a multiple of 8, the slabs of one
+// (sequence, head) get workgroup ids congruent mod 8, which places them on
+// one XCD: the chunk operands they all read are then fetched into one L2.
+__device__ inline void gen_slab(const GenArgs& a, int slabs, int32_t& n, int& h, int& col0) {
+    const int32_t bid = blockIdx.x, NH = a.n_seqs * a.H;
+    int32_t nh, sl;
+    if (NH % 8 == 0) {
+        sl = (bid / 8) % slabs;
+        nh = (bid % 8) + 8 * (bid / (8 * slabs));
+    } else {
+        sl = bid % slabs;
+        nh = bid / slabs;
+    }
+    n = nh / a.H;
+    h = nh % a.H;
+    col0 = kGenCols * sl;
 }
 
 template <typename E>
@@ -113,12 +137,12 @@ struct Vec16 {
 // one exponential per (row, channel) instead of one per (pair, channel).
 // Every global load is a 16-byte vector, and a thread issues all of its
 // loads of a tile before it uses any.
-template <typename E>
+template <typename E, int CC>
 __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
     constexpr int P = kGenMaxD + 4;   // row pitch (floats): 16-byte rows, lanes of consecutive rows on distinct banks
     constexpr int NV = Vec16<E>::N;
-    constexpr int kTileVec = kGenMaxC * kGenMaxD / NV / 256;   // 16-byte vectors per thread of a full tile
-    __shared__ __attribute__((aligned(16))) float sKi[kGenMaxC * P];   // g, then b, then k_i e^{rho - b_i}
+    constexpr int kTileVec = CC * kGenMaxD / NV / 256;   // 16-byte vectors per thread of a full tile
+    __shared__ __attribute__((aligned(16))) float sKi[CC * P];   // g, then b, then k_i e^{rho - b_i}
     __shared__ __attribute__((aligned(16))) float sKr[kGenRows * P];   // k_r e^{b_r - rho}, rows of this block
     __shared__ __attribute__((aligned(16))) float sQr[kGenRows * P];   // q_r e^{b_r - rho}
     __shared__ float sRho[kGenMaxD];
@@ -128,7 +152,8 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
     int64_t tok0;
     int len;
     if (!gen_chunk(a, ci, tok0, len)) return;
-    const int C = a.C, DK = a.DK, tid = threadIdx.x;
+    constexpr int C = CC;
+    const int DK = a.DK, tid = threadIdx.x;
     const int nrow = r0 + kGenRows;   // columns i <= r for the block's rows r
     const int64_t rs = (int64_t)a.H * DK;
     const int64_t base = tok0 * rs + (int64_t)h * DK;
@@ -219,24 +244,24 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
                 sKi[t * P + c + e] = kv[u * NV + e] * __expf(sRho[c + e] - sKi[t * P + c + e]);
     }
     __syncthreads();
-    // column i = tid % 128 against rows 8 * (tid / 128) .. +7 of the block
-    const int i = tid % 128, rb = 8 * (tid / 128);
-    if (i >= C) return;
-    float accA[8], accM[8];
+    // column i = tid % C against rows RPT * (tid / C) .. + RPT - 1 of the block
+    constexpr int RPT = kGenRows * C / 256;
+    const int i = tid % C, rb = RPT * (tid / C);
+    float accA[RPT], accM[RPT];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) accA[m] = accM[m] = 0.f;
+    for (int m = 0; m < RPT; ++m) accA[m] = accM[m] = 0.f;
     if (i < nrow) {
         for (int c = 0; c < DK; c += 4) {
             const float4 ki = *reinterpret_cast<const float4*>(&sKi[i * P + c]);
 #pragma unroll
-            for (int m = 0; m < 8; ++m) {
+            for (int m = 0; m < RPT; ++m) {
                 accA[m] += dot4(*reinterpret_cast<const float4*>(&sKr[(rb + m) * P + c]), ki);
                 accM[m] += dot4(*reinterpret_cast<const float4*>(&sQr[(rb + m) * P + c]), ki);
             }
         }
     }
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < RPT; ++m) {
         const int r = r0 + rb + m;
         a.TB[(slot * C + r) * C + i] = i < r ? sBeta[rb + m] * accA[m] : 0.f;
         a.M[(slot * C + r) * C + i] = i <= r ? accM[m] : 0.f;
@@ -250,18 +275,19 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
 // r takes away A[r][i] times it).  Then block row by block row,
 //   T_KL = -T_KK sum_{L <= M < K} A_KM T_ML     (L < K),
 // which only needs block rows above K.  T diag(beta) is written over A.
-template <typename E>
+template <typename E, int CC>
 __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
-    constexpr int P = kGenMaxC + 1;
+    constexpr int P = CC + 1;
     constexpr int B = 16;
-    __shared__ float sA[kGenMaxC * P];
-    __shared__ float sT[kGenMaxC * P];
+    __shared__ float sA[CC * P];
+    __shared__ float sT[CC * P];
     const int32_t ci = blockIdx.x;
     const int h = blockIdx.y;
     int64_t tok0;
     int len;
     if (!gen_chunk(a, ci, tok0, len)) return;
-    const int C = a.C, tid = threadIdx.x, NB = C / B;
+    constexpr int C = CC, NB = C / B;
+    const int tid = threadIdx.x;
     const int64_t slot = (int64_t)h * a.max_chunks + ci;
     float* A = a.TB + slot * C * C;
     for (int x = tid; x < C * C; x += 256) {
@@ -286,9 +312,9 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
     // (r, j) of the block, looping over L), then T_KL = -T_KK X_KL
     const int r = tid / B, j = tid % B;
     for (int K = 1; K < NB; ++K) {
-        float x[kGenMaxC / B];
+        float x[NB];
 #pragma unroll
-        for (int L = 0; L < kGenMaxC / B; ++L) {
+        for (int L = 0; L < NB; ++L) {
             float acc = 0.f;
             if (L < K)
                 for (int m = B * L; m < B * K; ++m) acc += sA[(B * K + r) * P + m] * sT[m * P + B * L + j];
@@ -296,11 +322,11 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
         }
         __syncthreads();   // X is in registers; the block row's T entries are written below
 #pragma unroll
-        for (int L = 0; L < kGenMaxC / B; ++L)
+        for (int L = 0; L < NB; ++L)
             if (L < K) sT[(B * K + r) * P + B * L + j] = x[L];
         __syncthreads();
 #pragma unroll
-        for (int L = 0; L < kGenMaxC / B; ++L) {
+        for (int L = 0; L < NB; ++L) {
             if (L >= K) continue;
             float acc = 0.f;
             for (int m = 0; m <= r; ++m) acc += sT[(B * K + r) * P + B * K + m] * sT[(B * K + m) * P + B * L + j];
@@ -308,7 +334,7 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int L = 0; L < kGenMaxC / B; ++L)
+        for (int L = 0; L < NB; ++L)
             if (L < K) sT[(B * K + r) * P + B * L + j] = x[L];
         __syncthreads();
     }
@@ -321,11 +347,13 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
 
 // ------------------------------------------------------------------ kg_recur
 // One workgroup per (sequence, head, 16 value columns), sequential over the
-// sequence's chunks.  A thread owns 4 columns (4 cq .. 4 cq + 3) of up to two
-// rows (t = tr and tr + 64) of each C x 16 product, or of two channels of
-// the state update, and reads 16-byte vectors from LDS.
-template <typename E>
-__global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
+// sequence's chunks.  A thread owns 4 columns (4 cq .. 4 cq + 3) of the rows
+// t = tr + (NT / 4) m of each C x 16 product, or of those channels of the
+// state update, and reads 16-byte vectors from LDS.
+template <typename E, int NT>
+__global__ __launch_bounds__(NT) void kg_recur(GenArgs a) {
+    constexpr int TS = NT / 4;                 // thread rows: 4 threads per token row
+    constexpr int RP = kGenMaxC / TS;          // token rows (or channels) per thread
     constexpr int PO = kGenMaxD + 4;   // pitch of the staged operands (kGenMaxC == kGenMaxD)
     constexpr int W = kGenCols;
     static_assert(kGenMaxC == kGenMaxD, "one pitch for [token][channel], [token][token] and [channel][token]");
@@ -336,9 +364,9 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
     __shared__ __attribute__((aligned(16))) float sU[kGenMaxC * W];
     const int C = a.C, DK = a.DK, DV = a.DV, tid = threadIdx.x;
     const int slabs = DV / W;
-    const int32_t wg = blockIdx.x;
-    const int32_t n = wg / (a.H * slabs);
-    const int h = (wg / slabs) % a.H, col0 = W * (wg % slabs);
+    int32_t n;
+    int h, col0;
+    gen_slab(a, slabs, n, h, col0);
     const int cq = tid % 4, tr = tid / 4;
     int64_t s_start, s_len;
     if (a.cu) {
@@ -359,7 +387,7 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         c0 = n * nch;
     }
     const int64_t sbase = ((int64_t)n * a.H + h) * DK * DV;
-    for (int x = tid; x < DK * W; x += 256) {
+    for (int x = tid; x < DK * W; x += NT) {
         const int c = x / W, jj = x % W;
         sS[x] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
     }
@@ -369,7 +397,7 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
     // them to dst as rows (transposed = false) or as columns (dst[k][r]).
     // Each operand is fetched one phase before it is put, so that the loads'
     // latency overlaps the phase in between.
-    constexpr int kMaxV = kGenMaxC * kGenMaxD / 4 / 256;
+    constexpr int kMaxV = kGenMaxC * kGenMaxD / 4 / NT;
     struct Fetched {
         float4 f[kMaxV];
     };
@@ -377,7 +405,7 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         const int n4 = R * (K / 4);
 #pragma unroll
         for (int u = 0; u < kMaxV; ++u) {
-            const int x = tid + 256 * u;
+            const int x = tid + NT * u;
             pr.f[u] = x < n4 ? reinterpret_cast<const float4*>(src)[x] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
     };
@@ -385,7 +413,7 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         const int kv = K / 4, n4 = R * kv;
 #pragma unroll
         for (int u = 0; u < kMaxV; ++u) {
-            const int x = tid + 256 * u;
+            const int x = tid + NT * u;
             if (x >= n4) continue;
             const int r = x / kv, c4 = 4 * (x % kv);
             if (transposed) {
@@ -401,10 +429,10 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
     // acc[m] += rows t_m of `op` (16-byte vectors along the contraction, up
     // to `kend` rounded up to 4; entries past a row's end must be zero in
     // `op`) times the 4 columns of `rhs` ([k][16] in LDS)
-    auto rows_times = [&](const float* op, const float* rhs, int kend0, bool tri, float4 acc[2]) {
+    auto rows_times = [&](const float* op, const float* rhs, int kend0, bool tri, float4 acc[RP]) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int t = tr + 64 * m;
+        for (int m = 0; m < RP; ++m) {
+            const int t = tr + TS * m;
             if (t >= C) continue;
             const int kend = tri ? ((t + 4) & ~3) : kend0;
             float4 s = acc[m];
@@ -416,6 +444,35 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
                 s = fma4(o4.w, *reinterpret_cast<const float4*>(&rhs[(k + 3) * W + 4 * cq]), s);
             }
             acc[m] = s;
+        }
+    };
+    // the same over the full contraction for two operands sharing rhs (one
+    // read of rhs for both)
+    auto rows_times2 = [&](const float* opa, const float* opb, const float* rhs, int kend, float4 acca[RP],
+                           float4 accb[RP]) {
+#pragma unroll
+        for (int m = 0; m < RP; ++m) {
+            const int t = tr + TS * m;
+            if (t >= C) continue;
+            float4 sa = acca[m], sb = accb[m];
+            for (int k = 0; k < kend; k += 4) {
+                const float4 a4 = *reinterpret_cast<const float4*>(&opa[t * PO + k]);
+                const float4 b4 = *reinterpret_cast<const float4*>(&opb[t * PO + k]);
+                const float4 r0 = *reinterpret_cast<const float4*>(&rhs[(k + 0) * W + 4 * cq]);
+                const float4 r1 = *reinterpret_cast<const float4*>(&rhs[(k + 1) * W + 4 * cq]);
+                const float4 r2 = *reinterpret_cast<const float4*>(&rhs[(k + 2) * W + 4 * cq]);
+                const float4 r3 = *reinterpret_cast<const float4*>(&rhs[(k + 3) * W + 4 * cq]);
+                sa = fma4(a4.x, r0, sa);
+                sb = fma4(b4.x, r0, sb);
+                sa = fma4(a4.y, r1, sa);
+                sb = fma4(b4.y, r1, sb);
+                sa = fma4(a4.z, r2, sa);
+                sb = fma4(b4.z, r2, sb);
+                sa = fma4(a4.w, r3, sa);
+                sb = fma4(b4.w, r3, sb);
+            }
+            acca[m] = sa;
+            accb[m] = sb;
         }
     };
     Fetched fa, fb;
@@ -434,10 +491,10 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         // this step's T diag(beta), M, value rows and e^{b_L}, ahead of use
         fetch(fa, a.TB + slot * C * C, C, C);
         fetch(fb, a.M + slot * C * C, C, C);
-        float vr[2][4], gm[2];
+        float vr[RP][4], gm[RP];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int t = tr + 64 * m, c = tr + 64 * m;
+        for (int m = 0; m < RP; ++m) {
+            const int t = tr + TS * m, c = tr + TS * m;
             if (t < len) {
                 const int64_t vo = (tok0 + t) * vrs + (int64_t)h * DV + col0 + 4 * cq;
 #pragma unroll
@@ -449,13 +506,13 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
             gm[m] = c < DK ? a.gam[slot * DK + c] : 0.f;
         }
         // X = (K.e^b) S, P = (Q.e^b) S; Y = V - X
-        float4 accX[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
-        float4 accP[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
-        rows_times(bufA, sS, DK, false, accX);
-        rows_times(bufB, sS, DK, false, accP);
+        float4 accX[RP], accP[RP];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int t = tr + 64 * m;
+        for (int m = 0; m < RP; ++m) accX[m] = accP[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+        rows_times2(bufA, bufB, sS, DK, accX, accP);
+#pragma unroll
+        for (int m = 0; m < RP; ++m) {
+            const int t = tr + TS * m;
             if (t >= C) continue;
             const float4 y = t < len ? make_float4(vr[m][0] - accX[m].x, vr[m][1] - accX[m].y,
                                                    vr[m][2] - accX[m].z, vr[m][3] - accX[m].w)
@@ -469,11 +526,13 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         fetch(fa, a.Kh + slot * C * DK, C, DK);
         // U~ = T diag(beta) Y (lower triangular)
         {
-            float4 accU[2] = {make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+            float4 accU[RP];
+#pragma unroll
+            for (int m = 0; m < RP; ++m) accU[m] = make_float4(0.f, 0.f, 0.f, 0.f);
             rows_times(bufA, sY, 0, true, accU);
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int t = tr + 64 * m;
+            for (int m = 0; m < RP; ++m) {
+                const int t = tr + TS * m;
                 if (t < C) *reinterpret_cast<float4*>(&sU[t * W + 4 * cq]) = accU[m];
             }
         }
@@ -486,8 +545,8 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         // O = P + M U~
         rows_times(bufB, sU, 0, true, accP);
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int t = tr + 64 * m;
+        for (int m = 0; m < RP; ++m) {
+            const int t = tr + TS * m;
             if (t >= len) continue;
             E* op = static_cast<E*>(a.o) + (tok0 + t) * vrs + (int64_t)h * DV + col0 + 4 * cq;
             op[0] = from_f<E>(accP[m].x);
@@ -497,10 +556,10 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         }
         __syncthreads();   // (K.e^{b_L-b})^T is in LDS
         // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~: channels c = tr, tr + 64
-        float4 ns[2];
+        float4 ns[RP];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int c = tr + 64 * m;
+        for (int m = 0; m < RP; ++m) {
+            const int c = tr + TS * m;
             if (c >= DK) continue;
             const float4 s0 = *reinterpret_cast<const float4*>(&sS[c * W + 4 * cq]);
             float4 acc = make_float4(gm[m] * s0.x, gm[m] * s0.y, gm[m] * s0.z, gm[m] * s0.w);
@@ -515,8 +574,8 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
         }
         __syncthreads();   // every read of the old state, of M and of (K.e^{b_L-b})^T is done
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int c = tr + 64 * m;
+        for (int m = 0; m < RP; ++m) {
+            const int c = tr + TS * m;
             if (c < DK) *reinterpret_cast<float4*>(&sS[c * W + 4 * cq]) = ns[m];
         }
         if (j + 1 < nch) {
@@ -526,7 +585,7 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
     }
     __syncthreads();
     if (a.S_T)
-        for (int x = tid; x < DK * W; x += 256) {
+        for (int x = tid; x < DK * W; x += NT) {
             const int c = x / W, jj = x % W;
             a.S_T[sbase + (int64_t)c * DV + col0 + jj] = sS[x];
         }
@@ -538,28 +597,44 @@ __global__ __launch_bounds__(256) void kg_recur(GenArgs a) {
 // the next chunk (operands, value rows, e^{b_L}) into registers at its start
 // and puts them to LDS at its end, so one round of global loads per step
 // overlaps the whole step instead of each operand waiting for its own.
-template <typename E, int CM>
-__global__ __launch_bounds__(256) void kg_recur_res(GenArgs a) {
+//
+// With C tokens and NT / 4 = 128 thread rows, the two products over the key
+// channels (X = (K.e^b) S and P = (Q.e^b) S) split the channels into
+// ks = 128 / C parts: thread row tr takes token row tr / ks and channel part
+// tr % ks, and the parts of a row (4 ks adjacent lanes of one wave) are
+// summed by lane exchanges.  The first part's thread of a row then owns that
+// row through U~ and O.  The state slab's rows are stored with a 16-float
+// gap after every part's range of channels, so the parts' simultaneous reads
+// of their own channel rows fall in different LDS banks.
+template <typename E, int CM, int NT>
+__global__ __launch_bounds__(NT) void kg_recur_res(GenArgs a) {
     constexpr int W = kGenCols;
+    constexpr int TS = NT / 4;                // thread rows
     constexpr int PD = kGenMaxD + 4;          // pitch of [token][channel] rows
     constexpr int PC = CM + 4;                // pitch of [token][token] and [channel][token] rows
-    constexpr int kRowV = CM * kGenMaxD / 4 / 256;   // 16-byte vectors per thread of a [CM][d_k] operand
-    constexpr int kTriV = (CM * CM / 4 + 255) / 256;   // ... of a [CM][CM] operand
-    static_assert(CM <= 64, "one row of each product per thread");
+    constexpr int kRowV = CM * kGenMaxD / 4 / NT;     // 16-byte vectors per thread of a [CM][d_k] operand
+    constexpr int kTriV = (CM * CM / 4 + NT - 1) / NT;   // ... of a [CM][CM] operand
+    constexpr int kMaxParts = TS / 16;
+    static_assert(TS >= kGenMaxD && TS >= 2 * CM, "one channel per thread; at least two parts per row");
     __shared__ __attribute__((aligned(16))) float sKg[CM * PD];
     __shared__ __attribute__((aligned(16))) float sQg[CM * PD];
     __shared__ __attribute__((aligned(16))) float sKhT[kGenMaxD * PC];
     __shared__ __attribute__((aligned(16))) float sTB[CM * PC];
     __shared__ __attribute__((aligned(16))) float sM[CM * PC];
-    __shared__ __attribute__((aligned(16))) float sS[kGenMaxD * W];
+    __shared__ __attribute__((aligned(16))) float sS[kGenMaxD * W + W * kMaxParts];
     __shared__ __attribute__((aligned(16))) float sY[CM * W];
     __shared__ __attribute__((aligned(16))) float sU[CM * W];
     const int C = a.C, DK = a.DK, DV = a.DV, tid = threadIdx.x;
     const int slabs = DV / W;
-    const int32_t wg = blockIdx.x;
-    const int32_t n = wg / (a.H * slabs);
-    const int h = (wg / slabs) % a.H, col0 = W * (wg % slabs);
-    const int cq = tid % 4, tr = tid / 4;   // 4 columns of token row tr (or of channels tr, tr + 64)
+    int32_t n;
+    int h, col0;
+    gen_slab(a, slabs, n, h, col0);
+    const int cq = tid % 4, tr = tid / 4;
+    const int ks = TS / C, kc = DK / ks;                // channel parts per row, channels per part
+    const int sh = 31 - __builtin_clz(kc);              // kc is a power of two
+    const int row = tr / ks, part = tr % ks;
+    const bool lead = part == 0;
+    auto sidx = [&](int c) { return c * W + W * (c >> sh); };   // state row c in sS
     int64_t s_start, s_len;
     if (a.cu) {
         int64_t b0 = a.cu[n], b1 = a.cu[n + 1];
@@ -579,15 +654,17 @@ __global__ __launch_bounds__(256) void kg_recur_res(GenArgs a) {
         c0 = n * nch;
     }
     const int64_t sbase = ((int64_t)n * a.H + h) * DK * DV;
-    for (int x = tid; x < DK * W; x += 256) {
+    for (int x = tid; x < DK * W; x += NT) {
         const int c = x / W, jj = x % W;
-        sS[x] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
+        sS[sidx(c) + jj] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
     }
     const int64_t vrs = (int64_t)a.H * DV;
     // the next chunk's loads, in registers between fetch and put
     typedef float v4 __attribute__((ext_vector_type(4)));
     v4 nKg[kRowV], nQg[kRowV], nKh[kRowV], nTB[kTriV], nM[kTriV];
-    float nv[4], ng[2];
+    E nv[4];          // raw: converting at the load would make the compiler wait for it there
+    float ng;
+    bool nvok = false;
     auto fetch = [&](int j) __attribute__((always_inline)) {
         const int64_t slot = (int64_t)h * a.max_chunks + c0 + j;
         const int64_t tok0 = s_start + (int64_t)j * C;
@@ -600,7 +677,7 @@ __global__ __launch_bounds__(256) void kg_recur_res(GenArgs a) {
         const v4* mm = reinterpret_cast<const v4*>(a.M + slot * C * C);
 #pragma unroll
         for (int u = 0; u < kRowV; ++u) {
-            const int x = tid + 256 * u;
+            const int x = tid + NT * u;
             if (x < nr) {
                 nKg[u] = kg[x];
                 nQg[u] = qg[x];
@@ -609,26 +686,25 @@ __global__ __launch_bounds__(256) void kg_recur_res(GenArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < kTriV; ++u) {
-            const int x = tid + 256 * u;
+            const int x = tid + NT * u;
             if (x < nt) {
                 nTB[u] = tb[x];
                 nM[u] = mm[x];
             }
         }
-        const int64_t vo = (tok0 + tr) * vrs + (int64_t)h * DV + col0 + 4 * cq;
+        // value rows and e^{b_L}: loaded from a valid address on every lane
+        // and masked when used
+        nvok = lead && row < len;
+        const int64_t vo = (tok0 + (nvok ? row : 0)) * vrs + (int64_t)h * DV + col0 + 4 * cq;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) nv[e] = tr < len ? ldf<E>(a.v, vo + e) : 0.f;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int c = tr + 64 * m;
-            ng[m] = c < DK ? a.gam[slot * DK + c] : 0.f;
-        }
+        for (int e = 0; e < 4; ++e) nv[e] = static_cast<const E*>(a.v)[vo + e];
+        ng = a.gam[slot * DK + (tr < DK ? tr : 0)];
     };
     auto put = [&]() __attribute__((always_inline)) {
         const int kv = DK / 4, nr = C * kv, tv = C / 4, nt = C * tv;
 #pragma unroll
         for (int u = 0; u < kRowV; ++u) {
-            const int x = tid + 256 * u;
+            const int x = tid + NT * u;
             if (x >= nr) continue;
             const int r = x / kv, c4 = 4 * (x % kv);
             *reinterpret_cast<v4*>(&sKg[r * PD + c4]) = nKg[u];
@@ -640,12 +716,17 @@ __global__ __launch_bounds__(256) void kg_recur_res(GenArgs a) {
         }
 #pragma unroll
         for (int u = 0; u < kTriV; ++u) {
-            const int x = tid + 256 * u;
+            const int x = tid + NT * u;
             if (x >= nt) continue;
             const int r = x / tv, c4 = 4 * (x % tv);
             *reinterpret_cast<v4*>(&sTB[r * PC + c4]) = nTB[u];
             *reinterpret_cast<v4*>(&sM[r * PC + c4]) = nM[u];
         }
+        // Every load of the fetch has landed by now; saying so here keeps the
+        // compiler from waiting for the next fetch's fresh loads when it
+        // reuses these registers (it cannot tell that the loads and their
+        // uses above are under the same conditions).
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     };
     // acc += row t of `op` (pitch P, entries past the row's end zero) times
     // the 4 columns of `rhs` ([k][16]), over k < kend (a multiple of 4)
@@ -659,72 +740,97 @@ __global__ __launch_bounds__(256) void kg_recur_res(GenArgs a) {
         }
         return acc;
     };
-    float vr[4] = {0.f, 0.f, 0.f, 0.f}, gm[2] = {0.f, 0.f};
+    // x += row t of K.e^b and p += row t of Q.e^b (pitch PD) times the
+    // same 4 columns of `rhs`, over kend channels: one read of rhs for both
+    auto two_rows_times = [&](const float* opx, const float* opp, int t, const float* rhs, int kend, float4& x,
+                              float4& p) __attribute__((always_inline)) {
+        for (int k = 0; k < kend; k += 4) {
+            const float4 ox = *reinterpret_cast<const float4*>(&opx[t * PD + k]);
+            const float4 op = *reinterpret_cast<const float4*>(&opp[t * PD + k]);
+            const float4 r0 = *reinterpret_cast<const float4*>(&rhs[(k + 0) * W + 4 * cq]);
+            const float4 r1 = *reinterpret_cast<const float4*>(&rhs[(k + 1) * W + 4 * cq]);
+            const float4 r2 = *reinterpret_cast<const float4*>(&rhs[(k + 2) * W + 4 * cq]);
+            const float4 r3 = *reinterpret_cast<const float4*>(&rhs[(k + 3) * W + 4 * cq]);
+            x = fma4(ox.x, r0, x);
+            p = fma4(op.x, r0, p);
+            x = fma4(ox.y, r1, x);
+            p = fma4(op.y, r1, p);
+            x = fma4(ox.z, r2, x);
+            p = fma4(op.z, r2, p);
+            x = fma4(ox.w, r3, x);
+            p = fma4(op.w, r3, p);
+        }
+    };
+    float vr[4] = {0.f, 0.f, 0.f, 0.f}, gm = 0.f;
     if (nch > 0) {
         fetch(0);
         put();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vr[e] = nv[e];
-        gm[0] = ng[0];
-        gm[1] = ng[1];
+        for (int e = 0; e < 4; ++e) vr[e] = nvok ? to_f(nv[e]) : 0.f;
+        gm = ng;
     }
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    // this thread's part of the key channels, and its rows of the state slab
+    const int ch0 = part * kc;
+    const float* sSp = sS + sidx(ch0);
     for (int j = 0; j < nch; ++j) {
         const int64_t tok0 = s_start + (int64_t)j * C;
         const int len = (int)(s_len - (int64_t)j * C < C ? s_len - (int64_t)j * C : C);
         __syncthreads();   // chunk j's operands and the state are in LDS
-        if (j + 1 < nch) fetch(j + 1);
-        // X = (K.e^b) S, P = (Q.e^b) S; Y = V - X
-        float4 accP = z4;
-        if (tr < C) {
-            const float4 x = row_times(sKg, PD, tr, sS, DK, z4);
-            accP = row_times(sQg, PD, tr, sS, DK, z4);
-            const float4 y = tr < len ? make_float4(vr[0] - x.x, vr[1] - x.y, vr[2] - x.z, vr[3] - x.w) : z4;
-            *reinterpret_cast<float4*>(&sY[tr * W + 4 * cq]) = y;
+        // the next chunk's loads (the last step loads its own chunk again,
+        // unused: with the fetch and the put unconditional, the compiler
+        // sees every load consumed before the next fetch reuses its
+        // registers, and does not wait on the fresh loads at their issue)
+        fetch(j + 1 < nch ? j + 1 : j);
+        // X = (K.e^b) S, P = (Q.e^b) S over this part's channels, then summed
+        // over the parts; Y = V - X
+        float4 x = z4, accP = z4;
+        two_rows_times(sKg + ch0, sQg + ch0, row, sSp, kc, x, accP);
+        for (int o = 4; o < 4 * ks; o <<= 1) {
+            x.x += __shfl_xor(x.x, o);
+            x.y += __shfl_xor(x.y, o);
+            x.z += __shfl_xor(x.z, o);
+            x.w += __shfl_xor(x.w, o);
+            accP.x += __shfl_xor(accP.x, o);
+            accP.y += __shfl_xor(accP.y, o);
+            accP.z += __shfl_xor(accP.z, o);
+            accP.w += __shfl_xor(accP.w, o);
+        }
+        if (lead) {
+            const float4 y = row < len ? make_float4(vr[0] - x.x, vr[1] - x.y, vr[2] - x.z, vr[3] - x.w) : z4;
+            *reinterpret_cast<float4*>(&sY[row * W + 4 * cq]) = y;
         }
         __syncthreads();
         // U~ = T diag(beta) Y (lower triangular: row t needs k <= t)
-        if (tr < C) *reinterpret_cast<float4*>(&sU[tr * W + 4 * cq]) = row_times(sTB, PC, tr, sY, (tr + 4) & ~3, z4);
+        if (lead) *reinterpret_cast<float4*>(&sU[row * W + 4 * cq]) = row_times(sTB, PC, row, sY, (row + 4) & ~3, z4);
         __syncthreads();
         // O = P + M U~
-        if (tr < len) {
-            const float4 ov = row_times(sM, PC, tr, sU, (tr + 4) & ~3, accP);
-            E* op = static_cast<E*>(a.o) + (tok0 + tr) * vrs + (int64_t)h * DV + col0 + 4 * cq;
+        if (lead && row < len) {
+            const float4 ov = row_times(sM, PC, row, sU, (row + 4) & ~3, accP);
+            E* op = static_cast<E*>(a.o) + (tok0 + row) * vrs + (int64_t)h * DV + col0 + 4 * cq;
             op[0] = from_f<E>(ov.x);
             op[1] = from_f<E>(ov.y);
             op[2] = from_f<E>(ov.z);
             op[3] = from_f<E>(ov.w);
         }
-        // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~: channels tr, tr + 64
-        float4 ns[2];
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int c = tr + 64 * m;
-            ns[m] = z4;
-            if (c < DK) {
-                const float4 s0 = *reinterpret_cast<const float4*>(&sS[c * W + 4 * cq]);
-                ns[m] = row_times(sKhT, PC, c, sU, C, make_float4(gm[m] * s0.x, gm[m] * s0.y, gm[m] * s0.z, gm[m] * s0.w));
-            }
+        // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~: channel tr
+        float4 ns = z4;
+        if (tr < DK) {
+            const float4 s0 = *reinterpret_cast<const float4*>(&sS[sidx(tr) + 4 * cq]);
+            ns = row_times(sKhT, PC, tr, sU, C, make_float4(gm * s0.x, gm * s0.y, gm * s0.z, gm * s0.w));
         }
         __syncthreads();   // every read of chunk j's operands and of the old state is done
+        if (tr < DK) *reinterpret_cast<float4*>(&sS[sidx(tr) + 4 * cq]) = ns;
+        put();
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int c = tr + 64 * m;
-            if (c < DK) *reinterpret_cast<float4*>(&sS[c * W + 4 * cq]) = ns[m];
-        }
-        if (j + 1 < nch) {
-            put();
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vr[e] = nv[e];
-            gm[0] = ng[0];
-            gm[1] = ng[1];
-        }
+        for (int e = 0; e < 4; ++e) vr[e] = nvok ? to_f(nv[e]) : 0.f;
+        gm = ng;
     }
     __syncthreads();
     if (a.S_T)
-        for (int x = tid; x < DK * W; x += 256) {
+        for (int x = tid; x < DK * W; x += NT) {
             const int c = x / W, jj = x % W;
-            a.S_T[sbase + (int64_t)c * DV + col0 + jj] = sS[x];
+            a.S_T[sbase + (int64_t)c * DV + col0 + jj] = sS[sidx(c) + jj];
         }
 }
 
@@ -765,24 +871,41 @@ static hipError_t launch_gen(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     if (p.cu_seqlens) launch_chunk_table(p, p.chunk, st);
     mark(1);
     if (p.max_chunks > 0) {
-        hipLaunchKernelGGL(kg_gram<E>, dim3(p.max_chunks, p.n_heads, p.chunk / kGenRows), dim3(256), 0, st, a);
-        hipLaunchKernelGGL(kg_solve<E>, dim3(p.max_chunks, p.n_heads), dim3(256), 0, st, a);
+        const dim3 ggrid(p.max_chunks, p.n_heads, p.chunk / kGenRows), sgrid(p.max_chunks, p.n_heads);
+        switch (p.chunk) {
+            case 16:
+                hipLaunchKernelGGL((kg_gram<E, 16>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_solve<E, 16>), sgrid, dim3(256), 0, st, a);
+                break;
+            case 32:
+                hipLaunchKernelGGL((kg_gram<E, 32>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_solve<E, 32>), sgrid, dim3(256), 0, st, a);
+                break;
+            case 64:
+                hipLaunchKernelGGL((kg_gram<E, 64>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_solve<E, 64>), sgrid, dim3(256), 0, st, a);
+                break;
+            default:
+                hipLaunchKernelGGL((kg_gram<E, 128>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_solve<E, 128>), sgrid, dim3(256), 0, st, a);
+                break;
+        }
     }
     mark(2);
     const dim3 rgrid(p.n_seqs * p.n_heads * (p.d_v / kGenCols));
     if (p.chunk <= 32)
-        hipLaunchKernelGGL((kg_recur_res<E, 32>), rgrid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((kg_recur_res<E, 32, kGenRecurThreads>), rgrid, dim3(kGenRecurThreads), 0, st, a);
     else if (p.chunk <= 64)
-        hipLaunchKernelGGL((kg_recur_res<E, 64>), rgrid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((kg_recur_res<E, 64, kGenRecurThreads>), rgrid, dim3(kGenRecurThreads), 0, st, a);
     else
-        hipLaunchKernelGGL(kg_recur<E>, rgrid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((kg_recur<E, kGenRecurThreads>), rgrid, dim3(kGenRecurThreads), 0, st, a);
     mark(3);
     return hipGetLastError();
 }
 
 hipError_t launch_generic(const Plan& p, hipStream_t st, hipEvent_t* ev) {
-    if (p.chunk > kGenMaxC || p.chunk % kGenRows != 0 || p.d_k > kGenMaxD || p.d_v > kGenMaxD || p.d_v % kGenCols != 0 ||
-        p.d_k % 4 != 0 || p.chunk % 4 != 0)
+    if ((p.chunk != 16 && p.chunk != 32 && p.chunk != 64 && p.chunk != 128) || (p.d_k != 64 && p.d_k != 128) ||
+        (p.d_v != 64 && p.d_v != 128))
         return hipErrorInvalidValue;
     return p.bf16 ? launch_gen<__bf16>(p, st, ev) : launch_gen<float>(p, st, ev);
 }
