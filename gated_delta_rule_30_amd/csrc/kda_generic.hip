@@ -35,7 +35,7 @@ namespace kda {
 constexpr int kGenMaxC = 128, kGenMaxD = 128;
 constexpr int kGenRows = 16;    // A and M rows per kg_gram workgroup
 constexpr int kGenCols = 16;    // value columns per kg_recur workgroup
-constexpr int kGenRecurThreads = 512;   // kg_recur and kg_recur_res threads
+constexpr int kGenRecurThreads = 512;   // kg_recur threads
 
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt unconstrained
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -137,11 +137,11 @@ struct Vec16 {
 // one exponential per (row, channel) instead of one per (pair, channel).
 // Every global load is a 16-byte vector, and a thread issues all of its
 // loads of a tile before it uses any.
-template <typename E, int CC>
-__global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
+template <typename E, int CC, int NT>
+__global__ __launch_bounds__(NT) void kg_gram(GenArgs a) {
     constexpr int P = kGenMaxD + 4;   // row pitch (floats): 16-byte rows, lanes of consecutive rows on distinct banks
     constexpr int NV = Vec16<E>::N;
-    constexpr int kTileVec = CC * kGenMaxD / NV / 256;   // 16-byte vectors per thread of a full tile
+    constexpr int kTileVec = CC * kGenMaxD / NV / NT;   // 16-byte vectors per thread of a full tile
     __shared__ __attribute__((aligned(16))) float sKi[CC * P];   // g, then b, then k_i e^{rho - b_i}
     __shared__ __attribute__((aligned(16))) float sKr[kGenRows * P];   // k_r e^{b_r - rho}, rows of this block
     __shared__ __attribute__((aligned(16))) float sQr[kGenRows * P];   // q_r e^{b_r - rho}
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
     float gv[kTileVec * NV], kv[kTileVec * NV];
 #pragma unroll
     for (int u = 0; u < kTileVec; ++u) {
-        const int x = tid + 256 * u, t = x / vpr, c = (x % vpr) * NV;
+        const int x = tid + NT * u, t = x / vpr, c = (x % vpr) * NV;
         const bool in = x < C * vpr && t < len;
         if (in) Vec16<E>::load(a.g, base + t * rs + c, &gv[u * NV]);
         if (in && t < nrow) Vec16<E>::load(a.k, base + t * rs + c, &kv[u * NV]);
@@ -180,14 +180,14 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kTileVec; ++u) {
-        const int x = tid + 256 * u, t = x / vpr, c = (x % vpr) * NV;
+        const int x = tid + NT * u, t = x / vpr, c = (x % vpr) * NV;
         if (x < C * vpr)
 #pragma unroll
             for (int e = 0; e < NV; ++e) sKi[t * P + c + e] = gv[u * NV + e];
     }
     __syncthreads();
     // b: per-channel running sum over the chunk, eight rows read at a time
-    for (int c = tid; c < DK; c += 256) {
+    for (int c = tid; c < DK; c += NT) {
         float run = 0.f;
         for (int t0 = 0; t0 < C; t0 += 8) {
             float x[8];
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
     }
     __syncthreads();
     // the block's rows: scaled operands, and Q.e^b, K.e^b, K.e^{b_L - b}
-    for (int x = tid; x < kGenRows * vpr; x += 256) {
+    for (int x = tid; x < kGenRows * vpr; x += NT) {
         const int rr = x / vpr, r = r0 + rr, c = (x % vpr) * NV;
         float kr[NV], qr[NV];
         if (r < len) {
@@ -233,11 +233,11 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
         }
     }
     if (blockIdx.z == 0)
-        for (int c = tid; c < DK; c += 256) a.gam[slot * DK + c] = __expf(sKi[(C - 1) * P + c]);
+        for (int c = tid; c < DK; c += NT) a.gam[slot * DK + c] = __expf(sKi[(C - 1) * P + c]);
     __syncthreads();   // every read of b outside each thread's own elements is done
 #pragma unroll
     for (int u = 0; u < kTileVec; ++u) {
-        const int x = tid + 256 * u, t = x / vpr, c = (x % vpr) * NV;
+        const int x = tid + NT * u, t = x / vpr, c = (x % vpr) * NV;
         if (x < C * vpr && t < nrow)
 #pragma unroll
             for (int e = 0; e < NV; ++e)
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
     }
     __syncthreads();
     // column i = tid % C against rows RPT * (tid / C) .. + RPT - 1 of the block
-    constexpr int RPT = kGenRows * C / 256;
+    constexpr int RPT = kGenRows * C / NT;
     const int i = tid % C, rb = RPT * (tid / C);
     float accA[RPT], accM[RPT];
 #pragma unroll
@@ -277,10 +277,11 @@ __global__ __launch_bounds__(256) void kg_gram(GenArgs a) {
 // which only needs block rows above K.  T diag(beta) is written over A.
 template <typename E, int CC>
 __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
-    constexpr int P = CC + 1;
     constexpr int B = 16;
-    __shared__ float sA[CC * P];
-    __shared__ float sT[CC * P];
+    constexpr int kTri = CC * (CC + 1) / 2;   // lower triangles, row r at r (r + 1) / 2
+    __shared__ float sA[kTri];
+    __shared__ float sT[kTri];
+    auto at = [](int r, int j) { return r * (r + 1) / 2 + j; };   // (r, j), j <= r
     const int32_t ci = blockIdx.x;
     const int h = blockIdx.y;
     int64_t tok0;
@@ -292,8 +293,10 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
     float* A = a.TB + slot * C * C;
     for (int x = tid; x < C * C; x += 256) {
         const int r = x / C, j = x % C;
-        sA[r * P + j] = A[x];
-        sT[r * P + j] = r == j ? 1.f : 0.f;
+        if (j <= r) {
+            sA[at(r, j)] = A[x];
+            sT[at(r, j)] = r == j ? 1.f : 0.f;
+        }
     }
     __syncthreads();
     // diagonal blocks: thread -> block K = tid / 32, column j, rows of parity g
@@ -301,9 +304,9 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
         const int K = tid / 32, j = tid % B, g = (tid / B) % 2, o = B * K;
         for (int i = 0; i < B - 1; ++i) {
             if (K < NB && j <= i) {
-                const float ti = sT[(o + i) * P + o + j];
+                const float ti = sT[at(o + i, o + j)];
                 for (int r = i + 1 + ((g - (i + 1)) % 2 + 2) % 2; r < B; r += 2)
-                    sT[(o + r) * P + o + j] -= sA[(o + r) * P + o + i] * ti;
+                    sT[at(o + r, o + j)] -= sA[at(o + r, o + i)] * ti;
             }
             __syncthreads();
         }
@@ -317,31 +320,31 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
         for (int L = 0; L < NB; ++L) {
             float acc = 0.f;
             if (L < K)
-                for (int m = B * L; m < B * K; ++m) acc += sA[(B * K + r) * P + m] * sT[m * P + B * L + j];
+                for (int m = B * L + j; m < B * K; ++m) acc += sA[at(B * K + r, m)] * sT[at(m, B * L + j)];
             x[L] = acc;
         }
         __syncthreads();   // X is in registers; the block row's T entries are written below
 #pragma unroll
         for (int L = 0; L < NB; ++L)
-            if (L < K) sT[(B * K + r) * P + B * L + j] = x[L];
+            if (L < K) sT[at(B * K + r, B * L + j)] = x[L];
         __syncthreads();
 #pragma unroll
         for (int L = 0; L < NB; ++L) {
             if (L >= K) continue;
             float acc = 0.f;
-            for (int m = 0; m <= r; ++m) acc += sT[(B * K + r) * P + B * K + m] * sT[(B * K + m) * P + B * L + j];
+            for (int m = 0; m <= r; ++m) acc += sT[at(B * K + r, B * K + m)] * sT[at(B * K + m, B * L + j)];
             x[L] = -acc;
         }
         __syncthreads();
 #pragma unroll
         for (int L = 0; L < NB; ++L)
-            if (L < K) sT[(B * K + r) * P + B * L + j] = x[L];
+            if (L < K) sT[at(B * K + r, B * L + j)] = x[L];
         __syncthreads();
     }
     for (int x = tid; x < C * C; x += 256) {
         const int rr = x / C, jj = x % C;
         const float bj = jj < len ? ldf<E>(a.beta, (tok0 + jj) * a.H + h) : 0.f;
-        A[x] = sT[rr * P + jj] * bj;
+        A[x] = jj <= rr ? sT[at(rr, jj)] * bj : 0.f;
     }
 }
 
@@ -592,49 +595,47 @@ __global__ __launch_bounds__(NT) void kg_recur(GenArgs a) {
 }
 
 // ------------------------------------------------------------------ kg_recur_res
-// kg_recur for chunks of at most CM tokens (CM = 32 or 64), where all five
-// operands of a chunk fit in LDS together: each step issues every load of
-// the next chunk (operands, value rows, e^{b_L}) into registers at its start
-// and puts them to LDS at its end, so one round of global loads per step
-// overlaps the whole step instead of each operand waiting for its own.
+// kg_recur for chunks of at most CM tokens (CM = 16, 32 or 64), on fp32 matrix
+// cores.  All five operands of a chunk fit in LDS together: each step issues
+// every load of the next chunk (operands, value rows, e^{b_L}) into
+// registers right after its first barrier and writes them to LDS after its
+// last one, so one round of loads per step overlaps the whole step.
 //
-// With C tokens and NT / 4 = 128 thread rows, the two products over the key
-// channels (X = (K.e^b) S and P = (Q.e^b) S) split the channels into
-// ks = 128 / C parts: thread row tr takes token row tr / ks and channel part
-// tr % ks, and the parts of a row (4 ks adjacent lanes of one wave) are
-// summed by lane exchanges.  The first part's thread of a row then owns that
-// row through U~ and O.  The state slab's rows are stored with a 16-float
-// gap after every part's range of channels, so the parts' simultaneous reads
-// of their own channel rows fall in different LDS banks.
-template <typename E, int CM, int NT>
-__global__ __launch_bounds__(NT) void kg_recur_res(GenArgs a) {
+// Every product is a set of 16 x 16 fp32 output tiles (16 tokens or key
+// channels by the slab's 16 value columns) from 16x16x4 MFMA steps; a lane's
+// A and B fragments for four consecutive steps are one 16-byte LDS read each
+// (the contraction index of step u is 4 g + u within each 16-wide block, for
+// lane group g), so B operands are kept column-major: S^T, Y^T and U~^T as
+// [value column][k].  With nT = C / 16 token tiles, wave w < nT forms X and
+// then U~ for tile w, wave nT + w forms P and then O for tile w, and wave c
+// forms the state update for channels 16c .. 16c + 15.
+template <typename E, int CM>
+__global__ __launch_bounds__(512) void kg_recur_res(GenArgs a) {
+    constexpr int NT = 512;
     constexpr int W = kGenCols;
-    constexpr int TS = NT / 4;                // thread rows
-    constexpr int PD = kGenMaxD + 4;          // pitch of [token][channel] rows
-    constexpr int PC = CM + 4;                // pitch of [token][token] and [channel][token] rows
-    constexpr int kRowV = CM * kGenMaxD / 4 / NT;     // 16-byte vectors per thread of a [CM][d_k] operand
+    constexpr int PD = kGenMaxD + 4;          // [token][channel] and [column][channel] rows
+    constexpr int PC = CM + 4;                // [token][token], [channel][token], [column][token] rows
+    constexpr int kRowV = CM * kGenMaxD / 4 / NT;        // 16-byte vectors per thread of a [CM][d_k] operand
     constexpr int kTriV = (CM * CM / 4 + NT - 1) / NT;   // ... of a [CM][CM] operand
-    constexpr int kMaxParts = TS / 16;
-    static_assert(TS >= kGenMaxD && TS >= 2 * CM, "one channel per thread; at least two parts per row");
+    static_assert(W == 16 && 2 * CM / 16 <= NT / 64 && kGenMaxD / 16 <= NT / 64, "one tile per wave and phase");
     __shared__ __attribute__((aligned(16))) float sKg[CM * PD];
     __shared__ __attribute__((aligned(16))) float sQg[CM * PD];
     __shared__ __attribute__((aligned(16))) float sKhT[kGenMaxD * PC];
     __shared__ __attribute__((aligned(16))) float sTB[CM * PC];
     __shared__ __attribute__((aligned(16))) float sM[CM * PC];
-    __shared__ __attribute__((aligned(16))) float sS[kGenMaxD * W + W * kMaxParts];
-    __shared__ __attribute__((aligned(16))) float sY[CM * W];
-    __shared__ __attribute__((aligned(16))) float sU[CM * W];
+    __shared__ __attribute__((aligned(16))) float sSt[W * PD];
+    __shared__ __attribute__((aligned(16))) float sYt[W * PC];
+    __shared__ __attribute__((aligned(16))) float sUt[W * PC];
+    __shared__ unsigned sTouch[NT];   // L2 warm-up loads land here, never read
     const int C = a.C, DK = a.DK, DV = a.DV, tid = threadIdx.x;
     const int slabs = DV / W;
     int32_t n;
     int h, col0;
     gen_slab(a, slabs, n, h, col0);
-    const int cq = tid % 4, tr = tid / 4;
-    const int ks = TS / C, kc = DK / ks;                // channel parts per row, channels per part
-    const int sh = 31 - __builtin_clz(kc);              // kc is a power of two
-    const int row = tr / ks, part = tr % ks;
-    const bool lead = part == 0;
-    auto sidx = [&](int c) { return c * W + W * (c >> sh); };   // state row c in sS
+    const int wave = tid / 64, lane = tid % 64, li = lane % 16, g = lane / 16;
+    const int nT = C / 16;
+    const bool xw = wave < nT, pw = wave >= nT && wave < 2 * nT, sw = wave < DK / 16;
+    const int T = xw ? wave : wave - nT;       // token tile of an X / P wave
     int64_t s_start, s_len;
     if (a.cu) {
         int64_t b0 = a.cu[n], b1 = a.cu[n + 1];
@@ -656,15 +657,14 @@ __global__ __launch_bounds__(NT) void kg_recur_res(GenArgs a) {
     const int64_t sbase = ((int64_t)n * a.H + h) * DK * DV;
     for (int x = tid; x < DK * W; x += NT) {
         const int c = x / W, jj = x % W;
-        sS[sidx(c) + jj] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
+        sSt[jj * PD + c] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
     }
     const int64_t vrs = (int64_t)a.H * DV;
     // the next chunk's loads, in registers between fetch and put
     typedef float v4 __attribute__((ext_vector_type(4)));
-    v4 nKg[kRowV], nQg[kRowV], nKh[kRowV], nTB[kTriV], nM[kTriV];
+    v4 nKg[kRowV], nQg[kRowV], nKh[kRowV], nTB[kTriV], nM[kTriV], ng;
     E nv[4];          // raw: converting at the load would make the compiler wait for it there
-    float ng;
-    bool nvok = false;
+    int nlen = 0;
     auto fetch = [&](int j) __attribute__((always_inline)) {
         const int64_t slot = (int64_t)h * a.max_chunks + c0 + j;
         const int64_t tok0 = s_start + (int64_t)j * C;
@@ -675,30 +675,30 @@ __global__ __launch_bounds__(NT) void kg_recur_res(GenArgs a) {
         const v4* kh = reinterpret_cast<const v4*>(a.Kh + slot * C * DK);
         const v4* tb = reinterpret_cast<const v4*>(a.TB + slot * C * C);
         const v4* mm = reinterpret_cast<const v4*>(a.M + slot * C * C);
+        // unconditional loads (past the operand's end, its last vector again):
+        // loads under a condition get moved to their uses
 #pragma unroll
         for (int u = 0; u < kRowV; ++u) {
-            const int x = tid + NT * u;
-            if (x < nr) {
-                nKg[u] = kg[x];
-                nQg[u] = qg[x];
-                nKh[u] = kh[x];
-            }
+            const int x = tid + NT * u < nr ? tid + NT * u : nr - 1;
+            nKg[u] = kg[x];
+            nQg[u] = qg[x];
+            nKh[u] = kh[x];
         }
 #pragma unroll
         for (int u = 0; u < kTriV; ++u) {
-            const int x = tid + NT * u;
-            if (x < nt) {
-                nTB[u] = tb[x];
-                nM[u] = mm[x];
-            }
+            const int x = tid + NT * u < nt ? tid + NT * u : nt - 1;
+            nTB[u] = tb[x];
+            nM[u] = mm[x];
         }
-        // value rows and e^{b_L}: loaded from a valid address on every lane
-        // and masked when used
-        nvok = lead && row < len;
-        const int64_t vo = (tok0 + (nvok ? row : 0)) * vrs + (int64_t)h * DV + col0 + 4 * cq;
+        // an X wave's value rows 16 T + 4 g + r, column li (row 0 of the
+        // chunk stands in for rows past its end: loaded, masked when used)
+        nlen = len;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) nv[e] = static_cast<const E*>(a.v)[vo + e];
-        ng = a.gam[slot * DK + (tr < DK ? tr : 0)];
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * T + 4 * g + r;
+            nv[r] = static_cast<const E*>(a.v)[(tok0 + (t < len ? t : 0)) * vrs + (int64_t)h * DV + col0 + li];
+        }
+        ng = *reinterpret_cast<const v4*>(a.gam + slot * DK + (sw ? 16 * wave + 4 * g : 0));
     };
     auto put = [&]() __attribute__((always_inline)) {
         const int kv = DK / 4, nr = C * kv, tv = C / 4, nt = C * tv;
@@ -728,51 +728,60 @@ __global__ __launch_bounds__(NT) void kg_recur_res(GenArgs a) {
         // uses above are under the same conditions).
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     };
-    // acc += row t of `op` (pitch P, entries past the row's end zero) times
-    // the 4 columns of `rhs` ([k][16]), over k < kend (a multiple of 4)
-    auto row_times = [&](const float* op, int P, int t, const float* rhs, int kend, float4 acc) __attribute__((always_inline)) {
-        for (int k = 0; k < kend; k += 4) {
-            const float4 o4 = *reinterpret_cast<const float4*>(&op[t * P + k]);
-            acc = fma4(o4.x, *reinterpret_cast<const float4*>(&rhs[(k + 0) * W + 4 * cq]), acc);
-            acc = fma4(o4.y, *reinterpret_cast<const float4*>(&rhs[(k + 1) * W + 4 * cq]), acc);
-            acc = fma4(o4.z, *reinterpret_cast<const float4*>(&rhs[(k + 2) * W + 4 * cq]), acc);
-            acc = fma4(o4.w, *reinterpret_cast<const float4*>(&rhs[(k + 3) * W + 4 * cq]), acc);
+    // L2 warm-up: one dword of every 128-byte line of the operands of the
+    // chunk kAhead steps ahead, the slabs of a head taking every slabs-th
+    // line each, so that the fetch of that chunk finds its lines in the L2
+    // the slabs share instead of each waiting on HBM.  Direct loads into a
+    // never-read LDS array: no register waits on them; they are older than
+    // the next fetch's loads, so the wait at the end of the next put (loads
+    // complete in order) covers them.
+    constexpr int kAhead = 3;
+    const int lines_k = C * DK / 32, lines_t = C * C / 32;   // 128-byte lines per operand
+    const int n_lines = 3 * lines_k + 2 * lines_t;
+    const int my_line = col0 / W + slabs * tid;   // this thread's line, if below n_lines
+    auto touch = [&](int j) __attribute__((always_inline)) {
+        if (my_line >= n_lines) return;
+        const int64_t slot = (int64_t)h * a.max_chunks + c0 + j;
+        int l = my_line;
+        const float* base;
+        if (l < lines_k) base = a.Kg + slot * C * DK;
+        else if ((l -= lines_k) < lines_k) base = a.Qg + slot * C * DK;
+        else if ((l -= lines_k) < lines_k) base = a.Kh + slot * C * DK;
+        else if ((l -= lines_k) < lines_t) base = a.TB + slot * C * C;
+        else {
+            l -= lines_t;
+            base = a.M + slot * C * C;
+        }
+        __builtin_amdgcn_global_load_lds(base + 32 * l, (__attribute__((address_space(3))) void*)(sTouch + 64 * wave), 4,
+                                         0, 0);
+    };
+    // acc += A B over kend (a multiple of 16) contraction indices, with A's
+    // row li of this tile at `arow` and B's column li at `bcol`, both
+    // contiguous in the contraction index
+    auto tile_mma = [&](const float* arow, const float* bcol, int kend, f32x4 acc) __attribute__((always_inline)) {
+        for (int k0 = 0; k0 < kend; k0 += 16) {
+            const v4 av = *reinterpret_cast<const v4*>(arow + k0 + 4 * g);
+            const v4 bv = *reinterpret_cast<const v4*>(bcol + k0 + 4 * g);
+            acc = mma_f32(av.x, bv.x, acc);
+            acc = mma_f32(av.y, bv.y, acc);
+            acc = mma_f32(av.z, bv.z, acc);
+            acc = mma_f32(av.w, bv.w, acc);
         }
         return acc;
     };
-    // x += row t of K.e^b and p += row t of Q.e^b (pitch PD) times the
-    // same 4 columns of `rhs`, over kend channels: one read of rhs for both
-    auto two_rows_times = [&](const float* opx, const float* opp, int t, const float* rhs, int kend, float4& x,
-                              float4& p) __attribute__((always_inline)) {
-        for (int k = 0; k < kend; k += 4) {
-            const float4 ox = *reinterpret_cast<const float4*>(&opx[t * PD + k]);
-            const float4 op = *reinterpret_cast<const float4*>(&opp[t * PD + k]);
-            const float4 r0 = *reinterpret_cast<const float4*>(&rhs[(k + 0) * W + 4 * cq]);
-            const float4 r1 = *reinterpret_cast<const float4*>(&rhs[(k + 1) * W + 4 * cq]);
-            const float4 r2 = *reinterpret_cast<const float4*>(&rhs[(k + 2) * W + 4 * cq]);
-            const float4 r3 = *reinterpret_cast<const float4*>(&rhs[(k + 3) * W + 4 * cq]);
-            x = fma4(ox.x, r0, x);
-            p = fma4(op.x, r0, p);
-            x = fma4(ox.y, r1, x);
-            p = fma4(op.y, r1, p);
-            x = fma4(ox.z, r2, x);
-            p = fma4(op.z, r2, p);
-            x = fma4(ox.w, r3, x);
-            p = fma4(op.w, r3, p);
-        }
+    float vr[4] = {0.f, 0.f, 0.f, 0.f};
+    v4 gm = {0.f, 0.f, 0.f, 0.f};
+    auto take = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vr[r] = 16 * T + 4 * g + r < nlen ? to_f(nv[r]) : 0.f;
+        gm = ng;
     };
-    float vr[4] = {0.f, 0.f, 0.f, 0.f}, gm = 0.f;
     if (nch > 0) {
+        for (int jt = 1; jt < kAhead && jt < nch; ++jt) touch(jt);
         fetch(0);
         put();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vr[e] = nvok ? to_f(nv[e]) : 0.f;
-        gm = ng;
+        take();
     }
-    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    // this thread's part of the key channels, and its rows of the state slab
-    const int ch0 = part * kc;
-    const float* sSp = sS + sidx(ch0);
     for (int j = 0; j < nch; ++j) {
         const int64_t tok0 = s_start + (int64_t)j * C;
         const int len = (int)(s_len - (int64_t)j * C < C ? s_len - (int64_t)j * C : C);
@@ -782,55 +791,48 @@ __global__ __launch_bounds__(NT) void kg_recur_res(GenArgs a) {
         // sees every load consumed before the next fetch reuses its
         // registers, and does not wait on the fresh loads at their issue)
         fetch(j + 1 < nch ? j + 1 : j);
-        // X = (K.e^b) S, P = (Q.e^b) S over this part's channels, then summed
-        // over the parts; Y = V - X
-        float4 x = z4, accP = z4;
-        two_rows_times(sKg + ch0, sQg + ch0, row, sSp, kc, x, accP);
-        for (int o = 4; o < 4 * ks; o <<= 1) {
-            x.x += __shfl_xor(x.x, o);
-            x.y += __shfl_xor(x.y, o);
-            x.z += __shfl_xor(x.z, o);
-            x.w += __shfl_xor(x.w, o);
-            accP.x += __shfl_xor(accP.x, o);
-            accP.y += __shfl_xor(accP.y, o);
-            accP.z += __shfl_xor(accP.z, o);
-            accP.w += __shfl_xor(accP.w, o);
-        }
-        if (lead) {
-            const float4 y = row < len ? make_float4(vr[0] - x.x, vr[1] - x.y, vr[2] - x.z, vr[3] - x.w) : z4;
-            *reinterpret_cast<float4*>(&sY[row * W + 4 * cq]) = y;
+        // X = (K.e^b) S (X waves; Y = V - X to LDS as Y^T), P = (Q.e^b) S (P waves)
+        f32x4 acc = zero4();
+        if (xw || pw) acc = tile_mma((xw ? sKg : sQg) + (16 * T + li) * PD, sSt + li * PD, DK, acc);
+        if (xw) {
+            v4 y;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = 16 * T + 4 * g + r < len ? vr[r] - acc[r] : 0.f;
+            *reinterpret_cast<v4*>(&sYt[li * PC + 16 * T + 4 * g]) = y;
         }
         __syncthreads();
-        // U~ = T diag(beta) Y (lower triangular: row t needs k <= t)
-        if (lead) *reinterpret_cast<float4*>(&sU[row * W + 4 * cq]) = row_times(sTB, PC, row, sY, (row + 4) & ~3, z4);
-        __syncthreads();
-        // O = P + M U~
-        if (lead && row < len) {
-            const float4 ov = row_times(sM, PC, row, sU, (row + 4) & ~3, accP);
-            E* op = static_cast<E*>(a.o) + (tok0 + row) * vrs + (int64_t)h * DV + col0 + 4 * cq;
-            op[0] = from_f<E>(ov.x);
-            op[1] = from_f<E>(ov.y);
-            op[2] = from_f<E>(ov.z);
-            op[3] = from_f<E>(ov.w);
+        // U~ = T diag(beta) Y for tile T (lower triangular: k < 16 (T + 1))
+        if (xw) {
+            const f32x4 u = tile_mma(sTB + (16 * T + li) * PC, sYt + li * PC, 16 * (T + 1), zero4());
+            *reinterpret_cast<v4*>(&sUt[li * PC + 16 * T + 4 * g]) = u;
         }
-        // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~: channel tr
-        float4 ns = z4;
-        if (tr < DK) {
-            const float4 s0 = *reinterpret_cast<const float4*>(&sS[sidx(tr) + 4 * cq]);
-            ns = row_times(sKhT, PC, tr, sU, C, make_float4(gm * s0.x, gm * s0.y, gm * s0.z, gm * s0.w));
+        __syncthreads();
+        // O = P + M U~ for tile T
+        if (pw) {
+            acc = tile_mma(sM + (16 * T + li) * PC, sUt + li * PC, 16 * (T + 1), acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * T + 4 * g + r;
+                if (t < len) static_cast<E*>(a.o)[(tok0 + t) * vrs + (int64_t)h * DV + col0 + li] = from_f<E>(acc[r]);
+            }
+        }
+        // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~ for channels 16 wave ..
+        f32x4 ns = zero4();
+        if (sw) {
+            const v4 s0 = *reinterpret_cast<const v4*>(&sSt[li * PD + 16 * wave + 4 * g]);
+            ns = tile_mma(sKhT + (16 * wave + li) * PC, sUt + li * PC, C, gm * s0);
         }
         __syncthreads();   // every read of chunk j's operands and of the old state is done
-        if (tr < DK) *reinterpret_cast<float4*>(&sS[sidx(tr) + 4 * cq]) = ns;
+        if (sw) *reinterpret_cast<v4*>(&sSt[li * PD + 16 * wave + 4 * g]) = ns;
         put();
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vr[e] = nvok ? to_f(nv[e]) : 0.f;
-        gm = ng;
+        take();
+        if (j + kAhead < nch) touch(j + kAhead);
     }
     __syncthreads();
     if (a.S_T)
         for (int x = tid; x < DK * W; x += NT) {
             const int c = x / W, jj = x % W;
-            a.S_T[sbase + (int64_t)c * DV + col0 + jj] = sS[sidx(c) + jj];
+            a.S_T[sbase + (int64_t)c * DV + col0 + jj] = sSt[jj * PD + c];
         }
 }
 
@@ -874,29 +876,31 @@ static hipError_t launch_gen(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         const dim3 ggrid(p.max_chunks, p.n_heads, p.chunk / kGenRows), sgrid(p.max_chunks, p.n_heads);
         switch (p.chunk) {
             case 16:
-                hipLaunchKernelGGL((kg_gram<E, 16>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_gram<E, 16, 256>), ggrid, dim3(256), 0, st, a);
                 hipLaunchKernelGGL((kg_solve<E, 16>), sgrid, dim3(256), 0, st, a);
                 break;
             case 32:
-                hipLaunchKernelGGL((kg_gram<E, 32>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_gram<E, 32, 256>), ggrid, dim3(256), 0, st, a);
                 hipLaunchKernelGGL((kg_solve<E, 32>), sgrid, dim3(256), 0, st, a);
                 break;
             case 64:
-                hipLaunchKernelGGL((kg_gram<E, 64>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_gram<E, 64, 256>), ggrid, dim3(256), 0, st, a);
                 hipLaunchKernelGGL((kg_solve<E, 64>), sgrid, dim3(256), 0, st, a);
                 break;
             default:
-                hipLaunchKernelGGL((kg_gram<E, 128>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_gram<E, 128, 512>), ggrid, dim3(512), 0, st, a);
                 hipLaunchKernelGGL((kg_solve<E, 128>), sgrid, dim3(256), 0, st, a);
                 break;
         }
     }
     mark(2);
     const dim3 rgrid(p.n_seqs * p.n_heads * (p.d_v / kGenCols));
-    if (p.chunk <= 32)
-        hipLaunchKernelGGL((kg_recur_res<E, 32, kGenRecurThreads>), rgrid, dim3(kGenRecurThreads), 0, st, a);
+    if (p.chunk <= 16)
+        hipLaunchKernelGGL((kg_recur_res<E, 16>), rgrid, dim3(512), 0, st, a);
+    else if (p.chunk <= 32)
+        hipLaunchKernelGGL((kg_recur_res<E, 32>), rgrid, dim3(512), 0, st, a);
     else if (p.chunk <= 64)
-        hipLaunchKernelGGL((kg_recur_res<E, 64, kGenRecurThreads>), rgrid, dim3(kGenRecurThreads), 0, st, a);
+        hipLaunchKernelGGL((kg_recur_res<E, 64>), rgrid, dim3(512), 0, st, a);
     else
         hipLaunchKernelGGL((kg_recur<E, kGenRecurThreads>), rgrid, dim3(kGenRecurThreads), 0, st, a);
     mark(3);
