@@ -2,8 +2,9 @@
 //
 // The tuned kernels (kda_kernels.hip) cover chunk 64 with d_k = d_v: bf16 at
 // 64 and 128, fp32 at 64.  These kernels take any chunk C in {16, 32, 64,
-// 128}, any d_k, d_v in {64, 128} and either input type, with plain fp32
-// arithmetic throughout (no MFMA, operands staged through LDS).  They
+// 128}, any d_k, d_v in {64, 128} and either input type, with fp32
+// arithmetic throughout (fp32 operands in the workspace; fp32 matrix cores
+// in the recurrence for chunks up to 64, fp32 FMA elsewhere).  They
 // compute the same chunked form (ogis-ri NLP primer on Kimi K3, §3.1
 // "KDA（Kimi Delta Attention）": per chunk, the state carried in plus a
 // causal intra-chunk term; §3.1 "chunk 内の減衰と、その数値範囲": per-channel
@@ -25,8 +26,11 @@
 //                               rows of Q.e^b, K.e^b, K.e^{b_L-b}
 //   kg_solve (chunks, H)        T diag(beta) in LDS, by 16 x 16 blocks
 //   kg_recur (N*H*d_v/16)       sequential over one sequence's chunks for one
-//                               head and 16 value columns of the state
-//                               (kg_recur_res for chunks of at most 64 tokens)
+//                               head and 16 value columns of the state, at
+//                               chunk 128 (kg_recur_res for chunks of at
+//                               most 64 tokens)
+// kg_gram and kg_solve are instantiated per chunk size, so that their LDS
+// and thread layout fit it.
 #include "kda_device.h"
 #include "kda_internal.h"
 
