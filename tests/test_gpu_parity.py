@@ -276,16 +276,16 @@ def _run_torch_inputs(torch, inp, chunk=64):
 def test_config2_headline_full(torch_dev):
     """B=1, H=32, T=65536, d=128, S0 ~ 0.02 N(0,1), launched as the
     benchmark launches it: all 32 heads of o and S_T against the oracle; the
-    same at chunk 128 (the generic kernels) against the same oracle run."""
+    same at chunks 16, 32 and 128 (the generic kernels: 4096, 2048 and 512
+    chunk steps) against the same oracle run."""
     torch, dev = torch_dev
     spec = ki.headline_configs()[2]
     _say("config 2 generate (torch, on device)")
     inp = ki.generate_torch(spec, dev)
     o, ST = _run_torch_inputs(torch, inp)
-    o128, ST128 = _run_torch_inputs(torch, inp, chunk=128)
-    _full_check(torch, inp, o, ST, "config 2", [[0]], [list(range(0, 16)), list(range(16, 32))],
-                extra=[("config 2 chunk 128", o128, ST128)])
-    del inp, o, ST, o128, ST128
+    extra = [("config 2 chunk %d" % c,) + _run_torch_inputs(torch, inp, chunk=c) for c in (16, 32, 128)]
+    _full_check(torch, inp, o, ST, "config 2", [[0]], [list(range(0, 16)), list(range(16, 32))], extra=extra)
+    del inp, o, ST, extra
     torch.cuda.empty_cache()
 
 
@@ -293,19 +293,18 @@ def test_config2_headline_full(torch_dev):
 def test_config3_varlen_full(torch_dev):
     """64 packed sequences (L ~ U[512, 16384], 550,809 tokens), H=32, d=128,
     25 % of channels at g = -5: every (sequence, head) slice of o and S_T,
-    at chunk 64 and at chunk 128.  Sequences 60-63 sit at element offsets
-    past 2^31 (from token 524,288)."""
+    at chunk 64 and at chunks 16, 32 and 128.  Sequences 60-63 sit at
+    element offsets past 2^31 (from token 524,288)."""
     torch, dev = torch_dev
     spec = ki.headline_configs()[3]
     _say("config 3 generate (torch, on device), T_total=%d" % spec.total_tokens)
     inp = ki.generate_torch(spec, dev)
     o, ST = _run_torch_inputs(torch, inp)
-    o128, ST128 = _run_torch_inputs(torch, inp, chunk=128)
+    extra = [("config 3 chunk %d" % c,) + _run_torch_inputs(torch, inp, chunk=c) for c in (16, 32, 128)]
     groups = [list(range(i, min(i + 8, spec.n_seqs))) for i in range(0, spec.n_seqs, 8)]
-    _, big = _full_check(torch, inp, o, ST, "config 3", groups, [list(range(32))],
-                         extra=[("config 3 chunk 128", o128, ST128)])
+    _, big = _full_check(torch, inp, o, ST, "config 3", groups, [list(range(32))], extra=extra)
     assert big >= 4 * 32, "the slices past 2^31 element offsets must be among those compared"
-    del inp, o, ST, o128, ST128
+    del inp, o, ST, extra
     torch.cuda.empty_cache()
 
 
@@ -313,17 +312,17 @@ def test_config3_varlen_full(torch_dev):
 def test_config4_1m_full(torch_dev):
     """B=1, H=16, T=1,048,576, d=128, S0 ~ 0.02 N(0,1): all 16 heads, o on
     the seeded 8192-token window and S_T (the oracle runs all 1M tokens), at
-    chunk 64 and at chunk 128."""
+    chunk 64 and at chunks 32 and 128 (32,768 and 8192 chunk steps)."""
     torch, dev = torch_dev
     spec = ki.headline_configs()[4]
     _say("config 4 generate (torch, on device)")
     inp = ki.generate_torch(spec, dev)
     o, ST = _run_torch_inputs(torch, inp)
-    o128, ST128 = _run_torch_inputs(torch, inp, chunk=128)
+    extra = [("config 4 chunk %d" % c,) + _run_torch_inputs(torch, inp, chunk=c) for c in (32, 128)]
     _say("config 4 window %s" % (inp.window,))
     _full_check(torch, inp, o, ST, "config 4", [[0]], [list(range(h, h + 4)) for h in range(0, 16, 4)],
-                extra=[("config 4 chunk 128", o128, ST128)])
-    del inp, o, ST, o128, ST128
+                extra=extra)
+    del inp, o, ST, extra
     torch.cuda.empty_cache()
 
 
