@@ -39,7 +39,7 @@ namespace kda {
 constexpr int kGenMaxC = 128, kGenMaxD = 128;
 constexpr int kGenRows = 16;    // A and M rows per kg_gram workgroup
 constexpr int kGenCols = 16;    // value columns per kg_recur workgroup
-constexpr int kGenRecurThreads = 512;   // kg_recur threads
+constexpr int kGenRecurThreads = 512;   // kg_recur threads: one wave per 16-token tile of a 128-token chunk
 
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt unconstrained
 // (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -354,27 +354,32 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
 
 // ------------------------------------------------------------------ kg_recur
 // One workgroup per (sequence, head, 16 value columns), sequential over the
-// sequence's chunks.  A thread owns 4 columns (4 cq .. 4 cq + 3) of the rows
-// t = tr + (NT / 4) m of each C x 16 product, or of those channels of the
-// state update, and reads 16-byte vectors from LDS.
-template <typename E, int NT>
-__global__ __launch_bounds__(NT) void kg_recur(GenArgs a) {
-    constexpr int TS = NT / 4;                 // thread rows: 4 threads per token row
-    constexpr int RP = kGenMaxC / TS;          // token rows (or channels) per thread
-    constexpr int PO = kGenMaxD + 4;   // pitch of the staged operands (kGenMaxC == kGenMaxD)
+// sequence's 128-token chunks, on fp32 matrix cores: every product is a set
+// of 16 x 16 output tiles from 16x16x4 fp32 MFMA steps, wave w taking token
+// tile w (X, P, Y, U~, O) and channel tile w (the state update).  A chunk's
+// operands do not fit in LDS together, so they pass through two buffers in
+// three rounds (K.e^b and Q.e^b; T diag(beta) and M; (K.e^{b_L-b})^T), each
+// fetched into registers one phase before it is written to LDS.  As in
+// kg_recur_res, the B operands (S, Y, U~) are kept column-major, so that a
+// lane's fragments for four MFMA steps are one 16-byte LDS read each.
+template <typename E>
+__global__ __launch_bounds__(kGenRecurThreads) void kg_recur(GenArgs a) {
+    constexpr int NT = kGenRecurThreads;
+    constexpr int PO = kGenMaxD + 4;   // pitch of the staged operands and of S^T, Y^T, U~^T (kGenMaxC == kGenMaxD)
     constexpr int W = kGenCols;
-    static_assert(kGenMaxC == kGenMaxD, "one pitch for [token][channel], [token][token] and [channel][token]");
+    static_assert(kGenMaxC == kGenMaxD && NT == 64 * kGenMaxC / 16, "one token tile and one channel tile per wave");
     __shared__ __attribute__((aligned(16))) float bufA[kGenMaxC * PO];   // K.e^b, then T diag(beta), then (K.e^{b_L-b})^T
     __shared__ __attribute__((aligned(16))) float bufB[kGenMaxC * PO];   // Q.e^b, then M
-    __shared__ __attribute__((aligned(16))) float sS[kGenMaxD * W];      // the state's 16 columns, [channel][column]
-    __shared__ __attribute__((aligned(16))) float sY[kGenMaxC * W];
-    __shared__ __attribute__((aligned(16))) float sU[kGenMaxC * W];
+    __shared__ __attribute__((aligned(16))) float sSt[W * PO];           // S^T   [column][channel]
+    __shared__ __attribute__((aligned(16))) float sYt[W * PO];           // Y^T   [column][token]
+    __shared__ __attribute__((aligned(16))) float sUt[W * PO];           // U~^T  [column][token]
     const int C = a.C, DK = a.DK, DV = a.DV, tid = threadIdx.x;
     const int slabs = DV / W;
     int32_t n;
     int h, col0;
     gen_slab(a, slabs, n, h, col0);
-    const int cq = tid % 4, tr = tid / 4;
+    const int wave = tid / 64, lane = tid % 64, li = lane % 16, g = lane / 16;
+    const bool tw = 16 * wave < C, sw = 16 * wave < DK;   // this wave's token tile / channel tile exists
     int64_t s_start, s_len;
     if (a.cu) {
         int64_t b0 = a.cu[n], b1 = a.cu[n + 1];
@@ -396,27 +401,26 @@ __global__ __launch_bounds__(NT) void kg_recur(GenArgs a) {
     const int64_t sbase = ((int64_t)n * a.H + h) * DK * DV;
     for (int x = tid; x < DK * W; x += NT) {
         const int c = x / W, jj = x % W;
-        sS[x] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
+        sSt[jj * PO + c] = a.S0 ? a.S0[sbase + (int64_t)c * DV + col0 + jj] : 0.f;
     }
     const int64_t vrs = (int64_t)a.H * DV;
     // An R x K fp32 matrix (row-major, K a multiple of 4) is staged in two
     // halves: `fetch` issues its 16-byte loads into registers, `put` writes
     // them to dst as rows (transposed = false) or as columns (dst[k][r]).
-    // Each operand is fetched one phase before it is put, so that the loads'
-    // latency overlaps the phase in between.
     constexpr int kMaxV = kGenMaxC * kGenMaxD / 4 / NT;
+    typedef float v4 __attribute__((ext_vector_type(4)));
     struct Fetched {
-        float4 f[kMaxV];
+        v4 f[kMaxV];
     };
-    auto fetch = [&](Fetched& pr, const float* src, int R, int K) {
+    auto fetch = [&](Fetched& pr, const float* src, int R, int K) __attribute__((always_inline)) {
         const int n4 = R * (K / 4);
 #pragma unroll
         for (int u = 0; u < kMaxV; ++u) {
             const int x = tid + NT * u;
-            pr.f[u] = x < n4 ? reinterpret_cast<const float4*>(src)[x] : make_float4(0.f, 0.f, 0.f, 0.f);
+            pr.f[u] = reinterpret_cast<const v4*>(src)[x < n4 ? x : n4 - 1];
         }
     };
-    auto put = [&](float* dst, const Fetched& pr, int R, int K, bool transposed) {
+    auto put = [&](float* dst, const Fetched& pr, int R, int K, bool transposed) __attribute__((always_inline)) {
         const int kv = K / 4, n4 = R * kv;
 #pragma unroll
         for (int u = 0; u < kMaxV; ++u) {
@@ -429,58 +433,22 @@ __global__ __launch_bounds__(NT) void kg_recur(GenArgs a) {
                 dst[(c4 + 2) * PO + r] = pr.f[u].z;
                 dst[(c4 + 3) * PO + r] = pr.f[u].w;
             } else {
-                *reinterpret_cast<float4*>(&dst[r * PO + c4]) = pr.f[u];
+                *reinterpret_cast<v4*>(&dst[r * PO + c4]) = pr.f[u];
             }
         }
     };
-    // acc[m] += rows t_m of `op` (16-byte vectors along the contraction, up
-    // to `kend` rounded up to 4; entries past a row's end must be zero in
-    // `op`) times the 4 columns of `rhs` ([k][16] in LDS)
-    auto rows_times = [&](const float* op, const float* rhs, int kend0, bool tri, float4 acc[RP]) {
-#pragma unroll
-        for (int m = 0; m < RP; ++m) {
-            const int t = tr + TS * m;
-            if (t >= C) continue;
-            const int kend = tri ? ((t + 4) & ~3) : kend0;
-            float4 s = acc[m];
-            for (int k = 0; k < kend; k += 4) {
-                const float4 o4 = *reinterpret_cast<const float4*>(&op[t * PO + k]);
-                s = fma4(o4.x, *reinterpret_cast<const float4*>(&rhs[(k + 0) * W + 4 * cq]), s);
-                s = fma4(o4.y, *reinterpret_cast<const float4*>(&rhs[(k + 1) * W + 4 * cq]), s);
-                s = fma4(o4.z, *reinterpret_cast<const float4*>(&rhs[(k + 2) * W + 4 * cq]), s);
-                s = fma4(o4.w, *reinterpret_cast<const float4*>(&rhs[(k + 3) * W + 4 * cq]), s);
-            }
-            acc[m] = s;
+    // acc += A B over kend (a multiple of 16) contraction indices, with A's
+    // row li of this tile at `arow` and B's column li at `bcol`
+    auto tile_mma = [&](const float* arow, const float* bcol, int kend, f32x4 acc) __attribute__((always_inline)) {
+        for (int k0 = 0; k0 < kend; k0 += 16) {
+            const v4 av = *reinterpret_cast<const v4*>(arow + k0 + 4 * g);
+            const v4 bv = *reinterpret_cast<const v4*>(bcol + k0 + 4 * g);
+            acc = mma_f32(av.x, bv.x, acc);
+            acc = mma_f32(av.y, bv.y, acc);
+            acc = mma_f32(av.z, bv.z, acc);
+            acc = mma_f32(av.w, bv.w, acc);
         }
-    };
-    // the same over the full contraction for two operands sharing rhs (one
-    // read of rhs for both)
-    auto rows_times2 = [&](const float* opa, const float* opb, const float* rhs, int kend, float4 acca[RP],
-                           float4 accb[RP]) {
-#pragma unroll
-        for (int m = 0; m < RP; ++m) {
-            const int t = tr + TS * m;
-            if (t >= C) continue;
-            float4 sa = acca[m], sb = accb[m];
-            for (int k = 0; k < kend; k += 4) {
-                const float4 a4 = *reinterpret_cast<const float4*>(&opa[t * PO + k]);
-                const float4 b4 = *reinterpret_cast<const float4*>(&opb[t * PO + k]);
-                const float4 r0 = *reinterpret_cast<const float4*>(&rhs[(k + 0) * W + 4 * cq]);
-                const float4 r1 = *reinterpret_cast<const float4*>(&rhs[(k + 1) * W + 4 * cq]);
-                const float4 r2 = *reinterpret_cast<const float4*>(&rhs[(k + 2) * W + 4 * cq]);
-                const float4 r3 = *reinterpret_cast<const float4*>(&rhs[(k + 3) * W + 4 * cq]);
-                sa = fma4(a4.x, r0, sa);
-                sb = fma4(b4.x, r0, sb);
-                sa = fma4(a4.y, r1, sa);
-                sb = fma4(b4.y, r1, sb);
-                sa = fma4(a4.z, r2, sa);
-                sb = fma4(b4.z, r2, sb);
-                sa = fma4(a4.w, r3, sa);
-                sb = fma4(b4.w, r3, sb);
-            }
-            acca[m] = sa;
-            accb[m] = sb;
-        }
+        return acc;
     };
     Fetched fa, fb;
     if (nch > 0) {
@@ -490,6 +458,7 @@ __global__ __launch_bounds__(NT) void kg_recur(GenArgs a) {
         put(bufA, fa, C, DK, false);
         put(bufB, fb, C, DK, false);
     }
+    const int T = wave;
     for (int j = 0; j < nch; ++j) {
         const int64_t slot = (int64_t)h * a.max_chunks + c0 + j;
         const int64_t tok0 = s_start + (int64_t)j * C;
@@ -498,50 +467,46 @@ __global__ __launch_bounds__(NT) void kg_recur(GenArgs a) {
         // this step's T diag(beta), M, value rows and e^{b_L}, ahead of use
         fetch(fa, a.TB + slot * C * C, C, C);
         fetch(fb, a.M + slot * C * C, C, C);
-        float vr[RP][4], gm[RP];
+        float vr[4];
 #pragma unroll
-        for (int m = 0; m < RP; ++m) {
-            const int t = tr + TS * m, c = tr + TS * m;
-            if (t < len) {
-                const int64_t vo = (tok0 + t) * vrs + (int64_t)h * DV + col0 + 4 * cq;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vr[m][e] = ldf<E>(a.v, vo + e);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) vr[m][e] = 0.f;
-            }
-            gm[m] = c < DK ? a.gam[slot * DK + c] : 0.f;
+        for (int r = 0; r < 4; ++r) {
+            const int t = 16 * T + 4 * g + r;
+            vr[r] = ldf<E>(a.v, (tok0 + (t < len ? t : 0)) * vrs + (int64_t)h * DV + col0 + li);
         }
-        // X = (K.e^b) S, P = (Q.e^b) S; Y = V - X
-        float4 accX[RP], accP[RP];
+        const v4 gm = *reinterpret_cast<const v4*>(a.gam + slot * DK + (sw ? 16 * wave + 4 * g : 0));
+        // X = (K.e^b) S, P = (Q.e^b) S for token tile T; Y = V - X to LDS
+        f32x4 accX = zero4(), accP = zero4();
+        if (tw) {
+            const float* ax = bufA + (16 * T + li) * PO;
+            const float* ap = bufB + (16 * T + li) * PO;
+            const float* bs = sSt + li * PO;
+            for (int k0 = 0; k0 < DK; k0 += 16) {
+                const v4 xv = *reinterpret_cast<const v4*>(ax + k0 + 4 * g);
+                const v4 pv = *reinterpret_cast<const v4*>(ap + k0 + 4 * g);
+                const v4 sv = *reinterpret_cast<const v4*>(bs + k0 + 4 * g);
+                accX = mma_f32(xv.x, sv.x, accX);
+                accP = mma_f32(pv.x, sv.x, accP);
+                accX = mma_f32(xv.y, sv.y, accX);
+                accP = mma_f32(pv.y, sv.y, accP);
+                accX = mma_f32(xv.z, sv.z, accX);
+                accP = mma_f32(pv.z, sv.z, accP);
+                accX = mma_f32(xv.w, sv.w, accX);
+                accP = mma_f32(pv.w, sv.w, accP);
+            }
+            v4 y;
 #pragma unroll
-        for (int m = 0; m < RP; ++m) accX[m] = accP[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-        rows_times2(bufA, bufB, sS, DK, accX, accP);
-#pragma unroll
-        for (int m = 0; m < RP; ++m) {
-            const int t = tr + TS * m;
-            if (t >= C) continue;
-            const float4 y = t < len ? make_float4(vr[m][0] - accX[m].x, vr[m][1] - accX[m].y,
-                                                   vr[m][2] - accX[m].z, vr[m][3] - accX[m].w)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-            *reinterpret_cast<float4*>(&sY[t * W + 4 * cq]) = y;
+            for (int r = 0; r < 4; ++r) y[r] = 16 * T + 4 * g + r < len ? vr[r] - accX[r] : 0.f;
+            *reinterpret_cast<v4*>(&sYt[li * PO + 16 * T + 4 * g]) = y;
         }
         __syncthreads();   // K.e^b and Q.e^b are dead
         put(bufA, fa, C, C, false);
         put(bufB, fb, C, C, false);
         __syncthreads();
         fetch(fa, a.Kh + slot * C * DK, C, DK);
-        // U~ = T diag(beta) Y (lower triangular)
-        {
-            float4 accU[RP];
-#pragma unroll
-            for (int m = 0; m < RP; ++m) accU[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-            rows_times(bufA, sY, 0, true, accU);
-#pragma unroll
-            for (int m = 0; m < RP; ++m) {
-                const int t = tr + TS * m;
-                if (t < C) *reinterpret_cast<float4*>(&sU[t * W + 4 * cq]) = accU[m];
-            }
+        // U~ = T diag(beta) Y for tile T (lower triangular: k < 16 (T + 1))
+        if (tw) {
+            const f32x4 u = tile_mma(bufA + (16 * T + li) * PO, sYt + li * PO, 16 * (T + 1), zero4());
+            *reinterpret_cast<v4*>(&sUt[li * PO + 16 * T + 4 * g]) = u;
         }
         __syncthreads();   // U~ is in LDS; T diag(beta) is dead
         put(bufA, fa, C, DK, true);
@@ -549,42 +514,24 @@ __global__ __launch_bounds__(NT) void kg_recur(GenArgs a) {
             fetch(fa, a.Kg + (slot + 1) * C * DK, C, DK);
             fetch(fb, a.Qg + (slot + 1) * C * DK, C, DK);
         }
-        // O = P + M U~
-        rows_times(bufB, sU, 0, true, accP);
+        // O = P + M U~ for tile T
+        if (tw) {
+            accP = tile_mma(bufB + (16 * T + li) * PO, sUt + li * PO, 16 * (T + 1), accP);
 #pragma unroll
-        for (int m = 0; m < RP; ++m) {
-            const int t = tr + TS * m;
-            if (t >= len) continue;
-            E* op = static_cast<E*>(a.o) + (tok0 + t) * vrs + (int64_t)h * DV + col0 + 4 * cq;
-            op[0] = from_f<E>(accP[m].x);
-            op[1] = from_f<E>(accP[m].y);
-            op[2] = from_f<E>(accP[m].z);
-            op[3] = from_f<E>(accP[m].w);
+            for (int r = 0; r < 4; ++r) {
+                const int t = 16 * T + 4 * g + r;
+                if (t < len) static_cast<E*>(a.o)[(tok0 + t) * vrs + (int64_t)h * DV + col0 + li] = from_f<E>(accP[r]);
+            }
         }
         __syncthreads();   // (K.e^{b_L-b})^T is in LDS
-        // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~: channels c = tr, tr + 64
-        float4 ns[RP];
-#pragma unroll
-        for (int m = 0; m < RP; ++m) {
-            const int c = tr + TS * m;
-            if (c >= DK) continue;
-            const float4 s0 = *reinterpret_cast<const float4*>(&sS[c * W + 4 * cq]);
-            float4 acc = make_float4(gm[m] * s0.x, gm[m] * s0.y, gm[m] * s0.z, gm[m] * s0.w);
-            for (int t = 0; t < C; t += 4) {
-                const float4 k4 = *reinterpret_cast<const float4*>(&bufA[c * PO + t]);
-                acc = fma4(k4.x, *reinterpret_cast<const float4*>(&sU[(t + 0) * W + 4 * cq]), acc);
-                acc = fma4(k4.y, *reinterpret_cast<const float4*>(&sU[(t + 1) * W + 4 * cq]), acc);
-                acc = fma4(k4.z, *reinterpret_cast<const float4*>(&sU[(t + 2) * W + 4 * cq]), acc);
-                acc = fma4(k4.w, *reinterpret_cast<const float4*>(&sU[(t + 3) * W + 4 * cq]), acc);
-            }
-            ns[m] = acc;
+        // S <- Diag(e^{b_L}) S + (K.e^{b_L-b})^T U~ for channels 16 wave ..
+        f32x4 ns = zero4();
+        if (sw) {
+            const v4 s0 = *reinterpret_cast<const v4*>(&sSt[li * PO + 16 * wave + 4 * g]);
+            ns = tile_mma(bufA + (16 * wave + li) * PO, sUt + li * PO, C, gm * s0);
         }
         __syncthreads();   // every read of the old state, of M and of (K.e^{b_L-b})^T is done
-#pragma unroll
-        for (int m = 0; m < RP; ++m) {
-            const int c = tr + TS * m;
-            if (c < DK) *reinterpret_cast<float4*>(&sS[c * W + 4 * cq]) = ns[m];
-        }
+        if (sw) *reinterpret_cast<v4*>(&sSt[li * PO + 16 * wave + 4 * g]) = ns;
         if (j + 1 < nch) {
             put(bufA, fa, C, DK, false);
             put(bufB, fb, C, DK, false);
@@ -594,7 +541,7 @@ __global__ __launch_bounds__(NT) void kg_recur(GenArgs a) {
     if (a.S_T)
         for (int x = tid; x < DK * W; x += NT) {
             const int c = x / W, jj = x % W;
-            a.S_T[sbase + (int64_t)c * DV + col0 + jj] = sS[x];
+            a.S_T[sbase + (int64_t)c * DV + col0 + jj] = sSt[jj * PO + c];
         }
 }
 
@@ -906,7 +853,7 @@ static hipError_t launch_gen(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     else if (p.chunk <= 64)
         hipLaunchKernelGGL((kg_recur_res<E, 64>), rgrid, dim3(512), 0, st, a);
     else
-        hipLaunchKernelGGL((kg_recur<E, kGenRecurThreads>), rgrid, dim3(kGenRecurThreads), 0, st, a);
+        hipLaunchKernelGGL(kg_recur<E>, rgrid, dim3(kGenRecurThreads), 0, st, a);
     mark(3);
     return hipGetLastError();
 }
