@@ -248,27 +248,39 @@ __global__ __launch_bounds__(NT) void kg_gram(GenArgs a) {
                 sKi[t * P + c + e] = kv[u * NV + e] * __expf(sRho[c + e] - sKi[t * P + c + e]);
     }
     __syncthreads();
-    // column i = tid % C against rows RPT * (tid / C) .. + RPT - 1 of the block
-    constexpr int RPT = kGenRows * C / NT;
-    const int i = tid % C, rb = RPT * (tid / C);
-    float accA[RPT], accM[RPT];
-#pragma unroll
-    for (int m = 0; m < RPT; ++m) accA[m] = accM[m] = 0.f;
-    if (i < nrow) {
-        for (int c = 0; c < DK; c += 4) {
-            const float4 ki = *reinterpret_cast<const float4*>(&sKi[i * P + c]);
-#pragma unroll
-            for (int m = 0; m < RPT; ++m) {
-                accA[m] += dot4(*reinterpret_cast<const float4*>(&sKr[(rb + m) * P + c]), ki);
-                accM[m] += dot4(*reinterpret_cast<const float4*>(&sQr[(rb + m) * P + c]), ki);
+    // The block's rows of A and M by 16 x 16 tiles over columns i, on fp32
+    // matrix cores (16x16x4 steps over the key channels; a lane's A and B
+    // fragments for four steps are one 16-byte read each): task x < 2 C / 16
+    // is column tile x / 2 of A (x even) or of M (x odd), computed when it
+    // holds columns i < nrow and written as zeros past them.  Lane 16 g + li
+    // ends with rows 4 g + r of the block and column li of the tile.
+    typedef float v4 __attribute__((ext_vector_type(4)));
+    const int wave = tid / 64, lane = tid % 64, li = lane % 16, g = lane / 16;
+    for (int x = wave; x < 2 * (C / kGenRows); x += NT / 64) {
+        const int J = x / 2;
+        const bool isA = (x % 2) == 0;
+        f32x4 acc = zero4();
+        if (kGenRows * J < nrow) {
+            const float* arow = (isA ? sKr : sQr) + li * P;
+            const float* bcol = sKi + (kGenRows * J + li) * P;
+            for (int k0 = 0; k0 < DK; k0 += 16) {
+                const v4 av = *reinterpret_cast<const v4*>(arow + k0 + 4 * g);
+                const v4 bv = *reinterpret_cast<const v4*>(bcol + k0 + 4 * g);
+                acc = mma_f32(av.x, bv.x, acc);
+                acc = mma_f32(av.y, bv.y, acc);
+                acc = mma_f32(av.z, bv.z, acc);
+                acc = mma_f32(av.w, bv.w, acc);
             }
         }
-    }
+        const int i = kGenRows * J + li;
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) {
-        const int r = r0 + rb + m;
-        a.TB[(slot * C + r) * C + i] = i < r ? sBeta[rb + m] * accA[m] : 0.f;
-        a.M[(slot * C + r) * C + i] = i <= r ? accM[m] : 0.f;
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = r0 + 4 * g + rr;
+            if (isA)
+                a.TB[(slot * C + r) * C + i] = i < r ? sBeta[4 * g + rr] * acc[rr] : 0.f;
+            else
+                a.M[(slot * C + r) * C + i] = i <= r ? acc[rr] : 0.f;
+        }
     }
 }
 
@@ -278,77 +290,82 @@ __global__ __launch_bounds__(NT) void kg_gram(GenArgs a) {
 // inside each block (T_KK starts as I; once row i is final every later row
 // r takes away A[r][i] times it).  Then block row by block row,
 //   T_KL = -T_KK sum_{L <= M < K} A_KM T_ML     (L < K),
-// which only needs block rows above K.  T diag(beta) is written over A.
+// each block of a row one wave's task, on fp32 matrix cores (16x16x4
+// steps): A_KM comes from global memory as 16-byte fragments, T_ML from the
+// finished rows, kept transposed in LDS so that its fragments are 16-byte
+// reads too, and the product's accumulator is already the B operand of the
+// multiplication by T_KK.  T diag(beta) is written over A at the end.
 template <typename E, int CC>
 __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
-    constexpr int B = 16;
-    constexpr int kTri = CC * (CC + 1) / 2;   // lower triangles, row r at r (r + 1) / 2
-    __shared__ float sA[kTri];
-    __shared__ float sT[kTri];
-    auto at = [](int r, int j) { return r * (r + 1) / 2 + j; };   // (r, j), j <= r
+    constexpr int B = 16, C = CC, NB = C / B;
+    constexpr int PT = C + 4;                       // pitch of the transposed rows
+    constexpr int kRowsT = NB > 1 ? (NB - 1) * B : 1;   // T[r][j] kept at sTt[j][r] for column blocks < NB - 1
+    __shared__ __attribute__((aligned(16))) float sTt[kRowsT * PT];
+    __shared__ float sAd[NB][B][B + 1];            // diagonal blocks of A
+    __shared__ float sTd[NB][B][B + 1];            // diagonal blocks of T
+    typedef float v4 __attribute__((ext_vector_type(4)));
     const int32_t ci = blockIdx.x;
     const int h = blockIdx.y;
     int64_t tok0;
     int len;
     if (!gen_chunk(a, ci, tok0, len)) return;
-    constexpr int C = CC, NB = C / B;
     const int tid = threadIdx.x;
     const int64_t slot = (int64_t)h * a.max_chunks + ci;
     float* A = a.TB + slot * C * C;
-    for (int x = tid; x < C * C; x += 256) {
-        const int r = x / C, j = x % C;
-        if (j <= r) {
-            sA[at(r, j)] = A[x];
-            sT[at(r, j)] = r == j ? 1.f : 0.f;
-        }
+    for (int x = tid; x < NB * B * B; x += 256) {
+        const int K = x / (B * B), r = (x / B) % B, j = x % B;
+        sAd[K][r][j] = A[(B * K + r) * C + B * K + j];
+        sTd[K][r][j] = r == j ? 1.f : 0.f;
     }
     __syncthreads();
     // diagonal blocks: thread -> block K = tid / 32, column j, rows of parity g
     {
-        const int K = tid / 32, j = tid % B, g = (tid / B) % 2, o = B * K;
+        const int K = tid / 32, j = tid % B, g = (tid / B) % 2;
         for (int i = 0; i < B - 1; ++i) {
             if (K < NB && j <= i) {
-                const float ti = sT[at(o + i, o + j)];
-                for (int r = i + 1 + ((g - (i + 1)) % 2 + 2) % 2; r < B; r += 2)
-                    sT[at(o + r, o + j)] -= sA[at(o + r, o + i)] * ti;
+                const float ti = sTd[K][i][j];
+                for (int r = i + 1 + ((g - (i + 1)) % 2 + 2) % 2; r < B; r += 2) sTd[K][r][j] -= sAd[K][r][i] * ti;
             }
             __syncthreads();
         }
     }
-    // block row K: X_KL = sum_M A_KM T_ML for every L < K (thread -> element
-    // (r, j) of the block, looping over L), then T_KL = -T_KK X_KL
-    const int r = tid / B, j = tid % B;
+    // block rows
+    const int wave = tid / 64, lane = tid % 64, li = lane % 16, g = lane / 16;
     for (int K = 1; K < NB; ++K) {
-        float x[NB];
+        // T_KK's row li, as A fragments for the four steps over k = 4 g' + u
+        for (int L = wave; L < K; L += 4) {
+            f32x4 x = zero4();
+            for (int Mb = L; Mb < K; ++Mb) {
+                const v4 av = *reinterpret_cast<const v4*>(A + (B * K + li) * C + B * Mb + 4 * g);
+                v4 bv;
+                if (Mb == L) {
 #pragma unroll
-        for (int L = 0; L < NB; ++L) {
-            float acc = 0.f;
-            if (L < K)
-                for (int m = B * L + j; m < B * K; ++m) acc += sA[at(B * K + r, m)] * sT[at(m, B * L + j)];
-            x[L] = acc;
+                    for (int u = 0; u < 4; ++u) bv[u] = sTd[L][4 * g + u][li];
+                } else {
+                    bv = *reinterpret_cast<const v4*>(&sTt[(B * L + li) * PT + B * Mb + 4 * g]);
+                }
+                x = mma_f32(av.x, bv.x, x);
+                x = mma_f32(av.y, bv.y, x);
+                x = mma_f32(av.z, bv.z, x);
+                x = mma_f32(av.w, bv.w, x);
+            }
+            // T_KL = -T_KK X: lane (li, g) holds X[4 g + r][li], the B operand
+            // of step r (k = 4 g + r) of the 16-deep product
+            f32x4 y = zero4();
+#pragma unroll
+            for (int u = 0; u < 4; ++u) y = mma_f32(sTd[K][li][4 * g + u], x[u], y);
+            *reinterpret_cast<v4*>(&sTt[(B * L + li) * PT + B * K + 4 * g]) = -y;
         }
-        __syncthreads();   // X is in registers; the block row's T entries are written below
-#pragma unroll
-        for (int L = 0; L < NB; ++L)
-            if (L < K) sT[at(B * K + r, B * L + j)] = x[L];
-        __syncthreads();
-#pragma unroll
-        for (int L = 0; L < NB; ++L) {
-            if (L >= K) continue;
-            float acc = 0.f;
-            for (int m = 0; m <= r; ++m) acc += sT[at(B * K + r, B * K + m)] * sT[at(B * K + m, B * L + j)];
-            x[L] = -acc;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int L = 0; L < NB; ++L)
-            if (L < K) sT[at(B * K + r, B * L + j)] = x[L];
-        __syncthreads();
+        __syncthreads();   // block row K of T is final
     }
+    // T diag(beta) over A (A is not read any more)
     for (int x = tid; x < C * C; x += 256) {
         const int rr = x / C, jj = x % C;
         const float bj = jj < len ? ldf<E>(a.beta, (tok0 + jj) * a.H + h) : 0.f;
-        A[x] = jj <= rr ? sT[at(rr, jj)] * bj : 0.f;
+        float t = 0.f;
+        if (jj / B == rr / B) t = sTd[rr / B][rr % B][jj % B];
+        else if (jj < rr) t = sTt[jj * PT + rr];
+        A[x] = t * bj;
     }
 }
 
