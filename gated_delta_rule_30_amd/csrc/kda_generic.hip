@@ -22,8 +22,8 @@
 // log-decay), so every entry is a dot product of rows scaled once; factors
 // that underflow over a long chunk belong to negligible terms.
 //
-//   kg_gram  (chunks, H, C/16)  16 rows of A and M per workgroup, and those
-//                               rows of Q.e^b, K.e^b, K.e^{b_L-b}
+//   kg_gram  (chunks, H)        A and M of one chunk, 16 rows at a time, and
+//                               its rows of Q.e^b, K.e^b, K.e^{b_L-b}
 //   kg_solve (chunks, H)        T diag(beta) in LDS, by 16 x 16 blocks
 //   kg_recur (N*H*d_v/16)       sequential over one sequence's chunks for one
 //                               head and 16 value columns of the state, at
@@ -37,7 +37,7 @@
 namespace kda {
 
 constexpr int kGenMaxC = 128, kGenMaxD = 128;
-constexpr int kGenRows = 16;    // A and M rows per kg_gram workgroup
+constexpr int kGenRows = 16;    // rows of a sub-tile
 constexpr int kGenCols = 16;    // value columns per kg_recur workgroup
 constexpr int kGenRecurThreads = 512;   // kg_recur threads: one wave per 16-token tile of a 128-token chunk
 
@@ -132,62 +132,61 @@ struct Vec16 {
 };
 
 // ------------------------------------------------------------------ kg_gram
-// Rows r0 .. r0+15 (one 16-token sub-tile) of A and M.  With rho = b at
-// row r0, e^{b_r - b_i} = e^{b_r - rho} e^{rho - b_i}: for r in the
-// sub-tile the first factor lies in [e^-80, 1]; the second is <= 1 for
+// A and M of one chunk, sub-tile after sub-tile (rows r0 .. r0+15).  With
+// rho = b at row r0, e^{b_r - b_i} = e^{b_r - rho} e^{rho - b_i}: for r in
+// the sub-tile the first factor lies in [e^-80, 1]; the second is <= 1 for
 // i < r0 and <= e^80 for i in the sub-tile (16 tokens at log alpha >= -5),
 // which fp32 holds.  So each entry is a plain dot product over channels of
 // the rows scaled once, k_r e^{b_r - rho} (or q_r ...) and k_i e^{rho - b_i}:
 // one exponential per (row, channel) instead of one per (pair, channel).
-// Every global load is a 16-byte vector, and a thread issues all of its
-// loads of a tile before it uses any.
+// The chunk's log-decay rows are loaded and summed once, k stays in
+// registers, and each sub-tile's rows of A and M are 16 x 16 tiles on fp32
+// matrix cores.
 template <typename E, int CC, int NT>
 __global__ __launch_bounds__(NT) void kg_gram(GenArgs a) {
-    constexpr int P = kGenMaxD + 4;   // row pitch (floats): 16-byte rows, lanes of consecutive rows on distinct banks
+    constexpr int P = kGenMaxD + 4;
     constexpr int NV = Vec16<E>::N;
     constexpr int kTileVec = CC * kGenMaxD / NV / NT;   // 16-byte vectors per thread of a full tile
-    __shared__ __attribute__((aligned(16))) float sKi[CC * P];   // g, then b, then k_i e^{rho - b_i}
-    __shared__ __attribute__((aligned(16))) float sKr[kGenRows * P];   // k_r e^{b_r - rho}, rows of this block
-    __shared__ __attribute__((aligned(16))) float sQr[kGenRows * P];   // q_r e^{b_r - rho}
-    __shared__ float sRho[kGenMaxD];
-    __shared__ float sBeta[kGenRows];
+    static_assert(kTileVec >= 1 && CC <= NT, "whole tiles per thread; one thread per row for beta");
+    __shared__ __attribute__((aligned(16))) float sB[CC * P];    // g, then b
+    __shared__ __attribute__((aligned(16))) float sKi[CC * P];   // k_i e^{rho - b_i} for the current sub-tile
+    __shared__ __attribute__((aligned(16))) float sKr[kGenRows * P];
+    __shared__ __attribute__((aligned(16))) float sQr[kGenRows * P];
+    __shared__ float sBeta[CC];
+    typedef float v4 __attribute__((ext_vector_type(4)));
     const int32_t ci = blockIdx.x;
-    const int h = blockIdx.y, r0 = kGenRows * blockIdx.z;
+    const int h = blockIdx.y;
     int64_t tok0;
     int len;
     if (!gen_chunk(a, ci, tok0, len)) return;
     constexpr int C = CC;
     const int DK = a.DK, tid = threadIdx.x;
-    const int nrow = r0 + kGenRows;   // columns i <= r for the block's rows r
     const int64_t rs = (int64_t)a.H * DK;
     const int64_t base = tok0 * rs + (int64_t)h * DK;
     const int64_t slot = (int64_t)h * a.max_chunks + ci;
-    const int vpr = DK / NV;          // vectors per row
-    // g of every row (b_L needs the whole chunk) and k of rows < nrow, in
-    // registers; rows past the chunk end are zero
+    const int vpr = DK / NV;
+    // g and k of every row in registers; rows past the chunk end are zero
     float gv[kTileVec * NV], kv[kTileVec * NV];
 #pragma unroll
     for (int u = 0; u < kTileVec; ++u) {
         const int x = tid + NT * u, t = x / vpr, c = (x % vpr) * NV;
         const bool in = x < C * vpr && t < len;
-        if (in) Vec16<E>::load(a.g, base + t * rs + c, &gv[u * NV]);
-        if (in && t < nrow) Vec16<E>::load(a.k, base + t * rs + c, &kv[u * NV]);
+        if (in) {
+            Vec16<E>::load(a.g, base + t * rs + c, &gv[u * NV]);
+            Vec16<E>::load(a.k, base + t * rs + c, &kv[u * NV]);
+        }
 #pragma unroll
         for (int e = 0; e < NV; ++e) {
-            if (!in) gv[u * NV + e] = 0.f;
-            if (!in || t >= nrow) kv[u * NV + e] = 0.f;
+            if (!in) gv[u * NV + e] = kv[u * NV + e] = 0.f;
         }
     }
-    if (tid < kGenRows) {
-        const int t = r0 + tid;
-        sBeta[tid] = t < len ? ldf<E>(a.beta, (tok0 + t) * a.H + h) : 0.f;
-    }
+    if (tid < C) sBeta[tid] = tid < len ? ldf<E>(a.beta, (tok0 + tid) * a.H + h) : 0.f;
 #pragma unroll
     for (int u = 0; u < kTileVec; ++u) {
         const int x = tid + NT * u, t = x / vpr, c = (x % vpr) * NV;
         if (x < C * vpr)
 #pragma unroll
-            for (int e = 0; e < NV; ++e) sKi[t * P + c + e] = gv[u * NV + e];
+            for (int e = 0; e < NV; ++e) sB[t * P + c + e] = gv[u * NV + e];
     }
     __syncthreads();
     // b: per-channel running sum over the chunk, eight rows read at a time
@@ -196,91 +195,95 @@ __global__ __launch_bounds__(NT) void kg_gram(GenArgs a) {
         for (int t0 = 0; t0 < C; t0 += 8) {
             float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = sKi[(t0 + e) * P + c];
+            for (int e = 0; e < 8; ++e) x[e] = sB[(t0 + e) * P + c];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 run += x[e];
-                sKi[(t0 + e) * P + c] = run;
+                sB[(t0 + e) * P + c] = run;
             }
         }
-        sRho[c] = sKi[r0 * P + c];
+        a.gam[slot * DK + c] = __expf(run);
     }
     __syncthreads();
-    // the block's rows: scaled operands, and Q.e^b, K.e^b, K.e^{b_L - b}
-    for (int x = tid; x < kGenRows * vpr; x += NT) {
-        const int rr = x / vpr, r = r0 + rr, c = (x % vpr) * NV;
-        float kr[NV], qr[NV];
-        if (r < len) {
-            Vec16<E>::load(a.k, base + r * rs + c, kr);
-            Vec16<E>::load(a.q, base + r * rs + c, qr);
-        } else {
-#pragma unroll
-            for (int e = 0; e < NV; ++e) kr[e] = qr[e] = 0.f;
-        }
-        const int64_t at = (slot * C + r) * DK + c;
-#pragma unroll
-        for (int e4 = 0; e4 < NV; e4 += 4) {
-            float4 oq, ok, oh;
-#pragma unroll
-            for (int e = e4; e < e4 + 4; ++e) {
-                const float bv = sKi[r * P + c + e], bl = sKi[(C - 1) * P + c + e];
-                const float er = __expf(bv - sRho[c + e]), eb = __expf(bv);
-                sKr[rr * P + c + e] = kr[e] * er;
-                sQr[rr * P + c + e] = qr[e] * er;
-                (&oq.x)[e - e4] = qr[e] * eb;
-                (&ok.x)[e - e4] = kr[e] * eb;
-                (&oh.x)[e - e4] = kr[e] * __expf(bl - bv);
-            }
-            *reinterpret_cast<float4*>(a.Qg + at + e4) = oq;
-            *reinterpret_cast<float4*>(a.Kg + at + e4) = ok;
-            *reinterpret_cast<float4*>(a.Kh + at + e4) = oh;
-        }
-    }
-    if (blockIdx.z == 0)
-        for (int c = tid; c < DK; c += NT) a.gam[slot * DK + c] = __expf(sKi[(C - 1) * P + c]);
-    __syncthreads();   // every read of b outside each thread's own elements is done
+    // this thread's elements of b (gv is dead)
 #pragma unroll
     for (int u = 0; u < kTileVec; ++u) {
         const int x = tid + NT * u, t = x / vpr, c = (x % vpr) * NV;
-        if (x < C * vpr && t < nrow)
+        if (x < C * vpr)
 #pragma unroll
-            for (int e = 0; e < NV; ++e)
-                sKi[t * P + c + e] = kv[u * NV + e] * __expf(sRho[c + e] - sKi[t * P + c + e]);
+            for (int e = 0; e < NV; ++e) gv[u * NV + e] = sB[t * P + c + e];
     }
-    __syncthreads();
-    // The block's rows of A and M by 16 x 16 tiles over columns i, on fp32
-    // matrix cores (16x16x4 steps over the key channels; a lane's A and B
-    // fragments for four steps are one 16-byte read each): task x < 2 C / 16
-    // is column tile x / 2 of A (x even) or of M (x odd), computed when it
-    // holds columns i < nrow and written as zeros past them.  Lane 16 g + li
-    // ends with rows 4 g + r of the block and column li of the tile.
-    typedef float v4 __attribute__((ext_vector_type(4)));
     const int wave = tid / 64, lane = tid % 64, li = lane % 16, g = lane / 16;
-    for (int x = wave; x < 2 * (C / kGenRows); x += NT / 64) {
-        const int J = x / 2;
-        const bool isA = (x % 2) == 0;
-        f32x4 acc = zero4();
-        if (kGenRows * J < nrow) {
-            const float* arow = (isA ? sKr : sQr) + li * P;
-            const float* bcol = sKi + (kGenRows * J + li) * P;
-            for (int k0 = 0; k0 < DK; k0 += 16) {
-                const v4 av = *reinterpret_cast<const v4*>(arow + k0 + 4 * g);
-                const v4 bv = *reinterpret_cast<const v4*>(bcol + k0 + 4 * g);
-                acc = mma_f32(av.x, bv.x, acc);
-                acc = mma_f32(av.y, bv.y, acc);
-                acc = mma_f32(av.z, bv.z, acc);
-                acc = mma_f32(av.w, bv.w, acc);
+    for (int z = 0; z < C / kGenRows; ++z) {
+        const int r0 = kGenRows * z, nrow = r0 + kGenRows;
+        const float* rho = sB + r0 * P;   // b at the sub-tile's first row
+        // k_i e^{rho - b_i} for the rows i < nrow
+#pragma unroll
+        for (int u = 0; u < kTileVec; ++u) {
+            const int x = tid + NT * u, t = x / vpr, c = (x % vpr) * NV;
+            if (x < C * vpr && t < nrow)
+#pragma unroll
+                for (int e = 0; e < NV; ++e) sKi[t * P + c + e] = kv[u * NV + e] * __expf(rho[c + e] - gv[u * NV + e]);
+        }
+        // the sub-tile's rows: scaled operands, and Q.e^b, K.e^b, K.e^{b_L - b}
+        for (int x = tid; x < kGenRows * vpr; x += NT) {
+            const int rr = x / vpr, r = r0 + rr, c = (x % vpr) * NV;
+            float kr[NV], qr[NV];
+            if (r < len) {
+                Vec16<E>::load(a.k, base + r * rs + c, kr);
+                Vec16<E>::load(a.q, base + r * rs + c, qr);
+            } else {
+#pragma unroll
+                for (int e = 0; e < NV; ++e) kr[e] = qr[e] = 0.f;
+            }
+            const int64_t at = (slot * C + r) * DK + c;
+#pragma unroll
+            for (int e4 = 0; e4 < NV; e4 += 4) {
+                v4 oq, ok, oh;
+#pragma unroll
+                for (int e = e4; e < e4 + 4; ++e) {
+                    const float bv = sB[r * P + c + e], bl = sB[(C - 1) * P + c + e];
+                    const float er = __expf(bv - rho[c + e]), eb = __expf(bv);
+                    sKr[rr * P + c + e] = kr[e] * er;
+                    sQr[rr * P + c + e] = qr[e] * er;
+                    oq[e - e4] = qr[e] * eb;
+                    ok[e - e4] = kr[e] * eb;
+                    oh[e - e4] = kr[e] * __expf(bl - bv);
+                }
+                *reinterpret_cast<v4*>(a.Qg + at + e4) = oq;
+                *reinterpret_cast<v4*>(a.Kg + at + e4) = ok;
+                *reinterpret_cast<v4*>(a.Kh + at + e4) = oh;
             }
         }
-        const int i = kGenRows * J + li;
+        __syncthreads();
+        // the sub-tile's rows of A and M by 16 x 16 tiles over columns i
+        for (int x = wave; x < 2 * (C / kGenRows); x += NT / 64) {
+            const int J = x / 2;
+            const bool isA = (x % 2) == 0;
+            f32x4 acc = zero4();
+            if (J <= z) {
+                const float* arow = (isA ? sKr : sQr) + li * P;
+                const float* bcol = sKi + (kGenRows * J + li) * P;
+                for (int k0 = 0; k0 < DK; k0 += 16) {
+                    const v4 av = *reinterpret_cast<const v4*>(arow + k0 + 4 * g);
+                    const v4 bv = *reinterpret_cast<const v4*>(bcol + k0 + 4 * g);
+                    acc = mma_f32(av.x, bv.x, acc);
+                    acc = mma_f32(av.y, bv.y, acc);
+                    acc = mma_f32(av.z, bv.z, acc);
+                    acc = mma_f32(av.w, bv.w, acc);
+                }
+            }
+            const int i = kGenRows * J + li;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = r0 + 4 * g + rr;
-            if (isA)
-                a.TB[(slot * C + r) * C + i] = i < r ? sBeta[4 * g + rr] * acc[rr] : 0.f;
-            else
-                a.M[(slot * C + r) * C + i] = i <= r ? acc[rr] : 0.f;
+            for (int rr = 0; rr < 4; ++rr) {
+                const int r = r0 + 4 * g + rr;
+                if (isA)
+                    a.TB[(slot * C + r) * C + i] = i < r ? sBeta[r] * acc[rr] : 0.f;
+                else
+                    a.M[(slot * C + r) * C + i] = i <= r ? acc[rr] : 0.f;
+            }
         }
+        __syncthreads();   // sKi, sKr and sQr are rewritten for the next sub-tile
     }
 }
 
@@ -841,22 +844,22 @@ static hipError_t launch_gen(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     if (p.cu_seqlens) launch_chunk_table(p, p.chunk, st);
     mark(1);
     if (p.max_chunks > 0) {
-        const dim3 ggrid(p.max_chunks, p.n_heads, p.chunk / kGenRows), sgrid(p.max_chunks, p.n_heads);
+        const dim3 sgrid(p.max_chunks, p.n_heads);
         switch (p.chunk) {
             case 16:
-                hipLaunchKernelGGL((kg_gram<E, 16, 256>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_gram<E, 16, 256>), sgrid, dim3(256), 0, st, a);
                 hipLaunchKernelGGL((kg_solve<E, 16>), sgrid, dim3(256), 0, st, a);
                 break;
             case 32:
-                hipLaunchKernelGGL((kg_gram<E, 32, 256>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_gram<E, 32, 256>), sgrid, dim3(256), 0, st, a);
                 hipLaunchKernelGGL((kg_solve<E, 32>), sgrid, dim3(256), 0, st, a);
                 break;
             case 64:
-                hipLaunchKernelGGL((kg_gram<E, 64, 256>), ggrid, dim3(256), 0, st, a);
+                hipLaunchKernelGGL((kg_gram<E, 64, 512>), sgrid, dim3(512), 0, st, a);
                 hipLaunchKernelGGL((kg_solve<E, 64>), sgrid, dim3(256), 0, st, a);
                 break;
             default:
-                hipLaunchKernelGGL((kg_gram<E, 128, 512>), ggrid, dim3(512), 0, st, a);
+                hipLaunchKernelGGL((kg_gram<E, 128, 512>), sgrid, dim3(512), 0, st, a);
                 hipLaunchKernelGGL((kg_solve<E, 128>), sgrid, dim3(256), 0, st, a);
                 break;
         }
