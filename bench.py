@@ -391,7 +391,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", type=int, default=2, help="workload id (2 = headline)")
     ap.add_argument("--profile-reps", type=int, default=10)
     ap.add_argument("--cpu-heads", type=int, default=32, help="heads in the CPU-oracle sample")
