@@ -3,8 +3,8 @@
 // The tuned kernels (kda_kernels.hip) cover chunk 64 with d_k = d_v: bf16 at
 // 64 and 128, fp32 at 64.  These kernels take any chunk C in {16, 32, 64,
 // 128}, any d_k, d_v in {64, 128} and either input type, with fp32
-// arithmetic throughout (fp32 operands in the workspace; fp32 matrix cores
-// in the recurrence for chunks up to 64, fp32 FMA elsewhere).  They
+// arithmetic throughout (fp32 operands in the workspace, every product on
+// fp32 matrix cores: 16x16x4 MFMA steps accumulating in fp32).  They
 // compute the same chunked form (ogis-ri NLP primer on Kimi K3, §3.1
 // "KDA（Kimi Delta Attention）": per chunk, the state carried in plus a
 // causal intra-chunk term; §3.1 "chunk 内の減衰と、その数値範囲": per-channel
@@ -101,12 +101,6 @@ __device__ inline void gen_slab(const GenArgs& a, int slabs, int32_t& n, int& h,
 template <typename E>
 __device__ inline float ldf(const void* p, int64_t i) {
     return to_f(static_cast<const E*>(p)[i]);
-}
-
-__device__ inline float dot4(float4 x, float4 y) { return x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w; }
-
-__device__ inline float4 fma4(float s, float4 x, float4 acc) {
-    return make_float4(acc.x + s * x.x, acc.y + s * x.y, acc.z + s * x.z, acc.w + s * x.w);
 }
 
 // 16 bytes of E from element `i` of p, widened to fp32: 8 (bf16) or 4 (fp32)

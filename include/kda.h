@@ -93,9 +93,9 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_
  * recurrence).  Chunk 64 with d_k == d_v (bf16 at 64 or 128, fp32 at 64)
  * runs the tuned kernels (bf16 MFMA operands at bf16, fp32 at fp32); every
  * other supported size -- chunk 16, 32 or 128, d_k != d_v, fp32 at 128 --
- * runs generic kernels in fp32 arithmetic (fp32 operands; fp32 matrix cores
- * in the recurrence for chunks up to 64), correct to the same bars but
- * several times slower than the tuned path.  Their workspace is fp32: about
+ * runs generic kernels in fp32 arithmetic (fp32 operands, fp32 matrix
+ * cores), correct to the same bars but several times slower than the tuned
+ * path.  Their workspace is fp32: about
  * 4 (3 d_k + 2 chunk + d_k / chunk) bytes per (token, head). */
 kda_status kda_chunk_fwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
                          int32_t d_k, int32_t d_v, int32_t chunk,
