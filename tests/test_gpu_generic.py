@@ -170,3 +170,29 @@ def test_profile_entry_and_determinism(torch_dev):
     o3, S3 = _run(torch, dev, inp, 128, profile=True)
     assert np.array_equal(o1, o2) and np.array_equal(S1, S2)
     assert np.array_equal(o1, o3) and np.array_equal(S1, S3)
+
+
+RANDOM_CASES = 16
+
+
+@pytest.mark.parametrize("case", range(RANDOM_CASES))
+def test_random_cases(torch_dev, case):
+    """Seeded random (chunk, dtype, d_k, d_v, heads, lengths, S0) draws, the
+    lengths taken around the sub-tile and chunk edges (0, 1, 15..17, 31..33,
+    63..65, 127..129, and longer), each against the oracle."""
+    torch, dev = torch_dev
+    rng = np.random.default_rng(1000 + case)
+    C = int(rng.choice([16, 32, 64, 128]))
+    dtype = str(rng.choice(["f32", "bf16"]))
+    dk, dv = (int(x) for x in rng.choice([64, 128], size=2))
+    edges = [0, 1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 257]
+    lengths = [int(x) for x in rng.choice(edges, size=int(rng.integers(1, 6)))]
+    if sum(lengths) == 0:
+        lengths[0] = 33
+    H = int(rng.integers(1, 4))
+    s0 = float(rng.choice([0.0, 0.3]))
+    inp = ki.generate_numpy(_spec("random", dtype, lengths, H, dk, dv, seed=2000 + case, s0=s0))
+    what = "case %d: C=%d %s dk=%d dv=%d H=%d lengths %s S0 %.1f" % (case, C, dtype, dk, dv, H, lengths, s0)
+    _say(what)
+    o, ST = _run(torch, dev, inp, C)
+    _check(inp, o, ST, what)
