@@ -57,7 +57,8 @@ struct GenArgs {
     int64_t total_tokens, fixed_len;
     int32_t n_seqs, H, C, DK, DV, max_chunks;
     float *Qg, *Kg, *Kh;     // [H][max_chunks][C][DK]
-    float *TB, *M;           // [H][max_chunks][C][C] (TB holds A until kg_solve)
+    float *TB, *M;           // [H][max_chunks][C][C] (TB holds A until kg_solve); only the
+                             // 16 x 16 blocks on and below the diagonal are written
     float* gam;              // [H][max_chunks][DK]
 };
 
@@ -250,12 +251,14 @@ __global__ __launch_bounds__(NT) void kg_gram(GenArgs a) {
             }
         }
         __syncthreads();
-        // the sub-tile's rows of A and M by 16 x 16 tiles over columns i
-        for (int x = wave; x < 2 * (C / kGenRows); x += NT / 64) {
+        // the sub-tile's rows of A and M by 16 x 16 tiles over columns
+        // i < nrow (the blocks above the diagonal blocks are zero by
+        // structure: they are not written, and no kernel reads them)
+        for (int x = wave; x < 2 * (z + 1); x += NT / 64) {
             const int J = x / 2;
             const bool isA = (x % 2) == 0;
             f32x4 acc = zero4();
-            if (J <= z) {
+            {
                 const float* arow = (isA ? sKr : sQr) + li * P;
                 const float* bcol = sKi + (kGenRows * J + li) * P;
                 for (int k0 = 0; k0 < DK; k0 += 16) {
@@ -355,13 +358,13 @@ __global__ __launch_bounds__(256) void kg_solve(GenArgs a) {
         }
         __syncthreads();   // block row K of T is final
     }
-    // T diag(beta) over A (A is not read any more)
+    // T diag(beta) over A (A is not read any more), its lower blocks only:
+    // the recurrences' products stop at the diagonal block
     for (int x = tid; x < C * C; x += 256) {
         const int rr = x / C, jj = x % C;
+        if (jj / B > rr / B) continue;
         const float bj = jj < len ? ldf<E>(a.beta, (tok0 + jj) * a.H + h) : 0.f;
-        float t = 0.f;
-        if (jj / B == rr / B) t = sTd[rr / B][rr % B][jj % B];
-        else if (jj < rr) t = sTt[jj * PT + rr];
+        const float t = jj / B == rr / B ? sTd[rr / B][rr % B][jj % B] : sTt[jj * PT + rr];
         A[x] = t * bj;
     }
 }
