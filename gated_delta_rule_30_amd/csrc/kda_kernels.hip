@@ -45,6 +45,7 @@
 // also the B-operand fragment of column block w, so the diagonal sub-tile
 // products need no data exchange.  The per-channel cumulative sum over
 // tokens is a 16-lane row scan (DPP row shifts) plus carries between waves.
+#include <atomic>
 #include <mutex>
 
 #include "kda_device.h"
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
                                                    const ChunkInfo* __restrict__ tab,
                                                    const int32_t* __restrict__ n_chunks_p, int64_t fixed_len,
                                                    int32_t fixed_chunks, int32_t H, ChunkOps ops, ChunkOps ob,
-                                                   int32_t blk_j0, int32_t blk_nj) {
+                                                   int32_t blk_j0, int32_t blk_nj, int32_t xcd_hi) {
     constexpr bool kBwd = kBoth;
     using G = Geo<E, D>;
     using M = Mma<E>;
@@ -299,8 +300,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
     // the index (fixed_chunks chunks per sequence, in sequence order, as the
     // chunk table lists them); otherwise it is read from the chunk table.
     // With blk_nj > 0 (equal lengths only) the grid covers chunks
-    // blk_j0 .. blk_j0 + blk_nj - 1 of every sequence.
+    // blk_j0 .. blk_j0 + blk_nj - 1 of every sequence.  With xcd_hi the
+    // grid is twice the work (x a multiple of 8): workgroups on XCDs 0..3
+    // (id mod 8 < 4) leave at once, so that k_prep runs on XCDs 4..7 only.
     int32_t ci = blockIdx.x;
+    if (xcd_hi) {
+        if (ci % 8 < 4) return;
+        ci = (ci / 8) * 4 + ci % 8 - 4;
+    }
     ChunkInfo info;
     if (fixed_len > 0) {
         const int32_t per = (int32_t)((fixed_len + kChunk - 1) / kChunk);
@@ -951,6 +958,17 @@ __global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, Chu
 // Because of that sharing the slabs of a head have to stay within a few
 // steps of each other; on long sequences a ninth wave per workgroup (the
 // pacing wave) holds back a workgroup that runs too far ahead.
+//
+// Slab width: 16 value columns (CT = 1), or 32 (CT = 2, plain forward only)
+// with each compute wave owning two 16-column tiles and every A fragment it
+// reads from LDS serving both.  A chunk's operand fill is the same 64 KB
+// either way, so CT = 2 does twice the work per fill: the step is longer
+// (about 1.55 against 1.02 us at d = 128) but the work per CU and step is
+// doubled, which pays when more 16-column chains exist than CUs (many
+// sequences or heads: the whole chip's throughput sets the time), and not
+// when each chain has a CU to itself (its latency sets the time).  At
+// CT = 2 the value rows of a region fill its misc block, so Gamma_L comes in
+// by one more (4-byte) direct load per region into sGam0 / sGam1.
 #define KDA_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
@@ -1061,11 +1079,11 @@ struct ZeroHalf {
     __device__ static bool zero(int region) { return kMode == kBwd ? region >= 2 : region < 2; }
 };
 
-template <int D, int kMode>
+template <int D, int kMode, int CT>
 __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     const __bf16* __restrict__ v, ChunkOps ops, const int32_t* __restrict__ cu, int64_t total_tokens,
     int64_t fixed_len, const int32_t* __restrict__ seq_chunk0, int32_t NH, int32_t H, const float* __restrict__ S0,
-    float* __restrict__ ST, __bf16* __restrict__ o, RecurAux aux, int32_t jb, int32_t je) {
+    float* __restrict__ ST, __bf16* __restrict__ o, RecurAux aux, int32_t jb, int32_t je, int32_t xcd_lo) {
     constexpr bool kTransition = kMode == kTrans;
     constexpr bool kBack = kMode == kBwd;
     using E = __bf16;
@@ -1077,8 +1095,9 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     static_assert(G::VPL == G::NKC && G::NVT == G::NKT, "one 16-byte vector per bf16 fragment");
     static_assert(kRecurWaves == kNSub, "one compute wave per 16-token row tile");
     static_assert(G::NKT == 2, "the zero halves are the two 32-token halves of a 64-token chunk");
+    static_assert(CT == 1 || (CT == 2 && kMode == kFwd), "two column tiles per wave: plain forward only");
     constexpr int C = kChunk, CPL = G::CPL, RT = L::RT;
-    constexpr int SW = kSub;           // slab width (value columns)
+    constexpr int SW = kSub * CT;      // slab width (value columns): CT 16-column tiles per compute wave
     constexpr int NS = D / SW;         // slabs per head
     constexpr int PS = D + 8;          // pitch of S^T      [col][channel]
     constexpr int PY = C + 8;          // pitch of Y^T, U~^T [col][token]
@@ -1088,13 +1107,29 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     __shared__ __attribute__((aligned(16))) E sYt[SW * PY];
     __shared__ __attribute__((aligned(16))) E sUt[SW * PY];
     __shared__ unsigned sTouch[kProducers * 64];   // warm-up loads land here, never read
+    // CT = 2: the value rows fill the misc block, so Gamma_L of each region's
+    // 16 RT channels comes in by 4-byte direct loads into these (one per
+    // buffer; sized so that a load from all 64 lanes at the last region's
+    // base would still stay inside).
+    constexpr int kGamPer = 16 * RT;
+    constexpr int kGamLen = CT > 1 ? (kRecurWaves - 1) * kGamPer + 64 : 1;
+    __shared__ __attribute__((aligned(16))) float sGam0[kGamLen];
+    __shared__ __attribute__((aligned(16))) float sGam1[kGamLen];
 
     // Workgroup -> (sequence*head, slab); slabs of one (sequence, head) share
     // an XCD (and its L2) when the (sequence, head) count is a multiple of 8.
+    // With xcd_lo the grid is twice the work: workgroups on XCDs 4..7
+    // (workgroup id mod 8 >= 4) leave at once, so that the recurrence holds
+    // only XCDs 0..3 and their L2s (NH a multiple of 4).
     int nh, sl;
     {
         const int bid = blockIdx.x;
-        if (NH % 8 == 0) {
+        if (xcd_lo) {
+            if (bid % 8 >= 4) return;
+            const int r = bid / 8;
+            sl = r % NS;
+            nh = (bid % 8) + 4 * (r / NS);
+        } else if (NH % 8 == 0) {
             sl = (bid / 8) % NS;
             nh = (bid % 8) + 8 * (bid / (8 * NS));
         } else {
@@ -1193,7 +1228,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         const E* kt = static_cast<const E*>(ops.KhT) + cb * D * C + lane * G::EPV;
         const E* tb = static_cast<const E*>(ops.TB) + cb * C * C + lane * G::EPV;
         const E* mm = static_cast<const E*>(ops.Mm) + cb * C * C + lane * G::EPV;
-        const E* vv = v + (s_start * H + h) * D + col0 + 8 * (lane & 1);
+        constexpr int kVL = 2 * CT;   // lanes per value row of the slab (16 bytes each)
+        const E* vv = v + (s_start * H + h) * D + col0 + 8 * (lane % kVL);
         const int gi = (lane >= 32 && lane < 32 + 4 * RT) ? lane - 32 : 0;
         const float* gm = ops.gam + cb * D + 4 * gi;
         // kBwd: lanes 48..51 bring beta of the region's 16 rows (bytes 768..831)
@@ -1221,9 +1257,9 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             else if constexpr (b < L::kMisc)
                 dma(kt + oo + (cw * RT * G::NVT + b - L::kKt) * 64 * G::EPV, dst + b * 64);
             else {
-                int row = kSub * cw + (lane >> 1);
+                int row = kSub * cw + lane / kVL;
                 row = row < len ? row : len - 1;
-                const void* misc = (lane < 32 && !kTransition)
+                const void* misc = (lane < 32 * CT && !kTransition)
                                        ? static_cast<const void*>(vv + ((int64_t)j * C + row) * rs)
                                    : is_bet ? static_cast<const void*>(bt + (int64_t)j * C)
                                             : static_cast<const void*>(gm + (int64_t)j * D + kSub * RT * cw);
@@ -1254,6 +1290,13 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             static_for<kProdPerWave>([&](auto p_c) {
                 if (part == decltype(p_c)::value) issue_part(p_c, lo_c, hi_c, dst, j, len);
             });
+            if constexpr (CT > 1 && decltype(hi_c)::value == kDma) {
+                // Gamma_L of this region's channels (one more load per chunk)
+                float* sg = (buf == sBuf0 ? sGam0 : sGam1) + cw * kGamPer;
+                if (lane < kGamPer)
+                    __builtin_amdgcn_global_load_lds(ops.gam + (cb + j) * D + kSub * RT * cw + lane, KDA_LDS_PTR(sg),
+                                                     4, 0, 0);
+            }
         };
         using All0 = std::integral_constant<int, 0>;
         using AllN = std::integral_constant<int, kDma>;
@@ -1336,9 +1379,10 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         // Loads per chunk fill of this producer: kDma, or kDma - 2 when its
         // region skips the zero halves of the two triangular tiles.
         const bool lean = Z::zero(cw);
+        constexpr int kFill = kDma + (CT > 1 ? 1 : 0);   // loads per chunk fill (CT = 2: Gamma_L apart)
         auto wait_fill = [&]() {
-            if (lean) wait_counts<2 * kTouch + kDma - 2, 15>();
-            else wait_counts<2 * kTouch + kDma, 15>();
+            if (lean) wait_counts<2 * kTouch + kFill - 2, 15>();
+            else wait_counts<2 * kTouch + kFill, 15>();
         };
         // One step j: open it; after the compute waves' first inner barrier
         // (chunk j's operands are in their registers) refill chunk j's buffer
@@ -1391,23 +1435,28 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     // kFwdCk: slot of this sequence's first checkpoint
     int32_t ck_first = 0;
     if constexpr (kMode == kFwdCk) ck_first = cu ? aux.ck0[n] : n * (nch / aux.every);
-    // S[a][r] = state[channel 16*(RT*w + a) + 4*lg + r][column col0 + li]
-    // (kBwd: the state gradient)
-    f32x4 S[RT];
+    // S[a][c][r] = state[channel 16*(RT*w + a) + 4*lg + r][column col0 + 16*c + li]
+    // (kBwd: the state gradient); c is the wave's column tile (CT of them)
+    f32x4 S[RT][CT];
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
 #pragma unroll
     for (int a = 0; a < RT; ++a)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ch = kSub * (RT * w + a) + 4 * lg + r;
-            if constexpr (kTransition) S[a][r] = ch == col0 + li ? 1.f : 0.f;
-            else S[a][r] = S0 ? S0[sbase + (int64_t)ch * D + col0 + li] : 0.f;
-        }
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int ch = kSub * (RT * w + a) + 4 * lg + r, col = col0 + kSub * c + li;
+                if constexpr (kTransition) S[a][c][r] = ch == col ? 1.f : 0.f;
+                else S[a][c][r] = S0 ? S0[sbase + (int64_t)ch * D + col] : 0.f;
+            }
     auto put_state = [&]() {
 #pragma unroll
         for (int a = 0; a < RT; ++a)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sSt[li * PS + kSub * (RT * w + a) + 4 * lg + r] = from_f<E>(S[a][r]);
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sSt[(kSub * c + li) * PS + kSub * (RT * w + a) + 4 * lg + r] = from_f<E>(S[a][c][r]);
     };
     put_state();
     // kCkpt / kBwd: this slab's columns of the state (gradient) as chunk j
@@ -1418,7 +1467,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         for (int a = 0; a < RT; ++a)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                ck[state_swz<D>(kSub * (RT * w + a) + 4 * lg + r, col0 + li)] = from_f<E>(S[a][r]);
+                ck[state_swz<D>(kSub * (RT * w + a) + 4 * lg + r, col0 + li)] = from_f<E>(S[a][0][r]);
     };
 
     auto step = [&](const uint4* buf, int j) {
@@ -1433,26 +1482,33 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             fq[m] = fr[(L::kQg + m) * 64];
             fk[m] = fr[(L::kKg + m) * 64];
         }
-        // X = (K . Gamma) S and P = (Q . Gamma) S for token rows 16w..
-        f32x4 accX = zero4(), accO = zero4();
+        // X = (K . Gamma) S and P = (Q . Gamma) S for token rows 16w.. (each
+        // A fragment serves the wave's CT column tiles)
+        f32x4 accX[CT], accO[CT];
 #pragma unroll
-        for (int m = 0; m < G::NKC; ++m) {
-            const F bs = M::load(&sSt[li * PS + lg * CPL + m * M::KW]);
-            accX = M::mma(fk[m], bs, accX);
-            accO = M::mma(fq[m], bs, accO);
-        }
+        for (int c = 0; c < CT; ++c) accX[c] = accO[c] = zero4();
+#pragma unroll
+        for (int m = 0; m < G::NKC; ++m)
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+                const F bs = M::load(&sSt[(kSub * c + li) * PS + lg * CPL + m * M::KW]);
+                accX[c] = M::mma(fk[m], bs, accX[c]);
+                accO[c] = M::mma(fq[m], bs, accO[c]);
+            }
         // Y = V - X, transposed to LDS (rows past the chunk end are zero)
         const E* vrows = reinterpret_cast<const E*>(cur + L::kMisc * 64);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = kSub * w + 4 * lg + r;
-            const float vv = kTransition ? 0.f : to_f(vrows[(4 * lg + r) * SW + li]);
-            const E y = from_f<E>(t < len ? vv - accX[r] : 0.f);
-            sYt[li * PY + t] = y;
-            if constexpr (kMode == kCkpt) {
-                if (t < len) aux.y[o_off + ((int64_t)j * C + t) * rs] = y;
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = kSub * w + 4 * lg + r;
+                const float vv = kTransition ? 0.f : to_f(vrows[(4 * lg + r) * SW + kSub * c + li]);
+                const E y = from_f<E>(t < len ? vv - accX[c][r] : 0.f);
+                sYt[(kSub * c + li) * PY + t] = y;
+                if constexpr (kMode == kCkpt) {
+                    if (t < len) aux.y[o_off + ((int64_t)j * C + t) * rs] = y;
+                }
             }
-        }
         F ftb[G::NKT], fmm[G::NKT], fkt[RT][G::NKT];
         const bool zh = Z::zero(w);
 #pragma unroll
@@ -1470,21 +1526,23 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 #pragma unroll
             for (int m = 0; m < G::NKT; ++m) fkt[a][m] = fr[(L::kKt + a * G::NKT + m) * 64];
         f32x4 gam[RT];
-        const float* gl = reinterpret_cast<const float*>(cur + L::kMisc * 64) + 128;
+        const float* gl = CT > 1 ? (buf == sBuf0 ? sGam0 : sGam1) + w * kGamPer
+                                 : reinterpret_cast<const float*>(cur + L::kMisc * 64) + 128;
 #pragma unroll
         for (int a = 0; a < RT; ++a) gam[a] = *reinterpret_cast<const f32x4*>(gl + kSub * a + 4 * lg);
         barrier_lds();
         // U~ = T diag(beta) Y  (rows 16w..)
-        {
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
             f32x4 accU = zero4();
 #pragma unroll
             for (int m = 0; m < G::NKT; ++m)
-                accU = M::mma(ftb[m], M::load(&sYt[li * PY + m * M::KS + lg * M::KW]), accU);
+                accU = M::mma(ftb[m], M::load(&sYt[(kSub * c + li) * PY + m * M::KS + lg * M::KW]), accU);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = kSub * w + 4 * lg + r;
                 const E u = from_f<E>(accU[r]);
-                sUt[li * PY + t] = u;
+                sUt[(kSub * c + li) * PY + t] = u;
                 if constexpr (kMode == kCkpt) {
                     if (t < len) aux.u[o_off + ((int64_t)j * C + t) * rs] = u;
                 }
@@ -1492,17 +1550,21 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         }
         barrier_lds();
         // S <- Diag(Gamma_L) S + K^T U~, then O = P + M U~ (rows 16w..)
-        F bu[G::NKT];
+        F bu[CT][G::NKT];
 #pragma unroll
-        for (int m = 0; m < G::NKT; ++m) bu[m] = M::load(&sUt[li * PY + m * M::KS + lg * M::KW]);
+        for (int c = 0; c < CT; ++c)
 #pragma unroll
-        for (int a = 0; a < RT; ++a) {
-            f32x4 acc = zero4();
+            for (int m = 0; m < G::NKT; ++m) bu[c][m] = M::load(&sUt[(kSub * c + li) * PY + m * M::KS + lg * M::KW]);
 #pragma unroll
-            for (int m = 0; m < G::NKT; ++m) acc = M::mma(fkt[a][m], bu[m], acc);
+        for (int a = 0; a < RT; ++a)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[a][r] = gam[a][r] * S[a][r] + acc[r];
-        }
+            for (int c = 0; c < CT; ++c) {
+                f32x4 acc = zero4();
+#pragma unroll
+                for (int m = 0; m < G::NKT; ++m) acc = M::mma(fkt[a][m], bu[c][m], acc);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) S[a][c][r] = gam[a][r] * S[a][c][r] + acc[r];
+            }
         // kFwdCk: the state after this chunk, when it is a chosen checkpoint;
         // the checkpoints are packed, sequence after sequence
         if constexpr (kMode == kFwdCk) {
@@ -1512,21 +1574,25 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 #pragma unroll
                 for (int a = 0; a < RT; ++a)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) dst[(int64_t)(kSub * (RT * w + a) + 4 * lg + r) * D] = S[a][r];
+                    for (int r = 0; r < 4; ++r) dst[(int64_t)(kSub * (RT * w + a) + 4 * lg + r) * D] = S[a][0][r];
             }
         }
 #pragma unroll
-        for (int m = 0; m < G::NKT; ++m) accO = M::mma(fmm[m], bu[m], accO);
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int m = 0; m < G::NKT; ++m) accO[c] = M::mma(fmm[m], bu[c][m], accO[c]);
         // S^T is last read before the Y barrier of this step; the barrier at
         // the top of the next step publishes the new one.
         put_state();
         if (kMode == kFwd || kMode == kFwdCk || (kMode == kCkpt && o)) {
             E* oj = o + o_off + (int64_t)j * C * rs;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int t = kSub * w + 4 * lg + r;
-                if (t < len) oj[(int64_t)t * rs] = from_f<E>(accO[r]);
-            }
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = kSub * w + 4 * lg + r;
+                    if (t < len) oj[(int64_t)t * rs + kSub * c] = from_f<E>(accO[c][r]);
+                }
         }
     };
 
@@ -1615,7 +1681,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 acc = M::mma(fkt[a][m], bu[m], acc);
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[a][r] = gam[a][r] * S[a][r] + acc[r];
+            for (int r = 0; r < 4; ++r) S[a][0][r] = gam[a][r] * S[a][0][r] + acc[r];
         }
         put_state();
     };
@@ -1633,10 +1699,12 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 #pragma unroll
         for (int a = 0; a < RT; ++a)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int ch = kSub * (RT * w + a) + 4 * lg + r;
-                ST[sbase + (int64_t)ch * D + col0 + li] = S[a][r];
-            }
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int ch = kSub * (RT * w + a) + 4 * lg + r;
+                    ST[sbase + (int64_t)ch * D + col0 + kSub * c + li] = S[a][c][r];
+                }
     }
 }
 
@@ -1654,26 +1722,29 @@ static ChunkOps chunk_ops_bwd(const Plan& p) {
 
 // All chunks, or (equal lengths, nj > 0) chunks [j0, j0 + nj) of every sequence.
 template <typename E, int D, bool kBoth>
-static void launch_prep(const Plan& p, const E* q, hipStream_t st, int32_t j0 = 0, int32_t nj = 0) {
+static void launch_prep(const Plan& p, const E* q, hipStream_t st, int32_t j0 = 0, int32_t nj = 0,
+                        bool xcd_hi = false) {
     if (p.total_tokens <= 0) return;
-    const int32_t grid = nj > 0 ? p.n_seqs * nj : p.max_chunks;
+    int32_t grid = nj > 0 ? p.n_seqs * nj : p.max_chunks;
+    if (xcd_hi) grid = 8 * ((grid + 3) / 4);
     hipLaunchKernelGGL((k_prep<E, D, kBoth>), dim3(grid, p.n_heads), dim3(kThreads), 0, st, q,
                        static_cast<const E*>(p.k), static_cast<const E*>(p.g), static_cast<const E*>(p.beta),
                        p.ws_tab, p.ws_n_chunks, p.cu_seqlens ? (int64_t)0 : p.fixed_len,
                        p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk)), p.n_heads,
-                       chunk_ops(p), kBoth ? chunk_ops_bwd(p) : chunk_ops(p), j0, nj);
+                       chunk_ops(p), kBoth ? chunk_ops_bwd(p) : chunk_ops(p), j0, nj, (int32_t)xcd_hi);
 }
 
 // Chunks [jb, je) of every sequence (default: all of them).
-template <int D, int kMode>
+template <int D, int kMode, int CT = 1>
 static void launch_recur_lds(const Plan& p, const void* v, const float* S0, float* ST, void* o, RecurAux aux,
-                             hipStream_t st, int32_t jb = 0, int32_t je = 0x7fffffff) {
+                             hipStream_t st, int32_t jb = 0, int32_t je = 0x7fffffff, bool xcd_lo = false) {
     const int32_t NH = p.n_seqs * p.n_heads;
     aux.prog = p.ws_prog;
-    hipLaunchKernelGGL((k_recur_lds<D, kMode>), dim3(NH * (D / kSub)), dim3(kRecurLdsThreads), 0, st,
+    hipLaunchKernelGGL((k_recur_lds<D, kMode, CT>), dim3(NH * (D / (kSub * CT)) * (xcd_lo ? 2 : 1)),
+                       dim3(kRecurLdsThreads), 0, st,
                        static_cast<const __bf16*>(v), kMode == kBwd ? chunk_ops_bwd(p) : chunk_ops(p),
                        p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, p.n_heads, S0, ST,
-                       static_cast<__bf16*>(o), aux, jb, je);
+                       static_cast<__bf16*>(o), aux, jb, je, (int32_t)xcd_lo);
 }
 
 void launch_chunk_table(const Plan& p, int32_t chunk, hipStream_t st) {
@@ -1754,21 +1825,38 @@ static bool launch_pipelined(const Plan& p, hipStream_t st) {
     const size_t state = (size_t)p.n_seqs * p.n_heads * D * D;
     if (hipEventRecord(ss->ev[0], st) != hipSuccess || hipStreamWaitEvent(ss->s, ss->ev[0], 0) != hipSuccess)
         return false;
+    // On a device with 8 XCDs (256 CUs: workgroup i runs on XCD i mod 8),
+    // the recurrence keeps XCDs 0..3 and the k_prep beside it XCDs 4..7, so
+    // that the two do not share an L2 (1M tokens, 16 heads: 21.8 -> 18.6 ms
+    // per pass).
+    const bool xcd = ss->cus == 256 && (p.n_seqs * p.n_heads) % 4 == 0 &&
+                     (int64_t)p.n_seqs * p.n_heads * NS <= ss->cus / 2;
     launch_prep<__bf16, D, false>(p, q, ss->s, j0[0], j0[1] - j0[0]);
     (void)hipEventRecord(evp[0], ss->s);
     for (int b = 0; b < nb; ++b) {
         if (b + 1 < nb) {
             if (b >= 1) (void)hipStreamWaitEvent(ss->s, evr[b - 1], 0);
-            launch_prep<__bf16, D, false>(p, q, ss->s, j0[b + 1], j0[b + 2] - j0[b + 1]);
+            launch_prep<__bf16, D, false>(p, q, ss->s, j0[b + 1], j0[b + 2] - j0[b + 1], xcd);
             (void)hipEventRecord(evp[b + 1], ss->s);
         }
         (void)hipStreamWaitEvent(st, evp[b], 0);
         const float* s_in = b == 0 ? p.S0 : p.ws_state2 + (size_t)((b - 1) & 1) * state;
         float* s_out = b == nb - 1 ? p.S_T : p.ws_state2 + (size_t)(b & 1) * state;
-        launch_recur_lds<D, kFwd>(p, p.v, s_in, s_out, p.o, RecurAux{}, st, j0[b], j0[b + 1]);
+        launch_recur_lds<D, kFwd>(p, p.v, s_in, s_out, p.o, RecurAux{}, st, j0[b], j0[b + 1], xcd);
         (void)hipEventRecord(evr[b], st);
     }
     return true;
+}
+
+// CUs of the current device (cached per device; 0 if unknown).
+static int device_cus() {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c == 0 && hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        cache[dev].store(c, std::memory_order_relaxed);
+    return c;
 }
 
 template <typename E, int D, int kMode = kFwd>
@@ -1796,6 +1884,11 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
             launch_recur_lds<D, kFwdCk>(p, p.v, p.S0, p.S_T, p.o,
                                         RecurAux{nullptr, nullptr, nullptr, nullptr, p.S_ckpt, p.ck_every,
                                                  p.ck_slots, p.ws_ck0}, st);
+        else if (kMode == kFwd && (int64_t)NH * (D / kSub) > device_cus())
+            // more 16-column chains than CUs: the throughput of the whole
+            // chip, not one chain's latency, sets the time, and a 32-column
+            // workgroup does two slabs' work per chunk fill
+            launch_recur_lds<D, kFwd, 2>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
         else
             launch_recur_lds<D, kMode>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
     }
