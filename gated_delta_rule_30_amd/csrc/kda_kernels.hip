@@ -1470,7 +1470,9 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 ck[state_swz<D>(kSub * (RT * w + a) + 4 * lg + r, col0 + li)] = from_f<E>(S[a][0][r]);
     };
 
-    auto step = [&](const uint4* buf, int j) {
+    // (the step bodies are forced inline: were one called as a function, its
+    // captures would live in scratch memory)
+    auto step = [&](const uint4* buf, int j) __attribute__((always_inline)) {
         const int len = chunk_len(j);
         const uint4* cur = buf + w * L::kWaveVec;
         if constexpr (kMode == kCkpt) keep_state(j);
@@ -1600,7 +1602,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     // kKg (Q . Gamma)^T and kKt (K . Gamma)^T (channel tiles over tokens),
     // kTb T^T and kMm M^T (rows over tokens); the misc block holds the dO
     // rows, Gamma_L and beta.
-    auto step_bwd = [&](const uint4* buf, int j) {
+    auto step_bwd = [&](const uint4* buf, int j) __attribute__((always_inline)) {
         const int len = chunk_len(j);
         const uint4* cur = buf + w * L::kWaveVec;
         keep_state(j);
@@ -1686,7 +1688,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         put_state();
     };
 
-    auto run = [&](const uint4* buf, int s_) {
+    auto run = [&](const uint4* buf, int s_) __attribute__((always_inline)) {
         if constexpr (kBack) step_bwd(buf, chunk_at(s_));
         else step(buf, chunk_at(s_));
     };
