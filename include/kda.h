@@ -29,9 +29,12 @@
  *     no leakage across sequences.  o has the input dtype (rounded to nearest
  *     even for bf16); S_T is float32.
  *   - The caller owns every buffer, including the workspace.  The library
- *     never allocates, frees or synchronises; work is enqueued on `stream`
- *     and the call returns once it is queued.  There is no global mutable
- *     state; concurrent calls on different workspaces are safe.
+ *     never allocates device memory, frees or synchronises; work is enqueued
+ *     on `stream` and the call returns once it is queued.  Library-held
+ *     state is limited to one side stream per device with its events
+ *     (created on first use, default priority, guarded by a mutex; see
+ *     kda_chunk_fwd) and the array of kda_chunk_fwd_noalloc; concurrent
+ *     calls on different workspaces are safe.
  *   - Argument errors are detected on the host before anything is enqueued;
  *     on error nothing is written.  Value ranges are not checked: log_alpha
  *     must lie in [-5, 0] and beta in [0, 1] for the documented accuracy
@@ -96,7 +99,15 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t n_seqs, int32_
  * runs generic kernels in fp32 arithmetic (fp32 operands, fp32 matrix
  * cores), correct to the same bars but several times slower than the tuned
  * path.  Their workspace is fp32: about
- * 4 (3 d_k + 2 chunk + d_k / chunk) bytes per (token, head). */
+ * 4 (3 d_k + 2 chunk + d_k / chunk) bytes per (token, head).
+ * Launch shapes (results do not depend on them): the sequential pass takes
+ * 32 value columns per workgroup when the (sequence, head) chains at 16
+ * columns would outnumber the device's CUs, else 16.  Equal-length bf16
+ * batches of at least 2048 chunks per sequence whose 16-column chains fill
+ * at most half of the CUs are pipelined by token blocks: the chunk-parallel
+ * stage of the next block runs on the library's side stream beside the
+ * sequential pass of this one (on a 256-CU device on XCDs 4..7 and 0..3
+ * respectively); `stream` waits for all of it before any later work. */
 kda_status kda_chunk_fwd(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
                          int32_t d_k, int32_t d_v, int32_t chunk,
                          const void* q, const void* k, const void* v,
