@@ -959,7 +959,7 @@ __global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, Chu
 // steps of each other; on long sequences a ninth wave per workgroup (the
 // pacing wave) holds back a workgroup that runs too far ahead.
 //
-// Slab width: 16 value columns (CT = 1), or 32 (CT = 2, plain forward only)
+// Slab width: 16 value columns (CT = 1), or 32 (CT = 2, forward and transition)
 // with each compute wave owning two 16-column tiles and every A fragment it
 // reads from LDS serving both.  A chunk's operand fill is the same 64 KB
 // either way, so CT = 2 does twice the work per fill: the step is longer
@@ -1095,7 +1095,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     static_assert(G::VPL == G::NKC && G::NVT == G::NKT, "one 16-byte vector per bf16 fragment");
     static_assert(kRecurWaves == kNSub, "one compute wave per 16-token row tile");
     static_assert(G::NKT == 2, "the zero halves are the two 32-token halves of a 64-token chunk");
-    static_assert(CT == 1 || (CT == 2 && kMode == kFwd), "two column tiles per wave: plain forward only");
+    static_assert(CT == 1 || (CT == 2 && (kMode == kFwd || kMode == kTrans)),
+                  "two column tiles per wave: forward and transition passes only");
     constexpr int C = kChunk, CPL = G::CPL, RT = L::RT;
     constexpr int SW = kSub * CT;      // slab width (value columns): CT 16-column tiles per compute wave
     constexpr int NS = D / SW;         // slabs per head
@@ -1886,11 +1887,11 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
             launch_recur_lds<D, kFwdCk>(p, p.v, p.S0, p.S_T, p.o,
                                         RecurAux{nullptr, nullptr, nullptr, nullptr, p.S_ckpt, p.ck_every,
                                                  p.ck_slots, p.ws_ck0}, st);
-        else if (kMode == kFwd && (int64_t)NH * (D / kSub) > device_cus())
+        else if ((kMode == kFwd || kMode == kTrans) && (int64_t)NH * (D / kSub) > device_cus())
             // more 16-column chains than CUs: the throughput of the whole
             // chip, not one chain's latency, sets the time, and a 32-column
             // workgroup does two slabs' work per chunk fill
-            launch_recur_lds<D, kFwd, 2>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
+            launch_recur_lds<D, kMode == kTrans ? kTrans : kFwd, 2>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
         else
             launch_recur_lds<D, kMode>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
     }

@@ -149,6 +149,35 @@ def test_many_sequences(torch_dev):
     _check(inp, o, ST, what="many sequences")
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_wide_slabs_match_narrow(torch_dev, d):
+    """A batch whose 16-column recurrence chains outnumber the CUs runs the
+    32-column workgroups; three of its sequences on their own run the
+    16-column ones.  Each column's arithmetic is the same in both, so o and
+    S_T of those sequences must agree bit for bit; the whole batch is also
+    held to the oracle.  Lengths include empty, single-token, sub-tile and
+    chunk-boundary sequences."""
+    torch, dev = torch_dev
+    import gated_delta_rule_30_amd as kda
+    lengths = [int(x) for x in np.random.default_rng(23).integers(0, 301, size=40)]
+    lengths[:10] = [130, 0, 65, 1, 15, 16, 63, 64, 17, 300]
+    H = 4
+    spec = ki.custom("wide", "bf16", lengths, H, d, s0_std=0.3, varlen=True, seed=8)
+    inp = ki.generate_numpy(spec)
+    _say("wide slabs: N=%d H=%d d=%d (batch), sequences 0..2 alone" % (len(lengths), H, d))
+    q, k, v, beta, g = (_to_dev(torch, dev, a, "bf16") for a in (inp.q, inp.k, inp.v, inp.beta, inp.g))
+    S0 = torch.from_numpy(inp.S0).to(dev)
+    cu = torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
+    o_all, S_all = kda.chunk_fwd(q, k, v, beta, g, S0=S0, cu_seqlens=cu)
+    n3 = int(inp.cu_seqlens[3])
+    o_3, S_3 = kda.chunk_fwd(q[:n3].contiguous(), k[:n3].contiguous(), v[:n3].contiguous(), beta[:n3].contiguous(),
+                             g[:n3].contiguous(), S0=S0[:3].contiguous(), cu_seqlens=cu[:4].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(o_all[:n3], o_3), "o differs between 32- and 16-column workgroups"
+    assert torch.equal(S_all[:3], S_3), "S_T differs between 32- and 16-column workgroups"
+    _check(inp, o_all.float().cpu().numpy(), S_all.cpu().numpy(), what="wide slabs d=%d" % d)
+
+
 def test_s0_null_equals_zeros(torch_dev):
     torch, dev = torch_dev
     import gated_delta_rule_30_amd as kda

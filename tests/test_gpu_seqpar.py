@@ -34,9 +34,16 @@ def _bf(torch, dev, x):
 # With the workloads' decay (mean log-decay -2.5) a transition over more than
 # a few tokens is ~exp(-2.5 T) and compares as zero; `weak` rescales the
 # log-decay into (-0.025, 0) so the products of (I - beta k k^T) stay O(1).
+# 40 sequences x 4 heads: more 16-column chains than CUs, so the transition
+# runs on 32-column workgroups
+MANY = [int(x) for x in np.random.default_rng(31).integers(0, 200, size=40)]
+
+
 @pytest.mark.parametrize("lengths,H,d,weak", [([300], 2, 128, True), ([150, 77, 0, 64, 200], 3, 64, True),
-                                              ([1, 65], 2, 128, False), ([300], 2, 128, False)],
-                         ids=["one-seq-d128-weak", "varlen-d64-weak", "tiny-d128", "one-seq-d128"])
+                                              ([1, 65], 2, 128, False), ([300], 2, 128, False),
+                                              (MANY, 4, 128, True), (MANY, 4, 64, True)],
+                         ids=["one-seq-d128-weak", "varlen-d64-weak", "tiny-d128", "one-seq-d128",
+                              "many-d128-weak", "many-d64-weak"])
 def test_transition_matches_oracle(torch_dev, lengths, H, d, weak):
     """P = prod (I - beta k k^T) Diag(alpha): the oracle's recurrence with
     v = 0 from S0 = I gives it exactly (its S_T)."""
