@@ -501,8 +501,13 @@ def main():
             ent["hbm_bytes_counted"] = traffic_for(k_, wkey)
             ent["mfma_counters"] = mfma_counters_for(k_, wkey)
         if k_ == "k_recur":
+            # the library's launch rule: 32-column workgroups when the
+            # 16-column (sequence, head) chains outnumber the CUs
+            cus = torch.cuda.get_device_properties(dev).multi_processor_count
+            width = 32 if (not generic and spec.dtype == "bf16" and spec.n_seqs * H * dv // 16 > cus) else 16
+            ent["slab_columns"] = width
             ent["limiter"] = "the serial chain: %d chunk steps per (sequence, head), each fed its chunk's " \
-                             "operands from L2 into every 16-column slab workgroup" % n_chunk_steps
+                             "operands from L2 into every %d-column slab workgroup" % (n_chunk_steps, width)
             ent["us_per_chunk_step"] = stage_ms[k_] * 1e3 / n_chunk_steps
         per_kernel[k_] = ent
 
