@@ -959,16 +959,19 @@ __global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, Chu
 // steps of each other; on long sequences a ninth wave per workgroup (the
 // pacing wave) holds back a workgroup that runs too far ahead.
 //
-// Slab width: 16 value columns (CT = 1), or 32 (CT = 2, forward and transition)
-// with each compute wave owning two 16-column tiles and every A fragment it
-// reads from LDS serving both.  A chunk's operand fill is the same 64 KB
-// either way, so CT = 2 does twice the work per fill: the step is longer
-// (about 1.55 against 1.02 us at d = 128) but the work per CU and step is
-// doubled, which pays when more 16-column chains exist than CUs (many
-// sequences or heads: the whole chip's throughput sets the time), and not
-// when each chain has a CU to itself (its latency sets the time).  At
-// CT = 2 the value rows of a region fill its misc block, so Gamma_L comes in
-// by one more (4-byte) direct load per region into sGam0 / sGam1.
+// Slab width: 16 value columns, or 32 (forward and transition passes) with
+// XW = 2 groups of four compute waves, group x owning column tile x of the
+// slab; both groups read the same operand fill.  A chunk's fill is the same
+// 64 KB either way, so a 32-column workgroup does twice the work per fill:
+// its step is longer (about 1.3 against 1.02 us at d = 128) but it does the
+// work of two 16-column ones, which pays when more 16-column chains exist
+// than CUs (many sequences or heads: the whole chip's throughput sets the
+// time), and not when each chain has a CU to itself (its latency sets the
+// time).  The template also takes CT column tiles per compute wave; every
+// launch uses CT = 1 (one wave group taking both tiles, CT = 2, measured
+// about 1.55 us per step).  With 32 columns the value rows of a region fill
+// its misc block, so Gamma_L comes in by one more (4-byte) direct load per
+// region into sGam0 / sGam1.
 #define KDA_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
@@ -1002,7 +1005,6 @@ constexpr int kRecurWaves = 4;                              // compute waves
 constexpr int kProdPerWave = 1;                             // producer waves per compute wave
 constexpr int kProducers = kRecurWaves * kProdPerWave;
 constexpr int kPacerWave = kRecurWaves + kProducers;        // the pacing wave (see k_recur_lds)
-constexpr int kRecurLdsThreads = (kRecurWaves + kProducers + 1) * 64;
 
 // Buffer layout: one region per compute wave w, in 1 KB blocks (64 lanes x
 // 16 bytes: the fragment-major tiles of k_prep copied as they are):
@@ -1079,8 +1081,8 @@ struct ZeroHalf {
     __device__ static bool zero(int region) { return kMode == kBwd ? region >= 2 : region < 2; }
 };
 
-template <int D, int kMode, int CT>
-__global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
+template <int D, int kMode, int CT, int XW = 1>
+__global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_recur_lds(
     const __bf16* __restrict__ v, ChunkOps ops, const int32_t* __restrict__ cu, int64_t total_tokens,
     int64_t fixed_len, const int32_t* __restrict__ seq_chunk0, int32_t NH, int32_t H, const float* __restrict__ S0,
     float* __restrict__ ST, __bf16* __restrict__ o, RecurAux aux, int32_t jb, int32_t je, int32_t xcd_lo) {
@@ -1095,10 +1097,15 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     static_assert(G::VPL == G::NKC && G::NVT == G::NKT, "one 16-byte vector per bf16 fragment");
     static_assert(kRecurWaves == kNSub, "one compute wave per 16-token row tile");
     static_assert(G::NKT == 2, "the zero halves are the two 32-token halves of a 64-token chunk");
-    static_assert(CT == 1 || (CT == 2 && (kMode == kFwd || kMode == kTrans)),
-                  "two column tiles per wave: forward and transition passes only");
+    static_assert(CT * XW == 1 || (CT * XW == 2 && (kMode == kFwd || kMode == kTrans)),
+                  "32-column slabs: forward and transition passes only");
     constexpr int C = kChunk, CPL = G::CPL, RT = L::RT;
-    constexpr int SW = kSub * CT;      // slab width (value columns): CT 16-column tiles per compute wave
+    // Compute waves: XW groups of kRecurWaves, group x owning column tiles
+    // x CT .. x CT + CT - 1 of the slab (wave w: row tile w mod 4); then the
+    // producer waves, then the pacing wave.
+    constexpr int NCW = kRecurWaves * XW;
+    constexpr int kPacer = NCW + kProducers;
+    constexpr int SW = kSub * CT * XW; // slab width (value columns)
     constexpr int NS = D / SW;         // slabs per head
     constexpr int PS = D + 8;          // pitch of S^T      [col][channel]
     constexpr int PY = C + 8;          // pitch of Y^T, U~^T [col][token]
@@ -1108,12 +1115,12 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     __shared__ __attribute__((aligned(16))) E sYt[SW * PY];
     __shared__ __attribute__((aligned(16))) E sUt[SW * PY];
     __shared__ unsigned sTouch[kProducers * 64];   // warm-up loads land here, never read
-    // CT = 2: the value rows fill the misc block, so Gamma_L of each region's
+    // 32-column slabs: the value rows fill the misc block, so Gamma_L of each region's
     // 16 RT channels comes in by 4-byte direct loads into these (one per
     // buffer; sized so that a load from all 64 lanes at the last region's
     // base would still stay inside).
     constexpr int kGamPer = 16 * RT;
-    constexpr int kGamLen = CT > 1 ? (kRecurWaves - 1) * kGamPer + 64 : 1;
+    constexpr int kGamLen = SW > kSub ? (kRecurWaves - 1) * kGamPer + 64 : 1;
     __shared__ __attribute__((aligned(16))) float sGam0[kGamLen];
     __shared__ __attribute__((aligned(16))) float sGam1[kGamLen];
 
@@ -1160,7 +1167,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     // chunk processed at step s (the backward pass walks the chunks last to first)
     auto chunk_at = [&](int s_) -> int { return kBack ? j_lo + ns - 1 - s_ : j_lo + s_; };
 
-    if (w == kPacerWave) {
+    if (w == kPacer) {
         // ------------------------------------------------ pacing wave
         // The slab workgroups of a head share their chunk operands through
         // L2: each warms only its share of the lines ahead of use.  One that
@@ -1219,9 +1226,9 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         post(0x7fffffff);
         return;
     }
-    if (w >= kRecurWaves) {
+    if (w >= NCW) {
         // ------------------------------------------------ producer waves
-        const int pw = w - kRecurWaves;
+        const int pw = w - NCW;
         const int cw = pw / kProdPerWave;   // the compute wave whose operands this wave loads
         const int part = pw % kProdPerWave; // which of its blocks: part, part + kProdPerWave, ...
         const E* qg = static_cast<const E*>(ops.Qg) + cb * C * D + lane * G::EPV;
@@ -1229,7 +1236,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         const E* kt = static_cast<const E*>(ops.KhT) + cb * D * C + lane * G::EPV;
         const E* tb = static_cast<const E*>(ops.TB) + cb * C * C + lane * G::EPV;
         const E* mm = static_cast<const E*>(ops.Mm) + cb * C * C + lane * G::EPV;
-        constexpr int kVL = 2 * CT;   // lanes per value row of the slab (16 bytes each)
+        constexpr int kVL = SW / 8;   // lanes per value row of the slab (16 bytes each)
         const E* vv = v + (s_start * H + h) * D + col0 + 8 * (lane % kVL);
         const int gi = (lane >= 32 && lane < 32 + 4 * RT) ? lane - 32 : 0;
         const float* gm = ops.gam + cb * D + 4 * gi;
@@ -1260,7 +1267,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             else {
                 int row = kSub * cw + lane / kVL;
                 row = row < len ? row : len - 1;
-                const void* misc = (lane < 32 * CT && !kTransition)
+                const void* misc = (lane < 2 * SW && !kTransition)
                                        ? static_cast<const void*>(vv + ((int64_t)j * C + row) * rs)
                                    : is_bet ? static_cast<const void*>(bt + (int64_t)j * C)
                                             : static_cast<const void*>(gm + (int64_t)j * D + kSub * RT * cw);
@@ -1291,7 +1298,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             static_for<kProdPerWave>([&](auto p_c) {
                 if (part == decltype(p_c)::value) issue_part(p_c, lo_c, hi_c, dst, j, len);
             });
-            if constexpr (CT > 1 && decltype(hi_c)::value == kDma) {
+            if constexpr (SW > kSub && decltype(hi_c)::value == kDma) {
                 // Gamma_L of this region's channels (one more load per chunk)
                 float* sg = (buf == sBuf0 ? sGam0 : sGam1) + cw * kGamPer;
                 if (lane < kGamPer)
@@ -1380,7 +1387,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         // Loads per chunk fill of this producer: kDma, or kDma - 2 when its
         // region skips the zero halves of the two triangular tiles.
         const bool lean = Z::zero(cw);
-        constexpr int kFill = kDma + (CT > 1 ? 1 : 0);   // loads per chunk fill (CT = 2: Gamma_L apart)
+        constexpr int kFill = kDma + (SW > kSub ? 1 : 0);   // loads per chunk fill (32 columns: Gamma_L apart)
         auto wait_fill = [&]() {
             if (lean) wait_counts<2 * kTouch + kFill - 2, 15>();
             else wait_counts<2 * kTouch + kFill, 15>();
@@ -1432,11 +1439,13 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     }
 
     // ---------------------------------------------------- compute waves
-    const int64_t o_off = (s_start * H + h) * D + col0 + li;
+    // row tile rt of the chunk; first column cb0 of this wave within the slab
+    const int rt = w % kRecurWaves, cb0 = kSub * CT * (w / kRecurWaves);
+    const int64_t o_off = (s_start * H + h) * D + col0 + cb0 + li;
     // kFwdCk: slot of this sequence's first checkpoint
     int32_t ck_first = 0;
     if constexpr (kMode == kFwdCk) ck_first = cu ? aux.ck0[n] : n * (nch / aux.every);
-    // S[a][c][r] = state[channel 16*(RT*w + a) + 4*lg + r][column col0 + 16*c + li]
+    // S[a][c][r] = state[channel 16*(RT*rt + a) + 4*lg + r][column col0 + cb0 + 16*c + li]
     // (kBwd: the state gradient); c is the wave's column tile (CT of them)
     f32x4 S[RT][CT];
     const int64_t sbase = ((int64_t)n * H + h) * D * D;
@@ -1446,7 +1455,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         for (int c = 0; c < CT; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int ch = kSub * (RT * w + a) + 4 * lg + r, col = col0 + kSub * c + li;
+                const int ch = kSub * (RT * rt + a) + 4 * lg + r, col = col0 + cb0 + kSub * c + li;
                 if constexpr (kTransition) S[a][c][r] = ch == col ? 1.f : 0.f;
                 else S[a][c][r] = S0 ? S0[sbase + (int64_t)ch * D + col] : 0.f;
             }
@@ -1457,7 +1466,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             for (int c = 0; c < CT; ++c)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    sSt[(kSub * c + li) * PS + kSub * (RT * w + a) + 4 * lg + r] = from_f<E>(S[a][c][r]);
+                    sSt[(cb0 + kSub * c + li) * PS + kSub * (RT * rt + a) + 4 * lg + r] = from_f<E>(S[a][c][r]);
     };
     put_state();
     // kCkpt / kBwd: this slab's columns of the state (gradient) as chunk j
@@ -1468,14 +1477,14 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         for (int a = 0; a < RT; ++a)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                ck[state_swz<D>(kSub * (RT * w + a) + 4 * lg + r, col0 + li)] = from_f<E>(S[a][0][r]);
+                ck[state_swz<D>(kSub * (RT * rt + a) + 4 * lg + r, col0 + cb0 + li)] = from_f<E>(S[a][0][r]);
     };
 
     // (the step bodies are forced inline: were one called as a function, its
     // captures would live in scratch memory)
     auto step = [&](const uint4* buf, int j) __attribute__((always_inline)) {
         const int len = chunk_len(j);
-        const uint4* cur = buf + w * L::kWaveVec;
+        const uint4* cur = buf + rt * L::kWaveVec;
         if constexpr (kMode == kCkpt) keep_state(j);
         barrier_lds();   // chunk j's operands are in `buf`; S^T of the previous step is in LDS
         const F* fr = reinterpret_cast<const F*>(cur) + lane;
@@ -1494,7 +1503,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         for (int m = 0; m < G::NKC; ++m)
 #pragma unroll
             for (int c = 0; c < CT; ++c) {
-                const F bs = M::load(&sSt[(kSub * c + li) * PS + lg * CPL + m * M::KW]);
+                const F bs = M::load(&sSt[(cb0 + kSub * c + li) * PS + lg * CPL + m * M::KW]);
                 accX[c] = M::mma(fk[m], bs, accX[c]);
                 accO[c] = M::mma(fq[m], bs, accO[c]);
             }
@@ -1504,16 +1513,16 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         for (int c = 0; c < CT; ++c)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = kSub * w + 4 * lg + r;
-                const float vv = kTransition ? 0.f : to_f(vrows[(4 * lg + r) * SW + kSub * c + li]);
+                const int t = kSub * rt + 4 * lg + r;
+                const float vv = kTransition ? 0.f : to_f(vrows[(4 * lg + r) * SW + cb0 + kSub * c + li]);
                 const E y = from_f<E>(t < len ? vv - accX[c][r] : 0.f);
-                sYt[(kSub * c + li) * PY + t] = y;
+                sYt[(cb0 + kSub * c + li) * PY + t] = y;
                 if constexpr (kMode == kCkpt) {
                     if (t < len) aux.y[o_off + ((int64_t)j * C + t) * rs] = y;
                 }
             }
         F ftb[G::NKT], fmm[G::NKT], fkt[RT][G::NKT];
-        const bool zh = Z::zero(w);
+        const bool zh = Z::zero(rt);
 #pragma unroll
         for (int m = 0; m < G::NKT; ++m) {
             if (m == Z::kHalf && zh) {
@@ -1529,7 +1538,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 #pragma unroll
             for (int m = 0; m < G::NKT; ++m) fkt[a][m] = fr[(L::kKt + a * G::NKT + m) * 64];
         f32x4 gam[RT];
-        const float* gl = CT > 1 ? (buf == sBuf0 ? sGam0 : sGam1) + w * kGamPer
+        const float* gl = SW > kSub ? (buf == sBuf0 ? sGam0 : sGam1) + rt * kGamPer
                                  : reinterpret_cast<const float*>(cur + L::kMisc * 64) + 128;
 #pragma unroll
         for (int a = 0; a < RT; ++a) gam[a] = *reinterpret_cast<const f32x4*>(gl + kSub * a + 4 * lg);
@@ -1540,12 +1549,12 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             f32x4 accU = zero4();
 #pragma unroll
             for (int m = 0; m < G::NKT; ++m)
-                accU = M::mma(ftb[m], M::load(&sYt[(kSub * c + li) * PY + m * M::KS + lg * M::KW]), accU);
+                accU = M::mma(ftb[m], M::load(&sYt[(cb0 + kSub * c + li) * PY + m * M::KS + lg * M::KW]), accU);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = kSub * w + 4 * lg + r;
+                const int t = kSub * rt + 4 * lg + r;
                 const E u = from_f<E>(accU[r]);
-                sUt[(kSub * c + li) * PY + t] = u;
+                sUt[(cb0 + kSub * c + li) * PY + t] = u;
                 if constexpr (kMode == kCkpt) {
                     if (t < len) aux.u[o_off + ((int64_t)j * C + t) * rs] = u;
                 }
@@ -1557,7 +1566,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
 #pragma unroll
         for (int c = 0; c < CT; ++c)
 #pragma unroll
-            for (int m = 0; m < G::NKT; ++m) bu[c][m] = M::load(&sUt[(kSub * c + li) * PY + m * M::KS + lg * M::KW]);
+            for (int m = 0; m < G::NKT; ++m) bu[c][m] = M::load(&sUt[(cb0 + kSub * c + li) * PY + m * M::KS + lg * M::KW]);
 #pragma unroll
         for (int a = 0; a < RT; ++a)
 #pragma unroll
@@ -1573,11 +1582,11 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         if constexpr (kMode == kFwdCk) {
             const int32_t slot = ck_first + (j + 1) / aux.every - 1;
             if ((j + 1) % aux.every == 0 && slot < aux.n_slots) {
-                float* dst = aux.sck + ((int64_t)slot * H + h) * D * D + col0 + li;
+                float* dst = aux.sck + ((int64_t)slot * H + h) * D * D + col0 + cb0 + li;
 #pragma unroll
                 for (int a = 0; a < RT; ++a)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) dst[(int64_t)(kSub * (RT * w + a) + 4 * lg + r) * D] = S[a][0][r];
+                    for (int r = 0; r < 4; ++r) dst[(int64_t)(kSub * (RT * rt + a) + 4 * lg + r) * D] = S[a][0][r];
             }
         }
 #pragma unroll
@@ -1593,7 +1602,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             for (int c = 0; c < CT; ++c)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int t = kSub * w + 4 * lg + r;
+                    const int t = kSub * rt + 4 * lg + r;
                     if (t < len) oj[(int64_t)t * rs + kSub * c] = from_f<E>(accO[c][r]);
                 }
         }
@@ -1605,7 +1614,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
     // rows, Gamma_L and beta.
     auto step_bwd = [&](const uint4* buf, int j) __attribute__((always_inline)) {
         const int len = chunk_len(j);
-        const uint4* cur = buf + w * L::kWaveVec;
+        const uint4* cur = buf + rt * L::kWaveVec;
         keep_state(j);
         barrier_lds();   // chunk j's operands are in `buf`; dS'^T is in LDS
         const F* fr = reinterpret_cast<const F*>(cur) + lane;
@@ -1619,11 +1628,11 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         for (int m = 0; m < G::NKT; ++m) {
             const E* rows = reinterpret_cast<const E*>(buf + (2 * m + (lg >> 1)) * L::kWaveVec + L::kMisc * 64);
 #pragma unroll
-            for (int e = 0; e < M::KW; ++e) bo[m][e] = rows[(8 * (lg & 1) + e) * SW + li];
+            for (int e = 0; e < M::KW; ++e) bo[m][e] = rows[(8 * (lg & 1) + e) * SW + cb0 + li];
         }
         F fmt[G::NKT];
 #pragma unroll
-        for (int m = 0; m < G::NKT; ++m) fmt[m] = (m == Z::kHalf && Z::zero(w)) ? F{} : fr[(L::kMm + m) * 64];
+        for (int m = 0; m < G::NKT; ++m) fmt[m] = (m == Z::kHalf && Z::zero(rt)) ? F{} : fr[(L::kMm + m) * 64];
         // R = K^ dS' + M^T dO  (rows 16w..), transposed to LDS
         f32x4 accR = zero4();
 #pragma unroll
@@ -1633,12 +1642,12 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
         for (int m = 0; m < G::NKT; ++m) accR = M::mma(fmt[m], bo[m], accR);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = kSub * w + 4 * lg + r;
+            const int t = kSub * rt + 4 * lg + r;
             sYt[li * PY + t] = from_f<E>(t < len ? accR[r] : 0.f);
         }
         F ftt[G::NKT], fqt[RT][G::NKT], fkt[RT][G::NKT];
 #pragma unroll
-        for (int m = 0; m < G::NKT; ++m) ftt[m] = (m == Z::kHalf && Z::zero(w)) ? F{} : fr[(L::kTb + m) * 64];
+        for (int m = 0; m < G::NKT; ++m) ftt[m] = (m == Z::kHalf && Z::zero(rt)) ? F{} : fr[(L::kTb + m) * 64];
 #pragma unroll
         for (int a = 0; a < RT; ++a)
 #pragma unroll
@@ -1660,7 +1669,7 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
                 accZ = M::mma(ftt[m], M::load(&sYt[li * PY + m * M::KS + lg * M::KW]), accZ);
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = kSub * w + 4 * lg + r;
+                const int t = kSub * rt + 4 * lg + r;
                 const float dy = bet[r] * accZ[r];
                 if (t < len) {
                     const int64_t at = o_off + ((int64_t)j * C + t) * rs;
@@ -1705,8 +1714,8 @@ __global__ __launch_bounds__(kRecurLdsThreads) void k_recur_lds(
             for (int c = 0; c < CT; ++c)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int ch = kSub * (RT * w + a) + 4 * lg + r;
-                    ST[sbase + (int64_t)ch * D + col0 + kSub * c + li] = S[a][c][r];
+                    const int ch = kSub * (RT * rt + a) + 4 * lg + r;
+                    ST[sbase + (int64_t)ch * D + col0 + cb0 + kSub * c + li] = S[a][c][r];
                 }
     }
 }
@@ -1738,13 +1747,13 @@ static void launch_prep(const Plan& p, const E* q, hipStream_t st, int32_t j0 = 
 }
 
 // Chunks [jb, je) of every sequence (default: all of them).
-template <int D, int kMode, int CT = 1>
+template <int D, int kMode, int CT = 1, int XW = 1>
 static void launch_recur_lds(const Plan& p, const void* v, const float* S0, float* ST, void* o, RecurAux aux,
                              hipStream_t st, int32_t jb = 0, int32_t je = 0x7fffffff, bool xcd_lo = false) {
     const int32_t NH = p.n_seqs * p.n_heads;
     aux.prog = p.ws_prog;
-    hipLaunchKernelGGL((k_recur_lds<D, kMode, CT>), dim3(NH * (D / (kSub * CT)) * (xcd_lo ? 2 : 1)),
-                       dim3(kRecurLdsThreads), 0, st,
+    hipLaunchKernelGGL((k_recur_lds<D, kMode, CT, XW>), dim3(NH * (D / (kSub * CT * XW)) * (xcd_lo ? 2 : 1)),
+                       dim3((kRecurWaves * XW + kProducers + 1) * 64), 0, st,
                        static_cast<const __bf16*>(v), kMode == kBwd ? chunk_ops_bwd(p) : chunk_ops(p),
                        p.cu_seqlens, p.total_tokens, p.fixed_len, p.ws_seq_chunk0, NH, p.n_heads, S0, ST,
                        static_cast<__bf16*>(o), aux, jb, je, (int32_t)xcd_lo);
@@ -1905,8 +1914,9 @@ static hipError_t launch_all(const Plan& p, hipStream_t st, hipEvent_t* ev) {
         else if ((kMode == kFwd || kMode == kTrans) && (int64_t)NH * (D / kSub) > device_cus())
             // more 16-column chains than CUs: the throughput of the whole
             // chip, not one chain's latency, sets the time, and a 32-column
-            // workgroup does two slabs' work per chunk fill
-            launch_recur_lds<D, kMode == kTrans ? kTrans : kFwd, 2>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
+            // workgroup (two groups of compute waves) does two slabs' work
+            // per chunk fill
+            launch_recur_lds<D, kMode == kTrans ? kTrans : kFwd, 1, 2>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
         else
             launch_recur_lds<D, kMode>(p, p.v, p.S0, p.S_T, p.o, RecurAux{}, st);
     }
