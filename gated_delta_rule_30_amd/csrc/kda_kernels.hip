@@ -32,10 +32,11 @@
 //   k_chunk_table : chunk list from cu_seqlens (device side, no host sync)
 //   k_prep        : per (chunk, head), chunk-parallel: decay cumsum, A and M
 //                   by sub-tiled MFMA, T = (I + A)^-1 in LDS (fp32); writes
-//                   T diag(beta) and M
-//   k_recur       : per (sequence, head, 16-column slab of S), sequential over
-//                   the chunks: decay cumsum, Q . Gamma, K . Gamma,
-//                   K . exp(b_L - b), the state step and the chunk output
+//                   the chunk's operands Q . Gamma, K . Gamma,
+//                   (K . exp(b_L - b))^T, T diag(beta), M and Gamma_L
+//   k_recur_lds   : (bf16) per (sequence, head, slab of 16 or 32 columns of
+//   / k_recur       S), sequential over the chunks: the state step and the
+//                   chunk output from those operands (fp32 at d = 64: k_recur)
 //
 // Lane geometry shared by both kernels.  Wave w of a 256-thread workgroup
 // owns token rows 16w .. 16w+15 of the chunk; lane = 16 * lg + li holds token
@@ -930,7 +931,7 @@ __global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, Chu
 // bf16 form of k_recur with producer waves.  The chunk operands travel
 // global -> LDS by direct loads (global_load_lds_dwordx4: each lane moves 16
 // bytes to LDS at M0 + 16 * lane), issued by producer waves that do nothing
-// else, one per compute wave.  A wave issues its instructions in order, so a
+// else, one per 16-token row tile (four).  A wave issues its instructions in order, so a
 // compute wave that issued its own share of the loads would sit behind them
 // for as long as the CU needs to stream a chunk's operands; with producers
 // the streaming overlaps the compute waves' matrix work.  (A single producer
@@ -956,7 +957,7 @@ __global__ __launch_bounds__(kThreads) void k_recur(const E* __restrict__ v, Chu
 // slab later hit L2 rather than HBM.  Landing in LDS, these loads hold no
 // registers and nothing waits for them except the counted waits below.
 // Because of that sharing the slabs of a head have to stay within a few
-// steps of each other; on long sequences a ninth wave per workgroup (the
+// steps of each other; on long sequences the workgroup's last wave (the
 // pacing wave) holds back a workgroup that runs too far ahead.
 //
 // Slab width: 16 value columns, or 32 (forward and transition passes) with
@@ -1001,10 +1002,9 @@ __device__ inline void static_for(Fn&& f) {
     }
 }
 
-constexpr int kRecurWaves = 4;                              // compute waves
-constexpr int kProdPerWave = 1;                             // producer waves per compute wave
+constexpr int kRecurWaves = 4;                              // compute waves per group (one per row tile)
+constexpr int kProdPerWave = 1;                             // producer waves per row tile
 constexpr int kProducers = kRecurWaves * kProdPerWave;
-constexpr int kPacerWave = kRecurWaves + kProducers;        // the pacing wave (see k_recur_lds)
 
 // Buffer layout: one region per compute wave w, in 1 KB blocks (64 lanes x
 // 16 bytes: the fragment-major tiles of k_prep copied as they are):
