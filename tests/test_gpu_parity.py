@@ -178,6 +178,21 @@ def test_wide_slabs_match_narrow(torch_dev, d):
     _check(inp, o_all.float().cpu().numpy(), S_all.cpu().numpy(), what="wide slabs d=%d" % d)
 
 
+def test_wide_slabs_paced_long_sequence(torch_dev):
+    """32-column workgroups (40 sequences x 4 heads: more 16-column chains
+    than CUs) with one sequence of 140,000 tokens (2188 chunks), whose
+    workgroups run the pacing wave: every (sequence, head) slice against the
+    oracle."""
+    torch, dev = torch_dev
+    lengths = [int(x) for x in np.random.default_rng(29).integers(0, 400, size=40)]
+    lengths[7] = 140000
+    spec = ki.custom("wide paced", "bf16", lengths, 4, 128, s0_std=0.3, varlen=True, seed=12)
+    inp = ki.generate_numpy(spec)
+    _say("wide slabs with a paced sequence: N=%d T=%d H=4 d=128" % (len(lengths), sum(lengths)))
+    o, ST = _run_numpy_inputs(torch, dev, inp)
+    _check(inp, o, ST, what="wide slabs, paced long sequence")
+
+
 def test_s0_null_equals_zeros(torch_dev):
     torch, dev = torch_dev
     import gated_delta_rule_30_amd as kda
