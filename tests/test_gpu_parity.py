@@ -376,9 +376,11 @@ def test_pipelined_forward(torch_dev, lengths, H, d, s0):
     """Equal-length sequences of more than 2048 chunks whose recurrence fills
     at most half of the CUs take the pipelined path (k_prep of the next token
     block on a side stream while the recurrence works on this one, state
-    handed between blocks in fp32): every (sequence, head) slice against the
-    oracle, and bit for bit equal to the same kernels run one after another
-    (the measurement entry point does not pipeline)."""
+    handed between blocks in fp32; with 4 sequence-heads, the first case, on
+    a 256-CU device the recurrence holds XCDs 0..3 and k_prep XCDs 4..7; the
+    second, 3 sequence-heads, shares them): every (sequence, head) slice
+    against the oracle, and bit for bit equal to the same kernels run one
+    after another (the measurement entry point does not pipeline)."""
     torch, dev = torch_dev
     import gated_delta_rule_30_amd as kda
     spec = ki.custom("pipe", "bf16", list(lengths), H, d, s0_std=s0, varlen=False, seed=21)
