@@ -82,7 +82,7 @@ def _load():
                                             P, P, P, P, P, P, P, P, P, P, SZ, P, SZ, P]
         lib.kda_chunk_fwd_train.restype = ctypes.c_int
         lib.kda_chunk_bwd_ctx.argtypes = [ctypes.c_int, I64, I32, I32, I32, I32, I32,
-                                          P, P, P, P, P, P, SZ, P, P, P, P, P, P, P, P, P, SZ, P]
+                                          P, P, P, P, P, P, P, SZ, P, P, P, P, P, P, P, P, P, SZ, P]
         lib.kda_chunk_bwd_ctx.restype = ctypes.c_int
         lib.kda_output_gate.argtypes = [ctypes.c_int, I64, I32, P, P, P, ctypes.c_float, P, P]
         lib.kda_output_gate.restype = ctypes.c_int
@@ -393,8 +393,9 @@ def chunk_bwd(q, k, v, beta, log_alpha, dO, S0=None, dS_T=None, cu_seqlens=None,
     if context is not None:
         if _stage_ms is not None:
             raise ValueError("the context form has no per-kernel measurement entry point")
-        code = lib.kda_chunk_bwd_ctx(dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(beta), _ptr(log_alpha),
-                                     _ptr(cu_seqlens), _ptr(context), _nbytes(context), _ptr(dO), _ptr(dS_T),
+        code = lib.kda_chunk_bwd_ctx(dt, T, N, H, dk, dv, chunk, _ptr(q), _ptr(k), _ptr(v), _ptr(beta),
+                                     _ptr(log_alpha), _ptr(cu_seqlens), _ptr(context), _nbytes(context), _ptr(dO),
+                                     _ptr(dS_T),
                                      _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dbeta"]),
                                      _ptr(out["dg"]), _ptr(out["dS0"]), _ptr(workspace),
                                      _nbytes(workspace), ctypes.c_void_p(stream))

@@ -55,7 +55,6 @@ size_t carve_workspace(Plan* p, void* base) {
         p->ws_bQgT = take(es * mc * H * D * kChunkTokens);
         p->ws_bKgT = take(es * mc * H * D * kChunkTokens);
         p->ws_ckS = take(2 * mc * H * D * D);
-        p->ws_Y = take(2 * T * H * D);
         p->ws_U = take(2 * T * H * D);
     }
     if (kind == kWsBwd || kind == kWsBwdCtx) {
@@ -89,7 +88,6 @@ size_t carve_context(Plan* p, void* base) {
     p->ws_bQgT = take(es * mc * H * D * kChunkTokens);
     p->ws_bKgT = take(es * mc * H * D * kChunkTokens);
     p->ws_ckS = take(2 * mc * H * D * D);
-    p->ws_Y = take(2 * T * H * D);
     p->ws_U = take(2 * T * H * D);
     return off;
 }
@@ -438,15 +436,15 @@ kda_status kda_chunk_fwd_train(kda_dtype dt, int64_t total_tokens, int32_t n_seq
 }
 
 kda_status kda_chunk_bwd_ctx(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads, int32_t d_k,
-                             int32_t d_v, int32_t chunk, const void* q, const void* k, const void* beta,
-                             const void* log_alpha, const int32_t* cu_seqlens, const void* context,
+                             int32_t d_v, int32_t chunk, const void* q, const void* k, const void* v,
+                             const void* beta, const void* log_alpha, const int32_t* cu_seqlens, const void* context,
                              size_t context_bytes, const void* dO, const float* dS_T, void* dq, void* dk, void* dv,
                              void* dbeta, void* dlog_alpha, float* dS0, void* workspace, size_t workspace_bytes,
                              void* stream) {
     if (dt == KDA_F32) return KDA_ERR_UNSUPPORTED;
     Plan p{};
-    // v and S0 are not read: the context holds what they contributed (k stands in, sizes only)
-    kda_status s = prepare_bwd(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, k, beta, log_alpha,
+    // S0 is not read: the context holds what it contributed
+    kda_status s = prepare_bwd(&p, dt, total_tokens, n_seqs, n_heads, d_k, d_v, chunk, q, k, v, beta, log_alpha,
                                nullptr, cu_seqlens, dO, dS_T, dq, dk, dv, dbeta, dlog_alpha, dS0, workspace,
                                workspace_bytes, kda::kWsBwdCtx);
     if (s != KDA_OK) return s;

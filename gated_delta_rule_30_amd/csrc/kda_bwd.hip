@@ -4,8 +4,8 @@
 // §3.1 "KDA": the chunked form; orkas.ai "Kimi K3 architecture",
 // §"GPU のコードパスを一本消した「下界」": the 16-token sub-tiles) runs as
 //   k_prep + k_recur_lds<kCkpt>  forward again, keeping per chunk the
-//                                incoming state S and per token Y = V - (K.Gamma)S
-//                                and U~ = T diag(beta) Y
+//                                incoming state S and per token U~ = T diag(beta) Y
+//                                with Y = V - (K.Gamma)S
 //   k_prep<kBwd> + k_recur_lds<kBwd>  the state-gradient recurrence, last
 //                                chunk first: dv, dZ = T^T dU~ per token, the
 //                                outgoing-state gradient dS' per chunk, dS0
@@ -18,6 +18,8 @@
 //   dA  = -tril(dZ U~^T, -1)    (= -T^T dU~ Z^T T^T with Z = diag(beta) Y)
 //   dGq =  tril(dO U~^T)
 //   dbeta_r = sum_j dZ_rj Y_rj + sum_{i<r} dA_ri Gk_ri
+// Y itself is not kept: its term is sum_j dZ_rj V_rj - sum_c (K.Gamma)_rc (dZ S^T)_rc,
+// the second sum split between the two channel halves like the other products.
 // where Gk and Gq are the decayed Gram matrices sum_c x_rc k_ic exp(b_rc - b_ic)
 // of K and Q with K (A = diag(beta) Gk, M = Gq).  Their gradients reach the
 // tokens' q, k and b:
@@ -153,15 +155,15 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
         rg[i] = *reinterpret_cast<const uint2*>(a.g + at);
     }
     const E beta_raw = a.beta[(info.tok0 + (ok ? t : 0)) * H + h];
-    // token rows of dO, dY, U~, dZ (and Y) as fragments over value columns
-    uint4 fo[KV], fy[KV], fu[KV], fz[KV], fY[KV];
+    // token rows of dO, U~, dZ (and V) as fragments over value columns
+    uint4 fo[KV], fu[KV], fz[KV], fv[KV];
 #pragma unroll
     for (int m = 0; m < KV; ++m) {
         const int64_t at = row + M::KS * m + M::KW * lg;
         fo[m] = *reinterpret_cast<const uint4*>(a.dO + at);
         fu[m] = *reinterpret_cast<const uint4*>(a.U + at);
         fz[m] = *reinterpret_cast<const uint4*>(a.dZ + at);
-        if (hh == 0) fY[m] = *reinterpret_cast<const uint4*>(a.Y + at);
+        if (hh == 0) fv[m] = *reinterpret_cast<const uint4*>(a.v + at);
     }
     // ---- zero the rows past the chunk end (bit masks: no branches, so the
     // loads above stay in flight until their first use)
@@ -188,17 +190,11 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
         mask4(fo[m]);
         mask4(fu[m]);
         mask4(fz[m]);
-        // dY = beta dZ, row by row (the recurrence wrote the same product as dv)
-        const bf16x8 zf = as_frag(fz[m]);
-        bf16x8 yf;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) yf[e] = (E)(bt * (float)zf[e]);
-        fy[m] = __builtin_bit_cast(uint4, yf);
     }
-    if (hh == 0) {   // first dbeta term, sum_j dZ_tj Y_tj (the other half adds none)
+    if (hh == 0) {   // sum_j dZ_tj V_tj, of the first dbeta term (the other half adds none)
 #pragma unroll
         for (int m = 0; m < KV; ++m) {
-            const bf16x8 zf = as_frag(fz[m]), yf = as_frag(fY[m]);
+            const bf16x8 zf = as_frag(fz[m]), yf = as_frag(fv[m]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) dbeta += (float)zf[e] * (float)yf[e];
         }
@@ -250,11 +246,14 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
 #pragma unroll
         for (int r = 0; r < 4; ++r) b[4 * i + r] += sRho[w * HALF + lch(i, r)];
 
-    // ---- products with the states: d(Q.Gamma), d(K.Gamma), dK^
+    // ---- products with the states: d(Q.Gamma), dK^ and dZ S^T, which gives
+    // d(K.Gamma) = -dY S^T = -diag(beta) dZ S^T and the rest of the first
+    // dbeta term
     float dq[CH], dk[CH], db[CH];
+    float dbeta2 = 0.f;
 #pragma unroll
     for (int i = 0; i < NTH; ++i) {
-        f32x4 aq = zero4(), ak = zero4(), ah = zero4();
+        f32x4 aq = zero4(), ah = zero4(), az = zero4();
 #pragma unroll
         for (int m = 0; m < KV; ++m) {
             // row kSub*i + li, vector 4m + lg, permuted by the row (state_swz)
@@ -262,18 +261,20 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
             const F fs = M::load(&sS[at]);
             const F fd = M::load(&sdS[at]);
             aq = M::mma(fs, as_frag(fo[m]), aq);
-            ak = M::mma(fs, as_frag(fy[m]), ak);
+            az = M::mma(fs, as_frag(fz[m]), az);
             ah = M::mma(fd, as_frag(fu[m]), ah);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int x = 4 * i + r, c = lch(i, r);
             const float G = __expf(b[x]), eh = __expf(sRho[kNSub * HALF + c] - b[x]);
-            const float dqg = aq[r], dkg = -ak[r], dkh = ah[r];
+            const float dqg = aq[r], dkg = -bt * az[r], dkh = ah[r];
             dq[x] = dqg * G;
             dk[x] = dkg * G + dkh * eh;
-            const float hk = dkh * kf[x] * eh;   // dK^ . K^
-            db[x] = (dqg * qf[x] + dkg * kf[x]) * G - hk;
+            const float kz = kf[x] * G * az[r];   // (K.Gamma) . (dZ S^T)
+            dbeta2 -= kz;
+            const float hk = dkh * kf[x] * eh;    // dK^ . K^
+            db[x] = dqg * qf[x] * G - bt * kz - hk;
             const float cs = row_scan16(hk);      // column sum over the tile's tokens
             if (li == 15) sCol[w * HALF + c] = cs;
         }
@@ -331,7 +332,6 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
     __syncthreads();
 
     // ---- Gram gradients
-    float dbeta2 = 0.f;
 #pragma unroll
     for (int i = 0; i < NTH; ++i) {
         const int cA = kSub * i + li;   // local channel of this lane's A-operand row

@@ -53,7 +53,7 @@ struct Plan {
     // What the workspace holds (carve_workspace) -- kWsFwd: the forward pass;
     // kWsBwd: the backward with the forward evaluated again inside;
     // kWsFwdTrain / kWsBwdCtx: the training pair, whose shared regions (Gamma_L,
-    // beta, the backward operand set, S per chunk, Y, U~) live in a separate
+    // beta, the backward operand set, S per chunk, U~) live in a separate
     // context buffer (carve_context).
     int ws_kind;
     const void* dO;           // [T, H, D] output gradients
@@ -69,7 +69,7 @@ struct Plan {
     void* ws_bKgT;            // (K . Gamma)^T             [H, max_chunks, D, 64]
     void* ws_ckS;             // [H, max_chunks, D, D] state entering each chunk (bf16)
     void* ws_ckdS;            // [H, max_chunks, D, D] gradient of each chunk's outgoing state (bf16)
-    void *ws_Y, *ws_U, *ws_dZ;   // [T, H, D] bf16: Y, U~ and dZ per token
+    void *ws_U, *ws_dZ;       // [T, H, D] bf16: U~ and dZ per token
     float* ws_dbp;            // [2, H, T] float32 dbeta shares of the two channel halves
     int32_t* ws_ck0;          // [n_seqs + 1] first checkpoint slot of each sequence (varlen checkpoints)
     int32_t* ws_prog;         // [n_seqs * H, d_v / 16] steps done per recurrence workgroup (pacing)
@@ -77,7 +77,7 @@ struct Plan {
 
 // Arguments of the per-chunk gradient kernel (kda_bwd.hip); bf16 tensors.
 struct GradArgs {
-    const __bf16 *q, *k, *g, *beta, *dO, *Y, *U, *dZ, *ckS, *ckdS;
+    const __bf16 *q, *k, *v, *g, *beta, *dO, *U, *dZ, *ckS, *ckdS;
     const ChunkInfo* tab;
     const int32_t* n_chunks;
     int64_t fixed_len;        // > 0: equal-length sequences (chunk from the index)

@@ -1038,8 +1038,8 @@ struct LdsGeo {
 //          state plus its zero-start state).  v, S0 and o are not accessed.
 //   kCkpt  the forward steps keeping what the backward pass needs: the state
 //          entering every chunk (aux.ck, bf16 [slot][D][D]), and the
-//          per-token Y = V - (K . Gamma) S and U~ (aux.y, aux.u, bf16, laid out
-//          as v); o and S_T as kFwd when given (o may be NULL).
+//          per-token U~ = T diag(beta) (V - (K . Gamma) S) (aux.u, bf16, laid
+//          out as v); o and S_T as kFwd when given (o may be NULL).
 //   kBwd   the state-gradient recurrence, chunks last to first, on the
 //          backward operand set (see ChunkOps).  With dS' the gradient of a
 //          chunk's outgoing state and dO its output gradients:
@@ -1059,7 +1059,7 @@ enum { kFwd = 0, kTrans = 1, kCkpt = 2, kBwd = 3, kFwdCk = 4 };
 
 struct RecurAux {
     __bf16* ck;        // kCkpt: S entering each chunk; kBwd: dS' of each chunk
-    __bf16* y;         // kCkpt: Y;  kBwd: dZ
+    __bf16* y;         // kBwd: dZ
     __bf16* u;         // kCkpt: U~
     const float* bet;  // kBwd: per-chunk beta (ChunkOps::bet)
     float* sck;        // kFwdCk: fp32 state after every `every`-th chunk of a sequence
@@ -1515,11 +1515,7 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
             for (int r = 0; r < 4; ++r) {
                 const int t = kSub * rt + 4 * lg + r;
                 const float vv = kTransition ? 0.f : to_f(vrows[(4 * lg + r) * SW + cb0 + kSub * c + li]);
-                const E y = from_f<E>(t < len ? vv - accX[c][r] : 0.f);
-                sYt[(cb0 + kSub * c + li) * PY + t] = y;
-                if constexpr (kMode == kCkpt) {
-                    if (t < len) aux.y[o_off + ((int64_t)j * C + t) * rs] = y;
-                }
+                sYt[(cb0 + kSub * c + li) * PY + t] = from_f<E>(t < len ? vv - accX[c][r] : 0.f);
             }
         F ftb[G::NKT], fmm[G::NKT], fkt[RT][G::NKT];
         const bool zh = Z::zero(rt);
@@ -1963,7 +1959,7 @@ static hipError_t launch_grads(const Plan& p, hipStream_t st, hipEvent_t ev_mid)
         a.g = static_cast<const E*>(p.g);
         a.beta = static_cast<const E*>(p.beta);
         a.dO = static_cast<const E*>(p.dO);
-        a.Y = static_cast<const E*>(p.ws_Y);
+        a.v = static_cast<const E*>(p.v);
         a.U = static_cast<const E*>(p.ws_U);
         a.dZ = static_cast<const E*>(p.ws_dZ);
         a.ckS = static_cast<const E*>(p.ws_ckS);
@@ -1999,8 +1995,7 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     launch_prep<E, D, true>(p, static_cast<const E*>(p.q), st);
     mark(2);
     launch_recur_lds<D, kCkpt>(p, p.v, p.S0, nullptr, nullptr,
-                               RecurAux{static_cast<E*>(p.ws_ckS), static_cast<E*>(p.ws_Y),
-                                        static_cast<E*>(p.ws_U), nullptr}, st);
+                               RecurAux{static_cast<E*>(p.ws_ckS), nullptr, static_cast<E*>(p.ws_U), nullptr}, st);
     mark(3);
     launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, p.dv,
                               RecurAux{static_cast<E*>(p.ws_ckdS), static_cast<E*>(p.ws_dZ), nullptr, p.ws_bet}, st);
@@ -2018,8 +2013,7 @@ static hipError_t launch_fwd_train_d(const Plan& p, hipStream_t st) {
     launch_table(p, st);
     launch_prep<E, D, true>(p, static_cast<const E*>(p.q), st);
     launch_recur_lds<D, kCkpt>(p, p.v, p.S0, p.S_T, p.o,
-                               RecurAux{static_cast<E*>(p.ws_ckS), static_cast<E*>(p.ws_Y),
-                                        static_cast<E*>(p.ws_U), nullptr}, st);
+                               RecurAux{static_cast<E*>(p.ws_ckS), nullptr, static_cast<E*>(p.ws_U), nullptr}, st);
     return hipGetLastError();
 }
 

@@ -365,14 +365,14 @@ kda_status kda_chunk_bwd_profile(kda_dtype dt, int64_t total_tokens, int32_t n_s
 /* Training pair.  kda_chunk_fwd_train is kda_chunk_fwd that also keeps, in
  * a caller-owned context buffer, what the backward pass needs (the backward
  * operand set of every chunk, the state entering every chunk, and per token
- * Y = V - (K . Gamma) S and U~); kda_chunk_bwd_ctx then computes the
+ * U~); kda_chunk_bwd_ctx then computes the
  * gradients from that context without evaluating the forward again.  Same
  * math and results as kda_chunk_bwd (bit for bit), split across the two
  * calls; bf16 only.
  *   context : >= kda_chunk_train_context_size(...) bytes of device memory,
  *             256-byte aligned; written by kda_chunk_fwd_train, read by
- *             kda_chunk_bwd_ctx, which must get the same q, k, beta,
- *             log_alpha, cu_seqlens and sizes (v and S0 act through the
+ *             kda_chunk_bwd_ctx, which must get the same q, k, v, beta,
+ *             log_alpha, cu_seqlens and sizes (S0 acts through the
  *             context); nothing checks that they match
  *   kda_chunk_fwd_train : arguments of kda_chunk_fwd plus the context; its
  *             workspace is kda_chunk_fwd_workspace_size(...) bytes; o is
@@ -395,8 +395,9 @@ kda_status kda_chunk_fwd_train(kda_dtype dt, int64_t total_tokens, int32_t n_seq
                                void* workspace, size_t workspace_bytes, void* stream);
 kda_status kda_chunk_bwd_ctx(kda_dtype dt, int64_t total_tokens, int32_t n_seqs, int32_t n_heads,
                              int32_t d_k, int32_t d_v, int32_t chunk,
-                             const void* q, const void* k, const void* beta, const void* log_alpha,
-                             const int32_t* cu_seqlens, const void* context, size_t context_bytes,
+                             const void* q, const void* k, const void* v, const void* beta,
+                             const void* log_alpha, const int32_t* cu_seqlens,
+                             const void* context, size_t context_bytes,
                              const void* dO, const float* dS_T,
                              void* dq, void* dk, void* dv, void* dbeta, void* dlog_alpha, float* dS0,
                              void* workspace, size_t workspace_bytes, void* stream);

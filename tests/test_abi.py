@@ -292,13 +292,14 @@ def test_training_pair_rejects_bad_arguments(lib):
 
     need_bws = lib.kda_chunk_bwd_ctx_workspace_size(128, 1, 2, 64, 64, 64, kda.KDA_BF16)
 
-    def bc(dt=kda.KDA_BF16, ctx=0x200000, ctx_bytes=None, ws_bytes=None, dO=fake):
-        return lib.kda_chunk_bwd_ctx(dt, 128, 1, 2, 64, 64, 64, P(fake), P(fake), P(fake), P(fake), None, P(ctx),
-                                     need_ctx if ctx_bytes is None else ctx_bytes, P(dO), None, P(fake), P(fake),
+    def bc(dt=kda.KDA_BF16, ctx=0x200000, ctx_bytes=None, ws_bytes=None, dO=fake, v=fake):
+        return lib.kda_chunk_bwd_ctx(dt, 128, 1, 2, 64, 64, 64, P(fake), P(fake), P(v), P(fake), P(fake), None,
+                                     P(ctx), need_ctx if ctx_bytes is None else ctx_bytes, P(dO), None, P(fake), P(fake),
                                      P(fake), P(fake), P(fake), None, P(0x100000),
                                      need_bws if ws_bytes is None else ws_bytes, None)
     assert bc(dt=kda.KDA_F32) == ERR_UNSUPPORTED
     assert bc(dO=None) == ERR_NULL
+    assert bc(v=None) == ERR_NULL
     assert bc(ctx=None) == ERR_WORKSPACE
     assert bc(ctx_bytes=16) == ERR_WORKSPACE
     assert bc(ws_bytes=need_bws - 1) == ERR_WORKSPACE
