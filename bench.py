@@ -117,7 +117,7 @@ def mfma_counters_for(kernel, workload_key):
 
 def grad_bytes_per_token_head(C, D, es=2):
     """Algorithmic bytes of the per-chunk gradient kernel per (token, head):
-    reads q, k, log_alpha, dO, U~, dZ, Y (7 D) and beta, the chunk's two
+    reads q, k, log_alpha, v, dO, U~, dZ (7 D) and beta, the chunk's two
     d x d bf16 states spread over its C tokens; writes dq, dk, dlog_alpha and
     the two float32 dbeta shares."""
     return 7 * D * es + es + 2 * D * D * es / C + 3 * D * es + 2 * 4
