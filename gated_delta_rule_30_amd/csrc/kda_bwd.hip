@@ -7,9 +7,10 @@
 //                                incoming state S and per token U~ = T diag(beta) Y
 //                                with Y = V - (K.Gamma)S
 //   k_prep<kBwd> + k_recur_lds<kBwd>  the state-gradient recurrence, last
-//                                chunk first: dv, dZ = T^T dU~ per token, the
+//                                chunk first: dZ = T^T dU~ per token, the
 //                                outgoing-state gradient dS' per chunk, dS0
-//   k_grad (here)                everything else, chunk-parallel.
+//   k_grad (here)                everything else, chunk-parallel, dv = diag(beta) dZ
+//                                included.
 //
 // Per chunk (b = cumsum of log alpha inside the chunk, Gamma = exp(b),
 // gamma = Gamma at the last token, K^ = K . exp(b_L - b), dY = dv):
@@ -191,12 +192,17 @@ __global__ __launch_bounds__(kGradThreads) __attribute__((amdgpu_waves_per_eu(2,
         mask4(fu[m]);
         mask4(fz[m]);
     }
-    if (hh == 0) {   // sum_j dZ_tj V_tj, of the first dbeta term (the other half adds none)
+    if (hh == 0) {   // dv = beta dZ, and sum_j dZ_tj V_tj of the first dbeta term (the other half adds none)
 #pragma unroll
         for (int m = 0; m < KV; ++m) {
             const bf16x8 zf = as_frag(fz[m]), yf = as_frag(fv[m]);
+            bf16x8 dvf;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dbeta += (float)zf[e] * (float)yf[e];
+            for (int e = 0; e < 8; ++e) {
+                dbeta += (float)zf[e] * (float)yf[e];
+                dvf[e] = (E)(bt * (float)zf[e]);
+            }
+            if (ok) *reinterpret_cast<bf16x8*>(a.dv + row + M::KS * m + M::KW * lg) = dvf;
         }
         dbeta += __shfl_xor(dbeta, 16);
         dbeta += __shfl_xor(dbeta, 32);

@@ -85,7 +85,7 @@ struct GradArgs {
     int32_t H;
     int64_t max_chunks;
     int64_t total_tokens;
-    __bf16 *dq, *dk, *dbeta, *dg;
+    __bf16 *dq, *dk, *dv, *dbeta, *dg;
     float* dbp;               // [2, H, total_tokens] the halves' dbeta shares
 };
 hipError_t launch_grad(const GradArgs& a, int d, int32_t max_chunks, hipStream_t stream);

@@ -1046,8 +1046,9 @@ struct LdsGeo {
 //            R  = (K . exp(b_L - b)) dS' + M^T dO        (= dU~)
 //            dZ = T^T R,  dY = diag(beta) dZ             (dY is dv)
 //            dS = Diag(Gamma_L) dS' + (Q . Gamma)^T dO - (K . Gamma)^T dY
-//          Inputs: v = dO, S0 = dS_T (may be NULL); outputs: o = dv, ST = dS0,
-//          aux.ck = dS' of every chunk (bf16 [slot][D][D]), aux.y = dZ.
+//          Inputs: v = dO, S0 = dS_T (may be NULL); outputs: ST = dS0,
+//          aux.ck = dS' of every chunk (bf16 [slot][D][D]), aux.y = dZ (dv is
+//          written by the gradient kernel from dZ; o is not accessed).
 //          These are the adjoints of the kFwd step (the chain rule through
 //          U~ = T diag(beta) Y, O = (Q . Gamma) S + M U~ and
 //          S' = Diag(Gamma_L) S + K^T U~).
@@ -1657,7 +1658,7 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
         for (int a = 0; a < RT; ++a) gam[a] = *reinterpret_cast<const f32x4*>(gl + kSub * a + 4 * lg);
         const f32x4 bet = *reinterpret_cast<const f32x4*>(gl + 64 + 4 * lg);   // bytes 768.. of the block
         barrier_lds();
-        // dZ = T^T R, dY = diag(beta) dZ  (rows 16w..); -dY^T to LDS
+        // dZ = T^T R (rows 16w..) out; -dY^T = -(diag(beta) dZ)^T to LDS
         {
             f32x4 accZ = zero4();
 #pragma unroll
@@ -1666,13 +1667,8 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = kSub * rt + 4 * lg + r;
-                const float dy = bet[r] * accZ[r];
-                if (t < len) {
-                    const int64_t at = o_off + ((int64_t)j * C + t) * rs;
-                    o[at] = from_f<E>(dy);
-                    aux.y[at] = from_f<E>(accZ[r]);
-                }
-                sUt[li * PY + t] = from_f<E>(t < len ? -dy : 0.f);
+                if (t < len) aux.y[o_off + ((int64_t)j * C + t) * rs] = from_f<E>(accZ[r]);
+                sUt[li * PY + t] = from_f<E>(t < len ? -bet[r] * accZ[r] : 0.f);
             }
         }
         barrier_lds();
@@ -1973,6 +1969,7 @@ static hipError_t launch_grads(const Plan& p, hipStream_t st, hipEvent_t ev_mid)
         a.total_tokens = p.total_tokens;
         a.dbp = p.ws_dbp;
         a.dq = static_cast<E*>(p.dq);
+        a.dv = static_cast<E*>(p.dv);
         a.dk = static_cast<E*>(p.dk);
         a.dbeta = static_cast<E*>(p.dbeta);
         a.dg = static_cast<E*>(p.dg);
@@ -1997,7 +1994,7 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     launch_recur_lds<D, kCkpt>(p, p.v, p.S0, nullptr, nullptr,
                                RecurAux{static_cast<E*>(p.ws_ckS), nullptr, static_cast<E*>(p.ws_U), nullptr}, st);
     mark(3);
-    launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, p.dv,
+    launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, nullptr,
                               RecurAux{static_cast<E*>(p.ws_ckdS), static_cast<E*>(p.ws_dZ), nullptr, p.ws_bet}, st);
     mark(4);
     const hipError_t e = launch_grads<D>(p, st, ev ? ev[5] : nullptr);
@@ -2021,7 +2018,7 @@ template <int D>
 static hipError_t launch_bwd_ctx_d(const Plan& p, hipStream_t st) {
     using E = __bf16;
     launch_table(p, st);
-    launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, p.dv,
+    launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, nullptr,
                               RecurAux{static_cast<E*>(p.ws_ckdS), static_cast<E*>(p.ws_dZ), nullptr, p.ws_bet}, st);
     return launch_grads<D>(p, st, nullptr);
 }
