@@ -247,8 +247,10 @@ struct ChunkOps {
 // kBoth also writes the backward set of operands (see ChunkOps) into `ob`
 // from the same quantities: K . exp(b_L - b) row-wise, (K . Gamma)^T and
 // (Q . Gamma)^T through the transposing LDS stages, T^T and M^T, and beta
-// (Gamma_L is shared: ob.gam is ops.gam).
-template <typename E, int D, bool kBoth = false>
+// (Gamma_L is shared: ob.gam is ops.gam).  kLean (with kBoth) leaves out Q .
+// Gamma and M of the forward set: the backward pass that evaluates the
+// forward again never reads them.
+template <typename E, int D, bool kBoth = false, bool kLean = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth && sizeof(E) == 2 ? 3 : 1))) void k_prep(const E* __restrict__ q, const E* __restrict__ k,
                                                    const E* __restrict__ g, const E* __restrict__ beta,
                                                    const ChunkInfo* __restrict__ tab,
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
                 }
                 if (cv == EPV - 1) {
                     const int i = c / EPV;
-                    store_nt(&qg[(w * G::VPL + i) * 64 + lane_id()], vq);
+                    if constexpr (!kLean) store_nt(&qg[(w * G::VPL + i) * 64 + lane_id()], vq);
                     store_nt(&kg[(w * G::VPL + i) * 64 + lane_id()], vk);
                     if constexpr (kBwd) store_nt(&kh[(w * G::VPL + i) * 64 + lane_id()], vh);
                     if (w < kNSub - 1) cbv[i] = vc;
@@ -612,7 +614,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(!kBoth
         constexpr bool kSkipZero = M::KW == EPV && G::NVT == 2;
         if (!(kSkipZero && wr < 2 && v == 1)) {
             store_nt(&otb[vi], pt);
-            store_nt(&omm[vi], pm);
+            if constexpr (!kLean) store_nt(&omm[vi], pm);
         }
         if constexpr (kBwd) {
             if (!(kSkipZero && wr >= 2 && v == 0)) {
@@ -1052,11 +1054,15 @@ struct LdsGeo {
 //          These are the adjoints of the kFwd step (the chain rule through
 //          U~ = T diag(beta) Y, O = (Q . Gamma) S + M U~ and
 //          S' = Diag(Gamma_L) S + K^T U~).
+//   kCkptLean kCkpt without o, for the backward pass that evaluates the
+//          forward again: Q . Gamma and M are neither loaded nor used (its
+//          k_prep does not write them), which takes 6 of the 17 blocks out of
+//          every region's fill.
 //   kFwdCk kFwd that also writes the fp32 state after every aux.every-th
 //          chunk of a sequence to aux.sck (slot = the chunk's global index):
 //          the prefix-cache checkpoints.  A mode of its own, so that the plain
 //          forward carries no test for it.
-enum { kFwd = 0, kTrans = 1, kCkpt = 2, kBwd = 3, kFwdCk = 4 };
+enum { kFwd = 0, kTrans = 1, kCkpt = 2, kBwd = 3, kFwdCk = 4, kCkptLean = 5 };
 
 struct RecurAux {
     __bf16* ck;        // kCkpt: S entering each chunk; kBwd: dS' of each chunk
@@ -1089,6 +1095,8 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
     float* __restrict__ ST, __bf16* __restrict__ o, RecurAux aux, int32_t jb, int32_t je, int32_t xcd_lo) {
     constexpr bool kTransition = kMode == kTrans;
     constexpr bool kBack = kMode == kBwd;
+    constexpr bool kCk = kMode == kCkpt || kMode == kCkptLean;   // keeps the backward's inputs
+    constexpr bool kNoQM = kMode == kCkptLean;                   // no Q . Gamma, no M
     using E = __bf16;
     using G = Geo<E, D>;
     using L = LdsGeo<D>;
@@ -1284,7 +1292,8 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
                 if constexpr (i >= decltype(lo_c)::value && i < decltype(hi_c)::value) {
                     constexpr int b0 = pt + kProdPerWave * i;
                     constexpr int b = b0 < L::kBlocks ? b0 : b0 - kProdPerWave;
-                    if constexpr (b == L::kTb + Z::kHalf || b == L::kMm + Z::kHalf) {
+                    if constexpr (kNoQM && ((b >= L::kQg && b < L::kKg) || (b >= L::kMm && b < L::kKt))) {
+                    } else if constexpr (b == L::kTb + Z::kHalf || b == L::kMm + Z::kHalf) {
                         if (!Z::zero(cw)) block(std::integral_constant<int, b>{}, dst, j, len);
                     } else {
                         block(std::integral_constant<int, b>{}, dst, j, len);
@@ -1314,7 +1323,7 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
         // forward 6 (3, 6, 9, 12, 15, 17: 1.10, 1.10, 1.11, 1.12, 1.12,
         // 1.15 ms); kCkpt and kBwd 12 (3, 6, 9, 12, 17: 1.45 / 1.49,
         // 1.47 / 1.52, 1.46 / 1.46, 1.45 / 1.44, 1.51 / 1.47 ms)
-        constexpr int kCut17 = (kMode == kCkpt || kMode == kBwd) ? 12 : 6;
+        constexpr int kCut17 = (kCk || kMode == kBwd) ? 12 : 6;
         using Cut = std::integral_constant<int, (kDma * kCut17 + 8) / 17>;
 
         // Warm-up lines of this slab: kTouch per producer lane, over one
@@ -1323,7 +1332,8 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
         constexpr int64_t kBq = (int64_t)C * D * 2, kBs = (int64_t)C * C * 2;   // bytes per chunk slot
         constexpr int kQLines = (int)(kBq / 128);
         constexpr int kTriLines = (int)(kBs / 128) - 2 * 8;   // the two zero 1 KB halves skipped
-        constexpr int kOpsLines = 3 * kQLines + 2 * kTriLines;
+        constexpr int kFullOps = 3 * kQLines + 2 * kTriLines;
+        constexpr int kOpsLines = kNoQM ? 2 * kQLines + kTriLines : kFullOps;
         // byte offset of line t of a triangular tile's loaded blocks (tile
         // block 2 w + half; the zero ones are 1, 3 or, in kBwd, 4, 6)
         auto tri_off = [](int t) -> int64_t {
@@ -1345,6 +1355,8 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
             q = q < kPerSlab ? q : kPerSlab - 1;
             int line = sl * kPerSlab + q;
             line = line < kLines ? line : kLines - 1;
+            // kNoQM: its lines skip the Q . Gamma and M ones of the full list below
+            if (kNoQM) line += line < 2 * kQLines + kTriLines ? kQLines : kQLines + kTriLines;
             const int64_t off = (int64_t)line * 128;
             t_vrow[k] = -1;
             if (off < kBq) { t_base[k] = (const char*)ops.Qg + cb * kBq + off; t_step[k] = kBq; }
@@ -1353,17 +1365,17 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
             else if (line < 3 * kQLines + kTriLines) {
                 t_base[k] = (const char*)ops.TB + cb * kBs + tri_off(line - 3 * kQLines);
                 t_step[k] = kBs;
-            } else if (line < kOpsLines) {
+            } else if (line < kFullOps) {
                 t_base[k] = (const char*)ops.Mm + cb * kBs + tri_off(line - 3 * kQLines - kTriLines);
                 t_step[k] = kBs;
-            } else if (line < kOpsLines + kGamLines) {
-                t_base[k] = (const char*)(ops.gam + cb * D) + (int64_t)(line - kOpsLines) * 128;
+            } else if (line < kFullOps + kGamLines) {
+                t_base[k] = (const char*)(ops.gam + cb * D) + (int64_t)(line - kFullOps) * 128;
                 t_step[k] = (int64_t)D * 4;
             } else if (kTransition) {   // no value rows: warm Gamma_L again instead
                 t_base[k] = (const char*)(ops.gam + cb * D);
                 t_step[k] = (int64_t)D * 4;
             } else {
-                const int vl = line - kOpsLines - kGamLines;
+                const int vl = line - kFullOps - kGamLines;
                 t_vrow[k] = vl / kVRowLines;
                 t_base[k] = (const char*)(v + (s_start * H + h) * D) + (int64_t)(vl % kVRowLines) * 128;
                 t_step[k] = 0;
@@ -1388,9 +1400,11 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
         // Loads per chunk fill of this producer: kDma, or kDma - 2 when its
         // region skips the zero halves of the two triangular tiles.
         const bool lean = Z::zero(cw);
-        constexpr int kFill = kDma + (SW > kSub ? 1 : 0);   // loads per chunk fill (32 columns: Gamma_L apart)
+        // loads per chunk fill (32 columns: Gamma_L apart; kNoQM: without Q . Gamma and M)
+        constexpr int kFill = kDma + (SW > kSub ? 1 : 0) - (kNoQM ? G::VPL + G::NVT : 0);
+        constexpr int kZeroSkip = kNoQM ? 1 : 2;   // zero-half blocks a lean region skips
         auto wait_fill = [&]() {
-            if (lean) wait_counts<2 * kTouch + kFill - 2, 15>();
+            if (lean) wait_counts<2 * kTouch + kFill - kZeroSkip, 15>();
             else wait_counts<2 * kTouch + kFill, 15>();
         };
         // One step j: open it; after the compute waves' first inner barrier
@@ -1486,13 +1500,13 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
     auto step = [&](const uint4* buf, int j) __attribute__((always_inline)) {
         const int len = chunk_len(j);
         const uint4* cur = buf + rt * L::kWaveVec;
-        if constexpr (kMode == kCkpt) keep_state(j);
+        if constexpr (kCk) keep_state(j);
         barrier_lds();   // chunk j's operands are in `buf`; S^T of the previous step is in LDS
         const F* fr = reinterpret_cast<const F*>(cur) + lane;
         F fq[G::NKC], fk[G::NKC];
 #pragma unroll
         for (int m = 0; m < G::NKC; ++m) {
-            fq[m] = fr[(L::kQg + m) * 64];
+            if constexpr (!kNoQM) fq[m] = fr[(L::kQg + m) * 64];
             fk[m] = fr[(L::kKg + m) * 64];
         }
         // X = (K . Gamma) S and P = (Q . Gamma) S for token rows 16w.. (each
@@ -1506,7 +1520,7 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
             for (int c = 0; c < CT; ++c) {
                 const F bs = M::load(&sSt[(cb0 + kSub * c + li) * PS + lg * CPL + m * M::KW]);
                 accX[c] = M::mma(fk[m], bs, accX[c]);
-                accO[c] = M::mma(fq[m], bs, accO[c]);
+                if constexpr (!kNoQM) accO[c] = M::mma(fq[m], bs, accO[c]);
             }
         // Y = V - X, transposed to LDS (rows past the chunk end are zero)
         const E* vrows = reinterpret_cast<const E*>(cur + L::kMisc * 64);
@@ -1527,7 +1541,7 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
                 fmm[m] = F{};
             } else {
                 ftb[m] = fr[(L::kTb + m) * 64];
-                fmm[m] = fr[(L::kMm + m) * 64];
+                if constexpr (!kNoQM) fmm[m] = fr[(L::kMm + m) * 64];
             }
         }
 #pragma unroll
@@ -1552,7 +1566,7 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
                 const int t = kSub * rt + 4 * lg + r;
                 const E u = from_f<E>(accU[r]);
                 sUt[(cb0 + kSub * c + li) * PY + t] = u;
-                if constexpr (kMode == kCkpt) {
+                if constexpr (kCk) {
                     if (t < len) aux.u[o_off + ((int64_t)j * C + t) * rs] = u;
                 }
             }
@@ -1589,7 +1603,8 @@ __global__ __launch_bounds__((kRecurWaves * XW + kProducers + 1) * 64) void k_re
 #pragma unroll
         for (int c = 0; c < CT; ++c)
 #pragma unroll
-            for (int m = 0; m < G::NKT; ++m) accO[c] = M::mma(fmm[m], bu[c][m], accO[c]);
+            for (int m = 0; m < G::NKT; ++m)
+                if constexpr (!kNoQM) accO[c] = M::mma(fmm[m], bu[c][m], accO[c]);
         // S^T is last read before the Y barrier of this step; the barrier at
         // the top of the next step publishes the new one.
         put_state();
@@ -1725,13 +1740,13 @@ static ChunkOps chunk_ops_bwd(const Plan& p) {
 }
 
 // All chunks, or (equal lengths, nj > 0) chunks [j0, j0 + nj) of every sequence.
-template <typename E, int D, bool kBoth>
+template <typename E, int D, bool kBoth, bool kLean = false>
 static void launch_prep(const Plan& p, const E* q, hipStream_t st, int32_t j0 = 0, int32_t nj = 0,
                         bool xcd_hi = false) {
     if (p.total_tokens <= 0) return;
     int32_t grid = nj > 0 ? p.n_seqs * nj : p.max_chunks;
     if (xcd_hi) grid = 8 * ((grid + 3) / 4);
-    hipLaunchKernelGGL((k_prep<E, D, kBoth>), dim3(grid, p.n_heads), dim3(kThreads), 0, st, q,
+    hipLaunchKernelGGL((k_prep<E, D, kBoth, kLean>), dim3(grid, p.n_heads), dim3(kThreads), 0, st, q,
                        static_cast<const E*>(p.k), static_cast<const E*>(p.g), static_cast<const E*>(p.beta),
                        p.ws_tab, p.ws_n_chunks, p.cu_seqlens ? (int64_t)0 : p.fixed_len,
                        p.cu_seqlens ? 0 : (int32_t)(p.n_seqs * ((p.fixed_len + kChunk - 1) / kChunk)), p.n_heads,
@@ -1989,9 +2004,9 @@ static hipError_t launch_bwd_d(const Plan& p, hipStream_t st, hipEvent_t* ev) {
     mark(0);
     launch_table(p, st);
     mark(1);
-    launch_prep<E, D, true>(p, static_cast<const E*>(p.q), st);
+    launch_prep<E, D, true, true>(p, static_cast<const E*>(p.q), st);
     mark(2);
-    launch_recur_lds<D, kCkpt>(p, p.v, p.S0, nullptr, nullptr,
+    launch_recur_lds<D, kCkptLean>(p, p.v, p.S0, nullptr, nullptr,
                                RecurAux{static_cast<E*>(p.ws_ckS), nullptr, static_cast<E*>(p.ws_U), nullptr}, st);
     mark(3);
     launch_recur_lds<D, kBwd>(p, p.dO, p.dS_T, p.dS0, nullptr,
