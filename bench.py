@@ -118,9 +118,9 @@ def mfma_counters_for(kernel, workload_key):
 def grad_bytes_per_token_head(C, D, es=2):
     """Algorithmic bytes of the per-chunk gradient kernel per (token, head):
     reads q, k, log_alpha, v, dO, U~, dZ (7 D) and beta, the chunk's two
-    d x d bf16 states spread over its C tokens; writes dq, dk, dlog_alpha and
-    the two float32 dbeta shares."""
-    return 7 * D * es + es + 2 * D * D * es / C + 3 * D * es + 2 * 4
+    d x d bf16 states spread over its C tokens; writes dq, dk, dlog_alpha, dv
+    and the two float32 dbeta shares."""
+    return 7 * D * es + es + 2 * D * D * es / C + 4 * D * es + 2 * 4
 
 
 def cpu_baseline(inp, n_heads_sample):
