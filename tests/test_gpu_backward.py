@@ -196,7 +196,10 @@ def test_backward_headline_full(torch_dev):
                          ids=["varlen-d64", "equal-d128"])
 def test_training_pair_matches_recompute(torch_dev, lengths, H, d, varlen):
     """kda_chunk_fwd_train + kda_chunk_bwd_ctx give kda_chunk_fwd's o and S_T
-    and kda_chunk_bwd's gradients bit for bit (same kernels, same inputs)."""
+    and kda_chunk_bwd's gradients bit for bit (same kernels, same inputs).
+    kda_chunk_bwd re-evaluates the forward with the lean checkpointing forms
+    (no Q . Gamma, no M), the training forward with the full ones: equal
+    gradients also show that the lean forms keep U~ and the states as they are."""
     torch, dev = torch_dev
     import gated_delta_rule_30_amd as kda
     spec = ki.Spec("pair", "bf16", tuple(lengths), H, d, d, s0_std=0.02, varlen=varlen, seed=3)
